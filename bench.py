@@ -1,0 +1,186 @@
+#!/usr/bin/env python3
+"""Throughput of the batch-invariant logprob recompute on one MI355X.
+
+One step = the training-side recompute of every valid response token of a
+GRPO-style batch: 128 prompts x 8 responses on a Qwen3-1.7B-shaped dense
+decoder (28 layers, hidden 2048, 16 q / 8 kv heads of 128, MLP 6144, vocab
+151936, tied embeddings), random-init bf16 weights, synthetic token ids
+(prompt lengths U[80, 250], response lengths U[100, 400]).  Sequences are packed
+into varlen calls of at most 16384 tokens; each call is one
+bci_forward_logprobs (all kernels of the path: embedding, 28 x [add+RMSNorm,
+QKV GEMM, RoPE + KV write, attention, O GEMM, add+RMSNorm, gate_up GEMM with
+SiLU*up, down GEMM], final norm, lm_head + log-softmax + gather).
+
+Reported on one JSON line: scored tokens/s, the roofline of the dominant
+kernel (the gate_up GEMM, timed live with HIP events on its own stream), the
+acceptance statistics of a bounded rollout-vs-recompute comparison (must be
+exactly 0), and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_baseline(cfg, weights, seqs):
+    """The oracle, as it stands, on one sequence of the workload (fp64, NumPy BLAS)."""
+    import numpy as np
+    import synth
+    from oracle import model as om
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        cores = os.cpu_count()
+    s = min(seqs[:8], key=lambda q: q.length)
+    W = om.Weights({k: synth.bf16_bits(v) for k, v in weights.items()}, cache=False)
+    t0 = time.perf_counter()
+    om.sequence_logprobs(cfg, W, s.tokens, s.prompt_len)
+    dt = time.perf_counter() - t0
+    return {"value": round(s.n_scored / dt, 3), "unit": "scored tokens/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"1 sequence of the workload (L={s.length}, {s.n_scored} scored tokens), "
+                      f"fp64 NumPy forward, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--prompts", type=int, default=128)
+    ap.add_argument("--responses", type=int, default=8)
+    ap.add_argument("--max-tokens", type=int, default=16384)
+    ap.add_argument("--accept-seqs", type=int, default=64)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: every sequence is independent, so N GPUs would "
+              "each run their own share with no exchange; run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from bitwise_consistent_rl_amd import _abi as abi
+    from bitwise_consistent_rl_amd import engine
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cfg = synth.QWEN3_1P7B
+    log("generating weights and workload")
+    weights = synth.make_weights(cfg)
+    seqs = synth.rl_sequences(cfg, n_prompts=args.prompts, n_responses=args.responses)
+    scored = sum(s.n_scored for s in seqs)
+    processed = sum(s.length - 1 for s in seqs)
+    n_blocks = args.max_tokens // 64 + 64
+    model = engine.Model(cfg, weights, kv_dtype="bf16", max_tokens=args.max_tokens, max_seqs=64,
+                         max_scored=args.max_tokens, max_position=1024, seg_keys=2048)
+    cache = model.new_cache(n_blocks)
+    model.bind_cache(cache)
+    calls = engine.plan_recompute(seqs, range(len(seqs)), args.max_tokens, 64, args.max_tokens,
+                                  n_blocks)
+    lp_all = torch.empty(scored, dtype=torch.float32, device="cuda")
+    offs = np.cumsum([0] + [len(p.score_rows) for p, _ in calls])
+    stream = torch.cuda.current_stream()
+    log(f"{len(seqs)} sequences, {processed} processed / {scored} scored tokens, {len(calls)} calls")
+
+    def step():
+        for (plan, _), o in zip(calls, offs[:-1]):
+            abi.bci_set_batch(model.ctx, plan.tokens, plan.cu_q, plan.pos0, plan.block_table,
+                              plan.score_rows, plan.score_ids, stream)
+            abi.bci_forward_logprobs(model.ctx, lp_all[o:o + len(plan.score_rows)], stream)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"warmup step {i + 1}/{args.warmup} done")
+    first = lp_all.clone()
+    torch.cuda.synchronize()
+    abi.bci_profile_begin(model.ctx)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    gu_ms, gu_launches = abi.bci_profile_end(model.ctx)
+    log(f"timed {args.steps} steps: {dt:.3f} s")
+    assert torch.equal(first.view(torch.int32), lp_all.view(torch.int32)), "run-to-run bits differ"
+
+    # gate_up GEMM: 2 * M * (2 I) * H flops per launch, M = tokens of the call
+    per_step_gu = sum(2.0 * len(p.tokens) * 2 * cfg.intermediate * cfg.hidden * cfg.n_layers
+                      for p, _ in calls)
+    gu_flops = per_step_gu * args.steps
+    achieved = gu_flops / (gu_ms * 1e-3) / 1e12 if gu_ms > 0 else 0.0
+    ms_per_step = dt * 1e3 / args.steps
+
+    # whole-step algorithmic work: linear + attention + lm_head flops
+    lin = 2.0 * cfg.n_layers * cfg.hidden * (cfg.qkv_rows + cfg.hidden + 2 * cfg.intermediate
+                                             + cfg.intermediate)
+    attn = sum(2.0 * 2 * cfg.n_layers * cfg.n_q_heads * cfg.head_dim * (t + 1)
+               for s in seqs for t in range(s.length - 1))
+    head = 2.0 * cfg.hidden * cfg.vocab * scored
+    step_flops = lin * processed + attn + head
+
+    # acceptance on a bounded subset: rollout (continuous batching, decode) vs recompute
+    sub = seqs[: args.accept_seqs]
+    log(f"acceptance: rollout of {len(sub)} sequences vs recompute")
+    roll_cache = model.new_cache(len(sub) * 11 + 8)
+    roll = engine.rollout(model, sub, roll_cache, cap=min(64, len(sub)), prefill_chunk=None)
+    rec = engine.recompute(model, sub, cache)
+    acc = engine.acceptance(rec, roll)
+    lp_host = first.cpu().numpy()
+    # the timed step's rows for these sequences equal the standalone recompute
+    acc["bench_rows_equal"] = bool(np.concatenate(rec).tobytes() == lp_host[: sum(len(r) for r in rec)].tobytes())
+    del roll_cache
+
+    out = {
+        "metric": "invariant logprob-recompute tokens/sec @1 GPU, % roofline; diff/k3-KL must be 0",
+        "value": round(scored / (dt / args.steps), 1),
+        "unit": "scored tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "qwen3-1.7b-shaped logprob recompute, 128 prompts x 8 responses",
+                   "sequences": len(seqs), "processed_tokens": processed, "scored_tokens": scored,
+                   "max_tokens_per_call": args.max_tokens, "calls_per_step": len(calls),
+                   "kv_cache": "bf16", "mode": "invariant"},
+        "roofline": {"bound": "mfma", "kernel": "gate_up GEMM (SiLU*up epilogue)",
+                     "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "launches": gu_launches, "avg_launch_us": round(gu_ms * 1e3 / max(gu_launches, 1), 2)},
+        "step_roofline": {"algorithmic_tflop_per_step": round(step_flops / 1e12, 3),
+                          "achieved_tflops": round(step_flops / (dt / args.steps) / 1e12, 1),
+                          "frac_of_mfma_peak": round(step_flops / (dt / args.steps) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+        "acceptance": acc,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(cfg, weights, seqs)
+    model.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,294 @@
+// Causal GQA attention over the paged KV cache; one kernel for prefill,
+// chunked prefill, decode and the training recompute.
+//
+// The pages trace train/inference mismatch partly to prefill and decode
+// running different attention algorithms, and require one attention
+// operator fed by the same gathered, dequantised KV in every phase (page
+// "Finish RL Training Faster" digest, sections "零差异需要一个精确的比较对象"
+// and "让训练前向使用推理的数值").
+//
+// Per query row (a token x a query head of the kv head's group) the kernel
+// performs exactly this sequence, whatever tile or phase the row is in:
+//   for segment s = 0, 1, ... (S keys each, S a multiple of 64):
+//     (m, l, acc) = (-inf, 0, 0)
+//     for chunk c of the segment (64 keys at absolute positions 64c..64c+63):
+//       t_j = (q . k_j) * (log2(e)/sqrt(d))   [MFMA, fp32]; t_j = -inf if j > pos
+//       m' = max(m, max_j t_j); a = 2^(m - m'); p_j = 2^(t_j - m')
+//       l = l * a + sum_j p_j   [fixed tree];  acc = acc * a + P.V  [MFMA, P in bf16]
+//     merge (m, l, acc) into (M, L, ACC) with the same exp2 rule
+//   o = bf(ACC / L)
+// A chunk or segment that lies wholly after the row's position is an exact
+// no-op (a = 2^0 = 1, p = 0, and keys past the tile's last position are
+// zeroed on load, so no 0 * NaN from unwritten cache slots), so a row gives the
+// same bits whether its tile stops at its own position (decode) or runs on
+// (prefill).  MFMA outputs depend only on their own operand row and column,
+// so the row's slot in the tile does not matter either.
+//
+// MFMA layout (v_mfma_f32_16x16x32_bf16, lane l, g = l >> 4, c = l & 15):
+//   scores are computed transposed, S^T = K . Q^T, so lane l holds keys
+//   16kt + 4g + r of query row c; after exp2 these are exactly the values the
+//   P^T operand of O^T = V^T . P^T needs in lane l (keys 4g..4g+3 and
+//   16+4g..16+4g+3 of each 32-key step), so P never leaves registers.  V is
+//   stored transposed in LDS (V^T[d][key]) so the V^T operand is two 8-byte
+//   reads.  O^T lands with query row c in lane l again, so the softmax
+//   statistics never move between lanes.
+#include "common.h"
+#include "kernels.h"
+
+namespace bci {
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int ATHREADS = 256;
+constexpr int CHUNK = 64;
+constexpr int VT_STRIDE = CHUNK + 8;  // bf16 elements per V^T row (pad: conflict-free reads)
+
+template <int D>
+__device__ __forceinline__ int kswz(int key, int ch) {
+  if constexpr (D == 128)
+    return key * (D / 8) + (ch ^ (key & 15));
+  else
+    return key * (D / 8) + (ch ^ ((key >> 1) & 7));
+}
+
+template <int D, bool FP8>
+__device__ __forceinline__ void load_chunk(const AttnArgs& p, int blk, int g, int key_lim,
+                                           u32x4_t* Ks, bf16_t* Vt, int tid) {
+  const size_t base = ((size_t)blk * p.nkv + g) * CHUNK;  // first cache row of the chunk
+  if constexpr (!FP8) {
+    const bf16_t* kg = reinterpret_cast<const bf16_t*>(p.kv.k) + base * D;
+    const bf16_t* vg = reinterpret_cast<const bf16_t*>(p.kv.v) + base * D;
+    constexpr int CH = D / 8;  // 16-byte chunks per key row
+    // K: straight copy, swizzled
+#pragma unroll
+    for (int u = tid; u < CHUNK * CH; u += ATHREADS) {
+      const int key = u / CH, ch = u % CH;
+      u32x4_t v = *reinterpret_cast<const u32x4_t*>(kg + key * D + ch * 8);
+      if (key > key_lim) v = u32x4_t{0, 0, 0, 0};
+      Ks[kswz<D>(key, ch)] = v;
+    }
+    // V: two consecutive keys per unit, written transposed as 4-byte pairs
+#pragma unroll
+    for (int u = tid; u < (CHUNK / 2) * CH; u += ATHREADS) {
+      const int kp = u / CH, ch = u % CH;
+      const int k0 = 2 * kp;
+      u32x4_t a = *reinterpret_cast<const u32x4_t*>(vg + k0 * D + ch * 8);
+      u32x4_t b = *reinterpret_cast<const u32x4_t*>(vg + (k0 + 1) * D + ch * 8);
+      if (k0 > key_lim) a = u32x4_t{0, 0, 0, 0};
+      if (k0 + 1 > key_lim) b = u32x4_t{0, 0, 0, 0};
+      const bf16_t* pa = reinterpret_cast<const bf16_t*>(&a);
+      const bf16_t* pb = reinterpret_cast<const bf16_t*>(&b);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        *reinterpret_cast<uint32_t*>(Vt + (ch * 8 + i) * VT_STRIDE + k0) = pack_bf2(pa[i], pb[i]);
+    }
+  } else {
+    const uint8_t* kg = reinterpret_cast<const uint8_t*>(p.kv.k) + base * D;
+    const uint8_t* vg = reinterpret_cast<const uint8_t*>(p.kv.v) + base * D;
+    const float* ksg = p.kv.ks + base;
+    const float* vsg = p.kv.vs + base;
+    constexpr int CH16 = D / 16;  // 16-code chunks per key row
+#pragma unroll
+    for (int u = tid; u < CHUNK * CH16; u += ATHREADS) {
+      const int key = u / CH16, c16 = u % CH16;
+      const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(kg + key * D + c16 * 16);
+      const float sc = ksg[key];
+      const uint8_t* cb = reinterpret_cast<const uint8_t*>(&raw);
+      u32x4_t lo, hi;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lo[i] = pack_bf2(kv_decode(cb[2 * i], sc), kv_decode(cb[2 * i + 1], sc));
+        hi[i] = pack_bf2(kv_decode(cb[8 + 2 * i], sc), kv_decode(cb[8 + 2 * i + 1], sc));
+      }
+      if (key > key_lim) {
+        lo = u32x4_t{0, 0, 0, 0};
+        hi = u32x4_t{0, 0, 0, 0};
+      }
+      Ks[kswz<D>(key, 2 * c16)] = lo;
+      Ks[kswz<D>(key, 2 * c16 + 1)] = hi;
+    }
+#pragma unroll
+    for (int u = tid; u < (CHUNK / 2) * CH16; u += ATHREADS) {
+      const int kp = u / CH16, c16 = u % CH16;
+      const int k0 = 2 * kp;
+      const u32x4_t ra = *reinterpret_cast<const u32x4_t*>(vg + k0 * D + c16 * 16);
+      const u32x4_t rb = *reinterpret_cast<const u32x4_t*>(vg + (k0 + 1) * D + c16 * 16);
+      const float sa = vsg[k0], sb = vsg[k0 + 1];
+      const uint8_t* ca = reinterpret_cast<const uint8_t*>(&ra);
+      const uint8_t* cb = reinterpret_cast<const uint8_t*>(&rb);
+      const bool za = k0 > key_lim, zb = k0 + 1 > key_lim;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const bf16_t va = za ? (bf16_t)0 : kv_decode(ca[i], sa);
+        const bf16_t vb = zb ? (bf16_t)0 : kv_decode(cb[i], sb);
+        *reinterpret_cast<uint32_t*>(Vt + (c16 * 16 + i) * VT_STRIDE + k0) = pack_bf2(va, vb);
+      }
+    }
+  }
+}
+
+template <int D, bool FP8>
+__global__ __launch_bounds__(ATHREADS, 2) void attention_kernel(AttnArgs p) {
+  __shared__ __attribute__((aligned(16))) u32x4_t Ks[CHUNK * D / 8];
+  __shared__ __attribute__((aligned(16))) bf16_t Vt[D * VT_STRIDE];
+
+  const int tile = blockIdx.x, g = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lg = lane >> 4, lc = lane & 15;
+  const int seq = p.tiles[tile * 4 + 0];
+  const int tok_begin = p.tiles[tile * 4 + 1];
+  const int n_tok = p.tiles[tile * 4 + 2];
+  const int pos_begin = p.tiles[tile * 4 + 3];
+  const int group = p.nq / p.nkv;
+  const int kmax = pos_begin + n_tok - 1;  // last key position any row of the tile needs
+  const int* btab = p.block_table + (size_t)seq * p.max_blocks;
+  const size_t qstride = (size_t)p.nq * D;
+
+  // this lane's query row (B operand of S^T and column of O^T)
+  const int row = wave * 16 + lc;
+  const int tk = row / group;
+  const int hq = g * group + row % group;
+  const bool row_ok = tk < n_tok;
+  const int qpos = row_ok ? pos_begin + tk : -1;
+
+  bf16x8_t qf[D / 32];
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) {
+    u32x4_t v = u32x4_t{0, 0, 0, 0};
+    if (row_ok)
+      v = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const bf16_t*>(p.q) +
+                                            (size_t)(tok_begin + tk) * qstride + hq * D + ks * 32 +
+                                            8 * lg);
+    qf[ks] = __builtin_bit_cast(bf16x8_t, v);
+  }
+
+  float M = -INFINITY, L = 0.0f;
+  f32x4_t ACC[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) ACC[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int last_chunk = kmax / CHUNK;
+  const int seg_chunks = p.seg_keys / CHUNK;
+  for (int c0 = 0; c0 <= last_chunk; c0 += seg_chunks) {
+    const int c1 = min(c0 + seg_chunks - 1, last_chunk);
+    float m = -INFINITY, l = 0.0f;
+    f32x4_t acc[D / 16];
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    for (int c = c0; c <= c1; ++c) {
+      __syncthreads();  // previous chunk's LDS reads are done
+      load_chunk<D, FP8>(p, btab[c], g, kmax - c * CHUNK, Ks, Vt, tid);
+      __syncthreads();
+
+      // S^T = K . Q^T : 4 key blocks of 16, D/32 steps
+      f32x4_t sacc[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        sacc[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+          const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, Ks[kswz<D>(kt * 16 + lc, ks * 4 + lg)]);
+          sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sacc[kt], 0, 0, 0);
+        }
+      }
+      float t[4][4];
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = c * CHUNK + kt * 16 + 4 * lg + r;
+          const float v = sacc[kt][r] * p.scale_log2;
+          t[kt][r] = key <= qpos ? v : -INFINITY;
+          mloc = fmaxf(mloc, t[kt][r]);
+        }
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 16, WAVE));
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, WAVE));
+      const float mn = fmaxf(m, mloc);
+      const float mu = (mn == -INFINITY) ? 0.0f : mn;
+      const float alpha = fexp2(m - mu);
+      float rs = 0.0f;
+      float pr[4][4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pr[kt][r] = fexp2(t[kt][r] - mu);
+          rs = rs + pr[kt][r];
+        }
+      rs = rs + __shfl_xor(rs, 16, WAVE);
+      rs = rs + __shfl_xor(rs, 32, WAVE);
+      l = l * alpha + rs;
+      m = mn;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[dt][r] = acc[dt][r] * alpha;
+
+      // O^T += V^T . P^T over two 32-key steps
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        u32x4_t pw;
+        pw[0] = pack_bf2(f2bf(pr[2 * k2][0]), f2bf(pr[2 * k2][1]));
+        pw[1] = pack_bf2(f2bf(pr[2 * k2][2]), f2bf(pr[2 * k2][3]));
+        pw[2] = pack_bf2(f2bf(pr[2 * k2 + 1][0]), f2bf(pr[2 * k2 + 1][1]));
+        pw[3] = pack_bf2(f2bf(pr[2 * k2 + 1][2]), f2bf(pr[2 * k2 + 1][3]));
+        const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pw);
+        const int ko = k2 * 32 + 4 * lg;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+          const bf16_t* vr = Vt + (dt * 16 + lc) * VT_STRIDE;
+          const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vr + ko);
+          const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vr + ko + 16);
+          const u32x4_t vw = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vw), pf,
+                                                            acc[dt], 0, 0, 0);
+        }
+      }
+    }
+    // merge the segment into the running state (ascending segment order)
+    const float Mn = fmaxf(M, m);
+    const float Mu = (Mn == -INFINITY) ? 0.0f : Mn;
+    const float a = fexp2(M - Mu), b = fexp2(m - Mu);
+    L = L * a + l * b;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ACC[dt][r] = ACC[dt][r] * a + acc[dt][r] * b;
+    M = Mn;
+  }
+
+  if (row_ok) {
+    bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + (size_t)(tok_begin + tk) * qstride + hq * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      u32x2_t w;
+      w[0] = pack_bf2(f2bf(ACC[dt][0] / L), f2bf(ACC[dt][1] / L));
+      w[1] = pack_bf2(f2bf(ACC[dt][2] / L), f2bf(ACC[dt][3] / L));
+      *reinterpret_cast<u32x2_t*>(orow + dt * 16 + 4 * lg) = w;
+    }
+  }
+}
+
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
+  if (a.n_tiles == 0) return hipSuccess;
+  const dim3 grid(a.n_tiles, a.nkv);
+  if (a.d == 128) {
+    if (a.fp8)
+      hipLaunchKernelGGL((attention_kernel<128, true>), grid, dim3(ATHREADS), 0, s, a);
+    else
+      hipLaunchKernelGGL((attention_kernel<128, false>), grid, dim3(ATHREADS), 0, s, a);
+  } else if (a.d == 64) {
+    if (a.fp8)
+      hipLaunchKernelGGL((attention_kernel<64, true>), grid, dim3(ATHREADS), 0, s, a);
+    else
+      hipLaunchKernelGGL((attention_kernel<64, false>), grid, dim3(ATHREADS), 0, s, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace bci

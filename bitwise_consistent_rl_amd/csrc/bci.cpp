@@ -1,0 +1,566 @@
+// C-ABI layer of libbci: context, validation, batch metadata upload, the
+// forward orchestration and the per-operator entry points.
+//
+// Everything here runs on the host.  Every argument is checked before any
+// launch, so a bad request enqueues nothing; device work is only ever
+// launched through the kernels of the *.hip translation units.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/bci.h"
+#include "kernels.h"
+
+using namespace bci;
+
+namespace {
+
+constexpr int KV_BLOCK = 64;
+constexpr int MAX_PROFILE = 8192;
+
+struct DevBuf {
+  void* p = nullptr;
+  size_t bytes = 0;
+};
+
+}  // namespace
+
+struct bci_ctx {
+  bci_model_config cfg{};
+  int device = 0;
+  std::string err;
+  // derived shape
+  int qkv_w = 0, qd = 0, group = 0, max_blocks = 0, max_tiles = 0, n_chunks = 0, tpt = 0;
+  // workspace (one allocation, carved)
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  uint16_t *bufR = nullptr, *bufH = nullptr, *bufQKV = nullptr, *bufQ = nullptr,
+           *bufO = nullptr, *bufX = nullptr, *bufACT = nullptr;
+  float *part_m = nullptr, *part_s = nullptr, *zid = nullptr;
+  float *rope_cos = nullptr, *rope_sin = nullptr;
+  int32_t* meta = nullptr;  // device metadata region
+  size_t meta_words = 0;
+  // metadata offsets (int32 words)
+  size_t o_tok = 0, o_pos = 0, o_slot = 0, o_tiles = 0, o_btab = 0, o_srow = 0, o_sid = 0;
+  // pinned staging for uploads (2 slots, each guarded by an event)
+  int32_t* stage[2] = {nullptr, nullptr};
+  hipEvent_t stage_ev[2] = {nullptr, nullptr};
+  bool stage_used[2] = {false, false};
+  int stage_next = 0;
+  // bindings
+  std::vector<const void*> w;
+  uint64_t weight_version = 0;
+  bool weights_bound = false;
+  void *kc = nullptr, *vc = nullptr;
+  float *kscale = nullptr, *vscale = nullptr;
+  int n_blocks = 0;
+  bool cache_bound = false;
+  // current batch (host copy of what was uploaded)
+  bool batch_valid = false;
+  int n_seqs = 0, n_tokens = 0, n_scored = 0, n_tiles = 0;
+  std::vector<int32_t> h_cu, h_pos0, h_btab;  // h_btab with stride max_blocks
+  // profiling of the gate_up GEMM launches (HIP events on the launch stream)
+  bool prof_on = false;
+  int prof_n = 0;
+  std::vector<hipEvent_t> prof_ev;
+};
+
+static bci_status fail(bci_ctx* c, bci_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  if (c) c->err = buf;
+  return st;
+}
+
+static bci_status hipfail(bci_ctx* c, hipError_t e, const char* what) {
+  return fail(c, BCI_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIP_TRY(c, expr)                                         \
+  do {                                                           \
+    hipError_t e_ = (expr);                                      \
+    if (e_ != hipSuccess) return hipfail((c), e_, #expr);        \
+  } while (0)
+
+static inline hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+static KvLayer kv_layer(const bci_ctx* c, int layer) {
+  const auto& g = c->cfg;
+  const size_t rows = (size_t)c->n_blocks * g.n_kv_heads * KV_BLOCK;  // cache rows per layer
+  const size_t esz = (g.kv_dtype == BCI_KV_FP8_E4M3) ? 1 : 2;
+  KvLayer kv;
+  kv.k = (char*)c->kc + (size_t)layer * rows * g.head_dim * esz;
+  kv.v = (char*)c->vc + (size_t)layer * rows * g.head_dim * esz;
+  kv.ks = c->kscale ? c->kscale + (size_t)layer * rows : nullptr;
+  kv.vs = c->vscale ? c->vscale + (size_t)layer * rows : nullptr;
+  return kv;
+}
+
+extern "C" {
+
+bci_status bci_create(const bci_model_config* cfg_in, int32_t device, bci_ctx** out) {
+  if (!out) return BCI_E_INVALID;
+  *out = nullptr;
+  if (!cfg_in) return BCI_E_INVALID;
+  bci_model_config g = *cfg_in;
+  if (g.attn_segment_keys == 0) g.attn_segment_keys = 2048;
+  if (g.n_layers < 1 || g.hidden < 128 || g.hidden % 128 || g.hidden > 8192 || g.n_q_heads < 1 ||
+      g.n_kv_heads < 1 || g.n_q_heads % g.n_kv_heads || (g.head_dim != 64 && g.head_dim != 128) ||
+      (g.n_q_heads * g.head_dim) % 128 || g.intermediate < 64 || g.intermediate % 128 ||
+      g.vocab < 1 || !(g.rms_eps >= 0.0f) || !(g.rope_theta > 0.0f))
+    return BCI_E_INVALID;
+  if (64 % (g.n_q_heads / g.n_kv_heads)) return BCI_E_INVALID;  // GQA group must divide 64
+  if (g.kv_dtype != BCI_KV_BF16 && g.kv_dtype != BCI_KV_FP8_E4M3) return BCI_E_INVALID;
+  if (g.kv_block_tokens != KV_BLOCK) return BCI_E_INVALID;
+  if (g.attn_segment_keys < KV_BLOCK || g.attn_segment_keys % KV_BLOCK) return BCI_E_INVALID;
+  if (g.max_tokens_per_call < 1 || g.max_seqs_per_call < 1 || g.max_scored_per_call < 0 ||
+      g.max_position < 1)
+    return BCI_E_INVALID;
+  if (g.mode == BCI_MODE_FAST) return BCI_E_UNSUPPORTED;
+  if (g.mode != BCI_MODE_INVARIANT) return BCI_E_INVALID;
+  if (hipSetDevice(device) != hipSuccess) return BCI_E_HIP;
+
+  bci_ctx* c = new bci_ctx();
+  c->cfg = g;
+  c->device = device;
+  c->qkv_w = (g.n_q_heads + 2 * g.n_kv_heads) * g.head_dim;
+  c->qd = g.n_q_heads * g.head_dim;
+  c->group = g.n_q_heads / g.n_kv_heads;
+  c->tpt = ATTN_ROWS / c->group;
+  c->max_blocks = (g.max_position + KV_BLOCK - 1) / KV_BLOCK;
+  c->max_tiles = g.max_tokens_per_call / c->tpt + g.max_seqs_per_call;
+  c->n_chunks = (g.vocab + LM_CHUNK - 1) / LM_CHUNK;
+  c->w.assign(2 + 6 * g.n_layers, nullptr);
+
+  const size_t T = g.max_tokens_per_call, H = g.hidden, R = std::max(1, g.max_scored_per_call);
+  // metadata words
+  c->o_tok = 0;
+  c->o_pos = c->o_tok + T;
+  c->o_slot = c->o_pos + T;
+  c->o_tiles = c->o_slot + T;
+  c->o_btab = c->o_tiles + 4 * (size_t)c->max_tiles;
+  c->o_srow = c->o_btab + (size_t)g.max_seqs_per_call * c->max_blocks;
+  c->o_sid = c->o_srow + R;
+  c->meta_words = c->o_sid + R;
+
+  struct Part {
+    void** dst;
+    size_t bytes;
+  };
+  std::vector<Part> parts = {
+      {(void**)&c->bufR, T * H * 2},
+      {(void**)&c->bufH, T * H * 2},
+      {(void**)&c->bufQKV, T * c->qkv_w * 2},
+      {(void**)&c->bufQ, T * c->qd * 2},
+      {(void**)&c->bufO, T * c->qd * 2},
+      {(void**)&c->bufX, T * H * 2},
+      {(void**)&c->bufACT, T * (size_t)g.intermediate * 2},
+      {(void**)&c->part_m, (size_t)c->n_chunks * R * 4},
+      {(void**)&c->part_s, (size_t)c->n_chunks * R * 4},
+      {(void**)&c->zid, R * 4},
+      {(void**)&c->rope_cos, (size_t)g.max_position * (g.head_dim / 2) * 4},
+      {(void**)&c->rope_sin, (size_t)g.max_position * (g.head_dim / 2) * 4},
+      {(void**)&c->meta, c->meta_words * 4},
+  };
+  size_t total = 0;
+  for (auto& p : parts) total += align_up(p.bytes, 256);
+  if (hipMalloc(&c->ws, total) != hipSuccess) {
+    delete c;
+    return BCI_E_WORKSPACE;
+  }
+  c->ws_bytes = total;
+  size_t off = 0;
+  for (auto& p : parts) {
+    *p.dst = (char*)c->ws + off;
+    off += align_up(p.bytes, 256);
+  }
+  for (int i = 0; i < 2; ++i) {
+    if (hipHostMalloc((void**)&c->stage[i], c->meta_words * 4, hipHostMallocDefault) != hipSuccess ||
+        hipEventCreateWithFlags(&c->stage_ev[i], hipEventDisableTiming) != hipSuccess) {
+      bci_destroy(c);
+      return BCI_E_WORKSPACE;
+    }
+  }
+  // RoPE table: cos/sin(t * theta^(-2i/d)) in double, rounded to fp32.
+  {
+    const int half = g.head_dim / 2;
+    std::vector<float> cs((size_t)g.max_position * half), sn((size_t)g.max_position * half);
+    for (int i = 0; i < half; ++i) {
+      const double inv = std::pow((double)g.rope_theta, -2.0 * i / g.head_dim);
+      for (int t = 0; t < g.max_position; ++t) {
+        const double a = (double)t * inv;
+        cs[(size_t)t * half + i] = (float)std::cos(a);
+        sn[(size_t)t * half + i] = (float)std::sin(a);
+      }
+    }
+    if (hipMemcpy(c->rope_cos, cs.data(), cs.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(c->rope_sin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice) != hipSuccess) {
+      bci_destroy(c);
+      return BCI_E_HIP;
+    }
+  }
+  c->prof_ev.assign(2 * MAX_PROFILE, nullptr);
+  *out = c;
+  return BCI_OK;
+}
+
+void bci_destroy(bci_ctx* c) {
+  if (!c) return;
+  hipSetDevice(c->device);
+  for (auto& e : c->prof_ev)
+    if (e) hipEventDestroy(e);
+  for (int i = 0; i < 2; ++i) {
+    if (c->stage_ev[i]) {
+      hipEventSynchronize(c->stage_ev[i]);
+      hipEventDestroy(c->stage_ev[i]);
+    }
+    if (c->stage[i]) hipHostFree(c->stage[i]);
+  }
+  if (c->ws) hipFree(c->ws);
+  delete c;
+}
+
+const char* bci_last_error(const bci_ctx* c) { return c ? c->err.c_str() : "null context"; }
+
+uint64_t bci_workspace_bytes(const bci_ctx* c) { return c ? c->ws_bytes : 0; }
+
+bci_status bci_bind_weights(bci_ctx* c, const void* const* ptrs, int32_t n, uint64_t version) {
+  if (!c) return BCI_E_INVALID;
+  if (!ptrs || n != (int32_t)c->w.size())
+    return fail(c, BCI_E_INVALID, "bind_weights: expected %d pointers, got %d", (int)c->w.size(), n);
+  for (int i = 0; i < n; ++i)
+    if (!ptrs[i]) return fail(c, BCI_E_INVALID, "bind_weights: pointer %d is null", i);
+  for (int i = 0; i < n; ++i) c->w[i] = ptrs[i];
+  c->weight_version = version;
+  c->weights_bound = true;
+  return BCI_OK;
+}
+
+uint64_t bci_weight_version(const bci_ctx* c) { return c ? c->weight_version : 0; }
+
+bci_status bci_bind_kv_cache(bci_ctx* c, void* k, void* v, float* ks, float* vs, int32_t n_blocks) {
+  if (!c) return BCI_E_INVALID;
+  const bool fp8 = c->cfg.kv_dtype == BCI_KV_FP8_E4M3;
+  if (!k || !v || n_blocks < 1) return fail(c, BCI_E_INVALID, "bind_kv_cache: null buffer or n_blocks < 1");
+  if (fp8 && (!ks || !vs)) return fail(c, BCI_E_INVALID, "bind_kv_cache: FP8 cache needs scales");
+  if (!fp8 && (ks || vs)) return fail(c, BCI_E_INVALID, "bind_kv_cache: bf16 cache takes no scales");
+  c->kc = k;
+  c->vc = v;
+  c->kscale = ks;
+  c->vscale = vs;
+  c->n_blocks = n_blocks;
+  c->cache_bound = true;
+  c->batch_valid = false;  // block ids were validated against the old cache
+  return BCI_OK;
+}
+
+bci_status bci_set_batch(bci_ctx* c, const bci_batch* b, void* stream) {
+  if (!c) return BCI_E_INVALID;
+  c->batch_valid = false;
+  const auto& g = c->cfg;
+  if (!b) return fail(c, BCI_E_INVALID, "set_batch: null batch");
+  if (!c->cache_bound) return fail(c, BCI_E_STATE, "set_batch: bind a KV cache first");
+  if (b->n_seqs < 1 || b->n_seqs > g.max_seqs_per_call)
+    return fail(c, BCI_E_WORKSPACE, "set_batch: n_seqs %d outside [1, %d]", b->n_seqs, g.max_seqs_per_call);
+  if (b->n_tokens < 1 || b->n_tokens > g.max_tokens_per_call)
+    return fail(c, BCI_E_WORKSPACE, "set_batch: n_tokens %d outside [1, %d]", b->n_tokens, g.max_tokens_per_call);
+  if (b->n_scored < 0 || b->n_scored > g.max_scored_per_call)
+    return fail(c, BCI_E_WORKSPACE, "set_batch: n_scored %d outside [0, %d]", b->n_scored, g.max_scored_per_call);
+  if (b->max_blocks_per_seq < 1) return fail(c, BCI_E_INVALID, "set_batch: max_blocks_per_seq < 1");
+  if (!b->tokens || !b->cu_q || !b->pos0 || !b->block_table || (b->n_scored && (!b->score_rows || !b->score_ids)))
+    return fail(c, BCI_E_INVALID, "set_batch: null array");
+  if (b->cu_q[0] != 0 || b->cu_q[b->n_seqs] != b->n_tokens)
+    return fail(c, BCI_E_INVALID, "set_batch: cu_q must start at 0 and end at n_tokens");
+  for (int i = 0; i < b->n_seqs; ++i) {
+    const int ql = b->cu_q[i + 1] - b->cu_q[i];
+    if (ql < 1) return fail(c, BCI_E_INVALID, "set_batch: sequence %d has q_len %d", i, ql);
+    const int p0 = b->pos0[i];
+    if (p0 < 0 || (int64_t)p0 + ql > g.max_position)
+      return fail(c, BCI_E_INVALID, "set_batch: sequence %d positions [%d, %d) exceed max_position %d", i, p0,
+                  p0 + ql, g.max_position);
+    const int need = (p0 + ql + KV_BLOCK - 1) / KV_BLOCK;
+    if (need > b->max_blocks_per_seq)
+      return fail(c, BCI_E_INVALID, "set_batch: sequence %d needs %d blocks, table has %d", i, need,
+                  b->max_blocks_per_seq);
+    for (int j = 0; j < need; ++j) {
+      const int blk = b->block_table[(size_t)i * b->max_blocks_per_seq + j];
+      if (blk < 0 || blk >= c->n_blocks)
+        return fail(c, BCI_E_INVALID, "set_batch: sequence %d block %d id %d outside [0, %d)", i, j, blk,
+                    c->n_blocks);
+    }
+  }
+  for (int t = 0; t < b->n_tokens; ++t)
+    if (b->tokens[t] < 0 || b->tokens[t] >= g.vocab)
+      return fail(c, BCI_E_INVALID, "set_batch: token %d id %d outside [0, %d)", t, b->tokens[t], g.vocab);
+  for (int r = 0; r < b->n_scored; ++r) {
+    if (b->score_rows[r] < 0 || b->score_rows[r] >= b->n_tokens)
+      return fail(c, BCI_E_INVALID, "set_batch: score row %d = %d outside [0, %d)", r, b->score_rows[r],
+                  b->n_tokens);
+    if (b->score_ids[r] < 0 || b->score_ids[r] >= g.vocab)
+      return fail(c, BCI_E_INVALID, "set_batch: score id %d = %d outside [0, %d)", r, b->score_ids[r], g.vocab);
+  }
+  // count tiles
+  int n_tiles = 0;
+  for (int i = 0; i < b->n_seqs; ++i) n_tiles += (b->cu_q[i + 1] - b->cu_q[i] + c->tpt - 1) / c->tpt;
+  if (n_tiles > c->max_tiles) return fail(c, BCI_E_WORKSPACE, "set_batch: %d attention tiles > %d", n_tiles, c->max_tiles);
+
+  // wait until the staging slot's previous upload has been consumed
+  const int sl = c->stage_next;
+  c->stage_next ^= 1;
+  if (c->stage_used[sl]) HIP_TRY(c, hipEventSynchronize(c->stage_ev[sl]));
+  int32_t* h = c->stage[sl];
+  std::memcpy(h + c->o_tok, b->tokens, sizeof(int32_t) * b->n_tokens);
+  c->h_cu.assign(b->cu_q, b->cu_q + b->n_seqs + 1);
+  c->h_pos0.assign(b->pos0, b->pos0 + b->n_seqs);
+  c->h_btab.assign((size_t)b->n_seqs * c->max_blocks, 0);
+  for (int i = 0; i < b->n_seqs; ++i) {
+    const int need = (b->pos0[i] + b->cu_q[i + 1] - b->cu_q[i] + KV_BLOCK - 1) / KV_BLOCK;
+    for (int j = 0; j < need; ++j)
+      c->h_btab[(size_t)i * c->max_blocks + j] = b->block_table[(size_t)i * b->max_blocks_per_seq + j];
+  }
+  std::memcpy(h + c->o_btab, c->h_btab.data(), c->h_btab.size() * sizeof(int32_t));
+  int tix = 0;
+  for (int i = 0; i < b->n_seqs; ++i) {
+    const int q0 = b->cu_q[i], ql = b->cu_q[i + 1] - q0, p0 = b->pos0[i];
+    for (int t = 0; t < ql; ++t) {
+      const int p = p0 + t;
+      h[c->o_pos + q0 + t] = p;
+      h[c->o_slot + q0 + t] = c->h_btab[(size_t)i * c->max_blocks + p / KV_BLOCK] * KV_BLOCK + p % KV_BLOCK;
+    }
+    for (int t0 = 0; t0 < ql; t0 += c->tpt) {
+      int32_t* tl = h + c->o_tiles + 4 * (size_t)tix++;
+      tl[0] = i;
+      tl[1] = q0 + t0;
+      tl[2] = std::min(c->tpt, ql - t0);
+      tl[3] = p0 + t0;
+    }
+  }
+  if (b->n_scored) {
+    std::memcpy(h + c->o_srow, b->score_rows, sizeof(int32_t) * b->n_scored);
+    std::memcpy(h + c->o_sid, b->score_ids, sizeof(int32_t) * b->n_scored);
+  }
+  HIP_TRY(c, hipSetDevice(c->device));
+  HIP_TRY(c, hipMemcpyAsync(c->meta, h, c->meta_words * 4, hipMemcpyHostToDevice, S(stream)));
+  HIP_TRY(c, hipEventRecord(c->stage_ev[sl], S(stream)));
+  c->stage_used[sl] = true;
+  c->n_seqs = b->n_seqs;
+  c->n_tokens = b->n_tokens;
+  c->n_scored = b->n_scored;
+  c->n_tiles = n_tiles;
+  c->batch_valid = true;
+  return BCI_OK;
+}
+
+// ---------------------------------------------------------------- ops
+
+static bci_status need_batch(bci_ctx* c, const char* who) {
+  if (!c->batch_valid) return fail(c, BCI_E_STATE, "%s: no current batch (call bci_set_batch)", who);
+  return BCI_OK;
+}
+
+static bci_status op_rope(bci_ctx* c, const void* qkv, void* q_out, int layer, hipStream_t s) {
+  const auto& g = c->cfg;
+  HIP_TRY(c, launch_rope_kv_write(qkv, q_out, c->meta + c->o_pos, c->meta + c->o_slot, c->rope_cos,
+                                  c->rope_sin, kv_layer(c, layer), c->n_tokens, g.n_q_heads,
+                                  g.n_kv_heads, g.head_dim, g.kv_dtype == BCI_KV_FP8_E4M3, s));
+  return BCI_OK;
+}
+
+static bci_status op_attn(bci_ctx* c, const void* q, void* o, int layer, hipStream_t s) {
+  const auto& g = c->cfg;
+  AttnArgs a{};
+  a.q = q;
+  a.o = o;
+  a.kv = kv_layer(c, layer);
+  a.tiles = c->meta + c->o_tiles;
+  a.block_table = c->meta + c->o_btab;
+  a.n_tiles = c->n_tiles;
+  a.max_blocks = c->max_blocks;
+  a.nq = g.n_q_heads;
+  a.nkv = g.n_kv_heads;
+  a.d = g.head_dim;
+  a.seg_keys = g.attn_segment_keys;
+  a.fp8 = g.kv_dtype == BCI_KV_FP8_E4M3;
+  a.scale_log2 = (float)(1.0 / std::sqrt((double)g.head_dim) * 1.4426950408889634);
+  HIP_TRY(c, launch_attention(a, s));
+  return BCI_OK;
+}
+
+static bci_status gemm_checked(bci_ctx* c, const void* A, const int32_t* rows, const void* W, void* C,
+                               int M, int N, int K, int epi, hipStream_t s) {
+  HIP_TRY(c, launch_gemm(A, rows, W, C, M, N, K, epi, s));
+  return BCI_OK;
+}
+
+bci_status bci_op_embed(bci_ctx* c, const void* E, void* r, void* stream) {
+  if (!c) return BCI_E_INVALID;
+  if (bci_status st = need_batch(c, "op_embed")) return st;
+  if (!E || !r) return fail(c, BCI_E_INVALID, "op_embed: null pointer");
+  HIP_TRY(c, launch_embed(c->meta + c->o_tok, E, r, c->n_tokens, c->cfg.hidden, S(stream)));
+  return BCI_OK;
+}
+
+bci_status bci_op_add_rmsnorm(bci_ctx* c, const void* a, void* r, void* h, const void* g, int32_t rows,
+                              int32_t cols, float eps, void* stream) {
+  if (!c) return BCI_E_INVALID;
+  if (!r || !h || !g || rows < 0) return fail(c, BCI_E_INVALID, "op_add_rmsnorm: null pointer or rows < 0");
+  if (cols < 8 || cols % 8 || cols > 8192) return fail(c, BCI_E_INVALID, "op_add_rmsnorm: cols %d", cols);
+  HIP_TRY(c, launch_add_rmsnorm(a, r, r, h, g, nullptr, nullptr, rows, cols, eps, S(stream)));
+  return BCI_OK;
+}
+
+bci_status bci_op_gemm_bf16(bci_ctx* c, const void* A, const void* W, void* C, int32_t M, int32_t N,
+                            int32_t K, int32_t epi, void* stream) {
+  if (!c) return BCI_E_INVALID;
+  if (!A || !W || !C || M < 0 || N < 1 || K < 1) return fail(c, BCI_E_INVALID, "op_gemm: bad pointer or shape");
+  if (K % GEMM_BK) return fail(c, BCI_E_INVALID, "op_gemm: K %d not a multiple of %d", K, GEMM_BK);
+  if (epi == BCI_EPI_SILU_MUL) {
+    if (N % 128) return fail(c, BCI_E_INVALID, "op_gemm: SILU_MUL needs N = 2*I with I %% 64 == 0 (N=%d)", N);
+  } else if (epi == BCI_EPI_BF16 || epi == BCI_EPI_F32) {
+    if (N % GEMM_BN) return fail(c, BCI_E_INVALID, "op_gemm: N %d not a multiple of %d", N, GEMM_BN);
+  } else {
+    return fail(c, BCI_E_INVALID, "op_gemm: unknown epilogue %d", epi);
+  }
+  return gemm_checked(c, A, nullptr, W, C, M, N, K, epi, S(stream));
+}
+
+bci_status bci_op_rope_kv_write(bci_ctx* c, const void* qkv, void* q_out, int32_t layer, void* stream) {
+  if (!c) return BCI_E_INVALID;
+  if (bci_status st = need_batch(c, "op_rope_kv_write")) return st;
+  if (!qkv || !q_out || layer < 0 || layer >= c->cfg.n_layers)
+    return fail(c, BCI_E_INVALID, "op_rope_kv_write: null pointer or layer %d", layer);
+  return op_rope(c, qkv, q_out, layer, S(stream));
+}
+
+bci_status bci_op_kv_gather_dequant(bci_ctx* c, int32_t seq, int32_t n_pos, int32_t layer, void* k_out,
+                                    void* v_out, void* stream) {
+  if (!c) return BCI_E_INVALID;
+  if (bci_status st = need_batch(c, "op_kv_gather_dequant")) return st;
+  if (seq < 0 || seq >= c->n_seqs || layer < 0 || layer >= c->cfg.n_layers || !k_out || !v_out)
+    return fail(c, BCI_E_INVALID, "op_kv_gather_dequant: bad seq/layer/pointer");
+  const int hi = c->h_pos0[seq] + c->h_cu[seq + 1] - c->h_cu[seq];  // positions known to the batch
+  if (n_pos < 0 || n_pos > hi)
+    return fail(c, BCI_E_INVALID, "op_kv_gather_dequant: n_pos %d outside [0, %d]", n_pos, hi);
+  const auto& g = c->cfg;
+  HIP_TRY(c, launch_kv_gather(kv_layer(c, layer), c->meta + c->o_btab + (size_t)seq * c->max_blocks, n_pos,
+                              g.n_kv_heads, g.head_dim, g.kv_dtype == BCI_KV_FP8_E4M3, k_out, v_out,
+                              S(stream)));
+  return BCI_OK;
+}
+
+bci_status bci_op_attention(bci_ctx* c, const void* q, int32_t layer, void* o, void* stream) {
+  if (!c) return BCI_E_INVALID;
+  if (bci_status st = need_batch(c, "op_attention")) return st;
+  if (!q || !o || layer < 0 || layer >= c->cfg.n_layers)
+    return fail(c, BCI_E_INVALID, "op_attention: null pointer or layer %d", layer);
+  return op_attn(c, q, o, layer, S(stream));
+}
+
+bci_status bci_op_gather_scored(bci_ctx* c, const void* src, int32_t cols, void* out, void* stream) {
+  if (!c) return BCI_E_INVALID;
+  if (bci_status st = need_batch(c, "op_gather_scored")) return st;
+  if (!src || !out || cols < 8 || cols % 8) return fail(c, BCI_E_INVALID, "op_gather_scored: bad args");
+  HIP_TRY(c, launch_gather_rows(src, c->meta + c->o_srow, out, c->n_scored, cols, S(stream)));
+  return BCI_OK;
+}
+
+bci_status bci_op_lmhead_logprob(bci_ctx* c, const void* hf, const void* E, const int32_t* ids, int32_t M,
+                                 int32_t H, int32_t V, float* lp, void* stream) {
+  if (!c) return BCI_E_INVALID;
+  if (!hf || !E || !ids || !lp || M < 0 || V < 1 || H < 64 || H % GEMM_BK)
+    return fail(c, BCI_E_INVALID, "op_lmhead_logprob: bad pointer or shape");
+  if (M > c->cfg.max_scored_per_call)
+    return fail(c, BCI_E_WORKSPACE, "op_lmhead_logprob: M %d > max_scored_per_call %d", M,
+                c->cfg.max_scored_per_call);
+  if ((V + LM_CHUNK - 1) / LM_CHUNK > c->n_chunks)
+    return fail(c, BCI_E_WORKSPACE, "op_lmhead_logprob: vocab %d larger than the context's %d", V, c->cfg.vocab);
+  HIP_TRY(c, launch_lmhead_partials(hf, nullptr, E, ids, M, V, H, c->part_m, c->part_s, c->zid, S(stream)));
+  HIP_TRY(c, launch_lmhead_combine(c->part_m, c->part_s, c->zid, ids, M, V, lp, S(stream)));
+  return BCI_OK;
+}
+
+// ------------------------------------------------------------ forward
+
+bci_status bci_forward_logprobs(bci_ctx* c, float* lp, void* stream) {
+  if (!c) return BCI_E_INVALID;
+  if (!c->weights_bound) return fail(c, BCI_E_STATE, "forward: bind weights first");
+  if (bci_status st = need_batch(c, "forward")) return st;
+  if (c->n_scored && !lp) return fail(c, BCI_E_INVALID, "forward: null logprob output");
+  const auto& g = c->cfg;
+  const hipStream_t s = S(stream);
+  HIP_TRY(c, hipSetDevice(c->device));
+  const int T = c->n_tokens, H = g.hidden;
+  const void* E = c->w[0];
+  // layer 0 norm: residual = E[token] (exact copy), no add
+  HIP_TRY(c, launch_add_rmsnorm(nullptr, nullptr, c->bufR, c->bufH, c->w[1], c->meta + c->o_tok, E, T, H,
+                                g.rms_eps, s));
+  for (int l = 0; l < g.n_layers; ++l) {
+    const void* const* lw = &c->w[1 + 6 * l];  // attn_norm, wqkv, wo, mlp_norm, wgu, wd
+    if (l > 0)
+      HIP_TRY(c, launch_add_rmsnorm(c->bufX, c->bufR, c->bufR, c->bufH, lw[0], nullptr, nullptr, T, H,
+                                    g.rms_eps, s));
+    if (bci_status st = gemm_checked(c, c->bufH, nullptr, lw[1], c->bufQKV, T, c->qkv_w, H, EPI_BF16, s)) return st;
+    if (bci_status st = op_rope(c, c->bufQKV, c->bufQ, l, s)) return st;
+    if (bci_status st = op_attn(c, c->bufQ, c->bufO, l, s)) return st;
+    if (bci_status st = gemm_checked(c, c->bufO, nullptr, lw[2], c->bufX, T, H, c->qd, EPI_BF16, s)) return st;
+    HIP_TRY(c, launch_add_rmsnorm(c->bufX, c->bufR, c->bufR, c->bufH, lw[3], nullptr, nullptr, T, H,
+                                  g.rms_eps, s));
+    const bool prof = c->prof_on && c->prof_n < MAX_PROFILE;
+    if (prof) HIP_TRY(c, hipEventRecord(c->prof_ev[2 * c->prof_n], s));
+    if (bci_status st = gemm_checked(c, c->bufH, nullptr, lw[4], c->bufACT, T, 2 * g.intermediate, H,
+                                     EPI_SILU, s))
+      return st;
+    if (prof) HIP_TRY(c, hipEventRecord(c->prof_ev[2 * c->prof_n++ + 1], s));
+    if (bci_status st = gemm_checked(c, c->bufACT, nullptr, lw[5], c->bufX, T, H, g.intermediate, EPI_BF16, s))
+      return st;
+  }
+  HIP_TRY(c, launch_add_rmsnorm(c->bufX, c->bufR, c->bufR, c->bufH, c->w[1 + 6 * g.n_layers], nullptr, nullptr,
+                                T, H, g.rms_eps, s));
+  if (c->n_scored) {
+    HIP_TRY(c, launch_lmhead_partials(c->bufH, c->meta + c->o_srow, E, c->meta + c->o_sid, c->n_scored, g.vocab,
+                                      H, c->part_m, c->part_s, c->zid, s));
+    HIP_TRY(c, launch_lmhead_combine(c->part_m, c->part_s, c->zid, c->meta + c->o_sid, c->n_scored, g.vocab, lp,
+                                     s));
+  }
+  return BCI_OK;
+}
+
+// ------------------------------------------------------------ profiling
+
+bci_status bci_profile_begin(bci_ctx* c) {
+  if (!c) return BCI_E_INVALID;
+  HIP_TRY(c, hipSetDevice(c->device));
+  for (auto& e : c->prof_ev)
+    if (!e) HIP_TRY(c, hipEventCreate(&e));
+  c->prof_on = true;
+  c->prof_n = 0;
+  return BCI_OK;
+}
+
+bci_status bci_profile_end(bci_ctx* c, double* total_ms, int32_t* launches) {
+  if (!c || !total_ms || !launches) return BCI_E_INVALID;
+  c->prof_on = false;
+  double tot = 0.0;
+  for (int i = 0; i < c->prof_n; ++i) {
+    HIP_TRY(c, hipEventSynchronize(c->prof_ev[2 * i + 1]));
+    float ms = 0.0f;
+    HIP_TRY(c, hipEventElapsedTime(&ms, c->prof_ev[2 * i], c->prof_ev[2 * i + 1]));
+    tot += ms;
+  }
+  *total_ms = tot;
+  *launches = c->prof_n;
+  return BCI_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,116 @@
+// Device-side helpers shared by the gfx950 kernels of libbci.
+//
+// Every kernel that touches the same quantity uses the same helper, so the
+// same inputs give the same bits in every phase: one bf16 rounding, one e4m3
+// encoder/decoder, one exp/exp2/log, one reduction tree per shape.  The
+// library is compiled with -ffp-contract=off, so a*b+c is never fused
+// behind our back; an FMA appears only where written as __builtin_fmaf.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bci {
+
+typedef uint16_t bf16_t;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+constexpr int WAVE = 64;
+constexpr float LOG2E = 1.4426950408889634f;
+
+// ---------------------------------------------------------------- bf16
+
+__device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round to nearest even; NaN -> quiet NaN; overflow -> inf.
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf2(bf16_t lo, bf16_t hi) {
+  return (uint32_t)lo | ((uint32_t)hi << 16);
+}
+
+// ------------------------------------------------------ e4m3fn (OCP FP8)
+// 1 sign, 4 exponent (bias 7), 3 mantissa bits; no infinities; S.1111.111 is
+// NaN; largest finite 448.
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  float v;
+  if ((c & 0x7fu) == 0x7fu) {
+    v = __uint_as_float(0x7fc00000u);
+  } else if (e == 0) {
+    v = (float)m * 0.001953125f;  // m/8 * 2^-6, exact
+  } else {
+    v = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  }
+  return (c & 0x80u) ? -v : v;
+}
+
+// x already clamped to [-448, 448] (NaN passes through to 0x7F).  Round to
+// nearest even.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = fabsf(x);
+  if (a != a) return 0x7fu;
+  uint32_t code;
+  if (a < 0.015625f) {                       // below 2^-6: subnormal grid of 2^-9
+    code = (uint32_t)__builtin_rintf(a * 512.0f);   // 8 -> 0x08 == 2^-6, consistent
+  } else {
+    const uint32_t ua = __float_as_uint(a);
+    uint32_t e = (ua >> 23) - 127u + 7u;     // biased e4m3 exponent (>= 1 here)
+    uint32_t m = (ua >> 20) & 7u;
+    const uint32_t rem = ua & 0xfffffu;
+    if (rem > 0x80000u || (rem == 0x80000u && (m & 1u))) {
+      if (++m == 8u) { m = 0; ++e; }
+    }
+    code = (e << 3) | m;
+  }
+  return code | sign;
+}
+
+// The one quantisation rule of the FP8 KV cache: per (token, head) row of d
+// values with amax a: s = a / 448 (fp32, correctly rounded), 1 when a == 0.
+__device__ __forceinline__ float kv_scale_from_amax(float amax) {
+  return amax == 0.0f ? 1.0f : amax / 448.0f;
+}
+__device__ __forceinline__ uint32_t kv_encode(float x, float s) {
+  float q = x / s;
+  q = fminf(fmaxf(q, -448.0f), 448.0f);
+  return f32_to_e4m3(q);
+}
+// ... and the one dequantisation: bf(fp32(code) * s).
+__device__ __forceinline__ bf16_t kv_decode(uint32_t code, float s) {
+  return f2bf(e4m3_to_f32(code) * s);
+}
+
+// ------------------------------------------------------------ math
+
+__device__ __forceinline__ float fexp(float x) { return expf(x); }
+__device__ __forceinline__ float fexp2(float x) { return exp2f(x); }
+__device__ __forceinline__ float flog(float x) { return logf(x); }
+__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + fexp(-g)); }
+
+// ------------------------------------------------------ wave reductions
+// Fixed xor butterflies over the 64 lanes (or a lane group).  For + the two
+// partners add the same two values in either order, which IEEE addition
+// makes bit-identical, so every lane ends with the same bits.
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = v + __shfl_xor(v, o, WAVE);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+  return v;
+}
+
+}  // namespace bci

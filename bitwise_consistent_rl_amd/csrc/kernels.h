@@ -1,0 +1,67 @@
+// Internal launch interface between the C-ABI layer (bci.cpp) and the kernel
+// translation units.  Not installed; no C++ type crosses the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bci {
+
+// ---- norm.hip
+// r/h: [rows, cols]; when ids != nullptr the residual input is E[ids[row]]
+// (embedding gather fused into the first norm; `a` must be null then).
+hipError_t launch_add_rmsnorm(const void* a, const void* r_in, void* r_out, void* h,
+                              const void* g, const int32_t* ids, const void* E, int rows,
+                              int cols, float eps, hipStream_t s);
+hipError_t launch_embed(const int32_t* ids, const void* E, void* out, int rows, int cols,
+                        hipStream_t s);
+hipError_t launch_gather_rows(const void* src, const int32_t* rows, void* dst, int n_rows,
+                              int cols, hipStream_t s);
+
+// ---- gemm.hip
+enum GemmEpi { EPI_BF16 = 0, EPI_F32 = 1, EPI_SILU = 2 };
+// C = A . W^T.  A [M, K] (rows gathered through a_rows when non-null), W [N, K].
+hipError_t launch_gemm(const void* A, const int32_t* a_rows, const void* W, void* C, int M, int N,
+                       int K, int epi, hipStream_t s);
+// lm_head partials: for each row i < M and vocab chunk c (128 columns):
+// part_m[c * M + i] = max_j z_ij, part_s[c * M + i] = sum_j exp(z_ij - max),
+// and zid[i] = z[i, ids[i]].
+hipError_t launch_lmhead_partials(const void* A, const int32_t* a_rows, const void* E,
+                                  const int32_t* ids, int M, int V, int K, float* part_m,
+                                  float* part_s, float* zid, hipStream_t s);
+hipError_t launch_lmhead_combine(const float* part_m, const float* part_s, const float* zid,
+                                 const int32_t* ids, int M, int V, float* lp, hipStream_t s);
+constexpr int LM_CHUNK = 128;
+constexpr int GEMM_BM = 256;
+constexpr int GEMM_BN = 128;
+constexpr int GEMM_BK = 64;
+
+// ---- rope_kv.hip
+struct KvLayer {
+  void* k;         // [n_blocks, nkv, 64, d] bf16 or u8
+  void* v;
+  float* ks;       // [n_blocks, nkv, 64] (fp8 only)
+  float* vs;
+};
+hipError_t launch_rope_kv_write(const void* qkv, void* q_out, const int32_t* tok_pos,
+                                const int32_t* tok_slot, const float* rope_cos,
+                                const float* rope_sin, KvLayer kv, int T, int nq, int nkv, int d,
+                                bool fp8, hipStream_t s);
+hipError_t launch_kv_gather(KvLayer kv, const int32_t* block_row, int n_pos, int nkv, int d,
+                            bool fp8, void* k_out, void* v_out, hipStream_t s);
+
+// ---- attention.hip
+struct AttnArgs {
+  const void* q;               // [T, nq*d] bf16
+  void* o;                     // [T, nq*d] bf16
+  KvLayer kv;
+  const int32_t* tiles;        // [n_tiles, 4]: seq, tok_begin, n_tok, pos_begin
+  const int32_t* block_table;  // [n_seqs, max_blocks]
+  int n_tiles, max_blocks, nq, nkv, d, seg_keys;
+  bool fp8;
+  float scale_log2;            // (1/sqrt(d)) * log2(e), fp32
+};
+constexpr int ATTN_ROWS = 64;  // query rows (token x head-in-group) per tile
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+
+}  // namespace bci

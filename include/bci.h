@@ -1,0 +1,227 @@
+/*
+ * bci.h -- C ABI of the batch-invariant logprob-recompute forward for MI355X (gfx950).
+ *
+ * What the library computes.  In on-policy RL the rollout engine samples tokens
+ * and the trainer recomputes the log-probability of every sampled token under
+ * the same weights; the two must agree bit for bit (page "Finish RL Training
+ * Faster" digest, section "零差异需要一个精确的比较对象"; news page "A vLLM bitre
+ * azonosította az RL-tréning és az inferencia eredményeit", section "A tréning
+ * közvetlenül a vLLM inferenciás kerneljeit használja").  The trainer's forward
+ * calls the same inference kernels (digest, section "让训练前向使用推理的数值";
+ * page "No More Train-Inference Mismatch", section "方法细节").  Every entry point
+ * below produces, for each row, a result that does not depend on the other rows
+ * of the call, on how the sequence was split into prefill chunks and decode
+ * steps, or on which entry point ran it.
+ *
+ * Conventions for every entry point
+ *   - All tensor arguments are DEVICE pointers unless the name says "host".
+ *     bf16 tensors are 16-bit bit patterns (void*); fp32 tensors are float*.
+ *     Matrices are row-major and dense (leading dimension = number of columns).
+ *   - The caller owns every tensor (weights, KV cache, inputs, outputs).  The
+ *     library owns only its context and the one workspace that bci_create
+ *     allocates; it never allocates again, so workspace addresses are stable.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     asynchronously on it; outputs are valid after the stream synchronises.
+ *     Use one stream per context at a time.
+ *   - Every argument is validated on the host before any launch; on error
+ *     nothing is enqueued and bci_last_error() explains.  A failed launch
+ *     returns BCI_E_HIP with the HIP error text.
+ *   - No entry point throws or aborts across the ABI.
+ *
+ * Numeric contract (identical in every entry point and every phase)
+ *   - GEMMs: bf16 operands, fp32 accumulation in ascending 32-wide K steps of
+ *     one MFMA instruction (v_mfma_f32_16x16x32_bf16), no split-K, one tile
+ *     shape for every M.
+ *   - Norm and softmax reductions: fixed shuffle/LDS trees that depend only on
+ *     the column position, never on the row count.
+ *   - Attention: keys walked in 64-key chunks at absolute positions (chunk c =
+ *     keys 64c..64c+63), grouped into segments of `attn_segment_keys` keys that
+ *     are computed from scratch and merged in ascending order, for prefill,
+ *     chunked prefill and decode alike.
+ *   - FP8 KV (e4m3fn, per-token-per-head fp32 scale): every phase quantises
+ *     through one rule and reads keys/values back as bf(fp32(code) * scale).
+ *   - lm_head: fp32 logits never materialised; per 128-column vocab chunk a
+ *     (max, sum-exp) pair, merged in ascending chunk order.
+ */
+#ifndef BCI_H
+#define BCI_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct bci_ctx bci_ctx;
+
+typedef enum {
+  BCI_OK = 0,
+  BCI_E_INVALID = -1,      /* bad argument (shape, range, null pointer)           */
+  BCI_E_UNSUPPORTED = -2,  /* valid request this build does not implement          */
+  BCI_E_HIP = -3,          /* a HIP call or kernel launch failed                   */
+  BCI_E_WORKSPACE = -4,    /* request exceeds the limits given at bci_create       */
+  BCI_E_STATE = -5         /* weights / cache / batch not bound yet                */
+} bci_status;
+
+typedef enum { BCI_MODE_INVARIANT = 0, BCI_MODE_FAST = 1 } bci_mode;
+typedef enum { BCI_KV_BF16 = 0, BCI_KV_FP8_E4M3 = 1 } bci_kv_dtype;
+typedef enum { BCI_EPI_BF16 = 0, BCI_EPI_F32 = 1, BCI_EPI_SILU_MUL = 2 } bci_epilogue;
+
+/* Model shape and numeric contract; copied by bci_create.
+ *   head_dim must be 64 or 128; hidden, n_q_heads*head_dim and intermediate
+ *   multiples of 128; n_q_heads a multiple of n_kv_heads.
+ *   kv_block_tokens must be 64 (= the attention chunk).  attn_segment_keys is a
+ *   positive multiple of 64 (default 2048 when 0).
+ *   max_* bound every later call and size the workspace. */
+typedef struct {
+  int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, intermediate, vocab;
+  float rms_eps, rope_theta;
+  int32_t kv_dtype;            /* bci_kv_dtype */
+  int32_t kv_block_tokens;     /* 64 */
+  int32_t attn_segment_keys;   /* S, multiple of 64; 0 -> 2048 */
+  int32_t max_tokens_per_call; /* T_max: new tokens in one forward call           */
+  int32_t max_seqs_per_call;
+  int32_t max_scored_per_call;
+  int32_t max_position;        /* context capacity per sequence (RoPE table size)  */
+  int32_t mode;                /* bci_mode; fixed for the life of the context      */
+} bci_model_config;
+
+/* One varlen forward call; HOST arrays.  Sequences are packed back to back:
+ * sequence i owns tokens [cu_q[i], cu_q[i+1]) at absolute positions
+ * pos0[i] .. pos0[i] + q_len - 1 (q_len >= 1).  Its keys/values for positions
+ * < pos0[i] must already be in the bound KV cache; this call writes the new
+ * ones.  block_table[i * max_blocks_per_seq + j] is the cache block holding
+ * positions 64j .. 64j+63 of sequence i.  score_rows[r] is a token index whose
+ * NEXT token score_ids[r] is scored (the logprob of a valid response token). */
+typedef struct {
+  int32_t n_seqs, n_tokens, n_scored, max_blocks_per_seq;
+  const int32_t* tokens;       /* [n_tokens], each in [0, vocab)                  */
+  const int32_t* cu_q;         /* [n_seqs + 1], cu_q[0] = 0, cu_q[n_seqs] = n_tokens */
+  const int32_t* pos0;         /* [n_seqs]                                         */
+  const int32_t* block_table;  /* [n_seqs * max_blocks_per_seq]                    */
+  const int32_t* score_rows;   /* [n_scored], each in [0, n_tokens)                */
+  const int32_t* score_ids;    /* [n_scored], each in [0, vocab)                   */
+} bci_batch;
+
+/* ---- context ------------------------------------------------------------ */
+
+/* Creates a context on HIP device `device` and allocates its workspace (sized
+ * from the max_* fields) and the fp32 RoPE table [max_position, head_dim/2].
+ * On failure *out is NULL and the status says why (no context to query). */
+bci_status bci_create(const bci_model_config* cfg, int32_t device, bci_ctx** out);
+/* Frees the workspace.  Safe on NULL.  The caller must have synchronised. */
+void bci_destroy(bci_ctx* ctx);
+/* Text of the last error on this context ("" if none).  Valid until the next call. */
+const char* bci_last_error(const bci_ctx* ctx);
+/* Bytes of device workspace the context holds. */
+uint64_t bci_workspace_bytes(const bci_ctx* ctx);
+
+/* Binds the weights (pointers are kept; the caller keeps the memory alive and
+ * rebinds after reallocating).  Order (n_ptrs = 2 + 6 * n_layers):
+ *   [0] embed [vocab, hidden] (tied lm_head), then per layer l:
+ *   attn_norm [hidden], wqkv [(nq + 2 nkv) * d, hidden] (q heads, k heads, v heads),
+ *   wo [hidden, nq * d], mlp_norm [hidden], wgu [2 * intermediate, hidden] (gate rows
+ *   then up rows), wd [hidden, intermediate]; last: final_norm [hidden].
+ * weight_version identifies the weights (same version => comparable logprobs). */
+bci_status bci_bind_weights(bci_ctx* ctx, const void* const* ptrs, int32_t n_ptrs,
+                            uint64_t weight_version);
+uint64_t bci_weight_version(const bci_ctx* ctx);
+
+/* Binds a paged KV cache.  Layout, per tensor:
+ *   k, v   : [n_layers, n_blocks, n_kv_heads, 64, head_dim]  bf16, or uint8 e4m3fn codes
+ *   k_scale, v_scale (FP8 only, else NULL): [n_layers, n_blocks, n_kv_heads, 64] fp32
+ * The rollout call and the training recompute bind different buffers (the
+ * private cache copy of the digest's FP8 paragraph), written through the same
+ * quantiser. */
+bci_status bci_bind_kv_cache(bci_ctx* ctx, void* k, void* v, float* k_scale, float* v_scale,
+                             int32_t n_blocks);
+
+/* Validates a host batch and uploads its metadata (token ids, positions, cache
+ * slots, attention tile list, scored rows) into the workspace on `stream`.  It
+ * stays the context's current batch for bci_forward_logprobs and the bci_op_*
+ * calls that take no explicit shape. */
+bci_status bci_set_batch(bci_ctx* ctx, const bci_batch* batch, void* stream);
+
+/* The whole forward of the current batch: embedding, n_layers x [add+RMSNorm,
+ * QKV GEMM, RoPE + KV write, attention, O GEMM, add+RMSNorm, gate_up GEMM with
+ * SiLU*up, down GEMM], final add+RMSNorm, lm_head + fp32 log-softmax + gather.
+ * Writes d_logprobs[n_scored] (fp32).  This is the "rollout" entry point. */
+bci_status bci_forward_logprobs(bci_ctx* ctx, float* d_logprobs, void* stream);
+
+/* ---- per-operator entry points ("the training forward calls the inference
+ *      kernels"); each is bitwise identical to its use inside the forward ---- */
+
+/* r[i] = E[tokens[i]] for the current batch (exact row copy).  E [vocab, hidden]. */
+bci_status bci_op_embed(bci_ctx* ctx, const void* E, void* r, void* stream);
+
+/* Fused residual add + RMSNorm over `rows` rows of `cols` bf16 values
+ * (page "No More Train-Inference Mismatch", section "方法细节"):
+ *   if a != NULL: r <- bf(fp32(a) + fp32(r))   (r is updated in place)
+ *   h <- bf(r * rsqrt(mean(r^2) + eps) * g), the mean over the rounded r.
+ * a, r, h: [rows, cols] bf16; g: [cols] bf16.  cols % 8 == 0, cols <= 8192. */
+bci_status bci_op_add_rmsnorm(bci_ctx* ctx, const void* a, void* r, void* h, const void* g,
+                              int32_t rows, int32_t cols, float eps, void* stream);
+
+/* C = A . W^T with A [M, K] bf16 and W [N, K] bf16 (nn.Linear layout), fp32
+ * accumulation in ascending K order, the same for every M (page "Finish RL
+ * Training Faster" digest, section "让训练前向使用推理的数值": batch-invariant
+ * dense GEMM).  Epilogues:
+ *   BCI_EPI_BF16:     C [M, N] bf16 = bf(acc)
+ *   BCI_EPI_F32:      C [M, N] fp32 = acc
+ *   BCI_EPI_SILU_MUL: W holds gate rows then up rows (N = 2 I); C [M, I] bf16 =
+ *                     bf(silu(bf(acc_gate)) * bf(acc_up))   (fused SiLU MLP)
+ * K % 64 == 0; N % 128 == 0 (BCI_EPI_SILU_MUL: I % 64 == 0); M >= 0. */
+bci_status bci_op_gemm_bf16(bci_ctx* ctx, const void* A, const void* W, void* C, int32_t M,
+                            int32_t N, int32_t K, int32_t epilogue, void* stream);
+
+/* For the current batch and layer: rotates q and k of qkv [n_tokens, (nq + 2 nkv) d]
+ * (half-split RoPE at each token's absolute position, fp32 table, bf16 result),
+ * writes q' to q_out [n_tokens, nq * d] and k', v into the bound cache (bf16, or
+ * e4m3 with the per-token-per-head scale rule a = max|x|, s = a / 448, code =
+ * e4m3_rne(clamp(x / s, +-448)); page "Finish RL Training Faster" digest, section
+ * "让训练前向使用推理的数值", FP8 KV paragraph). */
+bci_status bci_op_rope_kv_write(bci_ctx* ctx, const void* qkv, void* q_out, int32_t layer,
+                                void* stream);
+
+/* Gathers sequence `seq` of the current batch, positions 0 .. n_pos - 1, of one
+ * layer out of the paged cache and dequantises to bf16: k_out, v_out
+ * [n_pos, n_kv_heads, head_dim] = bf(fp32(code) * scale) (a plain copy for a
+ * bf16 cache).  The same conversion the attention kernel applies on load. */
+bci_status bci_op_kv_gather_dequant(bci_ctx* ctx, int32_t seq, int32_t n_pos, int32_t layer,
+                                    void* k_out, void* v_out, void* stream);
+
+/* Causal GQA attention of the current batch for one layer: q [n_tokens, nq * d]
+ * bf16 (rotated) against the bound cache, o [n_tokens, nq * d] bf16.  Query head
+ * h reads kv head h / (nq / nkv).  One kernel for prefill, chunked prefill and
+ * decode; keys in 64-key chunks at absolute positions, ascending; segments of S
+ * keys merged ascending (digest, sections "零差异需要一个精确的比较对象" and
+ * "让训练前向使用推理的数值"). */
+bci_status bci_op_attention(bci_ctx* ctx, const void* q, int32_t layer, void* o, void* stream);
+
+/* out[r] = src[score_rows[r]] for the current batch: [n_scored, cols] bf16. */
+bci_status bci_op_gather_scored(bci_ctx* ctx, const void* src, int32_t cols, void* out,
+                                void* stream);
+
+/* lm_head + fp32 log-softmax + gather of the sampled token (digest, section
+ * "零差异需要一个精确的比较对象": the compared quantity):
+ *   z = hf . E^T in fp32 (never stored), lp[i] = z[i, ids[i]] - logsumexp(z[i, :]).
+ * hf [M, H] bf16, E [V, H] bf16, ids [M] int32 (device; an id outside [0, V)
+ * yields NaN), lp [M] fp32.  H % 64 == 0; M <= max_scored_per_call (the
+ * partials live in the workspace). */
+bci_status bci_op_lmhead_logprob(bci_ctx* ctx, const void* hf, const void* E, const int32_t* ids,
+                                 int32_t M, int32_t H, int32_t V, float* lp, void* stream);
+
+/* ---- instrumentation ----------------------------------------------------- */
+
+/* While enabled, bci_forward_logprobs records a HIP event pair on its stream
+ * around every launch of the gate_up GEMM (the SiLU*up-epilogue kernel, the
+ * largest single kernel of the forward; up to 8192 launches).  bci_profile_end
+ * synchronises those events and returns the summed kernel time in ms and the
+ * number of launches timed. */
+bci_status bci_profile_begin(bci_ctx* ctx);
+bci_status bci_profile_end(bci_ctx* ctx, double* total_ms, int32_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BCI_H */

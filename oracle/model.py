@@ -61,15 +61,46 @@ def _embed(W: Weights, ids) -> np.ndarray:
     return bf16_decode(W.raw("embed")[np.asarray(ids, dtype=np.int64)])
 
 
+def decoder_layer(cfg, W: Weights, li: int, m_prev, r, pos, cache_k, cache_v,
+                  kv_dtype: str = "bf16") -> dict:
+    """One decoder layer for a chunk of consecutive positions ``pos``.
+
+    m_prev: the previous layer's MLP output (None for layer 0, whose first norm
+    takes no add); r: the residual entering the layer; cache_k/cache_v: this
+    layer's keys/values of the positions before the chunk.  Returns the layer's
+    tensors, including the updated residual ``r`` and MLP output ``m``.
+    """
+    nq, nkv, d = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    n = len(pos)
+    p = f"layers.{li}."
+    r, h = ops.add_rmsnorm(m_prev, r, W(p + "attn_norm"), cfg.rms_eps)
+    r_mid = r
+    qkv = ops.bf(ops.linear(h, W(p + "wqkv")))
+    q = qkv[:, : nq * d].reshape(n, nq, d)
+    k = qkv[:, nq * d: (nq + nkv) * d].reshape(n, nkv, d)
+    v = qkv[:, (nq + nkv) * d:].reshape(n, nkv, d)
+    q = ops.rope(q, pos, cfg.rope_theta)
+    k = ops.rope(k, pos, cfg.rope_theta)
+    if kv_dtype == "fp8":
+        k = ops.kv_roundtrip(k)
+        v = ops.kv_roundtrip(v)
+    K = np.concatenate([cache_k, k], axis=0)
+    V = np.concatenate([cache_v, v], axis=0)
+    o = ops.causal_gqa_attention(q, K, V, pos)
+    a = ops.bf(ops.linear(o.reshape(n, nq * d), W(p + "wo")))
+    r, h2 = ops.add_rmsnorm(a, r, W(p + "mlp_norm"), cfg.rms_eps)
+    m = ops.mlp(h2, W(p + "wgu"), W(p + "wd"), cfg.intermediate)
+    return dict(layer=li, r_mid=r_mid, h=h, q=q, k=k, v=v, K=K, V=V, o=o, a=a, r=r, h2=h2, m=m)
+
+
 def forward_chunks(cfg, W: Weights, tokens, chunks: List[int], kv_dtype: str = "bf16",
                    dump: Optional[list] = None) -> np.ndarray:
     """Forward positions 0 .. sum(chunks)-1 in consecutive chunks; returns the final
     normed hidden states hf (float64 on the bf16 grid) for every forwarded position.
 
-    ``dump``, when a list, receives per-layer dicts of intermediate tensors.
+    ``dump``, when a list, receives the per-layer dicts of ``decoder_layer``.
     """
-    nq, nkv, d = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
-    H, I = cfg.hidden, cfg.intermediate
+    nkv, d = cfg.n_kv_heads, cfg.head_dim
     tokens = np.asarray(tokens)
     cache_k = [np.zeros((0, nkv, d)) for _ in range(cfg.n_layers)]
     cache_v = [np.zeros((0, nkv, d)) for _ in range(cfg.n_layers)]
@@ -80,25 +111,12 @@ def forward_chunks(cfg, W: Weights, tokens, chunks: List[int], kv_dtype: str = "
         r = _embed(W, tokens[p0:p0 + n])
         m = None
         for li in range(cfg.n_layers):
-            p = f"layers.{li}."
-            r, h = ops.add_rmsnorm(m, r, W(p + "attn_norm"), cfg.rms_eps)
-            qkv = ops.bf(ops.linear(h, W(p + "wqkv")))
-            q = qkv[:, : nq * d].reshape(n, nq, d)
-            k = qkv[:, nq * d: (nq + nkv) * d].reshape(n, nkv, d)
-            v = qkv[:, (nq + nkv) * d:].reshape(n, nkv, d)
-            q = ops.rope(q, pos, cfg.rope_theta)
-            k = ops.rope(k, pos, cfg.rope_theta)
-            if kv_dtype == "fp8":
-                k = ops.kv_roundtrip(k)
-                v = ops.kv_roundtrip(v)
-            cache_k[li] = np.concatenate([cache_k[li], k], axis=0)
-            cache_v[li] = np.concatenate([cache_v[li], v], axis=0)
-            o = ops.causal_gqa_attention(q, cache_k[li], cache_v[li], pos)
-            a = ops.bf(ops.linear(o.reshape(n, nq * d), W(p + "wo")))
-            r, h2 = ops.add_rmsnorm(a, r, W(p + "mlp_norm"), cfg.rms_eps)
-            m = ops.mlp(h2, W(p + "wgu"), W(p + "wd"), I)
+            out = decoder_layer(cfg, W, li, m, r, pos, cache_k[li], cache_v[li], kv_dtype)
+            cache_k[li], cache_v[li] = out.pop("K"), out.pop("V")
+            r, m = out["r"], out["m"]
             if dump is not None:
-                dump.append(dict(layer=li, p0=p0, h=h, q=q, k=k, v=v, o=o, a=a, h2=h2, m=m))
+                out["p0"] = p0
+                dump.append(out)
         r, hf = ops.add_rmsnorm(m, r, W("final_norm"), cfg.rms_eps)
         outs.append(hf)
         p0 += n
