@@ -31,7 +31,10 @@ def assert_bf16_close(got, ref, abs_bound=None, max_ulp=2, frac_exact=0.99, what
     if abs_bound is not None:
         tol = tol + abs_bound
     bad = d > tol
-    assert not bad.any(), (what, int(bad.sum()), float(d.max()))
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        pairs = [(tuple(int(v) for v in i), float(got[tuple(i)]), float(ref[tuple(i)])) for i in idx]
+        raise AssertionError(f"{what}: {int(bad.sum())} elements out of tolerance, e.g. {pairs}")
     within1 = np.mean(d <= ulp + (0 if abs_bound is None else abs_bound))
     assert within1 >= frac_exact, (what, within1)
 
