@@ -58,6 +58,49 @@ def cpu_baseline(cfg, weights, seqs):
                       f"fp64 NumPy forward, {dt:.1f} s"}
 
 
+def micro(args, cfg):
+    """The gate_up GEMM alone (M = 16384 tokens of one packed call, N = 2 x 6144,
+    K = 2048, SiLU*up epilogue), then a plain 1 GiB device copy whose bytes are known,
+    for calibrating the HBM byte counters."""
+    import torch
+    import synth
+    from bitwise_consistent_rl_amd import _abi as abi
+    from bitwise_consistent_rl_amd import engine
+    M, N, K = args.max_tokens, 2 * cfg.intermediate, cfg.hidden
+    mc = abi.ModelConfig()
+    for k, v in dict(n_layers=1, hidden=K, n_q_heads=cfg.n_q_heads, n_kv_heads=cfg.n_kv_heads,
+                     head_dim=cfg.head_dim, intermediate=cfg.intermediate, vocab=128,
+                     rms_eps=1e-6, rope_theta=1e6, kv_block_tokens=64, max_tokens_per_call=64,
+                     max_seqs_per_call=1, max_scored_per_call=1, max_position=64).items():
+        setattr(mc, k, v)
+    ctx = abi.bci_create(mc, 0)
+    a, w = synth.gemm_inputs(M, N, K, index=90)
+    a, w = a.cuda(), w.cuda()
+    c = torch.empty(M, N // 2, dtype=torch.bfloat16, device="cuda")
+    src = torch.empty(1 << 29, dtype=torch.int16, device="cuda")   # 1 GiB
+    dst = torch.empty_like(src)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(2):
+        abi.bci_op_gemm_bf16(ctx, a, w, c, M, N, K, abi.BCI_EPI_SILU_MUL)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        abi.bci_op_gemm_bf16(ctx, a, w, c, M, N, K, abi.BCI_EPI_SILU_MUL)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    flops = 2.0 * M * N * K
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    abi.bci_destroy(ctx)
+    print(json.dumps({"micro": "gate_up", "M": M, "N": N, "K": K, "avg_ms": round(ms, 4),
+                      "tflops": round(flops / ms / 1e9, 1),
+                      "frac": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+                      "algorithmic_bytes": (M * K + N * K + M * N // 2) * 2,
+                      "copy_bytes": 2 * (1 << 30)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -68,6 +111,8 @@ def main():
     ap.add_argument("--max-tokens", type=int, default=16384)
     ap.add_argument("--accept-seqs", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--micro", choices=["gate_up"], default=None,
+                    help="time one kernel alone at the workload's shape (for counter runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: every sequence is independent, so N GPUs would "
@@ -83,6 +128,8 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     cfg = synth.QWEN3_1P7B
+    if args.micro:
+        return micro(args, cfg)
     log("generating weights and workload")
     weights = synth.make_weights(cfg)
     seqs = synth.rl_sequences(cfg, n_prompts=args.prompts, n_responses=args.responses)
@@ -146,7 +193,9 @@ def main():
     acc = engine.acceptance(rec, roll)
     lp_host = first.cpu().numpy()
     # the timed step's rows for these sequences equal the standalone recompute
-    acc["bench_rows_equal"] = bool(np.concatenate(rec).tobytes() == lp_host[: sum(len(r) for r in rec)].tobytes())
+    if rec:
+        acc["bench_rows_equal"] = bool(np.concatenate(rec).tobytes()
+                                       == lp_host[: sum(len(r) for r in rec)].tobytes())
     del roll_cache
 
     out = {

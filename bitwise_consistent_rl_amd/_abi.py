@@ -31,7 +31,8 @@ EXPORTS = [
     "bci_weight_version", "bci_bind_kv_cache", "bci_set_batch", "bci_forward_logprobs",
     "bci_op_embed", "bci_op_add_rmsnorm", "bci_op_gemm_bf16", "bci_op_rope_kv_write",
     "bci_op_kv_gather_dequant", "bci_op_attention", "bci_op_gather_scored",
-    "bci_op_lmhead_logprob", "bci_profile_begin", "bci_profile_end",
+    "bci_op_lmhead_logprob", "bci_op_moe_topk", "bci_op_moe_forward", "bci_profile_begin",
+    "bci_profile_end",
 ]
 
 
@@ -47,7 +48,8 @@ class ModelConfig(ctypes.Structure):
                [("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float)] + \
                [(n, ctypes.c_int32) for n in
                 ("kv_dtype", "kv_block_tokens", "attn_segment_keys", "max_tokens_per_call",
-                 "max_seqs_per_call", "max_scored_per_call", "max_position", "mode")]
+                 "max_seqs_per_call", "max_scored_per_call", "max_position", "mode",
+                 "n_experts", "top_k", "expert_intermediate", "n_shared_experts")]
 
 
 _P32 = ctypes.POINTER(ctypes.c_int32)
@@ -90,6 +92,8 @@ def load() -> ctypes.CDLL:
         "bci_op_attention": (st, [vp, vp, i32, vp, vp]),
         "bci_op_gather_scored": (st, [vp, vp, i32, vp, vp]),
         "bci_op_lmhead_logprob": (st, [vp, vp, vp, vp, i32, i32, i32, vp, vp]),
+        "bci_op_moe_topk": (st, [vp, vp, i32, vp, vp, vp]),
+        "bci_op_moe_forward": (st, [vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp]),
         "bci_profile_begin": (st, [vp]),
         "bci_profile_end": (st, [vp, ctypes.POINTER(ctypes.c_double), _P32]),
     }
@@ -226,6 +230,15 @@ def bci_op_gather_scored(ctx: int, src, cols: int, out, stream=None) -> None:
 def bci_op_lmhead_logprob(ctx: int, hf, E, ids, M: int, H: int, V: int, lp, stream=None) -> None:
     _check(ctx, load().bci_op_lmhead_logprob(ctx, _ptr(hf), _ptr(E), _ptr(ids), M, H, V, _ptr(lp),
                                              _stream(stream)))
+
+
+def bci_op_moe_topk(ctx: int, logits, T: int, ids, w, stream=None) -> None:
+    _check(ctx, load().bci_op_moe_topk(ctx, _ptr(logits), T, _ptr(ids), _ptr(w), _stream(stream)))
+
+
+def bci_op_moe_forward(ctx: int, h, ids, w, T: int, wgu, wd, swgu, swd, out, stream=None) -> None:
+    _check(ctx, load().bci_op_moe_forward(ctx, _ptr(h), _ptr(ids), _ptr(w), T, _ptr(wgu), _ptr(wd),
+                                          _ptr(swgu), _ptr(swd), _ptr(out), _stream(stream)))
 
 
 def bci_profile_begin(ctx: int) -> None:

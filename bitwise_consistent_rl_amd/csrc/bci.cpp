@@ -43,6 +43,11 @@ struct bci_ctx {
   uint16_t *bufR = nullptr, *bufH = nullptr, *bufQKV = nullptr, *bufQ = nullptr,
            *bufO = nullptr, *bufX = nullptr, *bufACT = nullptr;
   float *part_m = nullptr, *part_s = nullptr, *zid = nullptr;
+  // MoE workspace (n_experts > 0)
+  int32_t *moe_perm = nullptr, *moe_inv = nullptr, *moe_counts = nullptr, *moe_offsets = nullptr,
+          *moe_tiles = nullptr, *moe_ntiles = nullptr;
+  uint16_t *moe_act = nullptr, *moe_y = nullptr, *moe_act_s = nullptr, *moe_y_s = nullptr;
+  int moe_max_mtiles = 0;
   float *rope_cos = nullptr, *rope_sin = nullptr;
   int32_t* meta = nullptr;  // device metadata region
   size_t meta_words = 0;
@@ -127,6 +132,11 @@ bci_status bci_create(const bci_model_config* cfg_in, int32_t device, bci_ctx** 
   if (g.max_tokens_per_call < 1 || g.max_seqs_per_call < 1 || g.max_scored_per_call < 0 ||
       g.max_position < 1)
     return BCI_E_INVALID;
+  if (g.n_experts < 0 || g.n_experts > 64) return BCI_E_INVALID;
+  if (g.n_experts > 0 &&
+      (g.top_k < 1 || g.top_k > MOE_MAX_K || g.top_k > g.n_experts || g.expert_intermediate < 64 ||
+       g.expert_intermediate % 64 || g.n_shared_experts < 0 || g.n_shared_experts > 1))
+    return BCI_E_INVALID;
   if (g.mode == BCI_MODE_FAST) return BCI_E_UNSUPPORTED;
   if (g.mode != BCI_MODE_INVARIANT) return BCI_E_INVALID;
   if (hipSetDevice(device) != hipSuccess) return BCI_E_HIP;
@@ -173,6 +183,23 @@ bci_status bci_create(const bci_model_config* cfg_in, int32_t device, bci_ctx** 
       {(void**)&c->rope_sin, (size_t)g.max_position * (g.head_dim / 2) * 4},
       {(void**)&c->meta, c->meta_words * 4},
   };
+  if (g.n_experts > 0) {
+    const size_t P = T * (size_t)g.top_k, I = g.expert_intermediate;
+    c->moe_max_mtiles = (int)((P + GEMM_BM - 1) / GEMM_BM) + g.n_experts;
+    std::vector<Part> moe = {
+        {(void**)&c->moe_perm, P * 4},
+        {(void**)&c->moe_inv, P * 4},
+        {(void**)&c->moe_counts, (size_t)g.n_experts * 4},
+        {(void**)&c->moe_offsets, (size_t)(g.n_experts + 1) * 4},
+        {(void**)&c->moe_tiles, (size_t)c->moe_max_mtiles * 3 * 4},
+        {(void**)&c->moe_ntiles, 4},
+        {(void**)&c->moe_act, P * I * 2},
+        {(void**)&c->moe_y, P * H * 2},
+        {(void**)&c->moe_act_s, T * I * 2},
+        {(void**)&c->moe_y_s, T * H * 2},
+    };
+    parts.insert(parts.end(), moe.begin(), moe.end());
+  }
   size_t total = 0;
   for (auto& p : parts) total += align_up(p.bytes, 256);
   if (hipMalloc(&c->ws, total) != hipSuccess) {
@@ -428,7 +455,7 @@ bci_status bci_op_gemm_bf16(bci_ctx* c, const void* A, const void* W, void* C, i
   if (epi == BCI_EPI_SILU_MUL) {
     if (N % 128) return fail(c, BCI_E_INVALID, "op_gemm: SILU_MUL needs N = 2*I with I %% 64 == 0 (N=%d)", N);
   } else if (epi == BCI_EPI_BF16 || epi == BCI_EPI_F32) {
-    if (N % GEMM_BN) return fail(c, BCI_E_INVALID, "op_gemm: N %d not a multiple of %d", N, GEMM_BN);
+    // any N: columns past the last full 128-column tile are masked
   } else {
     return fail(c, BCI_E_INVALID, "op_gemm: unknown epilogue %d", epi);
   }
@@ -487,6 +514,50 @@ bci_status bci_op_lmhead_logprob(bci_ctx* c, const void* hf, const void* E, cons
     return fail(c, BCI_E_WORKSPACE, "op_lmhead_logprob: vocab %d larger than the context's %d", V, c->cfg.vocab);
   HIP_TRY(c, launch_lmhead_partials(hf, nullptr, E, ids, M, V, H, c->part_m, c->part_s, c->zid, S(stream)));
   HIP_TRY(c, launch_lmhead_combine(c->part_m, c->part_s, c->zid, ids, M, V, lp, S(stream)));
+  return BCI_OK;
+}
+
+// ------------------------------------------------------------ MoE
+
+bci_status bci_op_moe_topk(bci_ctx* c, const float* logits, int32_t T, int32_t* ids, float* w,
+                           void* stream) {
+  if (!c) return BCI_E_INVALID;
+  const auto& g = c->cfg;
+  if (g.n_experts == 0) return fail(c, BCI_E_STATE, "op_moe_topk: the context has no MoE layer");
+  if (!logits || !ids || !w || T < 0) return fail(c, BCI_E_INVALID, "op_moe_topk: bad pointer or T");
+  if (T > g.max_tokens_per_call)
+    return fail(c, BCI_E_WORKSPACE, "op_moe_topk: T %d > max_tokens_per_call %d", T, g.max_tokens_per_call);
+  HIP_TRY(c, launch_moe_topk(logits, T, g.n_experts, g.top_k, ids, w, S(stream)));
+  return BCI_OK;
+}
+
+bci_status bci_op_moe_forward(bci_ctx* c, const void* h, const int32_t* ids, const float* w, int32_t T,
+                              const void* wgu, const void* wd, const void* swgu, const void* swd, void* out,
+                              void* stream) {
+  if (!c) return BCI_E_INVALID;
+  const auto& g = c->cfg;
+  if (g.n_experts == 0) return fail(c, BCI_E_STATE, "op_moe_forward: the context has no MoE layer");
+  if (!h || !ids || !w || !wgu || !wd || !out || T < 0)
+    return fail(c, BCI_E_INVALID, "op_moe_forward: null pointer or T < 0");
+  if ((g.n_shared_experts > 0) != (swgu && swd))
+    return fail(c, BCI_E_INVALID, "op_moe_forward: shared-expert weights must match n_shared_experts");
+  if (T > g.max_tokens_per_call)
+    return fail(c, BCI_E_WORKSPACE, "op_moe_forward: T %d > max_tokens_per_call %d", T, g.max_tokens_per_call);
+  if (T == 0) return BCI_OK;
+  const hipStream_t s = S(stream);
+  const int H = g.hidden, I = g.expert_intermediate, E = g.n_experts, k = g.top_k, P = T * k;
+  const int max_mt = (P + GEMM_BM - 1) / GEMM_BM + E;
+  HIP_TRY(c, launch_moe_sort(ids, P, E, c->moe_counts, c->moe_offsets, c->moe_perm, c->moe_inv, c->moe_tiles,
+                             c->moe_ntiles, s));
+  HIP_TRY(c, launch_gemm_grouped(h, c->moe_perm, k, wgu, (size_t)2 * I * H, c->moe_act, c->moe_tiles,
+                                 c->moe_ntiles, max_mt, 2 * I, H, EPI_SILU, s));
+  HIP_TRY(c, launch_gemm_grouped(c->moe_act, nullptr, 1, wd, (size_t)H * I, c->moe_y, c->moe_tiles,
+                                 c->moe_ntiles, max_mt, H, I, EPI_BF16, s));
+  if (swgu) {
+    HIP_TRY(c, launch_gemm(h, nullptr, swgu, c->moe_act_s, T, 2 * I, H, EPI_SILU, s));
+    HIP_TRY(c, launch_gemm(c->moe_act_s, nullptr, swd, c->moe_y_s, T, H, I, EPI_BF16, s));
+  }
+  HIP_TRY(c, launch_moe_combine(c->moe_y, swgu ? c->moe_y_s : nullptr, ids, w, c->moe_inv, T, k, E, H, out, s));
   return BCI_OK;
 }
 

@@ -36,7 +36,8 @@ enum { K_BF16 = 0, K_F32 = 1, K_SILU = 2, K_LMHEAD = 3 };
 
 struct GemmArgs {
   const bf16_t* A;
-  const int32_t* a_rows;
+  const int32_t* a_rows;  // gather: A row of output row r is a_rows[r] / a_div
+  int a_div;
   const bf16_t* W;
   void* C;
   int M, N, K;  // N: W rows (K_SILU: 2 * I; K_LMHEAD: vocab)
@@ -45,6 +46,11 @@ struct GemmArgs {
   float* part_m;
   float* part_s;
   float* zid;
+  // grouped (per-expert) mode: m-tile i is gtiles[3i..3i+2] = (group, first row, rows),
+  // valid for i < *n_gtiles; group g uses W + g * w_group_stride.
+  const int32_t* gtiles;
+  const int32_t* n_gtiles;
+  size_t w_group_stride;
 };
 
 // Row r of an LDS tile holds 8 chunks of 16 bytes; chunk c is stored at
@@ -64,7 +70,7 @@ __device__ __forceinline__ int b_lds_row(int wn, int ni) {
   }
 }
 
-template <int KIND, bool GATHER>
+template <int KIND, bool GATHER, bool GROUPED>
 __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(GemmArgs p) {
   __shared__ u32x4_t smem[(BM + BN) * KCH];  // 48 KiB
   u32x4_t* As = smem;
@@ -86,13 +92,25 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(GemmArgs p) {
   const int wm = wave >> 1, wn = wave & 1;
   const int K = p.K;
 
+  // rows [row_base, row_base + row_cnt) of C belong to this tile
+  int row_base = tm * BM, row_cnt = min(BM, p.M - tm * BM);
+  const bf16_t* W = p.W;
+  if constexpr (GROUPED) {
+    if (tm >= *p.n_gtiles) return;
+    const int grp = p.gtiles[3 * tm];
+    row_base = p.gtiles[3 * tm + 1];
+    row_cnt = p.gtiles[3 * tm + 2];
+    W += (size_t)grp * p.w_group_stride;
+  }
+
   // ---- global load assignment: thread -> (row, 16-byte chunk)
   const int ld_ch = tid & 7, ld_row = tid >> 3;  // rows ld_row + 32 i
   const bf16_t* a_src[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    int r = min(tm * BM + ld_row + 32 * i, p.M - 1);  // rows past M: duplicate row M-1, never stored
-    if constexpr (GATHER) r = p.a_rows[r];
+    // rows past the tile's end duplicate its last row and are never stored
+    int r = row_base + min(ld_row + 32 * i, row_cnt - 1);
+    if constexpr (GATHER) r = p.a_rows[r] / p.a_div;
     a_src[i] = p.A + (size_t)r * K + ld_ch * 8;
   }
   const bf16_t* b_src[4];
@@ -104,9 +122,9 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(GemmArgs p) {
       const int I = p.N >> 1;
       n = (r < 64) ? tn * 64 + r : I + tn * 64 + (r - 64);
     } else {
-      n = min(tn * BN + r, p.N - 1);  // lm_head: columns past V are masked later
+      n = min(tn * BN + r, p.N - 1);  // columns past N are masked in the epilogue
     }
-    b_src[i] = p.W + (size_t)n * K + ld_ch * 8;
+    b_src[i] = W + (size_t)n * K + ld_ch * 8;
   }
 
   f32x4_t acc[8][4];
@@ -159,17 +177,19 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(GemmArgs p) {
   }
 
   // ---- epilogues.  Lane holds C[4*(lane>>4) + r][lane & 15] of each 16x16 block.
-  const int row0 = tm * BM + wm * 128 + 4 * (lane >> 4);
+  const int lrow0 = wm * 128 + 4 * (lane >> 4);  // row within the tile
+  const int row0 = row_base + lrow0;
   if constexpr (KIND == K_BF16 || KIND == K_F32) {
 #pragma unroll
     for (int mi = 0; mi < 8; ++mi)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = row0 + mi * 16 + r;
-        if (row < p.M) {
+        if (lrow0 + mi * 16 + r < row_cnt) {
 #pragma unroll
           for (int ni = 0; ni < 4; ++ni) {
             const int col = tn * BN + wn * 64 + ni * 16 + (lane & 15);
+            if (col >= p.N) continue;
             if constexpr (KIND == K_BF16)
               reinterpret_cast<bf16_t*>(p.C)[(size_t)row * p.N + col] = f2bf(acc[mi][ni][r]);
             else
@@ -184,7 +204,7 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(GemmArgs p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = row0 + mi * 16 + r;
-        if (row < p.M) {
+        if (lrow0 + mi * 16 + r < row_cnt) {
 #pragma unroll
           for (int ni = 0; ni < 2; ++ni) {
             const int col = tn * 64 + wn * 32 + ni * 16 + (lane & 15);
@@ -243,8 +263,8 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(GemmArgs p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int lr = wm * 128 + mi * 16 + 4 * (lane >> 4) + r;
-        const int row = tm * BM + lr;
-        if (row < p.M) {
+        const int row = row_base + lr;
+        if (lr < row_cnt) {
           if (wn == 0 && (lane & 15) == 0) {
             p.part_m[(size_t)tn * p.M + row] = mc[mi][r];
             p.part_s[(size_t)tn * p.M + row] = red[lr] + red[BM + lr];
@@ -265,9 +285,9 @@ static hipError_t dispatch(const GemmArgs& a, bool gather, hipStream_t s) {
   const int n_tiles = a.tiles_m * a.tiles_n;
   const int grid = (n_tiles + 7) / 8 * 8;
   if (gather)
-    hipLaunchKernelGGL((gemm_kernel<KIND, true>), dim3(grid), dim3(THREADS), 0, s, a);
+    hipLaunchKernelGGL((gemm_kernel<KIND, true, false>), dim3(grid), dim3(THREADS), 0, s, a);
   else
-    hipLaunchKernelGGL((gemm_kernel<KIND, false>), dim3(grid), dim3(THREADS), 0, s, a);
+    hipLaunchKernelGGL((gemm_kernel<KIND, false, false>), dim3(grid), dim3(THREADS), 0, s, a);
   return hipGetLastError();
 }
 
@@ -282,14 +302,48 @@ hipError_t launch_gemm(const void* A, const int32_t* a_rows, const void* W, void
   a.M = M;
   a.N = N;
   a.K = K;
+  a.a_div = 1;
   a.tiles_m = (M + BM - 1) / BM;
-  a.tiles_n = (epi == EPI_SILU) ? (N / 2) / 64 : N / BN;
+  a.tiles_n = (epi == EPI_SILU) ? (N / 2) / 64 : (N + BN - 1) / BN;
   switch (epi) {
     case EPI_BF16: return dispatch<K_BF16>(a, a_rows != nullptr, s);
     case EPI_F32: return dispatch<K_F32>(a, a_rows != nullptr, s);
     case EPI_SILU: return dispatch<K_SILU>(a, a_rows != nullptr, s);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_grouped(const void* A, const int32_t* a_rows, int a_div, const void* W,
+                               size_t w_group_stride, void* C, const int32_t* gtiles,
+                               const int32_t* n_gtiles, int max_mtiles, int N, int K, int epi,
+                               hipStream_t s) {
+  if (max_mtiles == 0) return hipSuccess;
+  GemmArgs a{};
+  a.A = (const bf16_t*)A;
+  a.a_rows = a_rows;
+  a.a_div = a_div;
+  a.W = (const bf16_t*)W;
+  a.C = C;
+  a.M = 0;
+  a.N = N;
+  a.K = K;
+  a.tiles_m = max_mtiles;
+  a.tiles_n = (epi == EPI_SILU) ? (N / 2) / 64 : (N + BN - 1) / BN;
+  a.gtiles = gtiles;
+  a.n_gtiles = n_gtiles;
+  a.w_group_stride = w_group_stride;
+  const int grid = (a.tiles_m * a.tiles_n + 7) / 8 * 8;
+  const bool g = a_rows != nullptr;
+  if (epi == EPI_SILU) {
+    if (g) hipLaunchKernelGGL((gemm_kernel<K_SILU, true, true>), dim3(grid), dim3(THREADS), 0, s, a);
+    else hipLaunchKernelGGL((gemm_kernel<K_SILU, false, true>), dim3(grid), dim3(THREADS), 0, s, a);
+  } else if (epi == EPI_BF16) {
+    if (g) hipLaunchKernelGGL((gemm_kernel<K_BF16, true, true>), dim3(grid), dim3(THREADS), 0, s, a);
+    else hipLaunchKernelGGL((gemm_kernel<K_BF16, false, true>), dim3(grid), dim3(THREADS), 0, s, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_lmhead_partials(const void* A, const int32_t* a_rows, const void* E,
@@ -299,6 +353,7 @@ hipError_t launch_lmhead_partials(const void* A, const int32_t* a_rows, const vo
   GemmArgs a{};
   a.A = (const bf16_t*)A;
   a.a_rows = a_rows;
+  a.a_div = 1;
   a.W = (const bf16_t*)E;
   a.M = M;
   a.N = V;
@@ -312,38 +367,52 @@ hipError_t launch_lmhead_partials(const void* A, const int32_t* a_rows, const vo
   return dispatch<K_LMHEAD>(a, a_rows != nullptr, s);
 }
 
-// Ascending merge of the per-chunk (max, sum exp) pairs of one row, then
-// lp = (z[id] - max) - log(sum).  One thread per row; chunk-major partials
-// make every load coalesced across the rows of a wave.
-__global__ __launch_bounds__(256) void lmhead_combine_kernel(const float* __restrict__ pm,
-                                                             const float* __restrict__ ps,
-                                                             const float* __restrict__ zid,
-                                                             const int32_t* __restrict__ ids,
-                                                             int M, int V, int nc,
-                                                             float* __restrict__ lp) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= M) return;
-  float mx = -INFINITY, s = 0.0f;
-  for (int c = 0; c < nc; ++c) {
-    const float m = pm[(size_t)c * M + i];
-    const float v = ps[(size_t)c * M + i];
-    if (m > mx) {
-      s = s * fexp(mx - m) + v;
-      mx = m;
-    } else {
-      s = s + v * fexp(m - mx);
-    }
+// Fixed merge order of the per-chunk (max, sum exp) pairs of one row: the
+// chunks are split into 8 contiguous ranges; thread (row, q) merges range q in
+// ascending chunk order; then range results 0..7 are merged in that order.
+// The order depends only on the chunk count, never on the row count.  Lanes
+// run over consecutive rows, so every load of the chunk-major partials is
+// coalesced.  lp = (z[id] - max) - log(sum).
+constexpr int COMB_ROWS = 64, COMB_SPLIT = 8;
+
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  if (m2 > m) {
+    s = s * fexp(m - m2) + s2;
+    m = m2;
+  } else if (m2 != -INFINITY) {
+    s = s + s2 * fexp(m2 - m);
   }
-  const int id = ids[i];
-  lp[i] = (id < 0 || id >= V) ? __uint_as_float(0x7fc00000u) : (zid[i] - mx) - flog(s);
+}
+
+__global__ __launch_bounds__(COMB_ROWS * COMB_SPLIT) void lmhead_combine_kernel(
+    const float* __restrict__ pm, const float* __restrict__ ps, const float* __restrict__ zid,
+    const int32_t* __restrict__ ids, int M, int V, int nc, float* __restrict__ lp) {
+  __shared__ float sm[COMB_SPLIT][COMB_ROWS], ss[COMB_SPLIT][COMB_ROWS];
+  const int r = threadIdx.x, q = threadIdx.y;
+  const int i = blockIdx.x * COMB_ROWS + r;
+  const int per = (nc + COMB_SPLIT - 1) / COMB_SPLIT;
+  float mx = -INFINITY, s = 0.0f;
+  if (i < M) {
+    const int c1 = min(nc, (q + 1) * per);
+    for (int c = q * per; c < c1; ++c)
+      lse_merge(mx, s, pm[(size_t)c * M + i], ps[(size_t)c * M + i]);
+  }
+  sm[q][r] = mx;
+  ss[q][r] = s;
+  __syncthreads();
+  if (q == 0 && i < M) {
+    for (int k = 1; k < COMB_SPLIT; ++k) lse_merge(mx, s, sm[k][r], ss[k][r]);
+    const int id = ids[i];
+    lp[i] = (id < 0 || id >= V) ? __uint_as_float(0x7fc00000u) : (zid[i] - mx) - flog(s);
+  }
 }
 
 hipError_t launch_lmhead_combine(const float* part_m, const float* part_s, const float* zid,
                                  const int32_t* ids, int M, int V, float* lp, hipStream_t s) {
   if (M == 0) return hipSuccess;
   const int nc = (V + BN - 1) / BN;
-  hipLaunchKernelGGL(lmhead_combine_kernel, dim3((M + 255) / 256), dim3(256), 0, s, part_m,
-                     part_s, zid, ids, M, V, nc, lp);
+  hipLaunchKernelGGL(lmhead_combine_kernel, dim3((M + COMB_ROWS - 1) / COMB_ROWS),
+                     dim3(COMB_ROWS, COMB_SPLIT), 0, s, part_m, part_s, zid, ids, M, V, nc, lp);
   return hipGetLastError();
 }
 

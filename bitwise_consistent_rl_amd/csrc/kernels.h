@@ -23,6 +23,13 @@ enum GemmEpi { EPI_BF16 = 0, EPI_F32 = 1, EPI_SILU = 2 };
 // C = A . W^T.  A [M, K] (rows gathered through a_rows when non-null), W [N, K].
 hipError_t launch_gemm(const void* A, const int32_t* a_rows, const void* W, void* C, int M, int N,
                        int K, int epi, hipStream_t s);
+// Grouped GEMM over a device tile list (see GemmArgs in gemm.hip): m-tile i covers
+// rows gtiles[3i+1] .. +gtiles[3i+2] of C with weight W + gtiles[3i] * w_group_stride;
+// A rows are a_rows[r] / a_div when a_rows is non-null, else r.
+hipError_t launch_gemm_grouped(const void* A, const int32_t* a_rows, int a_div, const void* W,
+                               size_t w_group_stride, void* C, const int32_t* gtiles,
+                               const int32_t* n_gtiles, int max_mtiles, int N, int K, int epi,
+                               hipStream_t s);
 // lm_head partials: for each row i < M and vocab chunk c (128 columns):
 // part_m[c * M + i] = max_j z_ij, part_s[c * M + i] = sum_j exp(z_ij - max),
 // and zid[i] = z[i, ids[i]].
@@ -63,5 +70,16 @@ struct AttnArgs {
 };
 constexpr int ATTN_ROWS = 64;  // query rows (token x head-in-group) per tile
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+
+// ---- moe.hip
+constexpr int MOE_MAX_K = 8;
+hipError_t launch_moe_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                           hipStream_t s);
+hipError_t launch_moe_sort(const int32_t* ids, int P, int E, int32_t* counts, int32_t* offsets,
+                           int32_t* perm, int32_t* inv, int32_t* tiles, int32_t* n_tiles,
+                           hipStream_t s);
+hipError_t launch_moe_combine(const void* y, const void* ys, const int32_t* ids, const float* w,
+                              const int32_t* inv, int T, int k, int E, int H, void* out,
+                              hipStream_t s);
 
 }  // namespace bci

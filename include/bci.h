@@ -41,7 +41,9 @@
  *   - FP8 KV (e4m3fn, per-token-per-head fp32 scale): every phase quantises
  *     through one rule and reads keys/values back as bf(fp32(code) * scale).
  *   - lm_head: fp32 logits never materialised; per 128-column vocab chunk a
- *     (max, sum-exp) pair, merged in ascending chunk order.
+ *     (max, sum-exp) pair; the pairs are merged in one fixed order that depends
+ *     only on the vocabulary size (8 contiguous chunk ranges, each ascending,
+ *     then the 8 range results in order).
  */
 #ifndef BCI_H
 #define BCI_H
@@ -84,6 +86,11 @@ typedef struct {
   int32_t max_scored_per_call;
   int32_t max_position;        /* context capacity per sequence (RoPE table size)  */
   int32_t mode;                /* bci_mode; fixed for the life of the context      */
+  /* MoE layer (0 experts = dense only).  n_experts <= 64, 1 <= top_k <= min(8,
+   * n_experts), expert_intermediate % 64 == 0, n_shared_experts 0 or 1.  The
+   * MoE entry points use `hidden` as the model width and size their workspace
+   * for max_tokens_per_call * top_k routed rows. */
+  int32_t n_experts, top_k, expert_intermediate, n_shared_experts;
 } bci_model_config;
 
 /* One varlen forward call; HOST arrays.  Sequences are packed back to back:
@@ -170,7 +177,7 @@ bci_status bci_op_add_rmsnorm(bci_ctx* ctx, const void* a, void* r, void* h, con
  *   BCI_EPI_F32:      C [M, N] fp32 = acc
  *   BCI_EPI_SILU_MUL: W holds gate rows then up rows (N = 2 I); C [M, I] bf16 =
  *                     bf(silu(bf(acc_gate)) * bf(acc_up))   (fused SiLU MLP)
- * K % 64 == 0; N % 128 == 0 (BCI_EPI_SILU_MUL: I % 64 == 0); M >= 0. */
+ * K % 64 == 0; N >= 1 (BCI_EPI_SILU_MUL: I % 64 == 0); M >= 0. */
 bci_status bci_op_gemm_bf16(bci_ctx* ctx, const void* A, const void* W, void* C, int32_t M,
                             int32_t N, int32_t K, int32_t epilogue, void* stream);
 
@@ -210,6 +217,32 @@ bci_status bci_op_gather_scored(bci_ctx* ctx, const void* src, int32_t cols, voi
  * partials live in the workspace). */
 bci_status bci_op_lmhead_logprob(bci_ctx* ctx, const void* hf, const void* E, const int32_t* ids,
                                  int32_t M, int32_t H, int32_t V, float* lp, void* stream);
+
+/* ---- MoE (configured through n_experts / top_k / expert_intermediate) ------ */
+
+/* Router top-K with a fixed tie rule (digest, section "零差异需要一个精确的比较对象":
+ * tie handling in discrete Top-K; section "让训练前向使用推理的数值": MoE).
+ * logits [T, n_experts] fp32 (device).  Experts are ranked by (logit descending,
+ * expert index ascending); slots 0..top_k-1 take them in that order.
+ * ids [T, top_k] int32, w [T, top_k] fp32 = softmax over the selected logits
+ * (the denominator summed in slot order).  NaN logits rank above every number. */
+bci_status bci_op_moe_topk(bci_ctx* ctx, const float* logits, int32_t T, int32_t* ids, float* w,
+                           void* stream);
+
+/* One MoE layer: out[t] = bf( sum over slots s = 0..top_k-1, in slot order, of
+ * fp32 w[t,s] * y_{ids[t,s]}(h[t]) accumulated with one fp32 FMA chain, then +
+ * y_shared(h[t]) ), where y_e(x) = bf( bf(silu(bf(x Wg_e^T)) * bf(x Wu_e^T)) Wd_e^T )
+ * (digest, section "让训练前向使用推理的数值": row-wise expert compute and an FP32
+ * combine in fixed slot order).  Pairs (t, s) are grouped by expert with a
+ * stable sort in (t, s) order and run through one grouped GEMM per projection.
+ *   h [T, hidden] bf16; ids, w as produced by bci_op_moe_topk (device; an id
+ *   outside [0, n_experts) makes that token's row NaN);
+ *   wgu [n_experts, 2 I, hidden] (gate rows then up rows), wd [n_experts, hidden, I];
+ *   swgu [2 I, hidden], swd [hidden, I] the ungated shared expert (NULL when
+ *   n_shared_experts == 0); out [T, hidden] bf16.  T <= max_tokens_per_call. */
+bci_status bci_op_moe_forward(bci_ctx* ctx, const void* h, const int32_t* ids, const float* w,
+                              int32_t T, const void* wgu, const void* wd, const void* swgu,
+                              const void* swd, void* out, void* stream);
 
 /* ---- instrumentation ----------------------------------------------------- */
 

@@ -123,9 +123,24 @@ def test_gemm_rejects_bad_shapes(ctx):
     a_ = abi()
     x = torch.empty(4, 64, dtype=BF, device="cuda")
     with pytest.raises(a_.BciError):
-        a_.bci_op_gemm_bf16(ctx, x, x, x, 4, 100, 64, a_.BCI_EPI_BF16)   # N % 128
-    with pytest.raises(a_.BciError):
         a_.bci_op_gemm_bf16(ctx, x, x, x, 4, 128, 48, a_.BCI_EPI_BF16)   # K % 64
+    with pytest.raises(a_.BciError):
+        a_.bci_op_gemm_bf16(ctx, x, x, x, 4, 192, 64, a_.BCI_EPI_SILU_MUL)   # I % 64
+    with pytest.raises(a_.BciError):
+        a_.bci_op_gemm_bf16(ctx, x, x, x, 4, 128, 64, 7)   # unknown epilogue
+
+
+def test_gemm_ragged_n_parity_and_invariance(ctx):
+    """N not a multiple of the 128-column tile: the tail columns are masked."""
+    M, N, K = 300, 200, 256
+    a, w = synth.gemm_inputs(M, N, K, index=16)
+    ga, gw = cuda(a), cuda(w)
+    C = gemm(ctx, ga, gw, abi().BCI_EPI_BF16)
+    A, W = f64(a), f64(w)
+    mag = np.abs(A) @ np.abs(W).T
+    assert_bf16_close(f64(C), ops.bf(ops.linear(A, W)), abs_bound=K * 2.0 ** -24 * mag,
+                      max_ulp=1, frac_exact=0.999, what="ragged N")
+    assert same_bits(gemm(ctx, ga[5:6].contiguous(), gw, abi().BCI_EPI_BF16), C[5:6])
 
 
 # ----------------------------------------------------------------- RMSNorm
