@@ -134,8 +134,8 @@ bci_status bci_create(const bci_model_config* cfg_in, int32_t device, bci_ctx** 
     return BCI_E_INVALID;
   if (g.n_experts < 0 || g.n_experts > 64) return BCI_E_INVALID;
   if (g.n_experts > 0 &&
-      (g.top_k < 1 || g.top_k > MOE_MAX_K || g.top_k > g.n_experts || g.expert_intermediate < 64 ||
-       g.expert_intermediate % 64 || g.n_shared_experts < 0 || g.n_shared_experts > 1))
+      (g.top_k < 1 || g.top_k > MOE_MAX_K || g.top_k > g.n_experts || g.expert_intermediate < 128 ||
+       g.expert_intermediate % 128 || g.n_shared_experts < 0 || g.n_shared_experts > 1))
     return BCI_E_INVALID;
   if (g.mode == BCI_MODE_FAST) return BCI_E_UNSUPPORTED;
   if (g.mode != BCI_MODE_INVARIANT) return BCI_E_INVALID;
@@ -453,7 +453,7 @@ bci_status bci_op_gemm_bf16(bci_ctx* c, const void* A, const void* W, void* C, i
   if (!A || !W || !C || M < 0 || N < 1 || K < 1) return fail(c, BCI_E_INVALID, "op_gemm: bad pointer or shape");
   if (K % GEMM_BK) return fail(c, BCI_E_INVALID, "op_gemm: K %d not a multiple of %d", K, GEMM_BK);
   if (epi == BCI_EPI_SILU_MUL) {
-    if (N % 128) return fail(c, BCI_E_INVALID, "op_gemm: SILU_MUL needs N = 2*I with I %% 64 == 0 (N=%d)", N);
+    if (N % 256) return fail(c, BCI_E_INVALID, "op_gemm: SILU_MUL needs N = 2*I with I %% 128 == 0 (N=%d)", N);
   } else if (epi == BCI_EPI_BF16 || epi == BCI_EPI_F32) {
     // any N: columns past the last full 128-column tile are masked
   } else {

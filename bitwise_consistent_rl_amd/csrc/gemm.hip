@@ -11,16 +11,20 @@
 // MFMA accumulator that starts at zero and receives
 // v_mfma_f32_16x16x32_bf16(A[i, k:k+32], W[j, k:k+32]) for k = 0, 32, 64, ...
 // in ascending order; nothing else is ever added to it.  The tile shape
-// (256 x 128 x 64, 4 waves) is the same for every M, there is no split-K, and
+// (256 x 256 x 64, 8 waves) is the same for every M, there is no split-K, and
 // an MFMA output element depends only on its own A row and W row, so the
 // bits of row i are the same whatever M is and wherever row i sits in a tile.
 //
-// Data path.  Global -> registers (16-byte loads, prefetching the next
-// K-slab) -> LDS (XOR-swizzled 16-byte chunks, conflict-free for the MFMA
-// operand reads) -> MFMA.  Each wave owns a 128 x 64 sub-tile, i.e. 8 x 4
-// MFMA blocks (128 fp32 accumulators per lane).  Workgroups are remapped so
-// each XCD (8 per chip, each with its own L2) gets a contiguous range of
-// tiles, grouped 8 M-tiles at a time so that they share W tiles in L2.
+// Data path.  Global -> LDS directly (global_load_lds_dwordx4 into two
+// buffers of XOR-swizzled 16-byte chunks, conflict-free for the MFMA operand
+// reads) -> MFMA.  While the waves multiply out of one LDS buffer, the next
+// K-slab streams into the other, so one barrier per 64-wide K-slab suffices
+// and a load has a whole slab of MFMA work to arrive.  8 waves (4 x 2) each own a 64 x 128 sub-tile, i.e.
+// 4 x 8 MFMA blocks (128 fp32 accumulators per lane); two waves per SIMD, and
+// a wave raises its priority while it issues MFMAs.
+// Workgroups are remapped so each XCD (8 per chip, each with its own L2) gets
+// a contiguous range of tiles, grouped 8 M-tiles at a time so that they share
+// W tiles in L2.
 #include "common.h"
 #include "kernels.h"
 
@@ -30,7 +34,11 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int BM = GEMM_BM, BN = GEMM_BN, BK = GEMM_BK;
 constexpr int KCH = BK / 8;  // 16-byte chunks per LDS row
-constexpr int THREADS = 256;
+constexpr int NWM = 4, NWN = 2;          // waves along M and N
+constexpr int WTM = BM / NWM, WTN = BN / NWN;  // 64 x 128 per wave
+constexpr int MI = WTM / 16, NI = WTN / 16;    // 4 x 8 MFMA blocks per wave
+constexpr int THREADS = NWM * NWN * 64;
+constexpr int STAGE = (BM + BN) * KCH;   // 16-byte chunks per LDS buffer
 
 enum { K_BF16 = 0, K_F32 = 1, K_SILU = 2, K_LMHEAD = 3 };
 
@@ -60,21 +68,21 @@ struct GemmArgs {
 // distinct 4-bank groups.
 __device__ __forceinline__ int swz(int row, int ch) { return row * KCH + (ch ^ ((row >> 1) & 7)); }
 
+// LDS row of a wave's n-th 16-column MFMA block.  SiLU tiles hold BN/2 gate
+// rows then the BN/2 matching up rows; a wave's first NI/2 blocks are gate
+// columns and its last NI/2 the up columns of the same outputs.
 template <int KIND>
 __device__ __forceinline__ int b_lds_row(int wn, int ni) {
   if constexpr (KIND == K_SILU) {
-    // sub-tiles 0,1: gate columns; 2,3: the matching up columns
-    return (ni < 2) ? wn * 32 + ni * 16 : 64 + wn * 32 + (ni - 2) * 16;
+    return (ni < NI / 2) ? wn * (WTN / 2) + ni * 16 : BN / 2 + wn * (WTN / 2) + (ni - NI / 2) * 16;
   } else {
-    return wn * 64 + ni * 16;
+    return wn * WTN + ni * 16;
   }
 }
 
 template <int KIND, bool GATHER, bool GROUPED>
-__global__ __launch_bounds__(THREADS, 2) void gemm_kernel(GemmArgs p) {
-  __shared__ u32x4_t smem[(BM + BN) * KCH];  // 48 KiB
-  u32x4_t* As = smem;
-  u32x4_t* Bs = smem + BM * KCH;
+__global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs p) {
+  __shared__ u32x4_t smem[2 * STAGE];  // 2 x 64 KiB
 
   // ---- tile id: XCD-contiguous ranges, then groups of 8 M-tiles
   const int n_tiles = p.tiles_m * p.tiles_n;
@@ -89,7 +97,7 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(GemmArgs p) {
   const int tn = (tile % width) / gsz;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / NWN, wn = wave % NWN;
   const int K = p.K;
 
   // rows [row_base, row_base + row_cnt) of C belong to this tile
@@ -103,92 +111,101 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(GemmArgs p) {
     W += (size_t)grp * p.w_group_stride;
   }
 
-  // ---- global load assignment: thread -> (row, 16-byte chunk)
-  const int ld_ch = tid & 7, ld_row = tid >> 3;  // rows ld_row + 32 i
-  const bf16_t* a_src[8];
+  // ---- loads: global -> LDS directly (global_load_lds_dwordx4, no VGPR staging).
+  // One such load of a wave fills 64 consecutive 16-byte LDS chunks, lane l the
+  // l-th, so the XOR swizzle is applied on the global side: the lane whose LDS
+  // chunk position is P loads logical chunk (P % 8) ^ ((row >> 1) & 7) of row
+  // P / 8 of the stacked [A tile; B tile].  Wave w issues loads i = 0..NL-1
+  // covering positions (w * NL + i) * 64 + lane (waves 0-3: A, 4-7: B).
+  constexpr int NL = STAGE / 64 / (THREADS / 64);
+  const bf16_t* src[NL];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    // rows past the tile's end duplicate its last row and are never stored
-    int r = row_base + min(ld_row + 32 * i, row_cnt - 1);
-    if constexpr (GATHER) r = p.a_rows[r] / p.a_div;
-    a_src[i] = p.A + (size_t)r * K + ld_ch * 8;
-  }
-  const bf16_t* b_src[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = ld_row + 32 * i;
-    int n;
-    if constexpr (KIND == K_SILU) {
-      const int I = p.N >> 1;
-      n = (r < 64) ? tn * 64 + r : I + tn * 64 + (r - 64);
+  for (int i = 0; i < NL; ++i) {
+    const int P = (wave * NL + i) * 64 + lane;
+    const int row = P / KCH;
+    const int ch = (P % KCH) ^ ((row >> 1) & 7);
+    if (row < BM) {
+      // rows past the tile's end duplicate its last row and are never stored
+      int r = row_base + min(row, row_cnt - 1);
+      if constexpr (GATHER) r = p.a_rows[r] / p.a_div;
+      src[i] = p.A + (size_t)r * K + ch * 8;
     } else {
-      n = min(tn * BN + r, p.N - 1);  // columns past N are masked in the epilogue
+      const int br = row - BM;
+      int n;
+      if constexpr (KIND == K_SILU) {
+        const int I = p.N >> 1;
+        n = (br < BN / 2) ? tn * (BN / 2) + br : I + tn * (BN / 2) + (br - BN / 2);
+      } else {
+        n = min(tn * BN + br, p.N - 1);  // columns past N are masked in the epilogue
+      }
+      src[i] = W + (size_t)n * K + ch * 8;
     }
-    b_src[i] = W + (size_t)n * K + ld_ch * 8;
   }
-
-  f32x4_t acc[8][4];
+  auto issue = [&](int st, int k0) {
 #pragma unroll
-  for (int mi = 0; mi < 8; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  u32x4_t ra[8], rb[4];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(a_src[i] + k0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) rb[i] = *reinterpret_cast<const u32x4_t*>(b_src[i] + k0);
-  };
-  auto sstore = [&]() {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) As[swz(ld_row + 32 * i, ld_ch)] = ra[i];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) Bs[swz(ld_row + 32 * i, ld_ch)] = rb[i];
+    for (int i = 0; i < NL; ++i)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(src[i] + k0),
+          (__attribute__((address_space(3))) void*)(smem + st * STAGE + (wave * NL + i) * 64), 16, 0,
+          0);
   };
 
-  const int nk = K / BK;
-  gload(0);
-  sstore();
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) gload((kt + 1) * BK);
+  f32x4_t acc[MI][NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int st) {
+    const u32x4_t* As = smem + st * STAGE;
+    const u32x4_t* Bs = As + BM * KCH;
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {
       const int ch = ks * 4 + (lane >> 4);
-      bf16x8_t fa[8], fb[4];
+      bf16x8_t fa[MI], fb[NI];
 #pragma unroll
-      for (int mi = 0; mi < 8; ++mi)
-        fa[mi] = __builtin_bit_cast(bf16x8_t, As[swz(wm * 128 + mi * 16 + (lane & 15), ch)]);
+      for (int mi = 0; mi < MI; ++mi)
+        fa[mi] = __builtin_bit_cast(bf16x8_t, As[swz(wm * WTM + mi * 16 + (lane & 15), ch)]);
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
+      for (int ni = 0; ni < NI; ++ni)
         fb[ni] = __builtin_bit_cast(bf16x8_t, Bs[swz(b_lds_row<KIND>(wn, ni) + (lane & 15), ch)]);
 #pragma unroll
-      for (int mi = 0; mi < 8; ++mi)
+      for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
+        for (int ni = 0; ni < NI; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
     }
+  };
+
+  // two-buffer pipeline, one barrier per slab: slab kt+1 is loaded into the
+  // other buffer while slab kt is multiplied; the barrier after the wait both
+  // publishes slab kt+1 and frees buffer kt&1 for slab kt+2.
+  const int nk = K / BK;
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) issue((kt + 1) & 1, (kt + 1) * BK);
+    __builtin_amdgcn_s_setprio(1);
+    compute(kt & 1);
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's loads of slab kt+1 have landed
     __syncthreads();
-    if (kt + 1 < nk) {
-      sstore();
-      __syncthreads();
-    }
   }
 
   // ---- epilogues.  Lane holds C[4*(lane>>4) + r][lane & 15] of each 16x16 block.
-  const int lrow0 = wm * 128 + 4 * (lane >> 4);  // row within the tile
+  const int lrow0 = wm * WTM + 4 * (lane >> 4);  // row within the tile
   const int row0 = row_base + lrow0;
   if constexpr (KIND == K_BF16 || KIND == K_F32) {
 #pragma unroll
-    for (int mi = 0; mi < 8; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = row0 + mi * 16 + r;
         if (lrow0 + mi * 16 + r < row_cnt) {
 #pragma unroll
-          for (int ni = 0; ni < 4; ++ni) {
-            const int col = tn * BN + wn * 64 + ni * 16 + (lane & 15);
+          for (int ni = 0; ni < NI; ++ni) {
+            const int col = tn * BN + wn * WTN + ni * 16 + (lane & 15);
             if (col >= p.N) continue;
             if constexpr (KIND == K_BF16)
               reinterpret_cast<bf16_t*>(p.C)[(size_t)row * p.N + col] = f2bf(acc[mi][ni][r]);
@@ -200,79 +217,83 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(GemmArgs p) {
   } else if constexpr (KIND == K_SILU) {
     const int I = p.N >> 1;
 #pragma unroll
-    for (int mi = 0; mi < 8; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = row0 + mi * 16 + r;
         if (lrow0 + mi * 16 + r < row_cnt) {
 #pragma unroll
-          for (int ni = 0; ni < 2; ++ni) {
-            const int col = tn * 64 + wn * 32 + ni * 16 + (lane & 15);
+          for (int ni = 0; ni < NI / 2; ++ni) {
+            const int col = tn * (BN / 2) + wn * (WTN / 2) + ni * 16 + (lane & 15);
             const float g = bf2f(f2bf(acc[mi][ni][r]));
-            const float u = bf2f(f2bf(acc[mi][ni + 2][r]));
+            const float u = bf2f(f2bf(acc[mi][ni + NI / 2][r]));
             reinterpret_cast<bf16_t*>(p.C)[(size_t)row * I + col] = f2bf(silu_f32(g) * u);
           }
         }
       }
-  } else {  // K_LMHEAD: per row, (max, sum exp) over this 128-column vocab chunk
+  } else {  // K_LMHEAD: per row, (max, sum exp) over this 256-column vocab chunk
+    // Row lr's chunk max is max over the NWN waves of redm[w][lr]; its sum is
+    // s_0 + s_1 (+ ...) over reds[w][lr] in wave order; within a wave the
+    // columns reduce over the NI sub-blocks in order, then a fixed xor butterfly.
     const int V = p.N;
-    float* red = reinterpret_cast<float*>(smem);  // [2][BM]
-    float mc[8][4];
-    __syncthreads();
+    float* redm = reinterpret_cast<float*>(smem);  // [NWN][BM]; the loop ended on a barrier
+    float* reds = redm + NWN * BM;                  // [NWN][BM]
 #pragma unroll
-    for (int mi = 0; mi < 8; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float mx = -INFINITY;
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-          const int col = tn * BN + wn * 64 + ni * 16 + (lane & 15);
+        for (int ni = 0; ni < NI; ++ni) {
+          const int col = tn * BN + wn * WTN + ni * 16 + (lane & 15);
           mx = fmaxf(mx, col < V ? acc[mi][ni][r] : -INFINITY);
         }
 #pragma unroll
         for (int o = 1; o <= 8; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, WAVE));
-        if ((lane & 15) == 0) red[wn * BM + wm * 128 + mi * 16 + 4 * (lane >> 4) + r] = mx;
+        if ((lane & 15) == 0) redm[wn * BM + lrow0 + mi * 16 + r] = mx;
       }
     __syncthreads();
 #pragma unroll
-    for (int mi = 0; mi < 8; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int lr = wm * 128 + mi * 16 + 4 * (lane >> 4) + r;
-        mc[mi][r] = fmaxf(red[lr], red[BM + lr]);
-      }
-    __syncthreads();
+        const int lr = lrow0 + mi * 16 + r;
+        float m = redm[lr];
 #pragma unroll
-    for (int mi = 0; mi < 8; ++mi)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
+        for (int w2 = 1; w2 < NWN; ++w2) m = fmaxf(m, redm[w2 * BM + lr]);
         float s = 0.0f;
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-          const int col = tn * BN + wn * 64 + ni * 16 + (lane & 15);
-          const float e = col < V ? fexp(acc[mi][ni][r] - mc[mi][r]) : 0.0f;
+        for (int ni = 0; ni < NI; ++ni) {
+          const int col = tn * BN + wn * WTN + ni * 16 + (lane & 15);
+          const float e = col < V ? fexp(acc[mi][ni][r] - m) : 0.0f;
           s = s + e;
         }
 #pragma unroll
         for (int o = 1; o <= 8; o <<= 1) s = s + __shfl_xor(s, o, WAVE);
-        if ((lane & 15) == 0) red[wn * BM + wm * 128 + mi * 16 + 4 * (lane >> 4) + r] = s;
+        if ((lane & 15) == 0) reds[wn * BM + lr] = s;
       }
     __syncthreads();
 #pragma unroll
-    for (int mi = 0; mi < 8; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int lr = wm * 128 + mi * 16 + 4 * (lane >> 4) + r;
+        const int lr = lrow0 + mi * 16 + r;
         const int row = row_base + lr;
         if (lr < row_cnt) {
           if (wn == 0 && (lane & 15) == 0) {
-            p.part_m[(size_t)tn * p.M + row] = mc[mi][r];
-            p.part_s[(size_t)tn * p.M + row] = red[lr] + red[BM + lr];
+            float m = redm[lr], s = reds[lr];
+#pragma unroll
+            for (int w2 = 1; w2 < NWN; ++w2) {
+              m = fmaxf(m, redm[w2 * BM + lr]);
+              s = s + reds[w2 * BM + lr];
+            }
+            p.part_m[(size_t)tn * p.M + row] = m;
+            p.part_s[(size_t)tn * p.M + row] = s;
           }
           const int id = p.ids[row];
 #pragma unroll
-          for (int ni = 0; ni < 4; ++ni) {
-            const int col = tn * BN + wn * 64 + ni * 16 + (lane & 15);
+          for (int ni = 0; ni < NI; ++ni) {
+            const int col = tn * BN + wn * WTN + ni * 16 + (lane & 15);
             if (col == id) p.zid[row] = acc[mi][ni][r];
           }
         }
@@ -304,7 +325,7 @@ hipError_t launch_gemm(const void* A, const int32_t* a_rows, const void* W, void
   a.K = K;
   a.a_div = 1;
   a.tiles_m = (M + BM - 1) / BM;
-  a.tiles_n = (epi == EPI_SILU) ? (N / 2) / 64 : (N + BN - 1) / BN;
+  a.tiles_n = (epi == EPI_SILU) ? (N / 2) / (BN / 2) : (N + BN - 1) / BN;
   switch (epi) {
     case EPI_BF16: return dispatch<K_BF16>(a, a_rows != nullptr, s);
     case EPI_F32: return dispatch<K_F32>(a, a_rows != nullptr, s);
@@ -328,7 +349,7 @@ hipError_t launch_gemm_grouped(const void* A, const int32_t* a_rows, int a_div, 
   a.N = N;
   a.K = K;
   a.tiles_m = max_mtiles;
-  a.tiles_n = (epi == EPI_SILU) ? (N / 2) / 64 : (N + BN - 1) / BN;
+  a.tiles_n = (epi == EPI_SILU) ? (N / 2) / (BN / 2) : (N + BN - 1) / BN;
   a.gtiles = gtiles;
   a.n_gtiles = n_gtiles;
   a.w_group_stride = w_group_stride;

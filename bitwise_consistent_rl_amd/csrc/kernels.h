@@ -30,7 +30,7 @@ hipError_t launch_gemm_grouped(const void* A, const int32_t* a_rows, int a_div, 
                                size_t w_group_stride, void* C, const int32_t* gtiles,
                                const int32_t* n_gtiles, int max_mtiles, int N, int K, int epi,
                                hipStream_t s);
-// lm_head partials: for each row i < M and vocab chunk c (128 columns):
+// lm_head partials: for each row i < M and vocab chunk c (256 columns):
 // part_m[c * M + i] = max_j z_ij, part_s[c * M + i] = sum_j exp(z_ij - max),
 // and zid[i] = z[i, ids[i]].
 hipError_t launch_lmhead_partials(const void* A, const int32_t* a_rows, const void* E,
@@ -38,9 +38,9 @@ hipError_t launch_lmhead_partials(const void* A, const int32_t* a_rows, const vo
                                   float* part_s, float* zid, hipStream_t s);
 hipError_t launch_lmhead_combine(const float* part_m, const float* part_s, const float* zid,
                                  const int32_t* ids, int M, int V, float* lp, hipStream_t s);
-constexpr int LM_CHUNK = 128;
+constexpr int LM_CHUNK = 256;
 constexpr int GEMM_BM = 256;
-constexpr int GEMM_BN = 128;
+constexpr int GEMM_BN = 256;
 constexpr int GEMM_BK = 64;
 
 // ---- rope_kv.hip

@@ -40,7 +40,7 @@
  *     chunked prefill and decode alike.
  *   - FP8 KV (e4m3fn, per-token-per-head fp32 scale): every phase quantises
  *     through one rule and reads keys/values back as bf(fp32(code) * scale).
- *   - lm_head: fp32 logits never materialised; per 128-column vocab chunk a
+ *   - lm_head: fp32 logits never materialised; per 256-column vocab chunk a
  *     (max, sum-exp) pair; the pairs are merged in one fixed order that depends
  *     only on the vocabulary size (8 contiguous chunk ranges, each ascending,
  *     then the 8 range results in order).
@@ -87,7 +87,7 @@ typedef struct {
   int32_t max_position;        /* context capacity per sequence (RoPE table size)  */
   int32_t mode;                /* bci_mode; fixed for the life of the context      */
   /* MoE layer (0 experts = dense only).  n_experts <= 64, 1 <= top_k <= min(8,
-   * n_experts), expert_intermediate % 64 == 0, n_shared_experts 0 or 1.  The
+   * n_experts), expert_intermediate % 128 == 0, n_shared_experts 0 or 1.  The
    * MoE entry points use `hidden` as the model width and size their workspace
    * for max_tokens_per_call * top_k routed rows. */
   int32_t n_experts, top_k, expert_intermediate, n_shared_experts;
@@ -177,7 +177,7 @@ bci_status bci_op_add_rmsnorm(bci_ctx* ctx, const void* a, void* r, void* h, con
  *   BCI_EPI_F32:      C [M, N] fp32 = acc
  *   BCI_EPI_SILU_MUL: W holds gate rows then up rows (N = 2 I); C [M, I] bf16 =
  *                     bf(silu(bf(acc_gate)) * bf(acc_up))   (fused SiLU MLP)
- * K % 64 == 0; N >= 1 (BCI_EPI_SILU_MUL: I % 64 == 0); M >= 0. */
+ * K % 64 == 0; N >= 1 (BCI_EPI_SILU_MUL: I % 128 == 0); M >= 0. */
 bci_status bci_op_gemm_bf16(bci_ctx* ctx, const void* A, const void* W, void* C, int32_t M,
                             int32_t N, int32_t K, int32_t epilogue, void* stream);
 

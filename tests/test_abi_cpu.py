@@ -56,10 +56,10 @@ def _cfg(**kw):
                                  dict(kv_block_tokens=32), dict(attn_segment_keys=100),
                                  dict(max_tokens_per_call=0), dict(kv_dtype=7), dict(mode=9),
                                  dict(intermediate=700), dict(n_q_heads=128, n_kv_heads=1),
-                                 dict(n_experts=65, top_k=2, expert_intermediate=64),
-                                 dict(n_experts=64, top_k=9, expert_intermediate=64),
+                                 dict(n_experts=65, top_k=2, expert_intermediate=128),
+                                 dict(n_experts=64, top_k=9, expert_intermediate=128),
                                  dict(n_experts=8, top_k=2, expert_intermediate=100),
-                                 dict(n_experts=8, top_k=2, expert_intermediate=64,
+                                 dict(n_experts=8, top_k=2, expert_intermediate=128,
                                       n_shared_experts=2)])
 def test_create_rejects_bad_config_before_any_device_call(lib, bad):
     from bitwise_consistent_rl_amd import _abi

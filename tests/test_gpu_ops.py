@@ -74,7 +74,7 @@ def test_gemm_f32_epilogue_parity(ctx):
 
 
 def test_gemm_silu_mul_epilogue_parity(ctx):
-    M, I, K = 77, 192, 256
+    M, I, K = 77, 384, 256
     a, w = synth.gemm_inputs(M, 2 * I, K, index=12, w_scale=0.1)
     C = gemm(ctx, cuda(a), cuda(w), abi().BCI_EPI_SILU_MUL, out_cols=I)
     A, W = f64(a), f64(w)
@@ -125,7 +125,7 @@ def test_gemm_rejects_bad_shapes(ctx):
     with pytest.raises(a_.BciError):
         a_.bci_op_gemm_bf16(ctx, x, x, x, 4, 128, 48, a_.BCI_EPI_BF16)   # K % 64
     with pytest.raises(a_.BciError):
-        a_.bci_op_gemm_bf16(ctx, x, x, x, 4, 192, 64, a_.BCI_EPI_SILU_MUL)   # I % 64
+        a_.bci_op_gemm_bf16(ctx, x, x, x, 4, 384, 64, a_.BCI_EPI_SILU_MUL)   # I % 128
     with pytest.raises(a_.BciError):
         a_.bci_op_gemm_bf16(ctx, x, x, x, 4, 128, 64, 7)   # unknown epilogue
 
