@@ -101,6 +101,106 @@ def micro(args, cfg):
                       "copy_bytes": 2 * (1 << 30)}), flush=True)
 
 
+def longctx(args):
+    """FP8-KV attention at 8K / 32K / 57K context (32 q / 4 kv heads of 128, e4m3 cache
+    with per-token-per-head scales, KV segments of 1024 keys).  For each context: a
+    decode step (one new query per sequence) at B = 1, 4, 16, 64 with the other
+    sequences' lengths uniform in [C/2, C], and a chunked prefill (chunk 2048) of one
+    sequence.  Decode is HBM-bound: 1056 B of K/V codes and scales per context token
+    (2 x 4 heads x (128 + 4) B) plus 16 KiB of q and o per sequence."""
+    import numpy as np
+    import torch
+    import synth
+    from bitwise_consistent_rl_amd import _abi as abi
+    NQ, NKV, D, SEG = 32, 4, 128, 1024
+    width = (NQ + 2 * NKV) * D
+    rng = np.random.default_rng(5678)
+    qkv = synth.normal_bf16((57344 + 64 * 131, width), index=60).cuda()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    for C in (8192, 32768, 57344):
+        lengths = [C] + [int(x) for x in rng.integers(C // 2, C + 1, size=63)]
+        mc = abi.ModelConfig()
+        for k, v in dict(n_layers=1, hidden=512, n_q_heads=NQ, n_kv_heads=NKV, head_dim=D,
+                         intermediate=512, vocab=128, rms_eps=1e-6, rope_theta=1e6,
+                         kv_dtype=abi.BCI_KV_FP8_E4M3, kv_block_tokens=64, attn_segment_keys=SEG,
+                         max_tokens_per_call=8192, max_seqs_per_call=64, max_scored_per_call=1,
+                         max_position=C + 64).items():
+            setattr(mc, k, v)
+        ctx = abi.bci_create(mc, 0)
+        blocks, nxt = [], 0
+        for L in lengths:
+            blocks.append(list(range(nxt, nxt + (L + 63) // 64)))
+            nxt += (L + 63) // 64
+        shape = (1, nxt, NKV, 64, D)
+        k = torch.empty(shape, dtype=torch.uint8, device="cuda")
+        v = torch.empty_like(k)
+        ks = torch.empty(shape[:-1], device="cuda")
+        vs = torch.empty_like(ks)
+        abi.bci_bind_kv_cache(ctx, k, v, ks, vs, nxt)
+        maxb = max(len(b) for b in blocks)
+
+        def batch(chunks):
+            T = sum(n for _, _, n in chunks)
+            cu = np.concatenate([[0], np.cumsum([n for _, _, n in chunks])]).astype(np.int32)
+            bt = np.array([blocks[s] + [0] * (maxb - len(blocks[s])) for s, _, _ in chunks], np.int32)
+            abi.bci_set_batch(ctx, np.zeros(T, np.int32), cu,
+                              np.array([p for _, p, _ in chunks], np.int32), bt, [], [])
+        # fill every sequence's cache (positions 0 .. L-2) through the FP8 writer
+        qbuf = torch.empty(8192, NQ * D, dtype=torch.bfloat16, device="cuda")
+        for sq, L in enumerate(lengths):
+            for s0 in range(0, L - 1, 8192):
+                n = min(8192, L - 1 - s0)
+                batch([(sq, s0, n)])
+                abi.bci_op_rope_kv_write(ctx, qkv[sq * 131 + s0: sq * 131 + s0 + n].contiguous(), qbuf, 0)
+        torch.cuda.synchronize()
+        log(f"context {C}: caches filled")
+        for B in (1, 4, 16, 64):
+            seqs = list(range(B))
+            rows = torch.cat([qkv[s * 131 + lengths[s] - 1: s * 131 + lengths[s]] for s in seqs]).contiguous()
+            q = torch.empty(B, NQ * D, dtype=torch.bfloat16, device="cuda")
+            o = torch.empty_like(q)
+            batch([(s, lengths[s] - 1, 1) for s in seqs])
+            abi.bci_op_rope_kv_write(ctx, rows, q, 0)
+            for _ in range(3):
+                abi.bci_op_attention(ctx, q, 0, o)
+            e0, e1 = ev(), ev()
+            reps = 20
+            e0.record()
+            for _ in range(reps):
+                abi.bci_op_attention(ctx, q, 0, o)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            ctx_tokens = sum(lengths[s] for s in seqs)
+            nbytes = ctx_tokens * 1056 + B * 16384
+            print(json.dumps({"workload": "fp8-kv long-context decode step", "context": C, "batch": B,
+                              "context_tokens": ctx_tokens, "us_per_step": round(us, 2),
+                              "tokens_per_s": round(B / us * 1e6, 1),
+                              "roofline": {"bound": "hbm", "achieved": round(nbytes / us / 1e3, 1),
+                                           "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                           "frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4)}}),
+                  flush=True)
+        # chunked prefill of sequence 0 (chunk 2048), attention included
+        q = torch.empty(2048, NQ * D, dtype=torch.bfloat16, device="cuda")
+        o = torch.empty_like(q)
+        e0, e1 = ev(), ev()
+        e0.record()
+        for s0 in range(0, C, 2048):
+            batch([(0, s0, 2048)])
+            abi.bci_op_rope_kv_write(ctx, qkv[s0: s0 + 2048].contiguous(), q, 0)
+            abi.bci_op_attention(ctx, q, 0, o)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        flops = 4.0 * NQ * D * C * (C + 1) / 2
+        print(json.dumps({"workload": "fp8-kv chunked prefill (2048)", "context": C, "ms": round(ms, 2),
+                          "roofline": {"bound": "mfma", "achieved": round(flops / ms / 1e9, 1),
+                                       "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                       "frac": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}}), flush=True)
+        abi.bci_destroy(ctx)
+        del k, v, ks, vs
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -113,6 +213,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--micro", choices=["gate_up"], default=None,
                     help="time one kernel alone at the workload's shape (for counter runs)")
+    ap.add_argument("--workload", choices=["recompute", "longctx"], default="recompute",
+                    help="longctx: FP8-KV long-context attention (decode steps, chunked prefill)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: every sequence is independent, so N GPUs would "
@@ -130,6 +232,8 @@ def main():
     cfg = synth.QWEN3_1P7B
     if args.micro:
         return micro(args, cfg)
+    if args.workload == "longctx":
+        return longctx(args)
     log("generating weights and workload")
     weights = synth.make_weights(cfg)
     seqs = synth.rl_sequences(cfg, n_prompts=args.prompts, n_responses=args.responses)

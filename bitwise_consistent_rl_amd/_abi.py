@@ -49,7 +49,8 @@ class ModelConfig(ctypes.Structure):
                [(n, ctypes.c_int32) for n in
                 ("kv_dtype", "kv_block_tokens", "attn_segment_keys", "max_tokens_per_call",
                  "max_seqs_per_call", "max_scored_per_call", "max_position", "mode",
-                 "n_experts", "top_k", "expert_intermediate", "n_shared_experts")]
+                 "n_experts", "top_k", "expert_intermediate", "n_shared_experts",
+                 "attn_split_mode")]
 
 
 _P32 = ctypes.POINTER(ctypes.c_int32)

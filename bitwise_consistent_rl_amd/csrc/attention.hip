@@ -128,7 +128,7 @@ __device__ __forceinline__ void load_chunk(const AttnArgs& p, int blk, int g, in
   }
 }
 
-template <int D, bool FP8>
+template <int D, bool FP8, bool SPLIT>
 __global__ __launch_bounds__(ATHREADS, 2) void attention_kernel(AttnArgs p) {
   __shared__ __attribute__((aligned(16))) u32x4_t Ks[CHUNK * D / 8];
   __shared__ __attribute__((aligned(16))) bf16_t Vt[D * VT_STRIDE];
@@ -170,7 +170,14 @@ __global__ __launch_bounds__(ATHREADS, 2) void attention_kernel(AttnArgs p) {
 
   const int last_chunk = kmax / CHUNK;
   const int seg_chunks = p.seg_keys / CHUNK;
-  for (int c0 = 0; c0 <= last_chunk; c0 += seg_chunks) {
+  int c_first = 0, c_stop = last_chunk;
+  if constexpr (SPLIT) {
+    // this workgroup computes one segment only; its partial goes to the workspace
+    c_first = blockIdx.z * seg_chunks;
+    if (c_first > last_chunk) return;
+    c_stop = min(c_first + seg_chunks - 1, last_chunk);
+  }
+  for (int c0 = c_first; c0 <= c_stop; c0 += seg_chunks) {
     const int c1 = min(c0 + seg_chunks - 1, last_chunk);
     float m = -INFINITY, l = 0.0f;
     f32x4_t acc[D / 16];
@@ -248,6 +255,20 @@ __global__ __launch_bounds__(ATHREADS, 2) void attention_kernel(AttnArgs p) {
         }
       }
     }
+    if constexpr (SPLIT) {
+      if (row_ok) {
+        const size_t prow = ((size_t)blockIdx.z * p.n_tokens + tok_begin + tk) * p.nq + hq;
+        float* pa = p.part_acc + prow * D;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt)
+          *reinterpret_cast<f32x4_t*>(pa + dt * 16 + 4 * lg) = acc[dt];
+        if (lg == 0) {
+          p.part_ml[prow * 2] = m;
+          p.part_ml[prow * 2 + 1] = l;
+        }
+      }
+      return;
+    }
     // merge the segment into the running state (ascending segment order)
     const float Mn = fmaxf(M, m);
     const float Mu = (Mn == -INFINITY) ? 0.0f : Mn;
@@ -272,19 +293,53 @@ __global__ __launch_bounds__(ATHREADS, 2) void attention_kernel(AttnArgs p) {
   }
 }
 
+// Split schedule, second pass: for each (token, head) row merge segments
+// 0 .. pos / S in ascending order with exactly the expressions of the
+// in-workgroup merge above (a later, fully masked segment of a deeper tile is
+// an exact no-op there), then o = bf(ACC / L).  One thread per output element.
+template <int D>
+__global__ __launch_bounds__(256) void attention_merge_kernel(AttnArgs p) {
+  const int t = blockIdx.x;
+  const int h = blockIdx.y * (256 / D) + threadIdx.x / D;
+  const int d = threadIdx.x % D;
+  if (h >= p.nq) return;
+  const int nseg = p.tok_pos[t] / p.seg_keys + 1;
+  float M = -INFINITY, L = 0.0f, ACC = 0.0f;
+  for (int z = 0; z < nseg; ++z) {
+    const size_t prow = ((size_t)z * p.n_tokens + t) * p.nq + h;
+    const float m = p.part_ml[prow * 2], l = p.part_ml[prow * 2 + 1];
+    const float a_ = p.part_acc[prow * D + d];
+    const float Mn = fmaxf(M, m);
+    const float Mu = (Mn == -INFINITY) ? 0.0f : Mn;
+    const float a = fexp2(M - Mu), b = fexp2(m - Mu);
+    L = L * a + l * b;
+    ACC = ACC * a + a_ * b;
+    M = Mn;
+  }
+  reinterpret_cast<bf16_t*>(p.o)[((size_t)t * p.nq + h) * D + d] = f2bf(ACC / L);
+}
+
+template <int D, bool FP8>
+static void launch_d(const AttnArgs& a, hipStream_t s) {
+  if (a.n_seg > 0) {
+    hipLaunchKernelGGL((attention_kernel<D, FP8, true>), dim3(a.n_tiles, a.nkv, a.n_seg),
+                       dim3(ATHREADS), 0, s, a);
+    hipLaunchKernelGGL((attention_merge_kernel<D>), dim3(a.n_tokens, (a.nq * D + 255) / 256),
+                       dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((attention_kernel<D, FP8, false>), dim3(a.n_tiles, a.nkv), dim3(ATHREADS),
+                       0, s, a);
+  }
+}
+
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   if (a.n_tiles == 0) return hipSuccess;
-  const dim3 grid(a.n_tiles, a.nkv);
   if (a.d == 128) {
-    if (a.fp8)
-      hipLaunchKernelGGL((attention_kernel<128, true>), grid, dim3(ATHREADS), 0, s, a);
-    else
-      hipLaunchKernelGGL((attention_kernel<128, false>), grid, dim3(ATHREADS), 0, s, a);
+    if (a.fp8) launch_d<128, true>(a, s);
+    else launch_d<128, false>(a, s);
   } else if (a.d == 64) {
-    if (a.fp8)
-      hipLaunchKernelGGL((attention_kernel<64, true>), grid, dim3(ATHREADS), 0, s, a);
-    else
-      hipLaunchKernelGGL((attention_kernel<64, false>), grid, dim3(ATHREADS), 0, s, a);
+    if (a.fp8) launch_d<64, true>(a, s);
+    else launch_d<64, false>(a, s);
   } else {
     return hipErrorInvalidValue;
   }

@@ -49,6 +49,9 @@ struct bci_ctx {
   uint16_t *moe_act = nullptr, *moe_y = nullptr, *moe_act_s = nullptr, *moe_y_s = nullptr;
   int moe_max_mtiles = 0;
   float *rope_cos = nullptr, *rope_sin = nullptr;
+  // split-attention partials: [max_seg][split_tokens][nq][d] and [..][2]
+  float *attn_part_acc = nullptr, *attn_part_ml = nullptr;
+  int max_seg = 1, split_tokens = 0;
   int32_t* meta = nullptr;  // device metadata region
   size_t meta_words = 0;
   // metadata offsets (int32 words)
@@ -68,7 +71,7 @@ struct bci_ctx {
   bool cache_bound = false;
   // current batch (host copy of what was uploaded)
   bool batch_valid = false;
-  int n_seqs = 0, n_tokens = 0, n_scored = 0, n_tiles = 0;
+  int n_seqs = 0, n_tokens = 0, n_scored = 0, n_tiles = 0, batch_seg = 1;
   std::vector<int32_t> h_cu, h_pos0, h_btab;  // h_btab with stride max_blocks
   // profiling of the gate_up GEMM launches (HIP events on the launch stream)
   bool prof_on = false;
@@ -137,6 +140,7 @@ bci_status bci_create(const bci_model_config* cfg_in, int32_t device, bci_ctx** 
       (g.top_k < 1 || g.top_k > MOE_MAX_K || g.top_k > g.n_experts || g.expert_intermediate < 128 ||
        g.expert_intermediate % 128 || g.n_shared_experts < 0 || g.n_shared_experts > 1))
     return BCI_E_INVALID;
+  if (g.attn_split_mode < 0 || g.attn_split_mode > 2) return BCI_E_INVALID;
   if (g.mode == BCI_MODE_FAST) return BCI_E_UNSUPPORTED;
   if (g.mode != BCI_MODE_INVARIANT) return BCI_E_INVALID;
   if (hipSetDevice(device) != hipSuccess) return BCI_E_HIP;
@@ -183,6 +187,13 @@ bci_status bci_create(const bci_model_config* cfg_in, int32_t device, bci_ctx** 
       {(void**)&c->rope_sin, (size_t)g.max_position * (g.head_dim / 2) * 4},
       {(void**)&c->meta, c->meta_words * 4},
   };
+  c->max_seg = (g.max_position + g.attn_segment_keys - 1) / g.attn_segment_keys;
+  if (c->max_seg > 1 && g.attn_split_mode != 1) {
+    c->split_tokens = g.max_seqs_per_call;
+    const size_t rows = (size_t)c->max_seg * c->split_tokens * g.n_q_heads;
+    parts.push_back({(void**)&c->attn_part_acc, rows * g.head_dim * 4});
+    parts.push_back({(void**)&c->attn_part_ml, rows * 2 * 4});
+  }
   if (g.n_experts > 0) {
     const size_t P = T * (size_t)g.top_k, I = g.expert_intermediate;
     c->moe_max_mtiles = (int)((P + GEMM_BM - 1) / GEMM_BM) + g.n_experts;
@@ -337,9 +348,12 @@ bci_status bci_set_batch(bci_ctx* c, const bci_batch* b, void* stream) {
     if (b->score_ids[r] < 0 || b->score_ids[r] >= g.vocab)
       return fail(c, BCI_E_INVALID, "set_batch: score id %d = %d outside [0, %d)", r, b->score_ids[r], g.vocab);
   }
-  // count tiles
-  int n_tiles = 0;
-  for (int i = 0; i < b->n_seqs; ++i) n_tiles += (b->cu_q[i + 1] - b->cu_q[i] + c->tpt - 1) / c->tpt;
+  // count tiles and the deepest segment
+  int n_tiles = 0, bseg = 1;
+  for (int i = 0; i < b->n_seqs; ++i) {
+    n_tiles += (b->cu_q[i + 1] - b->cu_q[i] + c->tpt - 1) / c->tpt;
+    bseg = std::max(bseg, (b->pos0[i] + b->cu_q[i + 1] - b->cu_q[i] - 1) / g.attn_segment_keys + 1);
+  }
   if (n_tiles > c->max_tiles) return fail(c, BCI_E_WORKSPACE, "set_batch: %d attention tiles > %d", n_tiles, c->max_tiles);
 
   // wait until the staging slot's previous upload has been consumed
@@ -385,6 +399,7 @@ bci_status bci_set_batch(bci_ctx* c, const bci_batch* b, void* stream) {
   c->n_tokens = b->n_tokens;
   c->n_scored = b->n_scored;
   c->n_tiles = n_tiles;
+  c->batch_seg = bseg;
   c->batch_valid = true;
   return BCI_OK;
 }
@@ -420,6 +435,15 @@ static bci_status op_attn(bci_ctx* c, const void* q, void* o, int layer, hipStre
   a.seg_keys = g.attn_segment_keys;
   a.fp8 = g.kv_dtype == BCI_KV_FP8_E4M3;
   a.scale_log2 = (float)(1.0 / std::sqrt((double)g.head_dim) * 1.4426950408889634);
+  a.tok_pos = c->meta + c->o_pos;
+  a.n_tokens = c->n_tokens;
+  // schedule: split the KV segments across workgroups when the call has few
+  // query tiles (decode, short chunks); bits are the same either way
+  const bool can_split = c->attn_part_acc && c->batch_seg > 1 && c->n_tokens <= c->split_tokens;
+  const bool want_split = g.attn_split_mode == 2 || (g.attn_split_mode == 0 && c->n_tiles * g.n_kv_heads < 1024);
+  a.n_seg = (can_split && want_split) ? c->batch_seg : 0;
+  a.part_acc = c->attn_part_acc;
+  a.part_ml = c->attn_part_ml;
   HIP_TRY(c, launch_attention(a, s));
   return BCI_OK;
 }

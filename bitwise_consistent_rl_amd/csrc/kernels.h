@@ -64,9 +64,16 @@ struct AttnArgs {
   KvLayer kv;
   const int32_t* tiles;        // [n_tiles, 4]: seq, tok_begin, n_tok, pos_begin
   const int32_t* block_table;  // [n_seqs, max_blocks]
+  const int32_t* tok_pos;      // [T] absolute position of each token (split merge)
   int n_tiles, max_blocks, nq, nkv, d, seg_keys;
   bool fp8;
   float scale_log2;            // (1/sqrt(d)) * log2(e), fp32
+  // split schedule: one workgroup per (tile, kv head, segment) writes the
+  // segment's (m, l, acc) to part_* and a merge kernel combines segments in
+  // ascending order; n_seg = segments of the deepest tile (0: no split).
+  int n_seg, n_tokens;
+  float* part_acc;             // [n_seg][T][nq][d]
+  float* part_ml;              // [n_seg][T][nq][2]
 };
 constexpr int ATTN_ROWS = 64;  // query rows (token x head-in-group) per tile
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);

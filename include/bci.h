@@ -91,6 +91,11 @@ typedef struct {
    * MoE entry points use `hidden` as the model width and size their workspace
    * for max_tokens_per_call * top_k routed rows. */
   int32_t n_experts, top_k, expert_intermediate, n_shared_experts;
+  /* Attention schedule (never changes a bit, only where the work runs):
+   * 0 = auto (split a call's KV segments across workgroups when it has few
+   * query tiles and at most max_seqs_per_call tokens), 1 = never split,
+   * 2 = split whenever the workspace allows. */
+  int32_t attn_split_mode;
 } bci_model_config;
 
 /* One varlen forward call; HOST arrays.  Sequences are packed back to back:

@@ -19,7 +19,7 @@ def abi():
 
 
 def make_ctx(n_layers=1, hidden=2048, nq=16, nkv=8, d=128, inter=6144, vocab=151936, kv="bf16",
-             max_tokens=4096, max_seqs=64, max_scored=8192, max_position=2048, seg=2048):
+             max_tokens=4096, max_seqs=64, max_scored=8192, max_position=2048, seg=2048, split=0):
     a = abi()
     c = a.ModelConfig()
     for k, v in dict(n_layers=n_layers, hidden=hidden, n_q_heads=nq, n_kv_heads=nkv, head_dim=d,
@@ -27,7 +27,8 @@ def make_ctx(n_layers=1, hidden=2048, nq=16, nkv=8, d=128, inter=6144, vocab=151
                      kv_dtype=a.BCI_KV_FP8_E4M3 if kv == "fp8" else a.BCI_KV_BF16,
                      kv_block_tokens=64, attn_segment_keys=seg, max_tokens_per_call=max_tokens,
                      max_seqs_per_call=max_seqs, max_scored_per_call=max_scored,
-                     max_position=max_position, mode=a.BCI_MODE_INVARIANT).items():
+                     max_position=max_position, mode=a.BCI_MODE_INVARIANT,
+                     attn_split_mode=split).items():
         setattr(c, k, v)
     return a.bci_create(c, 0)
 
@@ -332,11 +333,12 @@ def test_rope_kv_write_and_gather(nq, nkv, d, kv):
         a_.bci_destroy(h)
 
 
-def _attention_run(nq, nkv, d, kv, seg, lengths, qkv, calls):
+def _attention_run(nq, nkv, d, kv, seg, lengths, qkv, calls, split=0):
     """Runs RoPE+KV write then attention for a sequence of calls, each a list of
     (seq, start, n) chunks; returns o for every (seq, position) and the rotated q."""
     a_ = abi()
-    h = make_ctx(hidden=512, nq=nq, nkv=nkv, d=d, inter=512, vocab=4096, kv=kv, seg=seg)
+    h = make_ctx(hidden=512, nq=nq, nkv=nkv, d=d, inter=512, vocab=4096, kv=kv, seg=seg,
+                 split=split)
     n_blocks = sum((L + 63) // 64 for L in lengths)
     cache = _alloc_cache(1, n_blocks, nkv, d, kv)
     a_.bci_bind_kv_cache(h, *cache, n_blocks)
@@ -410,13 +412,15 @@ def test_attention_prefill_decode_chunked_bitwise(nq, nkv, d, seg, kv):
     T = sum(lengths)
     qkv = synth.normal_bf16((T, (nq + 2 * nkv) * d), index=42)
     full = [[(i, 0, L) for i, L in enumerate(lengths)]]
-    o_ref, _, _ = _attention_run(nq, nkv, d, kv, seg, lengths, qkv, full)
-    # decode: one token per sequence per call, all sequences in each call
+    o_ref, _, _ = _attention_run(nq, nkv, d, kv, seg, lengths, qkv, full, split=1)
+    # decode: one token per sequence per call, all sequences in each call; the KV
+    # segments run in one workgroup each (split) or in sequence (never split)
     dec = []
     for t in range(max(lengths)):
         dec.append([(i, t, 1) for i, L in enumerate(lengths) if t < L])
-    o_dec, _, _ = _attention_run(nq, nkv, d, kv, seg, lengths, qkv, dec)
-    assert same_bits(o_dec, o_ref)
+    for split in (1, 2, 0):
+        o_dec, _, _ = _attention_run(nq, nkv, d, kv, seg, lengths, qkv, dec, split=split)
+        assert same_bits(o_dec, o_ref), split
     # chunked prefill with chunk 17 for seq 0 and 3, alone per call, others whole
     ch = [[(1, 0, 67)], [(2, 0, 1)]]
     for i in (0, 3):
