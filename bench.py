@@ -101,6 +101,84 @@ def micro(args, cfg):
                       "copy_bytes": 2 * (1 << 30)}), flush=True)
 
 
+def rollout_bench(args, cfg):
+    """Rollout side of the Qwen3-shaped workload, invariant vs non-invariant mode.
+
+    (1) Continuous batching of the first 128 sequences (16 prompts x 8 responses): each
+    step runs every active sequence's prompt (once) or next response token, and takes
+    the logprob of each response token as it is "sampled".  Wall-clock scored tokens/s,
+    host scheduling included, the same for both modes.  (2) One decode step (one new
+    token per sequence at its response midpoint) for B = 1, 16, 64, 128, timed with HIP
+    events.  The non-invariant mode splits small-M GEMMs over K with atomics and sizes
+    attention segments per call; its results are not batch-invariant."""
+    import numpy as np
+    import torch
+    import synth
+    from bitwise_consistent_rl_amd import _abi as abi
+    from bitwise_consistent_rl_amd import engine
+    weights = synth.make_weights(cfg)
+    seqs = synth.rl_sequences(cfg, n_prompts=16, n_responses=8)
+    results = {}
+    for mode in ("invariant", "fast"):
+        m = engine.Model(cfg, weights, max_tokens=8192, max_seqs=128, max_scored=8192,
+                         max_position=1024, mode=mode)
+        cache = m.new_cache(128 * 11 + 16)
+        engine.rollout(m, seqs[:8], cache, cap=8)           # warm-up
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        lp = engine.rollout(m, seqs, cache, cap=128)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        scored = sum(len(x) for x in lp)
+        steps = {}
+        for B in (1, 16, 64, 128):
+            sub = seqs[:B]
+            m.bind_cache(cache)
+            # prefill each sequence up to its response midpoint, then time one decode step
+            mids = [s.prompt_len + s.n_scored // 2 for s in sub]
+            blocks = [list(range(i * 11, i * 11 + 11)) for i in range(B)]
+            for g0 in range(0, B, 16):                       # prefill, <= 16 sequences per call
+                g = range(g0, min(B, g0 + 16))
+                plan = engine.CallPlan(np.concatenate([sub[i].tokens[:mids[i]] for i in g]).astype(np.int32),
+                                       np.concatenate([[0], np.cumsum([mids[i] for i in g])]).astype(np.int32),
+                                       np.zeros(len(g), np.int32), np.array([blocks[i] for i in g], np.int32),
+                                       np.zeros(0, np.int32), np.zeros(0, np.int32), [])
+                engine.run_call(m, plan)
+            dec = engine.CallPlan(np.array([s.tokens[mid] for s, mid in zip(sub, mids)], np.int32),
+                                  np.arange(B + 1, dtype=np.int32), np.array(mids, np.int32),
+                                  np.array(blocks, np.int32), np.arange(B, dtype=np.int32),
+                                  np.array([s.tokens[mid + 1] for s, mid in zip(sub, mids)], np.int32), [])
+            out = torch.empty(B, dtype=torch.float32, device="cuda")
+            abi.bci_set_batch(m.ctx, dec.tokens, dec.cu_q, dec.pos0, dec.block_table, dec.score_rows,
+                              dec.score_ids)
+            for _ in range(3):
+                abi.bci_forward_logprobs(m.ctx, out)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(10):
+                abi.bci_forward_logprobs(m.ctx, out)
+            e1.record()
+            torch.cuda.synchronize()
+            steps[B] = e0.elapsed_time(e1) / 10
+        results[mode] = dict(lp=lp, tokens_per_s=scored / dt, seconds=dt, scored=scored, steps=steps)
+        m.close()
+        del cache
+        torch.cuda.empty_cache()
+    inv, fast = results["invariant"], results["fast"]
+    stats = engine.acceptance(fast["lp"], inv["lp"])
+    weight_bytes = sum(v.numel() for v in weights.values()) * 2
+    print(json.dumps({
+        "workload": "qwen3-1.7b-shaped rollout, 16 prompts x 8 responses, continuous batching cap 128",
+        "scored_tokens": inv["scored"],
+        "invariant_tokens_per_s": round(inv["tokens_per_s"], 1),
+        "fast_tokens_per_s": round(fast["tokens_per_s"], 1),
+        "invariant_over_fast": round(inv["tokens_per_s"] / fast["tokens_per_s"], 4),
+        "decode_step_ms": {"invariant": {str(b): round(v, 3) for b, v in inv["steps"].items()},
+                           "fast": {str(b): round(v, 3) for b, v in fast["steps"].items()}},
+        "decode_roofline_ms": round(weight_bytes / (PEAK_HBM_GBS * 1e6), 3),
+        "fast_vs_invariant_logprobs": stats}), flush=True)
+
+
 def longctx(args):
     """FP8-KV attention at 8K / 32K / 57K context (32 q / 4 kv heads of 128, e4m3 cache
     with per-token-per-head scales, KV segments of 1024 keys).  For each context: a
@@ -213,8 +291,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--micro", choices=["gate_up"], default=None,
                     help="time one kernel alone at the workload's shape (for counter runs)")
-    ap.add_argument("--workload", choices=["recompute", "longctx"], default="recompute",
-                    help="longctx: FP8-KV long-context attention (decode steps, chunked prefill)")
+    ap.add_argument("--workload", choices=["recompute", "longctx", "rollout"], default="recompute",
+                    help="longctx: FP8-KV long-context attention (decode steps, chunked prefill); "
+                         "rollout: continuous-batching decode, invariant vs non-invariant mode")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: every sequence is independent, so N GPUs would "
@@ -234,6 +313,8 @@ def main():
         return micro(args, cfg)
     if args.workload == "longctx":
         return longctx(args)
+    if args.workload == "rollout":
+        return rollout_bench(args, cfg)
     log("generating weights and workload")
     weights = synth.make_weights(cfg)
     seqs = synth.rl_sequences(cfg, n_prompts=args.prompts, n_responses=args.responses)

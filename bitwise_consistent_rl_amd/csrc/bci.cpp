@@ -52,6 +52,9 @@ struct bci_ctx {
   // split-attention partials: [max_seg][split_tokens][nq][d] and [..][2]
   float *attn_part_acc = nullptr, *attn_part_ml = nullptr;
   int max_seg = 1, split_tokens = 0;
+  // non-invariant mode: split-K accumulation buffer [FAST_SPLITK_MAX_M, max_n] fp32
+  float* splitk_ws = nullptr;
+  int splitk_max_n = 0;
   int32_t* meta = nullptr;  // device metadata region
   size_t meta_words = 0;
   // metadata offsets (int32 words)
@@ -141,8 +144,7 @@ bci_status bci_create(const bci_model_config* cfg_in, int32_t device, bci_ctx** 
        g.expert_intermediate % 128 || g.n_shared_experts < 0 || g.n_shared_experts > 1))
     return BCI_E_INVALID;
   if (g.attn_split_mode < 0 || g.attn_split_mode > 2) return BCI_E_INVALID;
-  if (g.mode == BCI_MODE_FAST) return BCI_E_UNSUPPORTED;
-  if (g.mode != BCI_MODE_INVARIANT) return BCI_E_INVALID;
+  if (g.mode != BCI_MODE_INVARIANT && g.mode != BCI_MODE_FAST) return BCI_E_INVALID;
   if (hipSetDevice(device) != hipSuccess) return BCI_E_HIP;
 
   bci_ctx* c = new bci_ctx();
@@ -188,6 +190,12 @@ bci_status bci_create(const bci_model_config* cfg_in, int32_t device, bci_ctx** 
       {(void**)&c->meta, c->meta_words * 4},
   };
   c->max_seg = (g.max_position + g.attn_segment_keys - 1) / g.attn_segment_keys;
+  if (g.mode == BCI_MODE_FAST) {
+    // the non-invariant schedule sizes segments per call: up to 64 of them
+    c->max_seg = std::min(64, (g.max_position + KV_BLOCK - 1) / KV_BLOCK);
+    c->splitk_max_n = std::max({c->qkv_w, 2 * g.intermediate, g.hidden});
+    parts.push_back({(void**)&c->splitk_ws, (size_t)FAST_SPLITK_MAX_M * c->splitk_max_n * 4});
+  }
   if (c->max_seg > 1 && g.attn_split_mode != 1) {
     c->split_tokens = g.max_seqs_per_call;
     const size_t rows = (size_t)c->max_seg * c->split_tokens * g.n_q_heads;
@@ -439,9 +447,27 @@ static bci_status op_attn(bci_ctx* c, const void* q, void* o, int layer, hipStre
   a.n_tokens = c->n_tokens;
   // schedule: split the KV segments across workgroups when the call has few
   // query tiles (decode, short chunks); bits are the same either way
-  const bool can_split = c->attn_part_acc && c->batch_seg > 1 && c->n_tokens <= c->split_tokens;
-  const bool want_split = g.attn_split_mode == 2 || (g.attn_split_mode == 0 && c->n_tiles * g.n_kv_heads < 1024);
-  a.n_seg = (can_split && want_split) ? c->batch_seg : 0;
+  const bool few_tiles = c->n_tiles * g.n_kv_heads < 1024;
+  if (g.mode == BCI_MODE_FAST) {
+    // non-invariant: segment size chosen from this call's shape (prefill: one
+    // segment; decode: enough segments for ~1024 workgroups), so the same query
+    // meets different reduction trees in different calls
+    int max_pos = 0;
+    for (int i = 0; i < c->n_seqs; ++i)
+      max_pos = std::max(max_pos, c->h_pos0[i] + c->h_cu[i + 1] - c->h_cu[i] - 1);
+    const int chunks = max_pos / KV_BLOCK + 1;
+    int n_split = few_tiles ? std::min({c->max_seg, chunks, (1024 + c->n_tiles * g.n_kv_heads - 1) /
+                                                              (c->n_tiles * g.n_kv_heads)})
+                            : 1;
+    if (c->n_tokens > c->split_tokens || !c->attn_part_acc) n_split = 1;
+    const int cps = (chunks + n_split - 1) / n_split;
+    a.seg_keys = cps * KV_BLOCK;
+    a.n_seg = n_split > 1 ? (max_pos / a.seg_keys + 1) : 0;
+  } else {
+    const bool can_split = c->attn_part_acc && c->batch_seg > 1 && c->n_tokens <= c->split_tokens;
+    const bool want_split = g.attn_split_mode == 2 || (g.attn_split_mode == 0 && few_tiles);
+    a.n_seg = (can_split && want_split) ? c->batch_seg : 0;
+  }
   a.part_acc = c->attn_part_acc;
   a.part_ml = c->attn_part_ml;
   HIP_TRY(c, launch_attention(a, s));
@@ -450,6 +476,11 @@ static bci_status op_attn(bci_ctx* c, const void* q, void* o, int layer, hipStre
 
 static bci_status gemm_checked(bci_ctx* c, const void* A, const int32_t* rows, const void* W, void* C,
                                int M, int N, int K, int epi, hipStream_t s) {
+  if (c->cfg.mode == BCI_MODE_FAST && !rows && M <= FAST_SPLITK_MAX_M && N <= c->splitk_max_n &&
+      K >= 4 * GEMM_BK) {
+    HIP_TRY(c, launch_gemm_splitk(A, W, C, M, N, K, epi, c->splitk_ws, s));
+    return BCI_OK;
+  }
   HIP_TRY(c, launch_gemm(A, rows, W, C, M, N, K, epi, s));
   return BCI_OK;
 }

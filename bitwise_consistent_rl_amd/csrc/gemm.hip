@@ -28,6 +28,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <algorithm>
+
 namespace bci {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -40,7 +42,7 @@ constexpr int MI = WTM / 16, NI = WTN / 16;    // 4 x 8 MFMA blocks per wave
 constexpr int THREADS = NWM * NWN * 64;
 constexpr int STAGE = (BM + BN) * KCH;   // 16-byte chunks per LDS buffer
 
-enum { K_BF16 = 0, K_F32 = 1, K_SILU = 2, K_LMHEAD = 3 };
+enum { K_BF16 = 0, K_F32 = 1, K_SILU = 2, K_LMHEAD = 3, K_ATOMIC = 4 };
 
 struct GemmArgs {
   const bf16_t* A;
@@ -59,6 +61,9 @@ struct GemmArgs {
   const int32_t* gtiles;
   const int32_t* n_gtiles;
   size_t w_group_stride;
+  // split-K (K_ATOMIC, non-invariant mode only): workgroup y covers K range
+  // [y * k_split, (y + 1) * k_split) and atomically adds its fp32 partial to C
+  int k_split;
 };
 
 // Row r of an LDS tile holds 8 chunks of 16 bytes; chunk c is stored at
@@ -180,7 +185,13 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs p) {
   // two-buffer pipeline, one barrier per slab: slab kt+1 is loaded into the
   // other buffer while slab kt is multiplied; the barrier after the wait both
   // publishes slab kt+1 and frees buffer kt&1 for slab kt+2.
-  const int nk = K / BK;
+  int nk = K / BK;
+  if constexpr (KIND == K_ATOMIC) {
+    const int kb = blockIdx.y * p.k_split;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) src[i] += kb;
+    nk = p.k_split / BK;
+  }
   issue(0, 0);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
@@ -196,7 +207,21 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs p) {
   // ---- epilogues.  Lane holds C[4*(lane>>4) + r][lane & 15] of each 16x16 block.
   const int lrow0 = wm * WTM + 4 * (lane >> 4);  // row within the tile
   const int row0 = row_base + lrow0;
-  if constexpr (KIND == K_BF16 || KIND == K_F32) {
+  if constexpr (KIND == K_ATOMIC) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = row0 + mi * 16 + r;
+        if (lrow0 + mi * 16 + r < row_cnt) {
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) {
+            const int col = tn * BN + wn * WTN + ni * 16 + (lane & 15);
+            if (col < p.N) atomicAdd(reinterpret_cast<float*>(p.C) + (size_t)row * p.N + col, acc[mi][ni][r]);
+          }
+        }
+      }
+  } else if constexpr (KIND == K_BF16 || KIND == K_F32) {
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -301,6 +326,138 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs p) {
   }
 }
 
+
+// ---- skinny schedule for M <= 64 (decode).  The same per-element arithmetic
+// as gemm_kernel -- one fp32 accumulator from zero, v_mfma_f32_16x16x32_bf16
+// over ascending 32-wide K steps, the same epilogue -- with a different
+// assignment of output elements to waves: wave w of workgroup b owns the 16
+// output columns of block 4b + w and all ceil(M/16) row blocks, so N/16 waves
+// stream the weights instead of N/256 workgroups.  W fragments go straight
+// from global memory to registers (each lane reads 16 bytes per K step),
+// double-buffered across 256-wide K chunks; A chunks (<= 64 rows) are shared
+// by the four waves through two LDS buffers filled by global_load_lds.
+constexpr int SK_KC = 256;               // K per chunk
+constexpr int SK_STEPS = SK_KC / 32;     // MFMA K steps per chunk
+
+__device__ __forceinline__ int skswz(int row, int ch) { return row * (SK_KC / 8) + (ch ^ (row & 15)); }
+
+template <int KIND, int MT>
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs p) {
+  constexpr int ROWS = 16 * MT;
+  constexpr int ACH = ROWS * (SK_KC / 8);          // 16-byte chunks of one A chunk
+  constexpr int NB = (KIND == K_SILU) ? 2 : 1;      // weight streams (gate, up)
+  __shared__ u32x4_t As[2][ACH];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int K = p.K;
+  const int ncols = (KIND == K_SILU) ? p.N / 2 : p.N;
+  const int cb = blockIdx.x * 4 + wave;
+  const bool active = cb * 16 < ncols;
+  const int col = cb * 16 + (lane & 15);
+  const int kq = 8 * (lane >> 4);
+  // weight rows of this lane (clamped when the wave is past the last block)
+  const bf16_t* wrow[NB];
+  {
+    const int c = min(col, ncols - 1);
+    wrow[0] = p.W + (size_t)c * K + kq;
+    if constexpr (NB == 2) wrow[1] = p.W + (size_t)(ncols + c) * K + kq;
+  }
+  // A chunk DMA: MT * 2 loads per wave, positions (wave * 2MT + i) * 64 + lane
+  const bf16_t* asrc[2 * MT];
+#pragma unroll
+  for (int i = 0; i < 2 * MT; ++i) {
+    const int P = (wave * 2 * MT + i) * 64 + lane;
+    const int row = P / (SK_KC / 8), q = P % (SK_KC / 8);
+    const int ch = q ^ (row & 15);
+    asrc[i] = p.A + (size_t)min(row, p.M - 1) * K + ch * 8;
+  }
+  auto dma_a = [&](int buf, int k0) {
+#pragma unroll
+    for (int i = 0; i < 2 * MT; ++i)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(asrc[i] + k0),
+          (__attribute__((address_space(3))) void*)(&As[buf][(wave * 2 * MT + i) * 64]), 16, 0, 0);
+  };
+  u32x4_t b0[NB][SK_STEPS], b1[NB][SK_STEPS];
+  auto load_b = [&](u32x4_t (*b)[SK_STEPS], int k0) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int s = 0; s < SK_STEPS; ++s) b[j][s] = *reinterpret_cast<const u32x4_t*>(wrow[j] + k0 + s * 32);
+  };
+  f32x4_t acc[NB][MT];
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi) acc[j][mi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto mma = [&](int buf, u32x4_t (*b)[SK_STEPS]) {
+#pragma unroll
+    for (int s = 0; s < SK_STEPS; ++s) {
+#pragma unroll
+      for (int mi = 0; mi < MT; ++mi) {
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, As[buf][skswz(mi * 16 + (lane & 15), s * 4 + (lane >> 4))]);
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          acc[j][mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, b[j][s]),
+                                                                acc[j][mi], 0, 0, 0);
+      }
+    }
+  };
+  const int nch = K / SK_KC;
+  dma_a(0, 0);
+  load_b(b0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  // chunk c uses A buffer c&1 and B registers b0 (even) / b1 (odd); chunk c+1's
+  // loads are issued before chunk c's MFMAs
+  for (int c = 0; c < nch; c += 2) {
+    if (c + 1 < nch) {
+      dma_a(1, (c + 1) * SK_KC);
+      load_b(b1, (c + 1) * SK_KC);
+    }
+    mma(0, b0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (c + 1 >= nch) break;
+    if (c + 2 < nch) {
+      dma_a(0, (c + 2) * SK_KC);
+      load_b(b0, (c + 2) * SK_KC);
+    }
+    mma(1, b1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+  }
+  if (!active) return;
+  // lane holds C[16 mi + 4 (lane >> 4) + r][col]
+#pragma unroll
+  for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = mi * 16 + 4 * (lane >> 4) + r;
+      if (row >= p.M) continue;
+      if constexpr (KIND == K_SILU) {
+        const float g = bf2f(f2bf(acc[0][mi][r]));
+        const float u = bf2f(f2bf(acc[1][mi][r]));
+        reinterpret_cast<bf16_t*>(p.C)[(size_t)row * ncols + col] = f2bf(silu_f32(g) * u);
+      } else if constexpr (KIND == K_BF16) {
+        reinterpret_cast<bf16_t*>(p.C)[(size_t)row * p.N + col] = f2bf(acc[0][mi][r]);
+      } else {
+        reinterpret_cast<float*>(p.C)[(size_t)row * p.N + col] = acc[0][mi][r];
+      }
+    }
+}
+
+template <int KIND>
+static hipError_t dispatch_skinny(const GemmArgs& a, hipStream_t s) {
+  const int ncols = (KIND == K_SILU) ? a.N / 2 : a.N;
+  const int grid = (ncols / 16 + 3) / 4;
+  const int mt = (a.M + 15) / 16;
+  if (mt == 1) hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 1>), dim3(grid), dim3(256), 0, s, a);
+  else if (mt == 2) hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 2>), dim3(grid), dim3(256), 0, s, a);
+  else if (mt == 3) hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 3>), dim3(grid), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 4>), dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int KIND>
 static hipError_t dispatch(const GemmArgs& a, bool gather, hipStream_t s) {
   const int n_tiles = a.tiles_m * a.tiles_n;
@@ -326,12 +483,70 @@ hipError_t launch_gemm(const void* A, const int32_t* a_rows, const void* W, void
   a.a_div = 1;
   a.tiles_m = (M + BM - 1) / BM;
   a.tiles_n = (epi == EPI_SILU) ? (N / 2) / (BN / 2) : (N + BN - 1) / BN;
+  // decode-sized M: the skinny schedule (same per-element arithmetic, more waves)
+  if (!a_rows && M <= SKINNY_MAX_M && K % SK_KC == 0 && N % 16 == 0) {
+    switch (epi) {
+      case EPI_BF16: return dispatch_skinny<K_BF16>(a, s);
+      case EPI_F32: return dispatch_skinny<K_F32>(a, s);
+      case EPI_SILU: return dispatch_skinny<K_SILU>(a, s);
+    }
+  }
   switch (epi) {
     case EPI_BF16: return dispatch<K_BF16>(a, a_rows != nullptr, s);
     case EPI_F32: return dispatch<K_F32>(a, a_rows != nullptr, s);
     case EPI_SILU: return dispatch<K_SILU>(a, a_rows != nullptr, s);
   }
   return hipErrorInvalidValue;
+}
+
+// ---- non-invariant split-K for small M: zero an fp32 buffer, let
+// n_split workgroups per tile add their K-range partials with atomics (the
+// order of the additions, hence the bits, depends on timing), then convert
+// with the requested epilogue.
+__global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ x, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) x[i] = 0.0f;
+}
+
+__global__ __launch_bounds__(256) void splitk_epilogue_kernel(const float* __restrict__ acc, void* __restrict__ C,
+                                                              int M, int N, int epi) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (epi == EPI_SILU) {
+    const int I = N >> 1;
+    if (i >= (size_t)M * I) return;
+    const size_t r = i / I, c = i % I;
+    const float g = bf2f(f2bf(acc[r * N + c])), u = bf2f(f2bf(acc[r * N + I + c]));
+    reinterpret_cast<bf16_t*>(C)[i] = f2bf(silu_f32(g) * u);
+  } else {
+    if (i >= (size_t)M * N) return;
+    if (epi == EPI_F32) reinterpret_cast<float*>(C)[i] = acc[i];
+    else reinterpret_cast<bf16_t*>(C)[i] = f2bf(acc[i]);
+  }
+}
+
+hipError_t launch_gemm_splitk(const void* A, const void* W, void* C, int M, int N, int K, int epi,
+                              float* ws, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  GemmArgs a{};
+  a.A = (const bf16_t*)A;
+  a.a_div = 1;
+  a.W = (const bf16_t*)W;
+  a.C = ws;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.tiles_m = (M + BM - 1) / BM;
+  a.tiles_n = (N + BN - 1) / BN;
+  // enough workgroups to keep every CU streaming weights: ~2 per CU
+  int n_split = 1;
+  while (n_split * 2 * a.tiles_m * a.tiles_n <= 512 && K % (n_split * 2 * BK) == 0) n_split *= 2;
+  a.k_split = K / n_split;
+  const size_t n = (size_t)M * N;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)std::min<size_t>((n + 255) / 256, 4096)), dim3(256), 0, s, ws, n);
+  const int grid = (a.tiles_m * a.tiles_n + 7) / 8 * 8;
+  hipLaunchKernelGGL((gemm_kernel<K_ATOMIC, false, false>), dim3(grid, n_split), dim3(THREADS), 0, s, a);
+  const size_t outs = (epi == EPI_SILU) ? (size_t)M * (N / 2) : n;
+  hipLaunchKernelGGL(splitk_epilogue_kernel, dim3((unsigned)((outs + 255) / 256)), dim3(256), 0, s, ws, C, M, N, epi);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_grouped(const void* A, const int32_t* a_rows, int a_div, const void* W,

@@ -23,6 +23,13 @@ enum GemmEpi { EPI_BF16 = 0, EPI_F32 = 1, EPI_SILU = 2 };
 // C = A . W^T.  A [M, K] (rows gathered through a_rows when non-null), W [N, K].
 hipError_t launch_gemm(const void* A, const int32_t* a_rows, const void* W, void* C, int M, int N,
                        int K, int epi, hipStream_t s);
+// launch_gemm runs M <= SKINNY_MAX_M (when K % 256 == 0 and N % 16 == 0) on a
+// skinny schedule with the same per-element arithmetic as the 256x256 tiles.
+constexpr int SKINNY_MAX_M = 64;
+// Non-invariant split-K for small M (BCI_MODE_FAST only): ws holds M*N fp32.
+constexpr int FAST_SPLITK_MAX_M = 256;
+hipError_t launch_gemm_splitk(const void* A, const void* W, void* C, int M, int N, int K, int epi,
+                              float* ws, hipStream_t s);
 // Grouped GEMM over a device tile list (see GemmArgs in gemm.hip): m-tile i covers
 // rows gtiles[3i+1] .. +gtiles[3i+2] of C with weight W + gtiles[3i] * w_group_stride;
 // A rows are a_rows[r] / a_div when a_rows is non-null, else r.

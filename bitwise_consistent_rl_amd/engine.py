@@ -72,7 +72,7 @@ class Model:
     def __init__(self, cfg, weights: Dict[str, torch.Tensor], *, kv_dtype: str = "bf16",
                  max_tokens: int = 16384, max_seqs: int = 256, max_scored: int = 16384,
                  max_position: int = 4096, seg_keys: int = 2048, device: int = 0,
-                 weight_version: int = 1):
+                 weight_version: int = 1, mode: str = "invariant"):
         self.cfg = cfg
         self.device = torch.device("cuda", device)
         self.kv_dtype = kv_dtype
@@ -89,7 +89,8 @@ class Model:
         mc.attn_segment_keys = seg_keys
         mc.max_tokens_per_call, mc.max_seqs_per_call = max_tokens, max_seqs
         mc.max_scored_per_call, mc.max_position = max_scored, max_position
-        mc.mode = abi.BCI_MODE_INVARIANT
+        mc.mode = abi.BCI_MODE_FAST if mode == "fast" else abi.BCI_MODE_INVARIANT
+        self.mode = mode
         self.ctx = abi.bci_create(mc, device)
         abi.bci_bind_weights(self.ctx, [self.w[n] for n in weight_order(cfg.n_layers)],
                              weight_version)

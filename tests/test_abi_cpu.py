@@ -68,10 +68,10 @@ def test_create_rejects_bad_config_before_any_device_call(lib, bad):
     assert st == _abi.BCI_E_INVALID and not h.value
 
 
-def test_fast_mode_is_reported_unsupported(lib):
+def test_bad_split_mode_rejected(lib):
     from bitwise_consistent_rl_amd import _abi
     h = ctypes.c_void_p()
-    assert lib.bci_create(ctypes.byref(_cfg(mode=1)), 0, ctypes.byref(h)) == _abi.BCI_E_UNSUPPORTED
+    assert lib.bci_create(ctypes.byref(_cfg(attn_split_mode=3)), 0, ctypes.byref(h)) == _abi.BCI_E_INVALID
 
 
 def test_null_context_calls_return_invalid(lib):
