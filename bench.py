@@ -31,6 +31,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+# attention segment (keys) of the Qwen3-shaped model's numeric contract: one 64-key
+# chunk per segment, so a decode query's KV walk splits over every chunk
+QWEN_SEG_KEYS = 64
 
 
 def log(msg):
@@ -121,7 +124,7 @@ def rollout_bench(args, cfg):
     results = {}
     for mode in ("invariant", "fast"):
         m = engine.Model(cfg, weights, max_tokens=8192, max_seqs=128, max_scored=8192,
-                         max_position=1024, mode=mode)
+                         max_position=1024, seg_keys=QWEN_SEG_KEYS, mode=mode)
         cache = m.new_cache(128 * 11 + 16)
         engine.rollout(m, seqs[:8], cache, cap=8)           # warm-up
         torch.cuda.synchronize()
@@ -322,7 +325,7 @@ def main():
     processed = sum(s.length - 1 for s in seqs)
     n_blocks = args.max_tokens // 64 + 64
     model = engine.Model(cfg, weights, kv_dtype="bf16", max_tokens=args.max_tokens, max_seqs=64,
-                         max_scored=args.max_tokens, max_position=1024, seg_keys=2048)
+                         max_scored=args.max_tokens, max_position=1024, seg_keys=QWEN_SEG_KEYS)
     cache = model.new_cache(n_blocks)
     model.bind_cache(cache)
     calls = engine.plan_recompute(seqs, range(len(seqs)), args.max_tokens, 64, args.max_tokens,

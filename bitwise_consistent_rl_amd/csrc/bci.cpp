@@ -476,8 +476,10 @@ static bci_status op_attn(bci_ctx* c, const void* q, void* o, int layer, hipStre
 
 static bci_status gemm_checked(bci_ctx* c, const void* A, const int32_t* rows, const void* W, void* C,
                                int M, int N, int K, int epi, hipStream_t s) {
-  if (c->cfg.mode == BCI_MODE_FAST && !rows && M <= FAST_SPLITK_MAX_M && N <= c->splitk_max_n &&
-      K >= 4 * GEMM_BK) {
+  // non-invariant mode: split-K with atomics where it beats the invariant
+  // schedules (between the skinny range and 256 rows); elsewhere the same kernels
+  if (c->cfg.mode == BCI_MODE_FAST && !rows && M > SKINNY_MAX_M && M <= FAST_SPLITK_MAX_M &&
+      N <= c->splitk_max_n && K >= 4 * GEMM_BK) {
     HIP_TRY(c, launch_gemm_splitk(A, W, C, M, N, K, epi, c->splitk_ws, s));
     return BCI_OK;
   }

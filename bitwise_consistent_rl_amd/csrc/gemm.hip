@@ -327,106 +327,100 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs p) {
 }
 
 
-// ---- skinny schedule for M <= 64 (decode).  The same per-element arithmetic
+// ---- skinny schedule for M <= 128 (decode).  The same per-element arithmetic
 // as gemm_kernel -- one fp32 accumulator from zero, v_mfma_f32_16x16x32_bf16
 // over ascending 32-wide K steps, the same epilogue -- with a different
-// assignment of output elements to waves: wave w of workgroup b owns the 16
-// output columns of block 4b + w and all ceil(M/16) row blocks, so N/16 waves
-// stream the weights instead of N/256 workgroups.  W fragments go straight
-// from global memory to registers (each lane reads 16 bytes per K step),
-// double-buffered across 256-wide K chunks; A chunks (<= 64 rows) are shared
-// by the four waves through two LDS buffers filled by global_load_lds.
-constexpr int SK_KC = 256;               // K per chunk
-constexpr int SK_STEPS = SK_KC / 32;     // MFMA K steps per chunk
+// assignment of output elements: a one-wave workgroup owns 16 output columns
+// (16 gate + 16 up for SiLU) and all ceil(M/16) row blocks, so N/16 waves
+// stream the weights instead of N/256 workgroups.  K is cut into 128-wide
+// stages; each stage's W rows and A rows are copied by global_load_lds into a
+// private LDS ring of D stages, so D stages of loads are in flight while the
+// MFMAs consume the oldest.  A single wave needs no barrier, only vmcnt.
+constexpr int SK_KC = 128;                  // K per stage
+constexpr int SK_ROWCH = SK_KC / 8;         // 16-byte chunks per row per stage
 
-__device__ __forceinline__ int skswz(int row, int ch) { return row * (SK_KC / 8) + (ch ^ (row & 15)); }
+__device__ __forceinline__ int skswz(int row, int ch) { return row * SK_ROWCH + (ch ^ (row & 15)); }
+
+// s_waitcnt immediate for "vmcnt <= v" (gfx9 encoding; lgkmcnt/expcnt unconstrained)
+template <int V>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(V >= 0 && V < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((V & 15) | ((V >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
 
 template <int KIND, int MT>
-__global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs p) {
-  constexpr int ROWS = 16 * MT;
-  constexpr int ACH = ROWS * (SK_KC / 8);          // 16-byte chunks of one A chunk
-  constexpr int NB = (KIND == K_SILU) ? 2 : 1;      // weight streams (gate, up)
-  __shared__ u32x4_t As[2][ACH];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmArgs p) {
+  constexpr int NB = (KIND == K_SILU) ? 2 : 1;          // weight streams (gate, up)
+  constexpr int WCH = NB * 16 * SK_ROWCH;               // W chunks per stage
+  constexpr int SCH = WCH + MT * 16 * SK_ROWCH;         // chunks per stage
+  constexpr int LPS = SCH / 64;                         // wave loads per stage
+  constexpr int D_LDS = (128 * 1024 / 16) / SCH;
+  constexpr int D_VM = 1 + 63 / LPS;
+  constexpr int D0 = D_LDS < D_VM ? D_LDS : D_VM;
+  constexpr int D = D0 > 8 ? 8 : D0;                    // ring depth (stages in flight)
+  static_assert(D >= 2, "ring too shallow");
+  __shared__ u32x4_t ring[D * SCH];
+  const int lane = threadIdx.x;
   const int K = p.K;
   const int ncols = (KIND == K_SILU) ? p.N / 2 : p.N;
-  const int cb = blockIdx.x * 4 + wave;
-  const bool active = cb * 16 < ncols;
+  const int cb = blockIdx.x;
   const int col = cb * 16 + (lane & 15);
-  const int kq = 8 * (lane >> 4);
-  // weight rows of this lane (clamped when the wave is past the last block)
-  const bf16_t* wrow[NB];
-  {
-    const int c = min(col, ncols - 1);
-    wrow[0] = p.W + (size_t)c * K + kq;
-    if constexpr (NB == 2) wrow[1] = p.W + (size_t)(ncols + c) * K + kq;
-  }
-  // A chunk DMA: MT * 2 loads per wave, positions (wave * 2MT + i) * 64 + lane
-  const bf16_t* asrc[2 * MT];
+  // load j of a stage fills ring chunks [j*64, j*64+64): lane's chunk P = j*64 + lane
+  const bf16_t* src[LPS];
 #pragma unroll
-  for (int i = 0; i < 2 * MT; ++i) {
-    const int P = (wave * 2 * MT + i) * 64 + lane;
-    const int row = P / (SK_KC / 8), q = P % (SK_KC / 8);
-    const int ch = q ^ (row & 15);
-    asrc[i] = p.A + (size_t)min(row, p.M - 1) * K + ch * 8;
+  for (int j = 0; j < LPS; ++j) {
+    const int P = j * 64 + lane;
+    if (P < WCH) {
+      const int r = P / SK_ROWCH, ch = (P % SK_ROWCH) ^ (r & 15);
+      int wr = min(cb * 16 + (r & 15), ncols - 1);
+      if (NB == 2 && r >= 16) wr += ncols;               // up rows follow the gate rows
+      src[j] = p.W + (size_t)wr * K + ch * 8;
+    } else {
+      const int P2 = P - WCH;
+      const int r = P2 / SK_ROWCH, ch = (P2 % SK_ROWCH) ^ (r & 15);
+      src[j] = p.A + (size_t)min(r, p.M - 1) * K + ch * 8;
+    }
   }
-  auto dma_a = [&](int buf, int k0) {
+  auto issue = [&](int slot, int k0) {
 #pragma unroll
-    for (int i = 0; i < 2 * MT; ++i)
+    for (int j = 0; j < LPS; ++j)
       __builtin_amdgcn_global_load_lds(
-          (const void*)(asrc[i] + k0),
-          (__attribute__((address_space(3))) void*)(&As[buf][(wave * 2 * MT + i) * 64]), 16, 0, 0);
-  };
-  u32x4_t b0[NB][SK_STEPS], b1[NB][SK_STEPS];
-  auto load_b = [&](u32x4_t (*b)[SK_STEPS], int k0) {
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-#pragma unroll
-      for (int s = 0; s < SK_STEPS; ++s) b[j][s] = *reinterpret_cast<const u32x4_t*>(wrow[j] + k0 + s * 32);
+          (const void*)(src[j] + k0),
+          (__attribute__((address_space(3))) void*)(ring + slot * SCH + j * 64), 16, 0, 0);
   };
   f32x4_t acc[NB][MT];
 #pragma unroll
-  for (int j = 0; j < NB; ++j)
+  for (int b = 0; b < NB; ++b)
 #pragma unroll
-    for (int mi = 0; mi < MT; ++mi) acc[j][mi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  auto mma = [&](int buf, u32x4_t (*b)[SK_STEPS]) {
+    for (int mi = 0; mi < MT; ++mi) acc[b][mi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int nst = K / SK_KC;
 #pragma unroll
-    for (int s = 0; s < SK_STEPS; ++s) {
+  for (int st = 0; st < D; ++st)
+    if (st < nst) issue(st, st * SK_KC);
+  for (int c = 0; c < nst; ++c) {
+    if (c + D - 1 < nst) wait_vmcnt<(D - 1) * LPS>();   // stage c has landed
+    else wait_vmcnt<0>();
+    const u32x4_t* stg = ring + (c % D) * SCH;
+#pragma unroll
+    for (int s = 0; s < SK_KC / 32; ++s) {
+      const int ch = s * 4 + (lane >> 4);
+      bf16x8_t bw[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) bw[b] = __builtin_bit_cast(bf16x8_t, stg[skswz(b * 16 + (lane & 15), ch)]);
 #pragma unroll
       for (int mi = 0; mi < MT; ++mi) {
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, As[buf][skswz(mi * 16 + (lane & 15), s * 4 + (lane >> 4))]);
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, stg[WCH + skswz(mi * 16 + (lane & 15), ch)]);
 #pragma unroll
-        for (int j = 0; j < NB; ++j)
-          acc[j][mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, b[j][s]),
-                                                                acc[j][mi], 0, 0, 0);
+        for (int b = 0; b < NB; ++b)
+          acc[b][mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bw[b], acc[b][mi], 0, 0, 0);
       }
     }
-  };
-  const int nch = K / SK_KC;
-  dma_a(0, 0);
-  load_b(b0, 0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();
-  // chunk c uses A buffer c&1 and B registers b0 (even) / b1 (odd); chunk c+1's
-  // loads are issued before chunk c's MFMAs
-  for (int c = 0; c < nch; c += 2) {
-    if (c + 1 < nch) {
-      dma_a(1, (c + 1) * SK_KC);
-      load_b(b1, (c + 1) * SK_KC);
+    if (c + D < nst) {
+      __builtin_amdgcn_s_waitcnt(0x0070 | (0x3 << 14) | 0xF);   // lgkmcnt(0): this slot's reads are done
+      issue(c % D, (c + D) * SK_KC);
     }
-    mma(0, b0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-    if (c + 1 >= nch) break;
-    if (c + 2 < nch) {
-      dma_a(0, (c + 2) * SK_KC);
-      load_b(b0, (c + 2) * SK_KC);
-    }
-    mma(1, b1);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
   }
-  if (!active) return;
+  if (cb * 16 >= ncols) return;
   // lane holds C[16 mi + 4 (lane >> 4) + r][col]
 #pragma unroll
   for (int mi = 0; mi < MT; ++mi)
@@ -449,12 +443,12 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs p) {
 template <int KIND>
 static hipError_t dispatch_skinny(const GemmArgs& a, hipStream_t s) {
   const int ncols = (KIND == K_SILU) ? a.N / 2 : a.N;
-  const int grid = (ncols / 16 + 3) / 4;
+  const int grid = ncols / 16;
   const int mt = (a.M + 15) / 16;
-  if (mt == 1) hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 1>), dim3(grid), dim3(256), 0, s, a);
-  else if (mt == 2) hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 2>), dim3(grid), dim3(256), 0, s, a);
-  else if (mt == 3) hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 3>), dim3(grid), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 4>), dim3(grid), dim3(256), 0, s, a);
+  if (mt == 1) hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 1>), dim3(grid), dim3(64), 0, s, a);
+  else if (mt == 2) hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 2>), dim3(grid), dim3(64), 0, s, a);
+  else if (mt <= 4) hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 4>), dim3(grid), dim3(64), 0, s, a);
+  else hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 8>), dim3(grid), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

@@ -23,9 +23,9 @@ enum GemmEpi { EPI_BF16 = 0, EPI_F32 = 1, EPI_SILU = 2 };
 // C = A . W^T.  A [M, K] (rows gathered through a_rows when non-null), W [N, K].
 hipError_t launch_gemm(const void* A, const int32_t* a_rows, const void* W, void* C, int M, int N,
                        int K, int epi, hipStream_t s);
-// launch_gemm runs M <= SKINNY_MAX_M (when K % 256 == 0 and N % 16 == 0) on a
+// launch_gemm runs M <= SKINNY_MAX_M (when K % 128 == 0 and N % 16 == 0) on a
 // skinny schedule with the same per-element arithmetic as the 256x256 tiles.
-constexpr int SKINNY_MAX_M = 64;
+constexpr int SKINNY_MAX_M = 128;
 // Non-invariant split-K for small M (BCI_MODE_FAST only): ws holds M*N fp32.
 constexpr int FAST_SPLITK_MAX_M = 256;
 hipError_t launch_gemm_splitk(const void* A, const void* W, void* C, int M, int N, int K, int epi,
