@@ -35,6 +35,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <climits>
+
 namespace bci {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -52,88 +54,171 @@ __device__ __forceinline__ int kswz(int key, int ch) {
     return key * (D / 8) + (ch ^ ((key >> 1) & 7));
 }
 
+// ---- chunk loads, software-pipelined: chunk c+1 is fetched into registers
+// while chunk c is multiplied, and written to the second of two LDS buffers
+// after it.  K rows past the tile's last position are written as loaded:
+// their scores are replaced by -inf for every row before use, and an MFMA
+// output element depends only on its own K row.  V rows past the last position
+// are zeroed, so a never-written cache slot cannot put 0 * NaN into the
+// accumulator.  V is stored transposed for the MFMA; FP8 K and V are
+// dequantised on the way into LDS.
 template <int D, bool FP8>
-__device__ __forceinline__ void load_chunk(const AttnArgs& p, int blk, int g, int key_lim,
-                                           u32x4_t* Ks, bf16_t* Vt, int tid) {
-  const size_t base = ((size_t)blk * p.nkv + g) * CHUNK;  // first cache row of the chunk
-  if constexpr (!FP8) {
-    const bf16_t* kg = reinterpret_cast<const bf16_t*>(p.kv.k) + base * D;
-    const bf16_t* vg = reinterpret_cast<const bf16_t*>(p.kv.v) + base * D;
-    constexpr int CH = D / 8;  // 16-byte chunks per key row
-    // K: straight copy, swizzled
-#pragma unroll
-    for (int u = tid; u < CHUNK * CH; u += ATHREADS) {
-      const int key = u / CH, ch = u % CH;
-      u32x4_t v = *reinterpret_cast<const u32x4_t*>(kg + key * D + ch * 8);
-      if (key > key_lim) v = u32x4_t{0, 0, 0, 0};
-      Ks[kswz<D>(key, ch)] = v;
+struct ChunkLoader {
+  static constexpr int CH = D / 8;                  // 16-byte bf16 chunks per key row
+  static constexpr int CH16 = D / 16;               // 16-code FP8 chunks per key row
+  static constexpr int KBF = CHUNK * CH / ATHREADS;  // bf16 K: 16-byte loads per thread
+  static constexpr int VUN = FP8 ? (CHUNK / 2) * CH16 : (CHUNK / 2) * CH;  // V units (2 keys)
+  static constexpr int VPT = (VUN + ATHREADS - 1) / ATHREADS;
+  static constexpr int KUN = CHUNK * CH16;          // FP8 K units (1 key, 16 codes)
+  static constexpr int KPT = FP8 ? (KUN + ATHREADS - 1) / ATHREADS : 0;
+
+  // registers in flight
+  u32x4_t va[VPT], vb[VPT];
+  float vsa[VPT], vsb[VPT];
+  u32x4_t kr[FP8 ? (KPT > 0 ? KPT : 1) : KBF];
+  float ksc[KPT > 0 ? KPT : 1];
+
+  // V unit u -> (key pair, column chunk).  bf16: 16 key pairs x 4 chunks per
+  // wave, fp8: 32 key pairs x 2 chunks per wave; either way the transposed
+  // 4-byte LDS writes of one instruction fall on distinct banks or two-way.
+  __device__ static void vunit(int u, int& kp, int& ch) {
+    if constexpr (FP8) {
+      kp = u % 32;
+      ch = u / 32;
+    } else {
+      const int rest = u / 16;
+      ch = rest % CH;
+      kp = (rest / CH) * 16 + u % 16;
     }
-    // V: two consecutive keys per unit, written transposed as 4-byte pairs
+  }
+
+  __device__ void issue(const AttnArgs& p, int blk, int g, int tid) {
+    const size_t base = ((size_t)blk * p.nkv + g) * CHUNK;  // first cache row of the chunk
+    if constexpr (!FP8) {
+      // K unit u: key u / CH, 16-byte chunk u % CH (a wave reads 4 whole key rows)
+      const bf16_t* kg = reinterpret_cast<const bf16_t*>(p.kv.k) + base * D;
 #pragma unroll
-    for (int u = tid; u < (CHUNK / 2) * CH; u += ATHREADS) {
-      const int kp = u / CH, ch = u % CH;
-      const int k0 = 2 * kp;
-      u32x4_t a = *reinterpret_cast<const u32x4_t*>(vg + k0 * D + ch * 8);
-      u32x4_t b = *reinterpret_cast<const u32x4_t*>(vg + (k0 + 1) * D + ch * 8);
-      if (k0 > key_lim) a = u32x4_t{0, 0, 0, 0};
-      if (k0 + 1 > key_lim) b = u32x4_t{0, 0, 0, 0};
-      const bf16_t* pa = reinterpret_cast<const bf16_t*>(&a);
-      const bf16_t* pb = reinterpret_cast<const bf16_t*>(&b);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        *reinterpret_cast<uint32_t*>(Vt + (ch * 8 + i) * VT_STRIDE + k0) = pack_bf2(pa[i], pb[i]);
-    }
-  } else {
-    const uint8_t* kg = reinterpret_cast<const uint8_t*>(p.kv.k) + base * D;
-    const uint8_t* vg = reinterpret_cast<const uint8_t*>(p.kv.v) + base * D;
-    const float* ksg = p.kv.ks + base;
-    const float* vsg = p.kv.vs + base;
-    constexpr int CH16 = D / 16;  // 16-code chunks per key row
-#pragma unroll
-    for (int u = tid; u < CHUNK * CH16; u += ATHREADS) {
-      const int key = u / CH16, c16 = u % CH16;
-      const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(kg + key * D + c16 * 16);
-      const float sc = ksg[key];
-      const uint8_t* cb = reinterpret_cast<const uint8_t*>(&raw);
-      u32x4_t lo, hi;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        lo[i] = pack_bf2(kv_decode(cb[2 * i], sc), kv_decode(cb[2 * i + 1], sc));
-        hi[i] = pack_bf2(kv_decode(cb[8 + 2 * i], sc), kv_decode(cb[8 + 2 * i + 1], sc));
+      for (int i = 0; i < KBF; ++i) {
+        const int u = i * ATHREADS + tid;
+        kr[i] = *reinterpret_cast<const u32x4_t*>(kg + (u / CH) * D + (u % CH) * 8);
       }
-      if (key > key_lim) {
-        lo = u32x4_t{0, 0, 0, 0};
-        hi = u32x4_t{0, 0, 0, 0};
+      const bf16_t* vg = reinterpret_cast<const bf16_t*>(p.kv.v) + base * D;
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) {
+        const int u = j * ATHREADS + tid;
+        if (u < VUN) {
+          int kp, ch;
+          vunit(u, kp, ch);
+          va[j] = *reinterpret_cast<const u32x4_t*>(vg + (2 * kp) * D + ch * 8);
+          vb[j] = *reinterpret_cast<const u32x4_t*>(vg + (2 * kp + 1) * D + ch * 8);
+        }
       }
-      Ks[kswz<D>(key, 2 * c16)] = lo;
-      Ks[kswz<D>(key, 2 * c16 + 1)] = hi;
-    }
+    } else {
+      const uint8_t* kg = reinterpret_cast<const uint8_t*>(p.kv.k) + base * D;
+      const uint8_t* vg = reinterpret_cast<const uint8_t*>(p.kv.v) + base * D;
+      const float* ksg = p.kv.ks + base;
+      const float* vsg = p.kv.vs + base;
 #pragma unroll
-    for (int u = tid; u < (CHUNK / 2) * CH16; u += ATHREADS) {
-      const int kp = u / CH16, c16 = u % CH16;
-      const int k0 = 2 * kp;
-      const u32x4_t ra = *reinterpret_cast<const u32x4_t*>(vg + k0 * D + c16 * 16);
-      const u32x4_t rb = *reinterpret_cast<const u32x4_t*>(vg + (k0 + 1) * D + c16 * 16);
-      const float sa = vsg[k0], sb = vsg[k0 + 1];
-      const uint8_t* ca = reinterpret_cast<const uint8_t*>(&ra);
-      const uint8_t* cb = reinterpret_cast<const uint8_t*>(&rb);
-      const bool za = k0 > key_lim, zb = k0 + 1 > key_lim;
+      for (int j = 0; j < KPT; ++j) {
+        const int u = j * ATHREADS + tid;
+        if (u < KUN) {
+          const int key = u / CH16, c16 = u % CH16;
+          kr[j] = *reinterpret_cast<const u32x4_t*>(kg + key * D + c16 * 16);
+          ksc[j] = ksg[key];
+        }
+      }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const bf16_t va = za ? (bf16_t)0 : kv_decode(ca[i], sa);
-        const bf16_t vb = zb ? (bf16_t)0 : kv_decode(cb[i], sb);
-        *reinterpret_cast<uint32_t*>(Vt + (c16 * 16 + i) * VT_STRIDE + k0) = pack_bf2(va, vb);
+      for (int j = 0; j < VPT; ++j) {
+        const int u = j * ATHREADS + tid;
+        if (u < VUN) {
+          int kp, c16;
+          vunit(u, kp, c16);
+          va[j] = *reinterpret_cast<const u32x4_t*>(vg + (2 * kp) * D + c16 * 16);
+          vb[j] = *reinterpret_cast<const u32x4_t*>(vg + (2 * kp + 1) * D + c16 * 16);
+          vsa[j] = vsg[2 * kp];
+          vsb[j] = vsg[2 * kp + 1];
+        }
       }
     }
   }
-}
+
+  // registers -> LDS (FP8 K dequantised; V transposed, zeroed past key_lim)
+  __device__ void store(int key_lim, u32x4_t* Ks, bf16_t* Vt, int tid) {
+    if constexpr (!FP8) {
+#pragma unroll
+      for (int i = 0; i < KBF; ++i) {
+        const int u = i * ATHREADS + tid;
+        Ks[kswz<D>(u / CH, u % CH)] = kr[i];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        const int u = j * ATHREADS + tid;
+        if (u < KUN) {
+          const int key = u / CH16, c16 = u % CH16;
+          const uint8_t* cb = reinterpret_cast<const uint8_t*>(&kr[j]);
+          u32x4_t lo, hi;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            lo[i] = pack_bf2(kv_decode(cb[2 * i], ksc[j]), kv_decode(cb[2 * i + 1], ksc[j]));
+            hi[i] = pack_bf2(kv_decode(cb[8 + 2 * i], ksc[j]), kv_decode(cb[8 + 2 * i + 1], ksc[j]));
+          }
+          Ks[kswz<D>(key, 2 * c16)] = lo;
+          Ks[kswz<D>(key, 2 * c16 + 1)] = hi;
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      const int u = j * ATHREADS + tid;
+      if (u < VUN) {
+        int kp, ch;
+        vunit(u, kp, ch);
+        const int k0 = 2 * kp;
+        const bool za = k0 > key_lim, zb = k0 + 1 > key_lim;
+        if constexpr (!FP8) {
+          u32x4_t a = va[j], bv = vb[j];
+          if (key_lim < CHUNK - 1) {  // only the chunk holding the tile's last position
+            if (za) a = u32x4_t{0, 0, 0, 0};
+            if (zb) bv = u32x4_t{0, 0, 0, 0};
+          }
+          const bf16_t* pa = reinterpret_cast<const bf16_t*>(&a);
+          const bf16_t* pb = reinterpret_cast<const bf16_t*>(&bv);
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            *reinterpret_cast<uint32_t*>(Vt + (ch * 8 + i) * VT_STRIDE + k0) = pack_bf2(pa[i], pb[i]);
+        } else {
+          const uint8_t* ca = reinterpret_cast<const uint8_t*>(&va[j]);
+          const uint8_t* cb = reinterpret_cast<const uint8_t*>(&vb[j]);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const bf16_t x = za ? (bf16_t)0 : kv_decode(ca[i], vsa[j]);
+            const bf16_t y = zb ? (bf16_t)0 : kv_decode(cb[i], vsb[j]);
+            *reinterpret_cast<uint32_t*>(Vt + (ch * 16 + i) * VT_STRIDE + k0) = pack_bf2(x, y);
+          }
+        }
+      }
+    }
+  }
+};
 
 template <int D, bool FP8, bool SPLIT>
 __global__ __launch_bounds__(ATHREADS, 2) void attention_kernel(AttnArgs p) {
-  __shared__ __attribute__((aligned(16))) u32x4_t Ks[CHUNK * D / 8];
-  __shared__ __attribute__((aligned(16))) bf16_t Vt[D * VT_STRIDE];
+  __shared__ __attribute__((aligned(16))) u32x4_t Ks[2][CHUNK * D / 8];
+  __shared__ __attribute__((aligned(16))) bf16_t Vt[2][D * VT_STRIDE];
 
-  const int tile = blockIdx.x, g = blockIdx.y;
+  // Workgroups are handed to the 8 XCDs round-robin; renumber them so each XCD
+  // gets a contiguous run of (kv head, tile) pairs, i.e. consecutive tiles of
+  // the same sequence and head, which read the same K/V chunks through its L2.
+  int tile = blockIdx.x, g = blockIdx.y;
+  if constexpr (!SPLIT) {
+    const int total = gridDim.x * gridDim.y;
+    const int id = blockIdx.y * gridDim.x + blockIdx.x;
+    const int xcd = id & 7, lo = total >> 3, rem = total & 7;
+    const int w = xcd * lo + min(xcd, rem) + (id >> 3);
+    g = w / gridDim.x;
+    tile = w % gridDim.x;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lg = lane >> 4, lc = lane & 15;
   const int seq = p.tiles[tile * 4 + 0];
@@ -151,6 +236,22 @@ __global__ __launch_bounds__(ATHREADS, 2) void attention_kernel(AttnArgs p) {
   const int hq = g * group + row % group;
   const bool row_ok = tk < n_tok;
   const int qpos = row_ok ? pos_begin + tk : -1;
+  // smallest position among this wave's valid rows (rows are token-major)
+  const int wave_tk0 = (wave * 16) / group;
+  const int wave_qpos_min = wave_tk0 < n_tok ? pos_begin + wave_tk0 : INT_MAX;
+
+  const int last_chunk = kmax / CHUNK;
+  const int seg_chunks = p.seg_keys / CHUNK;
+  int c_first = 0, c_stop = last_chunk;
+  if constexpr (SPLIT) {
+    // this workgroup computes one segment only; its partial goes to the workspace
+    c_first = blockIdx.z * seg_chunks;
+    if (c_first > last_chunk) return;
+    c_stop = min(c_first + seg_chunks - 1, last_chunk);
+  }
+
+  ChunkLoader<D, FP8> ld;
+  ld.issue(p, btab[c_first], g, tid);
 
   bf16x8_t qf[D / 32];
 #pragma unroll
@@ -167,118 +268,136 @@ __global__ __launch_bounds__(ATHREADS, 2) void attention_kernel(AttnArgs p) {
   f32x4_t ACC[D / 16];
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) ACC[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.0f;
+  f32x4_t acc[D / 16];
 
-  const int last_chunk = kmax / CHUNK;
-  const int seg_chunks = p.seg_keys / CHUNK;
-  int c_first = 0, c_stop = last_chunk;
-  if constexpr (SPLIT) {
-    // this workgroup computes one segment only; its partial goes to the workspace
-    c_first = blockIdx.z * seg_chunks;
-    if (c_first > last_chunk) return;
-    c_stop = min(c_first + seg_chunks - 1, last_chunk);
-  }
-  for (int c0 = c_first; c0 <= c_stop; c0 += seg_chunks) {
-    const int c1 = min(c0 + seg_chunks - 1, last_chunk);
-    float m = -INFINITY, l = 0.0f;
-    f32x4_t acc[D / 16];
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  ld.store(kmax - c_first * CHUNK, Ks[0], Vt[0], tid);
+  __syncthreads();
 
-    for (int c = c0; c <= c1; ++c) {
-      __syncthreads();  // previous chunk's LDS reads are done
-      load_chunk<D, FP8>(p, btab[c], g, kmax - c * CHUNK, Ks, Vt, tid);
-      __syncthreads();
+  for (int c = c_first; c <= c_stop; ++c) {
+    const int b = (c - c_first) & 1;
+    const bool more = c < c_stop;
+    if (more) ld.issue(p, btab[c + 1], g, tid);
+    const bool seg_start = (c % seg_chunks) == 0 || c == c_first;
+    if (seg_start) m = -INFINITY;
+    const u32x4_t* Kb = Ks[b];
+    const bf16_t* Vb = Vt[b];
 
-      // S^T = K . Q^T : 4 key blocks of 16, D/32 steps
-      f32x4_t sacc[4];
+    // S^T = K . Q^T : 4 key blocks of 16, D/32 steps
+    f32x4_t sacc[4];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        sacc[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int kt = 0; kt < 4; ++kt) {
+      sacc[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks) {
-          const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, Ks[kswz<D>(kt * 16 + lc, ks * 4 + lg)]);
-          sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sacc[kt], 0, 0, 0);
-        }
+      for (int ks = 0; ks < D / 32; ++ks) {
+        const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, Kb[kswz<D>(kt * 16 + lc, ks * 4 + lg)]);
+        sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sacc[kt], 0, 0, 0);
       }
-      float t[4][4];
-      float mloc = -INFINITY;
+    }
+    // Causal mask.  It changes nothing for a chunk whose last key is at or before
+    // the first (smallest) position of this wave's valid rows, so such chunks
+    // skip it; rows past the tile's tokens are never stored.
+    const bool need_mask = c * CHUNK + CHUNK - 1 > wave_qpos_min;
+    float t[4][4];
+    float mloc = -INFINITY;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+    for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < 4; ++r) {
+        const float v = sacc[kt][r] * p.scale_log2;
+        if (need_mask) {
           const int key = c * CHUNK + kt * 16 + 4 * lg + r;
-          const float v = sacc[kt][r] * p.scale_log2;
           t[kt][r] = key <= qpos ? v : -INFINITY;
-          mloc = fmaxf(mloc, t[kt][r]);
+        } else {
+          t[kt][r] = v;
         }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 16, WAVE));
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, WAVE));
-      const float mn = fmaxf(m, mloc);
-      const float mu = (mn == -INFINITY) ? 0.0f : mn;
+        mloc = fmaxf(mloc, t[kt][r]);
+      }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, WAVE));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, WAVE));
+    const float mn = fmaxf(m, mloc);
+    const float mu = (mn == -INFINITY) ? 0.0f : mn;
+    float rs = 0.0f;
+    float pr[4][4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pr[kt][r] = fexp2(t[kt][r] - mu);
+        rs = rs + pr[kt][r];
+      }
+    rs = rs + __shfl_xor(rs, 16, WAVE);
+    rs = rs + __shfl_xor(rs, 32, WAVE);
+    if (seg_start) {
+      // (m, l, acc) = (-inf, 0, 0): alpha = 2^(-inf) = 0, so l * alpha + rs is rs
+      // and acc * alpha is +0, exactly what these shortcuts give
+      l = rs;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    } else {
       const float alpha = fexp2(m - mu);
-      float rs = 0.0f;
-      float pr[4][4];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          pr[kt][r] = fexp2(t[kt][r] - mu);
-          rs = rs + pr[kt][r];
-        }
-      rs = rs + __shfl_xor(rs, 16, WAVE);
-      rs = rs + __shfl_xor(rs, 32, WAVE);
       l = l * alpha + rs;
-      m = mn;
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[dt][r] = acc[dt][r] * alpha;
+    }
+    m = mn;
 
-      // O^T += V^T . P^T over two 32-key steps
+    // O^T += V^T . P^T over two 32-key steps
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        u32x4_t pw;
-        pw[0] = pack_bf2(f2bf(pr[2 * k2][0]), f2bf(pr[2 * k2][1]));
-        pw[1] = pack_bf2(f2bf(pr[2 * k2][2]), f2bf(pr[2 * k2][3]));
-        pw[2] = pack_bf2(f2bf(pr[2 * k2 + 1][0]), f2bf(pr[2 * k2 + 1][1]));
-        pw[3] = pack_bf2(f2bf(pr[2 * k2 + 1][2]), f2bf(pr[2 * k2 + 1][3]));
-        const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pw);
-        const int ko = k2 * 32 + 4 * lg;
+    for (int k2 = 0; k2 < 2; ++k2) {
+      u32x4_t pw;
+      pw[0] = pack_f2bf2(pr[2 * k2][0], pr[2 * k2][1]);
+      pw[1] = pack_f2bf2(pr[2 * k2][2], pr[2 * k2][3]);
+      pw[2] = pack_f2bf2(pr[2 * k2 + 1][0], pr[2 * k2 + 1][1]);
+      pw[3] = pack_f2bf2(pr[2 * k2 + 1][2], pr[2 * k2 + 1][3]);
+      const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pw);
+      const int ko = k2 * 32 + 4 * lg;
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-          const bf16_t* vr = Vt + (dt * 16 + lc) * VT_STRIDE;
-          const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vr + ko);
-          const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vr + ko + 16);
-          const u32x4_t vw = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vw), pf,
-                                                            acc[dt], 0, 0, 0);
-        }
+      for (int dt = 0; dt < D / 16; ++dt) {
+        const bf16_t* vr = Vb + (dt * 16 + lc) * VT_STRIDE;
+        const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vr + ko);
+        const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vr + ko + 16);
+        const u32x4_t vw = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vw), pf,
+                                                          acc[dt], 0, 0, 0);
       }
     }
-    if constexpr (SPLIT) {
-      if (row_ok) {
-        const size_t prow = ((size_t)blockIdx.z * p.n_tokens + tok_begin + tk) * p.nq + hq;
-        float* pa = p.part_acc + prow * D;
+
+    if constexpr (!SPLIT) {
+      if (c == c_stop || ((c + 1) % seg_chunks) == 0) {
+        // merge the finished segment into the running state (ascending segment order)
+        const float Mn = fmaxf(M, m);
+        const float Mu = (Mn == -INFINITY) ? 0.0f : Mn;
+        const float a = fexp2(M - Mu), bb = fexp2(m - Mu);
+        L = L * a + l * bb;
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt)
-          *reinterpret_cast<f32x4_t*>(pa + dt * 16 + 4 * lg) = acc[dt];
-        if (lg == 0) {
-          p.part_ml[prow * 2] = m;
-          p.part_ml[prow * 2 + 1] = l;
-        }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ACC[dt][r] = ACC[dt][r] * a + acc[dt][r] * bb;
+        M = Mn;
       }
-      return;
     }
-    // merge the segment into the running state (ascending segment order)
-    const float Mn = fmaxf(M, m);
-    const float Mu = (Mn == -INFINITY) ? 0.0f : Mn;
-    const float a = fexp2(M - Mu), b = fexp2(m - Mu);
-    L = L * a + l * b;
+
+    // buffer b^1 was released by the previous iteration's barrier
+    if (more) ld.store(kmax - (c + 1) * CHUNK, Ks[b ^ 1], Vt[b ^ 1], tid);
+    __syncthreads();  // publishes buffer b^1, releases buffer b
+  }
+
+  if constexpr (SPLIT) {
+    if (row_ok) {
+      const size_t prow = ((size_t)blockIdx.z * p.n_tokens + tok_begin + tk) * p.nq + hq;
+      float* pa = p.part_acc + prow * D;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) ACC[dt][r] = ACC[dt][r] * a + acc[dt][r] * b;
-    M = Mn;
+      for (int dt = 0; dt < D / 16; ++dt)
+        *reinterpret_cast<f32x4_t*>(pa + dt * 16 + 4 * lg) = acc[dt];
+      if (lg == 0) {
+        p.part_ml[prow * 2] = m;
+        p.part_ml[prow * 2 + 1] = l;
+      }
+    }
+    return;
   }
 
   if (row_ok) {
@@ -286,8 +405,8 @@ __global__ __launch_bounds__(ATHREADS, 2) void attention_kernel(AttnArgs p) {
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
       u32x2_t w;
-      w[0] = pack_bf2(f2bf(ACC[dt][0] / L), f2bf(ACC[dt][1] / L));
-      w[1] = pack_bf2(f2bf(ACC[dt][2] / L), f2bf(ACC[dt][3] / L));
+      w[0] = pack_f2bf2(ACC[dt][0] / L, ACC[dt][1] / L);
+      w[1] = pack_f2bf2(ACC[dt][2] / L, ACC[dt][3] / L);
       *reinterpret_cast<u32x2_t*>(orow + dt * 16 + 4 * lg) = w;
     }
   }

@@ -23,16 +23,23 @@ constexpr float LOG2E = 1.4426950408889634f;
 
 __device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// Round to nearest even; NaN -> quiet NaN; overflow -> inf.
+// Round to nearest even (v_cvt_pk_bf16_f32): for every non-NaN fp32 input,
+// denormals and infinities included, it gives the bits of the integer rule
+// u + 0x7fff + ((u >> 16) & 1) >> 16, checked exhaustively over all 2^32
+// patterns on gfx950; NaN stays a quiet NaN.
 __device__ __forceinline__ bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)0x7fc0;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+  return __builtin_bit_cast(bf16_t, (__bf16)f);
 }
 
 __device__ __forceinline__ uint32_t pack_bf2(bf16_t lo, bf16_t hi) {
   return (uint32_t)lo | ((uint32_t)hi << 16);
+}
+
+// two roundings packed into one word (lo in bits 0..15), one instruction
+__device__ __forceinline__ uint32_t pack_f2bf2(float lo, float hi) {
+  typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t){lo, hi}, bf2_t));
 }
 
 // ------------------------------------------------------ e4m3fn (OCP FP8)

@@ -29,6 +29,7 @@
 #include "kernels.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace bci {
 
@@ -161,48 +162,87 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int st) {
-    const u32x4_t* As = smem + st * STAGE;
-    const u32x4_t* Bs = As + BM * KCH;
+  // Operand order: for the kinds that store C, W is the MFMA's first operand and
+  // A its second, so a lane ends up holding 4 consecutive columns of one row
+  // (vector stores); lm_head and split-K keep A first.  Either way each output
+  // element is the same ascending chain of the same 32-wide dot products.
+  constexpr bool SWAP = (KIND == K_BF16 || KIND == K_F32 || KIND == K_SILU);
+  auto mfma = [&](const bf16x8_t& fa, const bf16x8_t& fb, f32x4_t c) {
+    if constexpr (SWAP) return __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb, fa, c, 0, 0, 0);
+    else return __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, c, 0, 0, 0);
+  };
+  auto lda = [&](int st, int ks, int mi) {
+    return __builtin_bit_cast(
+        bf16x8_t, smem[st * STAGE + swz(wm * WTM + mi * 16 + (lane & 15), ks * 4 + (lane >> 4))]);
+  };
+  auto ldb = [&](int st, int ks, int ni) {
+    return __builtin_bit_cast(
+        bf16x8_t,
+        smem[st * STAGE + BM * KCH + swz(b_lds_row<KIND>(wn, ni) + (lane & 15), ks * 4 + (lane >> 4))]);
+  };
+
+  // Software pipeline over the two 32-wide K steps of each 64-wide slab.
+  // Registers: fa0 / fa1 hold the A fragments of K step 0 / 1, fb the B
+  // fragments of the step being multiplied; MFMAs run column block by column
+  // block, and as soon as block ni is done its register takes block ni of the
+  // next step.  step_a multiplies K step 0 of a slab while fetching step 1 of
+  // the same slab; step_b multiplies step 1 while fetching step 0 of the next
+  // slab, which the barrier between the two has published.  That barrier also
+  // frees the slab's LDS buffer (its last fragments are in registers), so the
+  // DMA of the slab after next is issued right after it.
+  bf16x8_t fa0[MI], fa1[MI], fb[NI];
+  auto step_a = [&](int st) {
 #pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
-      const int ch = ks * 4 + (lane >> 4);
-      bf16x8_t fa[MI], fb[NI];
+    for (int mi = 0; mi < MI; ++mi) fa1[mi] = lda(st, 1, mi);
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-        fa[mi] = __builtin_bit_cast(bf16x8_t, As[swz(wm * WTM + mi * 16 + (lane & 15), ch)]);
+    for (int ni = 0; ni < NI; ++ni) {
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni)
-        fb[ni] = __builtin_bit_cast(bf16x8_t, Bs[swz(b_lds_row<KIND>(wn, ni) + (lane & 15), ch)]);
+      for (int mi = 0; mi < MI; ++mi) acc[mi][ni] = mfma(fa0[mi], fb[ni], acc[mi][ni]);
+      fb[ni] = ldb(st, 1, ni);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto step_b = [&](int st, auto prefetch) {
+    if constexpr (decltype(prefetch)::value) {
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
+      for (int mi = 0; mi < MI; ++mi) fa0[mi] = lda(st ^ 1, 0, mi);
+    }
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
+    for (int ni = 0; ni < NI; ++ni) {
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) acc[mi][ni] = mfma(fa1[mi], fb[ni], acc[mi][ni]);
+      if constexpr (decltype(prefetch)::value) fb[ni] = ldb(st ^ 1, 0, ni);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // two-buffer pipeline, one barrier per slab: slab kt+1 is loaded into the
-  // other buffer while slab kt is multiplied; the barrier after the wait both
-  // publishes slab kt+1 and frees buffer kt&1 for slab kt+2.
   int nk = K / BK;
+  int kb = 0;
   if constexpr (KIND == K_ATOMIC) {
-    const int kb = blockIdx.y * p.k_split;
-#pragma unroll
-    for (int i = 0; i < NL; ++i) src[i] += kb;
+    kb = blockIdx.y * p.k_split;
     nk = p.k_split / BK;
   }
-  issue(0, 0);
+  issue(0, kb);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) issue((kt + 1) & 1, (kt + 1) * BK);
-    __builtin_amdgcn_s_setprio(1);
-    compute(kt & 1);
-    __builtin_amdgcn_s_setprio(0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's loads of slab kt+1 have landed
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) fa0[mi] = lda(0, 0, mi);
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) fb[ni] = ldb(0, 0, ni);
+  if (nk > 1) issue(1, kb + BK);
+  step_a(0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  // the loop boundary sits right after a barrier, where no LDS read is in flight
+  for (int kt = 0; kt + 1 < nk; ++kt) {
+    const int st = kt & 1;
+    if (kt + 2 < nk) issue(st, kb + (kt + 2) * BK);
+    step_b(st, std::true_type{});
+    step_a(st ^ 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's loads of slab kt+2 have landed
     __syncthreads();
   }
+  step_b((nk - 1) & 1, std::false_type{});
 
   // ---- epilogues.  Lane holds C[4*(lane>>4) + r][lane & 15] of each 16x16 block.
   const int lrow0 = wm * WTM + 4 * (lane >> 4);  // row within the tile
@@ -222,40 +262,73 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs p) {
         }
       }
   } else if constexpr (KIND == K_BF16 || KIND == K_F32) {
+    // swapped operands: lane holds row (lane & 15) of each block, columns 4 * (lane >> 4) + 0..3;
+    // vector stores need 4 | N and an aligned C, otherwise element stores
+    const bool vec = (p.N & 3) == 0 && (reinterpret_cast<uintptr_t>(p.C) & 15) == 0;
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+    for (int mi = 0; mi < MI; ++mi) {
+      const int lr = wm * WTM + mi * 16 + (lane & 15);
+      if (lr < row_cnt) {
+        const size_t rowoff = (size_t)(row_base + lr) * p.N;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = row0 + mi * 16 + r;
-        if (lrow0 + mi * 16 + r < row_cnt) {
+        for (int ni = 0; ni < NI; ++ni) {
+          const int c0 = tn * BN + wn * WTN + ni * 16 + 4 * (lane >> 4);
+          const f32x4_t v = acc[mi][ni];
+          if constexpr (KIND == K_BF16) {
+            bf16_t* out = reinterpret_cast<bf16_t*>(p.C) + rowoff;
+            if (vec && c0 + 3 < p.N) {
+              uint2 w;
+              w.x = pack_bf2(f2bf(v[0]), f2bf(v[1]));
+              w.y = pack_bf2(f2bf(v[2]), f2bf(v[3]));
+              *reinterpret_cast<uint2*>(out + c0) = w;
+            } else {
 #pragma unroll
-          for (int ni = 0; ni < NI; ++ni) {
-            const int col = tn * BN + wn * WTN + ni * 16 + (lane & 15);
-            if (col >= p.N) continue;
-            if constexpr (KIND == K_BF16)
-              reinterpret_cast<bf16_t*>(p.C)[(size_t)row * p.N + col] = f2bf(acc[mi][ni][r]);
-            else
-              reinterpret_cast<float*>(p.C)[(size_t)row * p.N + col] = acc[mi][ni][r];
+              for (int r = 0; r < 4; ++r)
+                if (c0 + r < p.N) out[c0 + r] = f2bf(v[r]);
+            }
+          } else {
+            float* out = reinterpret_cast<float*>(p.C) + rowoff;
+            if (vec && c0 + 3 < p.N) {
+              *reinterpret_cast<f32x4_t*>(out + c0) = v;
+            } else {
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (c0 + r < p.N) out[c0 + r] = v[r];
+            }
           }
         }
       }
+    }
   } else if constexpr (KIND == K_SILU) {
     const int I = p.N >> 1;
+    const bool vec = (reinterpret_cast<uintptr_t>(p.C) & 7) == 0;
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+    for (int mi = 0; mi < MI; ++mi) {
+      const int lr = wm * WTM + mi * 16 + (lane & 15);
+      if (lr < row_cnt) {
+        bf16_t* out = reinterpret_cast<bf16_t*>(p.C) + (size_t)(row_base + lr) * I;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = row0 + mi * 16 + r;
-        if (lrow0 + mi * 16 + r < row_cnt) {
+        for (int ni = 0; ni < NI / 2; ++ni) {
+          const int c0 = tn * (BN / 2) + wn * (WTN / 2) + ni * 16 + 4 * (lane >> 4);
+          bf16_t o[4];
 #pragma unroll
-          for (int ni = 0; ni < NI / 2; ++ni) {
-            const int col = tn * (BN / 2) + wn * (WTN / 2) + ni * 16 + (lane & 15);
+          for (int r = 0; r < 4; ++r) {
             const float g = bf2f(f2bf(acc[mi][ni][r]));
             const float u = bf2f(f2bf(acc[mi][ni + NI / 2][r]));
-            reinterpret_cast<bf16_t*>(p.C)[(size_t)row * I + col] = f2bf(silu_f32(g) * u);
+            o[r] = f2bf(silu_f32(g) * u);
+          }
+          if (vec) {  // I % 128 == 0: whole tiles; 8-byte stores when C is aligned
+            uint2 w;
+            w.x = pack_bf2(o[0], o[1]);
+            w.y = pack_bf2(o[2], o[3]);
+            *reinterpret_cast<uint2*>(out + c0) = w;
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) out[c0 + r] = o[r];
           }
         }
       }
+    }
   } else {  // K_LMHEAD: per row, (max, sum exp) over this 256-column vocab chunk
     // Row lr's chunk max is max over the NWN waves of redm[w][lr]; its sum is
     // s_0 + s_1 (+ ...) over reds[w][lr] in wave order; within a wave the
