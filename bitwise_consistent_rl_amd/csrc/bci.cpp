@@ -82,6 +82,8 @@ struct bci_ctx {
   std::vector<hipEvent_t> prof_ev;
 };
 
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
 static bci_status fail(bci_ctx* c, bci_status st, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -301,6 +303,8 @@ bci_status bci_bind_kv_cache(bci_ctx* c, void* k, void* v, float* ks, float* vs,
   if (!k || !v || n_blocks < 1) return fail(c, BCI_E_INVALID, "bind_kv_cache: null buffer or n_blocks < 1");
   if (fp8 && (!ks || !vs)) return fail(c, BCI_E_INVALID, "bind_kv_cache: FP8 cache needs scales");
   if (!fp8 && (ks || vs)) return fail(c, BCI_E_INVALID, "bind_kv_cache: bf16 cache takes no scales");
+  if (!aligned16(k) || !aligned16(v) || (fp8 && (!aligned16(ks) || !aligned16(vs))))
+    return fail(c, BCI_E_INVALID, "bind_kv_cache: buffers must be 16-byte aligned");
   c->kc = k;
   c->vc = v;
   c->kscale = ks;
@@ -524,6 +528,8 @@ bci_status bci_op_rope_kv_write(bci_ctx* c, const void* qkv, void* q_out, int32_
   if (bci_status st = need_batch(c, "op_rope_kv_write")) return st;
   if (!qkv || !q_out || layer < 0 || layer >= c->cfg.n_layers)
     return fail(c, BCI_E_INVALID, "op_rope_kv_write: null pointer or layer %d", layer);
+  if (!aligned16(qkv) || !aligned16(q_out))
+    return fail(c, BCI_E_INVALID, "op_rope_kv_write: qkv and q_out must be 16-byte aligned");
   return op_rope(c, qkv, q_out, layer, S(stream));
 }
 

@@ -162,11 +162,13 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Operand order: for the kinds that store C, W is the MFMA's first operand and
-  // A its second, so a lane ends up holding 4 consecutive columns of one row
-  // (vector stores); lm_head and split-K keep A first.  Either way each output
-  // element is the same ascending chain of the same 32-wide dot products.
-  constexpr bool SWAP = (KIND == K_BF16 || KIND == K_F32 || KIND == K_SILU);
+  // Operand order: for the SiLU kind W is the MFMA's first operand and A its
+  // second, so a lane ends up holding 4 consecutive output columns of one row
+  // (8-byte stores); the other kinds keep A first, where 16 lanes store 16
+  // consecutive columns of a row (measured faster for plain bf16 C than the
+  // 8-byte pattern).  Either way each output element is the same ascending
+  // chain of the same 32-wide dot products.
+  constexpr bool SWAP = (KIND == K_SILU);
   auto mfma = [&](const bf16x8_t& fa, const bf16x8_t& fb, f32x4_t c) {
     if constexpr (SWAP) return __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb, fa, c, 0, 0, 0);
     else return __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, c, 0, 0, 0);
@@ -262,43 +264,23 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs p) {
         }
       }
   } else if constexpr (KIND == K_BF16 || KIND == K_F32) {
-    // swapped operands: lane holds row (lane & 15) of each block, columns 4 * (lane >> 4) + 0..3;
-    // vector stores need 4 | N and an aligned C, otherwise element stores
-    const bool vec = (p.N & 3) == 0 && (reinterpret_cast<uintptr_t>(p.C) & 15) == 0;
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-      const int lr = wm * WTM + mi * 16 + (lane & 15);
-      if (lr < row_cnt) {
-        const size_t rowoff = (size_t)(row_base + lr) * p.N;
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni) {
-          const int c0 = tn * BN + wn * WTN + ni * 16 + 4 * (lane >> 4);
-          const f32x4_t v = acc[mi][ni];
-          if constexpr (KIND == K_BF16) {
-            bf16_t* out = reinterpret_cast<bf16_t*>(p.C) + rowoff;
-            if (vec && c0 + 3 < p.N) {
-              uint2 w;
-              w.x = pack_bf2(f2bf(v[0]), f2bf(v[1]));
-              w.y = pack_bf2(f2bf(v[2]), f2bf(v[3]));
-              *reinterpret_cast<uint2*>(out + c0) = w;
-            } else {
+      for (int r = 0; r < 4; ++r) {
+        const int row = row0 + mi * 16 + r;
+        if (lrow0 + mi * 16 + r < row_cnt) {
 #pragma unroll
-              for (int r = 0; r < 4; ++r)
-                if (c0 + r < p.N) out[c0 + r] = f2bf(v[r]);
-            }
-          } else {
-            float* out = reinterpret_cast<float*>(p.C) + rowoff;
-            if (vec && c0 + 3 < p.N) {
-              *reinterpret_cast<f32x4_t*>(out + c0) = v;
-            } else {
-#pragma unroll
-              for (int r = 0; r < 4; ++r)
-                if (c0 + r < p.N) out[c0 + r] = v[r];
-            }
+          for (int ni = 0; ni < NI; ++ni) {
+            const int col = tn * BN + wn * WTN + ni * 16 + (lane & 15);
+            if (col >= p.N) continue;
+            if constexpr (KIND == K_BF16)
+              reinterpret_cast<bf16_t*>(p.C)[(size_t)row * p.N + col] = f2bf(acc[mi][ni][r]);
+            else
+              reinterpret_cast<float*>(p.C)[(size_t)row * p.N + col] = acc[mi][ni][r];
           }
         }
       }
-    }
   } else if constexpr (KIND == K_SILU) {
     const int I = p.N >> 1;
     const bool vec = (reinterpret_cast<uintptr_t>(p.C) & 7) == 0;

@@ -17,66 +17,92 @@
 
 namespace bci {
 
-// One workgroup per token, one wave per head (heads strided over the 4
-// waves); lane i owns the rotation pair (i, i + d/2).  Scale rule: amax over
-// the head's d rounded values (an exact max), s = amax / 448.
+// One workgroup per token.  Work unit u = (head u / (d/16), chunk j = u % (d/16)):
+// one thread owns the 8 rotation pairs (8j + i, d/2 + 8j + i), i = 0..7, so
+// every load and store moves 16 bytes; the d/16 units of a head are
+// consecutive lanes of one wave.  Scale rule: amax over the head's d rounded
+// values (an exact max, so the reduction order is immaterial), s = amax / 448.
 __global__ __launch_bounds__(256) void rope_kv_write_kernel(
     const bf16_t* __restrict__ qkv, bf16_t* __restrict__ q_out, const int32_t* __restrict__ tok_pos,
     const int32_t* __restrict__ tok_slot, const float* __restrict__ rcos,
     const float* __restrict__ rsin, KvLayer kv, int nq, int nkv, int d, int fp8) {
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  typedef float f32x4v_t __attribute__((ext_vector_type(4)));
   const int t = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = d >> 1;
+  const int upr = d >> 4;  // units (threads) per head
   const int pos = tok_pos[t];
   const int slot = tok_slot[t];
   const int blk = slot >> 6, off = slot & 63;
-  const int width = (nq + 2 * nkv) * d;
-  const bf16_t* x = qkv + (size_t)t * width;
-  const bool active = lane < half;
-  const float c = active ? rcos[(size_t)pos * half + lane] : 0.0f;
-  const float s = active ? rsin[(size_t)pos * half + lane] : 0.0f;
-
-  for (int hd = wave; hd < nq + 2 * nkv; hd += 4) {
-    bf16_t y1 = 0, y2 = 0;
-    if (active) {
-      const float x1 = bf2f(x[hd * d + lane]);
-      const float x2 = bf2f(x[hd * d + lane + half]);
-      if (hd < nq + nkv) {  // q and k heads are rotated
-        const float a1 = x1 * c, b1 = x2 * s;
-        const float a2 = x2 * c, b2 = x1 * s;
-        y1 = f2bf(a1 - b1);
-        y2 = f2bf(a2 + b2);
-      } else {
-        y1 = f2bf(x1);
-        y2 = f2bf(x2);
-      }
-    }
-    if (hd < nq) {
-      if (active) {
-        q_out[(size_t)t * nq * d + hd * d + lane] = y1;
-        q_out[(size_t)t * nq * d + hd * d + lane + half] = y2;
-      }
-      continue;
-    }
-    const bool is_k = hd < nq + nkv;
-    const int g = is_k ? hd - nq : hd - nq - nkv;
-    const size_t row = ((size_t)blk * nkv + g) * 64 + off;  // cache row of (block, head, slot)
-    if (!fp8) {
-      bf16_t* dst = reinterpret_cast<bf16_t*>(is_k ? kv.k : kv.v) + row * d;
-      if (active) {
-        dst[lane] = y1;
-        dst[lane + half] = y2;
+  const int n_heads = nq + 2 * nkv;
+  const bf16_t* x = qkv + (size_t)t * n_heads * d;
+  for (int u = threadIdx.x; u < n_heads * upr; u += blockDim.x) {
+    const int hd = u / upr, j = u % upr;
+    const int e0 = 8 * j;  // first element of the pair's low half
+    const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(x + hd * d + e0);
+    const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(x + hd * d + half + e0);
+    const bf16_t* xl = reinterpret_cast<const bf16_t*>(&lo);
+    const bf16_t* xh = reinterpret_cast<const bf16_t*>(&hi);
+    float y1[8], y2[8];
+    if (hd < nq + nkv) {  // q and k heads are rotated
+      const f32x4v_t c0 = *reinterpret_cast<const f32x4v_t*>(rcos + (size_t)pos * half + e0);
+      const f32x4v_t c1 = *reinterpret_cast<const f32x4v_t*>(rcos + (size_t)pos * half + e0 + 4);
+      const f32x4v_t s0 = *reinterpret_cast<const f32x4v_t*>(rsin + (size_t)pos * half + e0);
+      const f32x4v_t s1 = *reinterpret_cast<const f32x4v_t*>(rsin + (size_t)pos * half + e0 + 4);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float c = i < 4 ? c0[i] : c1[i - 4];
+        const float sn = i < 4 ? s0[i] : s1[i - 4];
+        const float x1 = bf2f(xl[i]), x2 = bf2f(xh[i]);
+        const float a1 = x1 * c, b1 = x2 * sn;
+        const float a2 = x2 * c, b2 = x1 * sn;
+        y1[i] = bf2f(f2bf(a1 - b1));
+        y2[i] = bf2f(f2bf(a2 + b2));
       }
     } else {
-      const float f1 = bf2f(y1), f2 = bf2f(y2);
-      const float amax = wave_max(active ? fmaxf(fabsf(f1), fabsf(f2)) : 0.0f);
-      const float sc = kv_scale_from_amax(amax);
-      uint8_t* dst = reinterpret_cast<uint8_t*>(is_k ? kv.k : kv.v) + row * d;
-      if (active) {
-        dst[lane] = (uint8_t)kv_encode(f1, sc);
-        dst[lane + half] = (uint8_t)kv_encode(f2, sc);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        y1[i] = bf2f(xl[i]);
+        y2[i] = bf2f(xh[i]);
       }
-      if (lane == 0) (is_k ? kv.ks : kv.vs)[row] = sc;
+    }
+    if (hd < nq || !fp8) {
+      u32x4_t wl, wh;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        wl[i] = pack_f2bf2(y1[2 * i], y1[2 * i + 1]);
+        wh[i] = pack_f2bf2(y2[2 * i], y2[2 * i + 1]);
+      }
+      bf16_t* dst;
+      if (hd < nq) {
+        dst = q_out + (size_t)t * nq * d + hd * d;
+      } else {
+        const bool is_k = hd < nq + nkv;
+        const int g = is_k ? hd - nq : hd - nq - nkv;
+        const size_t row = ((size_t)blk * nkv + g) * 64 + off;  // cache row of (block, head, slot)
+        dst = reinterpret_cast<bf16_t*>(is_k ? kv.k : kv.v) + row * d;
+      }
+      *reinterpret_cast<u32x4_t*>(dst + e0) = wl;
+      *reinterpret_cast<u32x4_t*>(dst + half + e0) = wh;
+    } else {
+      const bool is_k = hd < nq + nkv;
+      const int g = is_k ? hd - nq : hd - nq - nkv;
+      const size_t row = ((size_t)blk * nkv + g) * 64 + off;
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fmaxf(fabsf(y1[i]), fabsf(y2[i])));
+      for (int o = 1; o < upr; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, WAVE));
+      const float sc = kv_scale_from_amax(amax);
+      uint32_t c1[2] = {0, 0}, c2[2] = {0, 0};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        c1[i >> 2] |= kv_encode(y1[i], sc) << (8 * (i & 3));
+        c2[i >> 2] |= kv_encode(y2[i], sc) << (8 * (i & 3));
+      }
+      uint8_t* dst = reinterpret_cast<uint8_t*>(is_k ? kv.k : kv.v) + row * d;
+      *reinterpret_cast<uint2*>(dst + e0) = make_uint2(c1[0], c1[1]);
+      *reinterpret_cast<uint2*>(dst + half + e0) = make_uint2(c2[0], c2[1]);
+      if (j == 0) (is_k ? kv.ks : kv.vs)[row] = sc;
     }
   }
 }
@@ -86,7 +112,9 @@ hipError_t launch_rope_kv_write(const void* qkv, void* q_out, const int32_t* tok
                                 const float* rope_sin, KvLayer kv, int T, int nq, int nkv, int d,
                                 bool fp8, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(rope_kv_write_kernel, dim3(T), dim3(256), 0, s, (const bf16_t*)qkv,
+  const int units = (nq + 2 * nkv) * (d / 16);
+  const int threads = units >= 256 ? 256 : (units + 63) / 64 * 64;
+  hipLaunchKernelGGL(rope_kv_write_kernel, dim3(T), dim3(threads), 0, s, (const bf16_t*)qkv,
                      (bf16_t*)q_out, tok_pos, tok_slot, rope_cos, rope_sin, kv, nq, nkv, d,
                      (int)fp8);
   return hipGetLastError();

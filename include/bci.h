@@ -149,6 +149,7 @@ uint64_t bci_weight_version(const bci_ctx* ctx);
 /* Binds a paged KV cache.  Layout, per tensor:
  *   k, v   : [n_layers, n_blocks, n_kv_heads, 64, head_dim]  bf16, or uint8 e4m3fn codes
  *   k_scale, v_scale (FP8 only, else NULL): [n_layers, n_blocks, n_kv_heads, 64] fp32
+ * Every buffer must be 16-byte aligned (BCI_E_INVALID otherwise).
  * The rollout call and the training recompute bind different buffers (the
  * private cache copy of the digest's FP8 paragraph), written through the same
  * quantiser. */
@@ -198,7 +199,8 @@ bci_status bci_op_gemm_bf16(bci_ctx* ctx, const void* A, const void* W, void* C,
  * writes q' to q_out [n_tokens, nq * d] and k', v into the bound cache (bf16, or
  * e4m3 with the per-token-per-head scale rule a = max|x|, s = a / 448, code =
  * e4m3_rne(clamp(x / s, +-448)); page "Finish RL Training Faster" digest, section
- * "让训练前向使用推理的数值", FP8 KV paragraph). */
+ * "让训练前向使用推理的数值", FP8 KV paragraph).  qkv and q_out must be 16-byte
+ * aligned (BCI_E_INVALID otherwise). */
 bci_status bci_op_rope_kv_write(bci_ctx* ctx, const void* qkv, void* q_out, int32_t layer,
                                 void* stream);
 
