@@ -21,13 +21,32 @@ exactly 0), and the CPU oracle timed on a bounded sample.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+
+def gate_up_traffic():
+    """HBM bytes of one gate_up launch at M = 16384 from the committed counter profile
+    (FETCH_SIZE + WRITE_SIZE, calibrated on a 1 GiB copy), or None when the GEMM source
+    has changed since the counters were taken."""
+    prof = os.path.join(ROOT, "profiles", "gate_up_gemm_hbm_counters.md")
+    src = os.path.join(ROOT, "bitwise_consistent_rl_amd", "csrc", "gemm.hip")
+    try:
+        text = open(prof).read()
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    m = re.search(r"traffic-record: gemm\.hip sha256=([0-9a-f]{64}) bytes_per_launch=(\d+) m=(\d+)", text)
+    if not m or m.group(1) != digest:
+        return None
+    return {"bytes_per_launch": int(m.group(2)), "m": int(m.group(3))}
+
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
@@ -386,6 +405,8 @@ def main():
                                        == lp_host[: sum(len(r) for r in rec)].tobytes())
     del roll_cache
 
+    tr = gate_up_traffic()
+    traffic = tr["bytes_per_launch"] if tr else None
     out = {
         "metric": "invariant logprob-recompute tokens/sec @1 GPU, % roofline; diff/k3-KL must be 0",
         "value": round(scored / (dt / args.steps), 1),
@@ -405,7 +426,9 @@ def main():
                    "kv_cache": "bf16", "mode": "invariant"},
         "roofline": {"bound": "mfma", "kernel": "gate_up GEMM (SiLU*up epilogue)",
                      "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "traffic_unit": "HBM bytes per launch at M = 16384 (rocprofv3 FETCH_SIZE + "
+                                     "WRITE_SIZE, copy-calibrated)",
                      "launches": gu_launches, "avg_launch_us": round(gu_ms * 1e3 / max(gu_launches, 1), 2)},
         "step_roofline": {"algorithmic_tflop_per_step": round(step_flops / 1e12, 3),
                           "achieved_tflops": round(step_flops / (dt / args.steps) / 1e12, 1),

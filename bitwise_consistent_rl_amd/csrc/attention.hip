@@ -202,10 +202,95 @@ struct ChunkLoader {
   }
 };
 
+// Synchronous chunk load for the single-buffer schedule: each unit is loaded,
+// converted and stored in turn, which keeps few registers live.
+template <int D, bool FP8>
+__device__ __forceinline__ void load_chunk_sync(const AttnArgs& p, int blk, int g, int key_lim,
+                                           u32x4_t* Ks, bf16_t* Vt, int tid) {
+  const size_t base = ((size_t)blk * p.nkv + g) * CHUNK;  // first cache row of the chunk
+  if constexpr (!FP8) {
+    const bf16_t* kg = reinterpret_cast<const bf16_t*>(p.kv.k) + base * D;
+    const bf16_t* vg = reinterpret_cast<const bf16_t*>(p.kv.v) + base * D;
+    constexpr int CH = D / 8;  // 16-byte chunks per key row
+    // K: straight copy, swizzled
+#pragma unroll
+    for (int u = tid; u < CHUNK * CH; u += ATHREADS) {
+      const int key = u / CH, ch = u % CH;
+      u32x4_t v = *reinterpret_cast<const u32x4_t*>(kg + key * D + ch * 8);
+      if (key > key_lim) v = u32x4_t{0, 0, 0, 0};
+      Ks[kswz<D>(key, ch)] = v;
+    }
+    // V: two consecutive keys per unit, written transposed as 4-byte pairs
+#pragma unroll
+    for (int u = tid; u < (CHUNK / 2) * CH; u += ATHREADS) {
+      const int kp = u / CH, ch = u % CH;
+      const int k0 = 2 * kp;
+      u32x4_t a = *reinterpret_cast<const u32x4_t*>(vg + k0 * D + ch * 8);
+      u32x4_t b = *reinterpret_cast<const u32x4_t*>(vg + (k0 + 1) * D + ch * 8);
+      if (k0 > key_lim) a = u32x4_t{0, 0, 0, 0};
+      if (k0 + 1 > key_lim) b = u32x4_t{0, 0, 0, 0};
+      const bf16_t* pa = reinterpret_cast<const bf16_t*>(&a);
+      const bf16_t* pb = reinterpret_cast<const bf16_t*>(&b);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        *reinterpret_cast<uint32_t*>(Vt + (ch * 8 + i) * VT_STRIDE + k0) = pack_bf2(pa[i], pb[i]);
+    }
+  } else {
+    const uint8_t* kg = reinterpret_cast<const uint8_t*>(p.kv.k) + base * D;
+    const uint8_t* vg = reinterpret_cast<const uint8_t*>(p.kv.v) + base * D;
+    const float* ksg = p.kv.ks + base;
+    const float* vsg = p.kv.vs + base;
+    constexpr int CH16 = D / 16;  // 16-code chunks per key row
+#pragma unroll
+    for (int u = tid; u < CHUNK * CH16; u += ATHREADS) {
+      const int key = u / CH16, c16 = u % CH16;
+      const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(kg + key * D + c16 * 16);
+      const float sc = ksg[key];
+      const uint8_t* cb = reinterpret_cast<const uint8_t*>(&raw);
+      u32x4_t lo, hi;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lo[i] = pack_bf2(kv_decode(cb[2 * i], sc), kv_decode(cb[2 * i + 1], sc));
+        hi[i] = pack_bf2(kv_decode(cb[8 + 2 * i], sc), kv_decode(cb[8 + 2 * i + 1], sc));
+      }
+      if (key > key_lim) {
+        lo = u32x4_t{0, 0, 0, 0};
+        hi = u32x4_t{0, 0, 0, 0};
+      }
+      Ks[kswz<D>(key, 2 * c16)] = lo;
+      Ks[kswz<D>(key, 2 * c16 + 1)] = hi;
+    }
+#pragma unroll
+    for (int u = tid; u < (CHUNK / 2) * CH16; u += ATHREADS) {
+      const int kp = u / CH16, c16 = u % CH16;
+      const int k0 = 2 * kp;
+      const u32x4_t ra = *reinterpret_cast<const u32x4_t*>(vg + k0 * D + c16 * 16);
+      const u32x4_t rb = *reinterpret_cast<const u32x4_t*>(vg + (k0 + 1) * D + c16 * 16);
+      const float sa = vsg[k0], sb = vsg[k0 + 1];
+      const uint8_t* ca = reinterpret_cast<const uint8_t*>(&ra);
+      const uint8_t* cb = reinterpret_cast<const uint8_t*>(&rb);
+      const bool za = k0 > key_lim, zb = k0 + 1 > key_lim;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const bf16_t va = za ? (bf16_t)0 : kv_decode(ca[i], sa);
+        const bf16_t vb = zb ? (bf16_t)0 : kv_decode(cb[i], sb);
+        *reinterpret_cast<uint32_t*>(Vt + (c16 * 16 + i) * VT_STRIDE + k0) = pack_bf2(va, vb);
+      }
+    }
+  }
+}
+
+// Two schedules of the same per-row arithmetic.  PIPE (tiles of many rows:
+// prefill, recompute): two LDS buffers, chunk c+1 in flight while chunk c is
+// multiplied.  !PIPE (the split schedule, used for decode-like calls with few
+// rows per tile): one LDS buffer and short register lifetimes, so twice as
+// many workgroups fit on a CU to hide the load latency.
 template <int D, bool FP8, bool SPLIT>
-__global__ __launch_bounds__(ATHREADS, 2) void attention_kernel(AttnArgs p) {
-  __shared__ __attribute__((aligned(16))) u32x4_t Ks[2][CHUNK * D / 8];
-  __shared__ __attribute__((aligned(16))) bf16_t Vt[2][D * VT_STRIDE];
+__global__ __launch_bounds__(ATHREADS, SPLIT ? 4 : 2) void attention_kernel(AttnArgs p) {
+  constexpr bool PIPE = !SPLIT;
+  constexpr int NBUF = PIPE ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) u32x4_t Ks[NBUF][CHUNK * D / 8];
+  __shared__ __attribute__((aligned(16))) bf16_t Vt[NBUF][D * VT_STRIDE];
 
   // Workgroups are handed to the 8 XCDs round-robin; renumber them so each XCD
   // gets a contiguous run of (kv head, tile) pairs, i.e. consecutive tiles of
@@ -251,7 +336,7 @@ __global__ __launch_bounds__(ATHREADS, 2) void attention_kernel(AttnArgs p) {
   }
 
   ChunkLoader<D, FP8> ld;
-  ld.issue(p, btab[c_first], g, tid);
+  if constexpr (PIPE) ld.issue(p, btab[c_first], g, tid);
 
   bf16x8_t qf[D / 32];
 #pragma unroll
@@ -271,13 +356,21 @@ __global__ __launch_bounds__(ATHREADS, 2) void attention_kernel(AttnArgs p) {
   float m = -INFINITY, l = 0.0f;
   f32x4_t acc[D / 16];
 
-  ld.store(kmax - c_first * CHUNK, Ks[0], Vt[0], tid);
-  __syncthreads();
+  if constexpr (PIPE) {
+    ld.store(kmax - c_first * CHUNK, Ks[0], Vt[0], tid);
+    __syncthreads();
+  }
 
   for (int c = c_first; c <= c_stop; ++c) {
-    const int b = (c - c_first) & 1;
+    const int b = PIPE ? (c - c_first) & 1 : 0;
     const bool more = c < c_stop;
-    if (more) ld.issue(p, btab[c + 1], g, tid);
+    if constexpr (PIPE) {
+      if (more) ld.issue(p, btab[c + 1], g, tid);
+    } else {
+      if (c > c_first) __syncthreads();  // the previous chunk's LDS reads are done
+      load_chunk_sync<D, FP8>(p, btab[c], g, kmax - c * CHUNK, Ks[0], Vt[0], tid);
+      __syncthreads();
+    }
     const bool seg_start = (c % seg_chunks) == 0 || c == c_first;
     if (seg_start) m = -INFINITY;
     const u32x4_t* Kb = Ks[b];
@@ -380,9 +473,11 @@ __global__ __launch_bounds__(ATHREADS, 2) void attention_kernel(AttnArgs p) {
       }
     }
 
-    // buffer b^1 was released by the previous iteration's barrier
-    if (more) ld.store(kmax - (c + 1) * CHUNK, Ks[b ^ 1], Vt[b ^ 1], tid);
-    __syncthreads();  // publishes buffer b^1, releases buffer b
+    if constexpr (PIPE) {
+      // buffer b^1 was released by the previous iteration's barrier
+      if (more) ld.store(kmax - (c + 1) * CHUNK, Ks[b ^ 1], Vt[b ^ 1], tid);
+      __syncthreads();  // publishes buffer b^1, releases buffer b
+    }
   }
 
   if constexpr (SPLIT) {
