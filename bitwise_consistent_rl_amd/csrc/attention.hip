@@ -406,8 +406,7 @@ __global__ __launch_bounds__(ATHREADS, SPLIT ? 4 : 2) void attention_kernel(Attn
         }
         mloc = fmaxf(mloc, t[kt][r]);
       }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, WAVE));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, WAVE));
+    mloc = xrow_max(mloc);
     const float mn = fmaxf(m, mloc);
     const float mu = (mn == -INFINITY) ? 0.0f : mn;
     float rs = 0.0f;
@@ -419,8 +418,7 @@ __global__ __launch_bounds__(ATHREADS, SPLIT ? 4 : 2) void attention_kernel(Attn
         pr[kt][r] = fexp2(t[kt][r] - mu);
         rs = rs + pr[kt][r];
       }
-    rs = rs + __shfl_xor(rs, 16, WAVE);
-    rs = rs + __shfl_xor(rs, 32, WAVE);
+    rs = xrow_sum(rs);
     if (seg_start) {
       // (m, l, acc) = (-inf, 0, 0): alpha = 2^(-inf) = 0, so l * alpha + rs is rs
       // and acc * alpha is +0, exactly what these shortcuts give

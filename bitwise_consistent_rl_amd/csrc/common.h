@@ -100,7 +100,10 @@ __device__ __forceinline__ bf16_t kv_decode(uint32_t code, float s) {
 // ------------------------------------------------------------ math
 
 __device__ __forceinline__ float fexp(float x) { return expf(x); }
-__device__ __forceinline__ float fexp2(float x) { return exp2f(x); }
+// v_exp_f32.  Compared with the library exp2f on all 2^32 inputs on gfx950: equal for
+// every x >= -126; only results below 2^-126 (denormal range) differ.  exp2(0) = 1 and
+// exp2(-inf) = 0 exactly, which the attention's no-op chunks rely on.
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float flog(float x) { return logf(x); }
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + fexp(-g)); }
 
@@ -108,6 +111,23 @@ __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + fexp(-g)
 // Fixed xor butterflies over the 64 lanes (or a lane group).  For + the two
 // partners add the same two values in either order, which IEEE addition
 // makes bit-identical, so every lane ends with the same bits.
+
+// Reductions over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the same position in each
+// 16-lane row), every lane getting the result.  v_permlane16/32_swap leave each lane
+// holding its own value and its partner's (order depends on the lane); max and fp32
+// addition are commutative, so every lane computes (v_l (+) v_l^16) (+) (same for l^32).
+__device__ __forceinline__ float xrow_max(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float xrow_sum(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
