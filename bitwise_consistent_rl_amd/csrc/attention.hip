@@ -156,12 +156,13 @@ struct ChunkLoader {
         const int u = j * ATHREADS + tid;
         if (u < KUN) {
           const int key = u / CH16, c16 = u % CH16;
-          const uint8_t* cb = reinterpret_cast<const uint8_t*>(&kr[j]);
+          float x[16];
+          kv_decode16_f32(reinterpret_cast<const uint32_t*>(&kr[j]), ksc[j], x);
           u32x4_t lo, hi;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            lo[i] = pack_bf2(kv_decode(cb[2 * i], ksc[j]), kv_decode(cb[2 * i + 1], ksc[j]));
-            hi[i] = pack_bf2(kv_decode(cb[8 + 2 * i], ksc[j]), kv_decode(cb[8 + 2 * i + 1], ksc[j]));
+            lo[i] = pack_f2bf2(x[2 * i], x[2 * i + 1]);
+            hi[i] = pack_f2bf2(x[8 + 2 * i], x[8 + 2 * i + 1]);
           }
           Ks[kswz<D>(key, 2 * c16)] = lo;
           Ks[kswz<D>(key, 2 * c16 + 1)] = hi;
@@ -188,13 +189,14 @@ struct ChunkLoader {
           for (int i = 0; i < 8; ++i)
             *reinterpret_cast<uint32_t*>(Vt + (ch * 8 + i) * VT_STRIDE + k0) = pack_bf2(pa[i], pb[i]);
         } else {
-          const uint8_t* ca = reinterpret_cast<const uint8_t*>(&va[j]);
-          const uint8_t* cb = reinterpret_cast<const uint8_t*>(&vb[j]);
+          float xa[16], xb[16];
+          kv_decode16_f32(reinterpret_cast<const uint32_t*>(&va[j]), vsa[j], xa);
+          kv_decode16_f32(reinterpret_cast<const uint32_t*>(&vb[j]), vsb[j], xb);
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const bf16_t x = za ? (bf16_t)0 : kv_decode(ca[i], vsa[j]);
-            const bf16_t y = zb ? (bf16_t)0 : kv_decode(cb[i], vsb[j]);
-            *reinterpret_cast<uint32_t*>(Vt + (ch * 16 + i) * VT_STRIDE + k0) = pack_bf2(x, y);
+            const uint32_t w = pack_f2bf2(xa[i], xb[i]);
+            *reinterpret_cast<uint32_t*>(Vt + (ch * 16 + i) * VT_STRIDE + k0) =
+                (za ? 0u : (w & 0xffffu)) | (zb ? 0u : (w & 0xffff0000u));
           }
         }
       }
@@ -246,12 +248,13 @@ __device__ __forceinline__ void load_chunk_sync(const AttnArgs& p, int blk, int 
       const int key = u / CH16, c16 = u % CH16;
       const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(kg + key * D + c16 * 16);
       const float sc = ksg[key];
-      const uint8_t* cb = reinterpret_cast<const uint8_t*>(&raw);
+      float x[16];
+      kv_decode16_f32(reinterpret_cast<const uint32_t*>(&raw), sc, x);
       u32x4_t lo, hi;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        lo[i] = pack_bf2(kv_decode(cb[2 * i], sc), kv_decode(cb[2 * i + 1], sc));
-        hi[i] = pack_bf2(kv_decode(cb[8 + 2 * i], sc), kv_decode(cb[8 + 2 * i + 1], sc));
+        lo[i] = pack_f2bf2(x[2 * i], x[2 * i + 1]);
+        hi[i] = pack_f2bf2(x[8 + 2 * i], x[8 + 2 * i + 1]);
       }
       if (key > key_lim) {
         lo = u32x4_t{0, 0, 0, 0};
@@ -267,14 +270,15 @@ __device__ __forceinline__ void load_chunk_sync(const AttnArgs& p, int blk, int 
       const u32x4_t ra = *reinterpret_cast<const u32x4_t*>(vg + k0 * D + c16 * 16);
       const u32x4_t rb = *reinterpret_cast<const u32x4_t*>(vg + (k0 + 1) * D + c16 * 16);
       const float sa = vsg[k0], sb = vsg[k0 + 1];
-      const uint8_t* ca = reinterpret_cast<const uint8_t*>(&ra);
-      const uint8_t* cb = reinterpret_cast<const uint8_t*>(&rb);
       const bool za = k0 > key_lim, zb = k0 + 1 > key_lim;
+      float xa[16], xb[16];
+      kv_decode16_f32(reinterpret_cast<const uint32_t*>(&ra), sa, xa);
+      kv_decode16_f32(reinterpret_cast<const uint32_t*>(&rb), sb, xb);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const bf16_t va = za ? (bf16_t)0 : kv_decode(ca[i], sa);
-        const bf16_t vb = zb ? (bf16_t)0 : kv_decode(cb[i], sb);
-        *reinterpret_cast<uint32_t*>(Vt + (c16 * 16 + i) * VT_STRIDE + k0) = pack_bf2(va, vb);
+        const uint32_t w = pack_f2bf2(xa[i], xb[i]);
+        *reinterpret_cast<uint32_t*>(Vt + (c16 * 16 + i) * VT_STRIDE + k0) =
+            (za ? 0u : (w & 0xffffu)) | (zb ? 0u : (w & 0xffff0000u));
       }
     }
   }

@@ -93,8 +93,30 @@ __device__ __forceinline__ uint32_t kv_encode(float x, float s) {
   return f32_to_e4m3(q);
 }
 // ... and the one dequantisation: bf(fp32(code) * s).
+// e4m3fn -> fp32 of the four codes of a word by v_cvt_pk_f32_fp8 (byte i -> element i).
+// On gfx950 this conversion is OCP e4m3fn; it equals e4m3_to_f32 above for all 256
+// codes (NaN for NaN), checked on the GPU.
+__device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float* f) {
+  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  f[0] = a[0];
+  f[1] = a[1];
+  f[2] = b[0];
+  f[3] = b[1];
+}
 __device__ __forceinline__ bf16_t kv_decode(uint32_t code, float s) {
-  return f2bf(e4m3_to_f32(code) * s);
+  float f[4];
+  e4m3x4_to_f32(code & 0xffu, f);
+  return f2bf(f[0] * s);
+}
+// sixteen codes (one 16-byte load) -> sixteen products fp32(code) * s, not yet rounded
+__device__ __forceinline__ void kv_decode16_f32(const uint32_t* w, float s, float* x) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    e4m3x4_to_f32(w[i], x + 4 * i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[4 * i + j] = x[4 * i + j] * s;
+  }
 }
 
 // ------------------------------------------------------------ math
