@@ -189,6 +189,32 @@ def rollout_bench(args, cfg):
     inv, fast = results["invariant"], results["fast"]
     stats = engine.acceptance(fast["lp"], inv["lp"])
     weight_bytes = sum(v.numel() for v in weights.values()) * 2
+
+    # (3) invariant rollout throughput at each batch cap, and one run with a random cap
+    # (1..256) per step; every run's logprobs must equal the recompute's bit for bit
+    seqs_all = synth.rl_sequences(cfg, n_prompts=32, n_responses=8)
+    m = engine.Model(cfg, weights, max_tokens=8192, max_seqs=256, max_scored=8192,
+                     max_position=1024, seg_keys=QWEN_SEG_KEYS)
+    cache = m.new_cache(256 * 11 + 16)
+    rec = engine.recompute(m, seqs_all, cache)
+    caps = {}
+    for cap, n in ((1, 2), (8, 16), (32, 64), (128, 128), (256, 256)):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        lp = engine.rollout(m, seqs_all[:n], cache, cap=cap)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        caps[str(cap)] = {"sequences": n, "tokens_per_s": round(sum(len(x) for x in lp) / dt, 1),
+                          "bitwise_equal_to_recompute": all(a.tobytes() == b.tobytes()
+                                                            for a, b in zip(lp, rec[:n]))}
+        log(f"rollout cap {cap}: {caps[str(cap)]}")
+    rng = np.random.default_rng(9012)
+    lp = engine.rollout(m, seqs_all, cache, cap=256,
+                        cap_schedule=lambda step: int(rng.integers(1, 257)))
+    random_cap_equal = all(a.tobytes() == b.tobytes() for a, b in zip(lp, rec))
+    m.close()
+    del cache
+    torch.cuda.empty_cache()
     print(json.dumps({
         "workload": "qwen3-1.7b-shaped rollout, 16 prompts x 8 responses, continuous batching cap 128",
         "scored_tokens": inv["scored"],
@@ -198,7 +224,9 @@ def rollout_bench(args, cfg):
         "decode_step_ms": {"invariant": {str(b): round(v, 3) for b, v in inv["steps"].items()},
                            "fast": {str(b): round(v, 3) for b, v in fast["steps"].items()}},
         "decode_roofline_ms": round(weight_bytes / (PEAK_HBM_GBS * 1e6), 3),
-        "fast_vs_invariant_logprobs": stats}), flush=True)
+        "fast_vs_invariant_logprobs": stats,
+        "invariant_by_cap": caps,
+        "random_cap_bitwise_equal_to_recompute": random_cap_equal}), flush=True)
 
 
 def longctx(args):
