@@ -141,6 +141,7 @@ def rollout_bench(args, cfg):
     weights = synth.make_weights(cfg)
     seqs = synth.rl_sequences(cfg, n_prompts=16, n_responses=8)
     results = {}
+    graph_steps, graph_equal, graph_rollout = {}, {}, {}
     for mode in ("invariant", "fast"):
         m = engine.Model(cfg, weights, max_tokens=8192, max_seqs=128, max_scored=8192,
                          max_position=1024, seg_keys=QWEN_SEG_KEYS, mode=mode)
@@ -182,7 +183,32 @@ def rollout_bench(args, cfg):
             e1.record()
             torch.cuda.synchronize()
             steps[B] = e0.elapsed_time(e1) / 10
+            if mode == "invariant":
+                # the same step replayed from a captured HIP graph (block table padded to
+                # the context's width, as the graphed rollout does); bits must not change
+                width = -(-m.max_position // engine.KV_BLOCK)
+                gbt = np.array([b + [0] * (width - len(b)) for b in blocks], np.int32)
+                abi.bci_set_batch(m.ctx, dec.tokens, dec.cu_q, dec.pos0, gbt, dec.score_rows,
+                                  dec.score_ids)
+                gout = torch.empty(B, dtype=torch.float32, device="cuda")
+                for _ in range(3):
+                    abi.bci_forward_logprobs_graph(m.ctx, gout)
+                e0.record()
+                for _ in range(10):
+                    abi.bci_forward_logprobs_graph(m.ctx, gout)
+                e1.record()
+                torch.cuda.synchronize()
+                graph_steps[B] = e0.elapsed_time(e1) / 10
+                graph_equal[B] = bool(torch.equal(gout.view(torch.int32), out.view(torch.int32)))
         results[mode] = dict(lp=lp, tokens_per_s=scored / dt, seconds=dt, scored=scored, steps=steps)
+        if mode == "invariant":
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            lp_g = engine.rollout(m, seqs, cache, cap=128, graph=True)
+            torch.cuda.synchronize()
+            graph_rollout = {"tokens_per_s": round(scored / (time.perf_counter() - t0), 1),
+                             "bitwise_equal_to_eager": all(a.tobytes() == b.tobytes()
+                                                           for a, b in zip(lp_g, lp))}
         m.close()
         del cache
         torch.cuda.empty_cache()
@@ -224,6 +250,9 @@ def rollout_bench(args, cfg):
         "decode_step_ms": {"invariant": {str(b): round(v, 3) for b, v in inv["steps"].items()},
                            "fast": {str(b): round(v, 3) for b, v in fast["steps"].items()}},
         "decode_roofline_ms": round(weight_bytes / (PEAK_HBM_GBS * 1e6), 3),
+        "decode_step_ms_graph": {str(b): round(v, 3) for b, v in graph_steps.items()},
+        "graph_step_bitwise_equal": graph_equal,
+        "graph_rollout_cap128": graph_rollout,
         "fast_vs_invariant_logprobs": stats,
         "invariant_by_cap": caps,
         "random_cap_bitwise_equal_to_recompute": random_cap_equal}), flush=True)

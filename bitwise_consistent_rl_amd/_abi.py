@@ -32,7 +32,7 @@ EXPORTS = [
     "bci_op_embed", "bci_op_add_rmsnorm", "bci_op_gemm_bf16", "bci_op_rope_kv_write",
     "bci_op_kv_gather_dequant", "bci_op_attention", "bci_op_gather_scored",
     "bci_op_lmhead_logprob", "bci_op_moe_topk", "bci_op_moe_forward", "bci_profile_begin",
-    "bci_profile_end",
+    "bci_profile_end", "bci_forward_logprobs_graph", "bci_graph_count", "bci_graph_reset",
 ]
 
 
@@ -85,6 +85,9 @@ def load() -> ctypes.CDLL:
         "bci_bind_kv_cache": (st, [vp, vp, vp, vp, vp, i32]),
         "bci_set_batch": (st, [vp, ctypes.POINTER(Batch), vp]),
         "bci_forward_logprobs": (st, [vp, vp, vp]),
+        "bci_forward_logprobs_graph": (st, [vp, vp, vp]),
+        "bci_graph_count": (i32, [vp]),
+        "bci_graph_reset": (st, [vp]),
         "bci_op_embed": (st, [vp, vp, vp, vp]),
         "bci_op_add_rmsnorm": (st, [vp, vp, vp, vp, vp, i32, i32, ctypes.c_float, vp]),
         "bci_op_gemm_bf16": (st, [vp, vp, vp, vp, i32, i32, i32, i32, vp]),
@@ -194,6 +197,18 @@ def bci_set_batch(ctx: int, tokens, cu_q, pos0, block_table, score_rows, score_i
 
 def bci_forward_logprobs(ctx: int, logprobs, stream=None) -> None:
     _check(ctx, load().bci_forward_logprobs(ctx, _ptr(logprobs), _stream(stream)))
+
+
+def bci_forward_logprobs_graph(ctx: int, logprobs, stream=None) -> None:
+    _check(ctx, load().bci_forward_logprobs_graph(ctx, _ptr(logprobs), _stream(stream)))
+
+
+def bci_graph_count(ctx: int) -> int:
+    return int(load().bci_graph_count(ctx))
+
+
+def bci_graph_reset(ctx: int) -> None:
+    _check(ctx, load().bci_graph_reset(ctx))
 
 
 def bci_op_embed(ctx: int, E, r, stream=None) -> None:

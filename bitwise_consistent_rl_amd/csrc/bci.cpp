@@ -80,6 +80,20 @@ struct bci_ctx {
   bool prof_on = false;
   int prof_n = 0;
   std::vector<hipEvent_t> prof_ev;
+  // captured forwards, keyed by batch shape; bind_epoch changes whenever a rebind
+  // moves a weight or cache buffer, which invalidates every captured graph
+  struct Graph {
+    int n_tokens, n_seqs, n_scored, n_tiles, max_blocks;
+    uint64_t epoch;
+    hipGraph_t graph;
+    hipGraphExec_t exec;
+    uint64_t last_use;
+  };
+  std::vector<Graph> graphs;
+  uint64_t bind_epoch = 1, graph_clock = 0;
+  bool graph_mode = false;  // set while capturing: attention schedule independent of positions
+  hipStream_t cap_stream = nullptr;
+  float* graph_lp = nullptr;  // logprob output of captured forwards [max_scored]
 };
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -187,6 +201,7 @@ bci_status bci_create(const bci_model_config* cfg_in, int32_t device, bci_ctx** 
       {(void**)&c->part_m, (size_t)c->n_chunks * R * 4},
       {(void**)&c->part_s, (size_t)c->n_chunks * R * 4},
       {(void**)&c->zid, R * 4},
+      {(void**)&c->graph_lp, R * 4},
       {(void**)&c->rope_cos, (size_t)g.max_position * (g.head_dim / 2) * 4},
       {(void**)&c->rope_sin, (size_t)g.max_position * (g.head_dim / 2) * 4},
       {(void**)&c->meta, c->meta_words * 4},
@@ -263,9 +278,19 @@ bci_status bci_create(const bci_model_config* cfg_in, int32_t device, bci_ctx** 
   return BCI_OK;
 }
 
+static void drop_graphs(bci_ctx* c) {
+  for (auto& g : c->graphs) {
+    (void)hipGraphExecDestroy(g.exec);
+    (void)hipGraphDestroy(g.graph);
+  }
+  c->graphs.clear();
+}
+
 void bci_destroy(bci_ctx* c) {
   if (!c) return;
   hipSetDevice(c->device);
+  drop_graphs(c);
+  if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
   for (auto& e : c->prof_ev)
     if (e) hipEventDestroy(e);
   for (int i = 0; i < 2; ++i) {
@@ -289,6 +314,9 @@ bci_status bci_bind_weights(bci_ctx* c, const void* const* ptrs, int32_t n, uint
     return fail(c, BCI_E_INVALID, "bind_weights: expected %d pointers, got %d", (int)c->w.size(), n);
   for (int i = 0; i < n; ++i)
     if (!ptrs[i]) return fail(c, BCI_E_INVALID, "bind_weights: pointer %d is null", i);
+  bool moved = !c->weights_bound;
+  for (int i = 0; i < n; ++i) moved = moved || c->w[i] != ptrs[i];
+  if (moved) ++c->bind_epoch;  // captured graphs hold the old addresses
   for (int i = 0; i < n; ++i) c->w[i] = ptrs[i];
   c->weight_version = version;
   c->weights_bound = true;
@@ -305,6 +333,9 @@ bci_status bci_bind_kv_cache(bci_ctx* c, void* k, void* v, float* ks, float* vs,
   if (!fp8 && (ks || vs)) return fail(c, BCI_E_INVALID, "bind_kv_cache: bf16 cache takes no scales");
   if (!aligned16(k) || !aligned16(v) || (fp8 && (!aligned16(ks) || !aligned16(vs))))
     return fail(c, BCI_E_INVALID, "bind_kv_cache: buffers must be 16-byte aligned");
+  if (!c->cache_bound || c->kc != k || c->vc != v || c->kscale != ks || c->vscale != vs ||
+      c->n_blocks != n_blocks)
+    ++c->bind_epoch;
   c->kc = k;
   c->vc = v;
   c->kscale = ks;
@@ -468,9 +499,13 @@ static bci_status op_attn(bci_ctx* c, const void* q, void* o, int layer, hipStre
     a.seg_keys = cps * KV_BLOCK;
     a.n_seg = n_split > 1 ? (max_pos / a.seg_keys + 1) : 0;
   } else {
-    const bool can_split = c->attn_part_acc && c->batch_seg > 1 && c->n_tokens <= c->split_tokens;
+    // a captured forward must not depend on positions: it launches every segment the
+    // context can have; segments past a tile's last position return at once and the
+    // merge stops at each row's own last segment, so the bits are the same
+    const int nseg = c->graph_mode ? c->max_seg : c->batch_seg;
+    const bool can_split = c->attn_part_acc && nseg > 1 && c->n_tokens <= c->split_tokens;
     const bool want_split = g.attn_split_mode == 2 || (g.attn_split_mode == 0 && few_tiles);
-    a.n_seg = (can_split && want_split) ? c->batch_seg : 0;
+    a.n_seg = (can_split && want_split) ? nseg : 0;
   }
   a.part_acc = c->attn_part_acc;
   a.part_ml = c->attn_part_ml;
@@ -626,14 +661,19 @@ bci_status bci_op_moe_forward(bci_ctx* c, const void* h, const int32_t* ids, con
 
 // ------------------------------------------------------------ forward
 
+static bci_status forward_impl(bci_ctx* c, float* lp, hipStream_t s);
+
 bci_status bci_forward_logprobs(bci_ctx* c, float* lp, void* stream) {
   if (!c) return BCI_E_INVALID;
   if (!c->weights_bound) return fail(c, BCI_E_STATE, "forward: bind weights first");
   if (bci_status st = need_batch(c, "forward")) return st;
   if (c->n_scored && !lp) return fail(c, BCI_E_INVALID, "forward: null logprob output");
-  const auto& g = c->cfg;
-  const hipStream_t s = S(stream);
   HIP_TRY(c, hipSetDevice(c->device));
+  return forward_impl(c, lp, S(stream));
+}
+
+static bci_status forward_impl(bci_ctx* c, float* lp, hipStream_t s) {
+  const auto& g = c->cfg;
   const int T = c->n_tokens, H = g.hidden;
   const void* E = c->w[0];
   // layer 0 norm: residual = E[token] (exact copy), no add
@@ -650,7 +690,7 @@ bci_status bci_forward_logprobs(bci_ctx* c, float* lp, void* stream) {
     if (bci_status st = gemm_checked(c, c->bufO, nullptr, lw[2], c->bufX, T, H, c->qd, EPI_BF16, s)) return st;
     HIP_TRY(c, launch_add_rmsnorm(c->bufX, c->bufR, c->bufR, c->bufH, lw[3], nullptr, nullptr, T, H,
                                   g.rms_eps, s));
-    const bool prof = c->prof_on && c->prof_n < MAX_PROFILE;
+    const bool prof = c->prof_on && !c->graph_mode && c->prof_n < MAX_PROFILE;
     if (prof) HIP_TRY(c, hipEventRecord(c->prof_ev[2 * c->prof_n], s));
     if (bci_status st = gemm_checked(c, c->bufH, nullptr, lw[4], c->bufACT, T, 2 * g.intermediate, H,
                                      EPI_SILU, s))
@@ -667,6 +707,83 @@ bci_status bci_forward_logprobs(bci_ctx* c, float* lp, void* stream) {
     HIP_TRY(c, launch_lmhead_combine(c->part_m, c->part_s, c->zid, c->meta + c->o_sid, c->n_scored, g.vocab, lp,
                                      s));
   }
+  return BCI_OK;
+}
+
+// ------------------------------------------------------------ captured forward
+
+bci_status bci_forward_logprobs_graph(bci_ctx* c, float* lp, void* stream) {
+  if (!c) return BCI_E_INVALID;
+  if (!c->weights_bound) return fail(c, BCI_E_STATE, "forward_graph: bind weights first");
+  if (bci_status st = need_batch(c, "forward_graph")) return st;
+  if (c->n_scored && !lp) return fail(c, BCI_E_INVALID, "forward_graph: null logprob output");
+  if (c->cfg.mode != BCI_MODE_INVARIANT)
+    return fail(c, BCI_E_UNSUPPORTED, "forward_graph: only the invariant mode is captured");
+  if (c->cfg.n_experts > 0)
+    return fail(c, BCI_E_UNSUPPORTED, "forward_graph: the MoE layer is not captured");
+  HIP_TRY(c, hipSetDevice(c->device));
+  const hipStream_t s = S(stream);
+  bci_ctx::Graph* hit = nullptr;
+  for (auto& g : c->graphs)
+    if (g.n_tokens == c->n_tokens && g.n_seqs == c->n_seqs && g.n_scored == c->n_scored &&
+        g.n_tiles == c->n_tiles && g.max_blocks == c->max_blocks && g.epoch == c->bind_epoch)
+      hit = &g;
+  if (!hit) {
+    // drop graphs of an older binding, then the least recently used beyond 16
+    for (size_t i = 0; i < c->graphs.size();) {
+      if (c->graphs[i].epoch != c->bind_epoch) {
+        (void)hipGraphExecDestroy(c->graphs[i].exec);
+        (void)hipGraphDestroy(c->graphs[i].graph);
+        c->graphs.erase(c->graphs.begin() + i);
+      } else {
+        ++i;
+      }
+    }
+    if (c->graphs.size() >= 16) {
+      size_t lru = 0;
+      for (size_t i = 1; i < c->graphs.size(); ++i)
+        if (c->graphs[i].last_use < c->graphs[lru].last_use) lru = i;
+      (void)hipGraphExecDestroy(c->graphs[lru].exec);
+      (void)hipGraphDestroy(c->graphs[lru].graph);
+      c->graphs.erase(c->graphs.begin() + lru);
+    }
+    if (!c->cap_stream) HIP_TRY(c, hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking));
+    // the capture only records launches; the batch metadata it reads is uploaded by
+    // bci_set_batch before every launch of the graph
+    HIP_TRY(c, hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal));
+    c->graph_mode = true;
+    const bci_status st = forward_impl(c, c->graph_lp, c->cap_stream);
+    c->graph_mode = false;
+    hipGraph_t graph = nullptr;
+    const hipError_t e = hipStreamEndCapture(c->cap_stream, &graph);
+    if (st != BCI_OK) {
+      if (graph) (void)hipGraphDestroy(graph);
+      return st;
+    }
+    if (e != hipSuccess) return hipfail(c, e, "hipStreamEndCapture");
+    hipGraphExec_t exec = nullptr;
+    const hipError_t ei = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    if (ei != hipSuccess) {
+      (void)hipGraphDestroy(graph);
+      return hipfail(c, ei, "hipGraphInstantiate");
+    }
+    c->graphs.push_back({c->n_tokens, c->n_seqs, c->n_scored, c->n_tiles, c->max_blocks, c->bind_epoch,
+                         graph, exec, 0});
+    hit = &c->graphs.back();
+  }
+  hit->last_use = ++c->graph_clock;
+  HIP_TRY(c, hipGraphLaunch(hit->exec, s));
+  if (c->n_scored)
+    HIP_TRY(c, hipMemcpyAsync(lp, c->graph_lp, (size_t)c->n_scored * 4, hipMemcpyDeviceToDevice, s));
+  return BCI_OK;
+}
+
+int32_t bci_graph_count(const bci_ctx* c) { return c ? (int32_t)c->graphs.size() : 0; }
+
+bci_status bci_graph_reset(bci_ctx* c) {
+  if (!c) return BCI_E_INVALID;
+  HIP_TRY(c, hipSetDevice(c->device));
+  drop_graphs(c);
   return BCI_OK;
 }
 

@@ -96,6 +96,23 @@ class Model:
                              weight_version)
         self.bound_cache: Optional[KVCache] = None
 
+    # ------------------------------------------------------------- weights
+    def update_weights(self, weights: Dict[str, torch.Tensor], version: int) -> None:
+        """In-place update (e.g. after an optimiser step): new values are copied into
+        the bound buffers, whose addresses do not change, so captured graphs stay valid
+        and their next replay reads the new weights."""
+        for k, v in weights.items():
+            self.w[k].copy_(v.to(self.device))
+        abi.bci_bind_weights(self.ctx, [self.w[n] for n in weight_order(self.cfg.n_layers)],
+                             version)
+
+    def reload_weights(self, weights: Dict[str, torch.Tensor], version: int) -> None:
+        """Reload into fresh buffers: the binding moves, so captured graphs are dropped
+        and the next graphed call captures again."""
+        self.w = {k: v.to(self.device).contiguous().clone() for k, v in weights.items()}
+        abi.bci_bind_weights(self.ctx, [self.w[n] for n in weight_order(self.cfg.n_layers)],
+                             version)
+
     def close(self):
         if self.ctx:
             torch.cuda.synchronize(self.device)
@@ -144,13 +161,17 @@ class CallPlan:
     owners: List[tuple]
 
 
-def run_call(model: Model, plan: CallPlan, op_by_op: bool = False, stream=None) -> torch.Tensor:
-    """Run one varlen forward call; returns fp32 logprobs [n_scored] on the GPU."""
+def run_call(model: Model, plan: CallPlan, op_by_op: bool = False, stream=None,
+             graph: bool = False) -> torch.Tensor:
+    """Run one varlen forward call; returns fp32 logprobs [n_scored] on the GPU.
+    ``graph``: replay (or capture) the forward as a HIP graph for this batch shape."""
     ctx = model.ctx
     abi.bci_set_batch(ctx, plan.tokens, plan.cu_q, plan.pos0, plan.block_table, plan.score_rows,
                       plan.score_ids, stream)
     lp = torch.empty(len(plan.score_rows), dtype=torch.float32, device=model.device)
-    if not op_by_op:
+    if graph:
+        abi.bci_forward_logprobs_graph(ctx, lp if len(plan.score_rows) else None, stream)
+    elif not op_by_op:
         abi.bci_forward_logprobs(ctx, lp if len(plan.score_rows) else None, stream)
     else:
         _forward_op_by_op(model, plan, lp, stream)
@@ -270,11 +291,13 @@ def recompute(model: Model, seqs, cache: KVCache, order: Optional[Sequence[int]]
 # ------------------------------------------------------------ rollout
 
 def rollout(model: Model, seqs, cache: KVCache, cap: int, prefill_chunk: Optional[int] = None,
-            order: Optional[Sequence[int]] = None, cap_schedule=None, stream=None
-            ) -> List[np.ndarray]:
+            order: Optional[Sequence[int]] = None, cap_schedule=None, stream=None,
+            graph: bool = False) -> List[np.ndarray]:
     """Continuous batching: each step runs, for every active sequence, either its next
     prompt chunk or one decode token (the given response token), in one varlen call.
-    ``cap_schedule`` (callable step -> cap) varies the batch cap per step."""
+    ``cap_schedule`` (callable step -> cap) varies the batch cap per step.  ``graph``:
+    steps that are pure decode (one token per sequence) replay captured HIP graphs, with
+    the block table padded to the context's full width so its shape stays fixed."""
     model.bind_cache(cache)
     alloc = BlockAllocator(cache.n_blocks)
     order = list(range(len(seqs))) if order is None else list(order)
@@ -317,12 +340,16 @@ def rollout(model: Model, seqs, cache: KVCache, cap: int, prefill_chunk: Optiona
                     sid.append(int(s.tokens[t + 1]))
                     owners.append(i)
             sel.append((i, n))
-        maxb = max(len(r) for r in rows)
+        decode_only = all(n == 1 for _, n in sel) and all(
+            state[i][0] >= seqs[i].prompt_len for i, _ in sel)
+        use_graph = graph and decode_only
+        maxb = (-(-model.max_position // KV_BLOCK) if use_graph
+                else max(len(r) for r in rows))
         btab = np.array([r + [0] * (maxb - len(r)) for r in rows], np.int32)
         plan = CallPlan(np.concatenate(toks).astype(np.int32), np.array(cu, np.int32),
                         np.array(pos0, np.int32), btab, np.array(srow, np.int32),
                         np.array(sid, np.int32), [])
-        lp = run_call(model, plan, False, stream).cpu().numpy()
+        lp = run_call(model, plan, False, stream, graph=use_graph).cpu().numpy()
         for j, i in enumerate(owners):
             out[i].append(lp[j])
         for i, n in sel:

@@ -168,6 +168,28 @@ bci_status bci_set_batch(bci_ctx* ctx, const bci_batch* batch, void* stream);
  * Writes d_logprobs[n_scored] (fp32).  This is the "rollout" entry point. */
 bci_status bci_forward_logprobs(bci_ctx* ctx, float* d_logprobs, void* stream);
 
+/* bci_forward_logprobs replayed from a HIP graph.  On the first call for a batch
+ * shape (n_tokens, n_seqs, n_scored, attention tiles, block-table width) the forward
+ * is captured on a private stream into a graph kept by the context (up to 16 shapes,
+ * least recently used dropped); later calls with the same shape launch that graph on
+ * `stream` and copy the logprobs to d_logprobs.  The graph reads the batch metadata
+ * that bci_set_batch uploads to the workspace's fixed addresses, so a decode loop
+ * calls bci_set_batch then this function each step; positions, tokens and block ids
+ * may change between replays.  Bits equal bci_forward_logprobs (the captured forward
+ * launches every KV segment the context can hold; the ones past a row's position are
+ * no-ops).  Weights updated in place (same buffers, e.g. after an optimiser step) are
+ * read by the next replay; a rebind that moves any weight or cache buffer drops the
+ * graphs and the next call captures again (the stable workspace and in-place weight
+ * update of the digest's section "让训练前向使用推理的数值", which also requires a
+ * stable batch shape for capture).  The block-table width is part of the shape, so a
+ * decode loop keeps it fixed (pads the table).  Invariant mode and dense models only
+ * (BCI_E_UNSUPPORTED otherwise); errors as bci_forward_logprobs, plus BCI_E_HIP when
+ * capture or instantiation fails (nothing is launched then). */
+bci_status bci_forward_logprobs_graph(bci_ctx* ctx, float* d_logprobs, void* stream);
+/* Number of graphs the context holds; bci_graph_reset drops them all. */
+int32_t bci_graph_count(const bci_ctx* ctx);
+bci_status bci_graph_reset(bci_ctx* ctx);
+
 /* ---- per-operator entry points ("the training forward calls the inference
  *      kernels"); each is bitwise identical to its use inside the forward ---- */
 
