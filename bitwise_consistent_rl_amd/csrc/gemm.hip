@@ -42,6 +42,7 @@ constexpr int WTM = BM / NWM, WTN = BN / NWN;  // 64 x 128 per wave
 constexpr int MI = WTM / 16, NI = WTN / 16;    // 4 x 8 MFMA blocks per wave
 constexpr int THREADS = NWM * NWN * 64;
 constexpr int STAGE = (BM + BN) * KCH;   // 16-byte chunks per LDS buffer
+constexpr int LM_SMALL_M = 16;           // lm_head rows up to which 16-row tiles are used
 
 enum { K_BF16 = 0, K_F32 = 1, K_SILU = 2, K_LMHEAD = 3, K_ATOMIC = 4 };
 
@@ -86,9 +87,19 @@ __device__ __forceinline__ int b_lds_row(int wn, int ni) {
   }
 }
 
-template <int KIND, bool GATHER, bool GROUPED>
-__global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs p) {
-  __shared__ u32x4_t smem[2 * STAGE];  // 2 x 64 KiB
+// TBM: rows per tile.  256 (4 waves along M) for every GEMM, or 16 (one wave along M)
+// for the lm_head over a handful of rows (decode), which would otherwise stream 256
+// duplicated A rows per tile; the per-element chain and the epilogue's reduction
+// order over the 256 columns are the same either way.
+template <int KIND, bool GATHER, bool GROUPED, int TBM = BM>
+__global__ __launch_bounds__((TBM >= 64 ? TBM / 64 : 1) * NWN * 64, 1) void gemm_kernel(GemmArgs p) {
+  constexpr int KBM = TBM;
+  constexpr int KNWM = TBM >= 64 ? TBM / 64 : 1;
+  constexpr int KWTM = KBM / KNWM;
+  constexpr int KMI = KWTM / 16;
+  constexpr int KTHREADS = KNWM * NWN * 64;
+  constexpr int KSTAGE = (KBM + BN) * KCH;
+  __shared__ u32x4_t smem[2 * KSTAGE];  // two buffers (2 x 64 KiB at TBM = 256)
 
   // ---- tile id: XCD-contiguous ranges, then groups of 8 M-tiles
   const int n_tiles = p.tiles_m * p.tiles_n;
@@ -107,7 +118,7 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs p) {
   const int K = p.K;
 
   // rows [row_base, row_base + row_cnt) of C belong to this tile
-  int row_base = tm * BM, row_cnt = min(BM, p.M - tm * BM);
+  int row_base = tm * KBM, row_cnt = min(KBM, p.M - tm * KBM);
   const bf16_t* W = p.W;
   if constexpr (GROUPED) {
     if (tm >= *p.n_gtiles) return;
@@ -123,20 +134,20 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs p) {
   // chunk position is P loads logical chunk (P % 8) ^ ((row >> 1) & 7) of row
   // P / 8 of the stacked [A tile; B tile].  Wave w issues loads i = 0..NL-1
   // covering positions (w * NL + i) * 64 + lane (waves 0-3: A, 4-7: B).
-  constexpr int NL = STAGE / 64 / (THREADS / 64);
+  constexpr int NL = KSTAGE / 64 / (KTHREADS / 64);
   const bf16_t* src[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const int P = (wave * NL + i) * 64 + lane;
     const int row = P / KCH;
     const int ch = (P % KCH) ^ ((row >> 1) & 7);
-    if (row < BM) {
+    if (row < KBM) {
       // rows past the tile's end duplicate its last row and are never stored
       int r = row_base + min(row, row_cnt - 1);
       if constexpr (GATHER) r = p.a_rows[r] / p.a_div;
       src[i] = p.A + (size_t)r * K + ch * 8;
     } else {
-      const int br = row - BM;
+      const int br = row - KBM;
       int n;
       if constexpr (KIND == K_SILU) {
         const int I = p.N >> 1;
@@ -152,13 +163,13 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs p) {
     for (int i = 0; i < NL; ++i)
       __builtin_amdgcn_global_load_lds(
           (const void*)(src[i] + k0),
-          (__attribute__((address_space(3))) void*)(smem + st * STAGE + (wave * NL + i) * 64), 16, 0,
+          (__attribute__((address_space(3))) void*)(smem + st * KSTAGE + (wave * NL + i) * 64), 16, 0,
           0);
   };
 
-  f32x4_t acc[MI][NI];
+  f32x4_t acc[KMI][NI];
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi)
+  for (int mi = 0; mi < KMI; ++mi)
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
@@ -175,12 +186,12 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs p) {
   };
   auto lda = [&](int st, int ks, int mi) {
     return __builtin_bit_cast(
-        bf16x8_t, smem[st * STAGE + swz(wm * WTM + mi * 16 + (lane & 15), ks * 4 + (lane >> 4))]);
+        bf16x8_t, smem[st * KSTAGE + swz(wm * KWTM + mi * 16 + (lane & 15), ks * 4 + (lane >> 4))]);
   };
   auto ldb = [&](int st, int ks, int ni) {
     return __builtin_bit_cast(
         bf16x8_t,
-        smem[st * STAGE + BM * KCH + swz(b_lds_row<KIND>(wn, ni) + (lane & 15), ks * 4 + (lane >> 4))]);
+        smem[st * KSTAGE + KBM * KCH + swz(b_lds_row<KIND>(wn, ni) + (lane & 15), ks * 4 + (lane >> 4))]);
   };
 
   // Software pipeline over the two 32-wide K steps of each 64-wide slab.
@@ -192,14 +203,14 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs p) {
   // slab, which the barrier between the two has published.  That barrier also
   // frees the slab's LDS buffer (its last fragments are in registers), so the
   // DMA of the slab after next is issued right after it.
-  bf16x8_t fa0[MI], fa1[MI], fb[NI];
+  bf16x8_t fa0[KMI], fa1[KMI], fb[NI];
   auto step_a = [&](int st) {
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) fa1[mi] = lda(st, 1, mi);
+    for (int mi = 0; mi < KMI; ++mi) fa1[mi] = lda(st, 1, mi);
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) acc[mi][ni] = mfma(fa0[mi], fb[ni], acc[mi][ni]);
+      for (int mi = 0; mi < KMI; ++mi) acc[mi][ni] = mfma(fa0[mi], fb[ni], acc[mi][ni]);
       fb[ni] = ldb(st, 1, ni);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -207,12 +218,12 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs p) {
   auto step_b = [&](int st, auto prefetch) {
     if constexpr (decltype(prefetch)::value) {
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) fa0[mi] = lda(st ^ 1, 0, mi);
+      for (int mi = 0; mi < KMI; ++mi) fa0[mi] = lda(st ^ 1, 0, mi);
     }
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) acc[mi][ni] = mfma(fa1[mi], fb[ni], acc[mi][ni]);
+      for (int mi = 0; mi < KMI; ++mi) acc[mi][ni] = mfma(fa1[mi], fb[ni], acc[mi][ni]);
       if constexpr (decltype(prefetch)::value) fb[ni] = ldb(st ^ 1, 0, ni);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -228,7 +239,7 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs p) {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi) fa0[mi] = lda(0, 0, mi);
+  for (int mi = 0; mi < KMI; ++mi) fa0[mi] = lda(0, 0, mi);
 #pragma unroll
   for (int ni = 0; ni < NI; ++ni) fb[ni] = ldb(0, 0, ni);
   if (nk > 1) issue(1, kb + BK);
@@ -247,11 +258,11 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs p) {
   step_b((nk - 1) & 1, std::false_type{});
 
   // ---- epilogues.  Lane holds C[4*(lane>>4) + r][lane & 15] of each 16x16 block.
-  const int lrow0 = wm * WTM + 4 * (lane >> 4);  // row within the tile
+  const int lrow0 = wm * KWTM + 4 * (lane >> 4);  // row within the tile
   const int row0 = row_base + lrow0;
   if constexpr (KIND == K_ATOMIC) {
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+    for (int mi = 0; mi < KMI; ++mi)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = row0 + mi * 16 + r;
@@ -265,7 +276,7 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs p) {
       }
   } else if constexpr (KIND == K_BF16 || KIND == K_F32) {
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+    for (int mi = 0; mi < KMI; ++mi)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = row0 + mi * 16 + r;
@@ -285,8 +296,8 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs p) {
     const int I = p.N >> 1;
     const bool vec = (reinterpret_cast<uintptr_t>(p.C) & 7) == 0;
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-      const int lr = wm * WTM + mi * 16 + (lane & 15);
+    for (int mi = 0; mi < KMI; ++mi) {
+      const int lr = wm * KWTM + mi * 16 + (lane & 15);
       if (lr < row_cnt) {
         bf16_t* out = reinterpret_cast<bf16_t*>(p.C) + (size_t)(row_base + lr) * I;
 #pragma unroll
@@ -316,10 +327,10 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs p) {
     // s_0 + s_1 (+ ...) over reds[w][lr] in wave order; within a wave the
     // columns reduce over the NI sub-blocks in order, then a fixed xor butterfly.
     const int V = p.N;
-    float* redm = reinterpret_cast<float*>(smem);  // [NWN][BM]; the loop ended on a barrier
-    float* reds = redm + NWN * BM;                  // [NWN][BM]
+    float* redm = reinterpret_cast<float*>(smem);  // [NWN][KBM]; the loop ended on a barrier
+    float* reds = redm + NWN * KBM;                  // [NWN][KBM]
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+    for (int mi = 0; mi < KMI; ++mi)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float mx = -INFINITY;
@@ -330,17 +341,17 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs p) {
         }
 #pragma unroll
         for (int o = 1; o <= 8; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, WAVE));
-        if ((lane & 15) == 0) redm[wn * BM + lrow0 + mi * 16 + r] = mx;
+        if ((lane & 15) == 0) redm[wn * KBM + lrow0 + mi * 16 + r] = mx;
       }
     __syncthreads();
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+    for (int mi = 0; mi < KMI; ++mi)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int lr = lrow0 + mi * 16 + r;
         float m = redm[lr];
 #pragma unroll
-        for (int w2 = 1; w2 < NWN; ++w2) m = fmaxf(m, redm[w2 * BM + lr]);
+        for (int w2 = 1; w2 < NWN; ++w2) m = fmaxf(m, redm[w2 * KBM + lr]);
         float s = 0.0f;
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) {
@@ -350,11 +361,11 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs p) {
         }
 #pragma unroll
         for (int o = 1; o <= 8; o <<= 1) s = s + __shfl_xor(s, o, WAVE);
-        if ((lane & 15) == 0) reds[wn * BM + lr] = s;
+        if ((lane & 15) == 0) reds[wn * KBM + lr] = s;
       }
     __syncthreads();
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+    for (int mi = 0; mi < KMI; ++mi)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int lr = lrow0 + mi * 16 + r;
@@ -364,8 +375,8 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(GemmArgs p) {
             float m = redm[lr], s = reds[lr];
 #pragma unroll
             for (int w2 = 1; w2 < NWN; ++w2) {
-              m = fmaxf(m, redm[w2 * BM + lr]);
-              s = s + reds[w2 * BM + lr];
+              m = fmaxf(m, redm[w2 * KBM + lr]);
+              s = s + reds[w2 * KBM + lr];
             }
             p.part_m[(size_t)tn * p.M + row] = m;
             p.part_s[(size_t)tn * p.M + row] = s;
@@ -643,12 +654,23 @@ hipError_t launch_lmhead_partials(const void* A, const int32_t* a_rows, const vo
   a.M = M;
   a.N = V;
   a.K = K;
-  a.tiles_m = (M + BM - 1) / BM;
   a.tiles_n = (V + BN - 1) / BN;
   a.ids = ids;
   a.part_m = part_m;
   a.part_s = part_s;
   a.zid = zid;
+  if (M <= LM_SMALL_M) {
+    // a few scored rows (decode): 16-row tiles, 2 waves, so the weight stream is not
+    // accompanied by 240 duplicated A rows per tile
+    a.tiles_m = (M + LM_SMALL_M - 1) / LM_SMALL_M;
+    const int grid = (a.tiles_m * a.tiles_n + 7) / 8 * 8;
+    if (a_rows)
+      hipLaunchKernelGGL((gemm_kernel<K_LMHEAD, true, false, LM_SMALL_M>), dim3(grid), dim3(NWN * 64), 0, s, a);
+    else
+      hipLaunchKernelGGL((gemm_kernel<K_LMHEAD, false, false, LM_SMALL_M>), dim3(grid), dim3(NWN * 64), 0, s, a);
+    return hipGetLastError();
+  }
+  a.tiles_m = (M + BM - 1) / BM;
   return dispatch<K_LMHEAD>(a, a_rows != nullptr, s);
 }
 
