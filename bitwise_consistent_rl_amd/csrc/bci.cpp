@@ -286,21 +286,23 @@ static void drop_graphs(bci_ctx* c) {
   c->graphs.clear();
 }
 
+// Teardown is best effort: there is no caller to report a failure to, so the
+// status of each release call is deliberately dropped.
 void bci_destroy(bci_ctx* c) {
   if (!c) return;
-  hipSetDevice(c->device);
+  (void)hipSetDevice(c->device);
   drop_graphs(c);
   if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
   for (auto& e : c->prof_ev)
-    if (e) hipEventDestroy(e);
+    if (e) (void)hipEventDestroy(e);
   for (int i = 0; i < 2; ++i) {
     if (c->stage_ev[i]) {
-      hipEventSynchronize(c->stage_ev[i]);
-      hipEventDestroy(c->stage_ev[i]);
+      (void)hipEventSynchronize(c->stage_ev[i]);  // the staging slot may still be read
+      (void)hipEventDestroy(c->stage_ev[i]);
     }
-    if (c->stage[i]) hipHostFree(c->stage[i]);
+    if (c->stage[i]) (void)hipHostFree(c->stage[i]);
   }
-  if (c->ws) hipFree(c->ws);
+  if (c->ws) (void)hipFree(c->ws);
   delete c;
 }
 
