@@ -378,6 +378,105 @@ def longctx(args):
         del k, v, ks, vs
 
 
+def _time_ms(fn, reps=10, warm=3):
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def lmhead_bench(args):
+    """lm_head + log-softmax + gather alone (config 3): hidden [M, 2048] N(0,1), W
+    [151936, 2048] N(0,0.02), ids uniform; M in {1, 7, 64, 512, 4096, 8192}.  Roofline
+    time max(622.33 MFLOP x M / 2.5 PF/s, (622.33 MB + 4104 B x M) / 8 TB/s)."""
+    import torch
+    import synth
+    from bitwise_consistent_rl_amd import _abi as abi
+    H, V = 2048, 151936
+    mc = abi.ModelConfig()
+    for k, v in dict(n_layers=1, hidden=H, n_q_heads=16, n_kv_heads=8, head_dim=128,
+                     intermediate=6144, vocab=V, rms_eps=1e-6, rope_theta=1e6, kv_block_tokens=64,
+                     attn_segment_keys=2048, max_tokens_per_call=8192, max_seqs_per_call=1,
+                     max_scored_per_call=8192, max_position=64).items():
+        setattr(mc, k, v)
+    ctx = abi.bci_create(mc, 0)
+    hs, w, ids = synth.lmhead_inputs(8192)
+    ghs, gw = hs.cuda(), w.cuda()
+    gids = torch.from_numpy(ids).cuda()
+    lp = torch.empty(8192, dtype=torch.float32, device="cuda")
+    for M in (1, 7, 64, 512, 4096, 8192):
+        a = ghs[:M].contiguous()
+        ms = _time_ms(lambda: abi.bci_op_lmhead_logprob(ctx, a, gw, gids, M, H, V, lp))
+        flops, nbytes = 622.33e6 * M, 622.33e6 + 4104.0 * M
+        t_roof = max(flops / (PEAK_BF16_TFLOPS * 1e12), nbytes / (PEAK_HBM_GBS * 1e9))
+        bound = "mfma" if flops / (PEAK_BF16_TFLOPS * 1e12) > nbytes / (PEAK_HBM_GBS * 1e9) else "hbm"
+        print(json.dumps({"workload": "lm_head + log-softmax + gather (config 3)", "M": M,
+                          "us": round(ms * 1e3, 2), "bound": bound,
+                          "achieved": round(flops / ms / 1e9, 1) if bound == "mfma"
+                          else round(nbytes / ms / 1e6, 1),
+                          "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
+                          "frac_of_roofline": round(t_roof / (ms * 1e-3), 4)}), flush=True)
+    abi.bci_destroy(ctx)
+
+
+def moe_bench(args):
+    """MoE layer alone (config 4): router GEMM (fp32 logits), top-6 with lowest-index
+    ties, stable permutation, grouped expert GEMMs + shared expert, FP32 slot-order
+    combine; h [T, 4096] N(0,1), T in {1, 64, 512, 2048, 8192}.  Roofline time
+    max(264.77 MFLOP x T / 2.5 PF/s, ((distinct experts + 1) x 37.75 MB + 16.4 KB x T)
+    / 8 TB/s)."""
+    import numpy as np
+    import torch
+    import synth
+    from bitwise_consistent_rl_amd import _abi as abi
+    cfg = synth.MOE
+    H, E = cfg.hidden, cfg.n_experts
+    mc = abi.ModelConfig()
+    for k, v in dict(n_layers=1, hidden=H, n_q_heads=32, n_kv_heads=8, head_dim=128,
+                     intermediate=cfg.expert_intermediate, vocab=128, rms_eps=1e-6, rope_theta=1e6,
+                     kv_block_tokens=64, attn_segment_keys=2048, max_tokens_per_call=8192,
+                     max_seqs_per_call=8, max_scored_per_call=8, max_position=64,
+                     n_experts=E, top_k=cfg.top_k, expert_intermediate=cfg.expert_intermediate,
+                     n_shared_experts=1).items():
+        setattr(mc, k, v)
+    ctx = abi.bci_create(mc, 0)
+    log("generating MoE weights")
+    g = {k: v.cuda() for k, v in synth.moe_weights(cfg).items()}
+    h_all = synth.normal_bf16((8192, H), index=50).cuda()
+    z = torch.empty(8192, E, dtype=torch.float32, device="cuda")
+    ids = torch.empty(8192, cfg.top_k, dtype=torch.int32, device="cuda")
+    wt = torch.empty(8192, cfg.top_k, dtype=torch.float32, device="cuda")
+    out = torch.empty(8192, H, dtype=torch.bfloat16, device="cuda")
+    expert_bytes = (2 * cfg.expert_intermediate * H + H * cfg.expert_intermediate) * 2
+    for T in (1, 64, 512, 2048, 8192):
+        h = h_all[:T].contiguous()
+
+        def step():
+            abi.bci_op_gemm_bf16(ctx, h, g["wr"], z, T, E, H, abi.BCI_EPI_F32)
+            abi.bci_op_moe_topk(ctx, z, T, ids, wt)
+            abi.bci_op_moe_forward(ctx, h, ids, wt, T, g["wgu"], g["wd"], g["swgu"], g["swd"], out)
+        ms = _time_ms(step)
+        touched = len(np.unique(ids[:T].cpu().numpy()))
+        flops = 264.77e6 * T
+        nbytes = (touched + 1) * expert_bytes + 16.4e3 * T
+        t_f, t_b = flops / (PEAK_BF16_TFLOPS * 1e12), nbytes / (PEAK_HBM_GBS * 1e9)
+        bound = "mfma" if t_f > t_b else "hbm"
+        print(json.dumps({"workload": "MoE layer (config 4)", "T": T, "experts_touched": touched,
+                          "us": round(ms * 1e3, 2), "bound": bound,
+                          "achieved": round(flops / ms / 1e9, 1) if bound == "mfma"
+                          else round(nbytes / ms / 1e6, 1),
+                          "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
+                          "frac_of_roofline": round(max(t_f, t_b) / (ms * 1e-3), 4)}), flush=True)
+    abi.bci_destroy(ctx)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -390,9 +489,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--micro", choices=["gate_up"], default=None,
                     help="time one kernel alone at the workload's shape (for counter runs)")
-    ap.add_argument("--workload", choices=["recompute", "longctx", "rollout"], default="recompute",
+    ap.add_argument("--workload", choices=["recompute", "longctx", "rollout", "lmhead", "moe"],
+                    default="recompute",
                     help="longctx: FP8-KV long-context attention (decode steps, chunked prefill); "
-                         "rollout: continuous-batching decode, invariant vs non-invariant mode")
+                         "rollout: continuous-batching decode, invariant vs non-invariant mode; "
+                         "lmhead: the lm_head log-softmax alone at M = 1 .. 8192; "
+                         "moe: the MoE layer alone at T = 1 .. 8192")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: every sequence is independent, so N GPUs would "
@@ -414,6 +516,10 @@ def main():
         return longctx(args)
     if args.workload == "rollout":
         return rollout_bench(args, cfg)
+    if args.workload == "lmhead":
+        return lmhead_bench(args)
+    if args.workload == "moe":
+        return moe_bench(args)
     log("generating weights and workload")
     weights = synth.make_weights(cfg)
     seqs = synth.rl_sequences(cfg, n_prompts=args.prompts, n_responses=args.responses)

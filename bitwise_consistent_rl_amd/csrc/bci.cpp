@@ -649,10 +649,11 @@ bci_status bci_op_moe_forward(bci_ctx* c, const void* h, const int32_t* ids, con
   const int max_mt = (P + GEMM_BM - 1) / GEMM_BM + E;
   HIP_TRY(c, launch_moe_sort(ids, P, E, c->moe_counts, c->moe_offsets, c->moe_perm, c->moe_inv, c->moe_tiles,
                              c->moe_ntiles, s));
+  // a token picks an expert at most once, so no expert gets more than T rows
   HIP_TRY(c, launch_gemm_grouped(h, c->moe_perm, k, wgu, (size_t)2 * I * H, c->moe_act, c->moe_tiles,
-                                 c->moe_ntiles, max_mt, 2 * I, H, EPI_SILU, s));
+                                 c->moe_ntiles, max_mt, T, 2 * I, H, EPI_SILU, s));
   HIP_TRY(c, launch_gemm_grouped(c->moe_act, nullptr, 1, wd, (size_t)H * I, c->moe_y, c->moe_tiles,
-                                 c->moe_ntiles, max_mt, H, I, EPI_BF16, s));
+                                 c->moe_ntiles, max_mt, T, H, I, EPI_BF16, s));
   if (swgu) {
     HIP_TRY(c, launch_gemm(h, nullptr, swgu, c->moe_act_s, T, 2 * I, H, EPI_SILU, s));
     HIP_TRY(c, launch_gemm(c->moe_act_s, nullptr, swd, c->moe_y_s, T, H, I, EPI_BF16, s));

@@ -43,6 +43,7 @@ constexpr int MI = WTM / 16, NI = WTN / 16;    // 4 x 8 MFMA blocks per wave
 constexpr int THREADS = NWM * NWN * 64;
 constexpr int STAGE = (BM + BN) * KCH;   // 16-byte chunks per LDS buffer
 constexpr int LM_SMALL_M = 16;           // lm_head rows up to which 16-row tiles are used
+constexpr int LM_MID_M = 128;            // ... and up to which 64-row tiles are used
 
 enum { K_BF16 = 0, K_F32 = 1, K_SILU = 2, K_LMHEAD = 3, K_ATOMIC = 4 };
 
@@ -87,10 +88,10 @@ __device__ __forceinline__ int b_lds_row(int wn, int ni) {
   }
 }
 
-// TBM: rows per tile.  256 (4 waves along M) for every GEMM, or 16 (one wave along M)
-// for the lm_head over a handful of rows (decode), which would otherwise stream 256
-// duplicated A rows per tile; the per-element chain and the epilogue's reduction
-// order over the 256 columns are the same either way.
+// TBM: rows per tile.  256 (4 waves along M) for every GEMM, or 16 / 64 (one wave
+// along M) for the lm_head over a few rows (decode, small batches), which would
+// otherwise stream up to 255 duplicated A rows per tile; the per-element chain and
+// the epilogue's reduction order over the 256 columns are the same either way.
 template <int KIND, bool GATHER, bool GROUPED, int TBM = BM>
 __global__ __launch_bounds__((TBM >= 64 ? TBM / 64 : 1) * NWN * 64, 1) void gemm_kernel(GemmArgs p) {
   constexpr int KBM = TBM;
@@ -414,7 +415,10 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((V & 15) | ((V >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <int KIND, int MT>
+// GROUPED (the MoE expert GEMMs with few rows per expert): blockIdx.y is an entry of
+// the device tile list (group, first row, rows <= 16), W is the group's slice, A rows
+// are gathered through a_rows when GATHER.
+template <int KIND, int MT, bool GATHER = false, bool GROUPED = false>
 __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmArgs p) {
   constexpr int NB = (KIND == K_SILU) ? 2 : 1;          // weight streams (gate, up)
   constexpr int WCH = NB * 16 * SK_ROWCH;               // W chunks per stage
@@ -431,6 +435,14 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmArgs p) {
   const int ncols = (KIND == K_SILU) ? p.N / 2 : p.N;
   const int cb = blockIdx.x;
   const int col = cb * 16 + (lane & 15);
+  int row_base = 0, M = p.M;
+  const bf16_t* W = p.W;
+  if constexpr (GROUPED) {
+    if ((int)blockIdx.y >= *p.n_gtiles) return;
+    W += (size_t)p.gtiles[3 * blockIdx.y] * p.w_group_stride;
+    row_base = p.gtiles[3 * blockIdx.y + 1];
+    M = p.gtiles[3 * blockIdx.y + 2];
+  }
   // load j of a stage fills ring chunks [j*64, j*64+64): lane's chunk P = j*64 + lane
   const bf16_t* src[LPS];
 #pragma unroll
@@ -440,11 +452,13 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmArgs p) {
       const int r = P / SK_ROWCH, ch = (P % SK_ROWCH) ^ (r & 15);
       int wr = min(cb * 16 + (r & 15), ncols - 1);
       if (NB == 2 && r >= 16) wr += ncols;               // up rows follow the gate rows
-      src[j] = p.W + (size_t)wr * K + ch * 8;
+      src[j] = W + (size_t)wr * K + ch * 8;
     } else {
       const int P2 = P - WCH;
       const int r = P2 / SK_ROWCH, ch = (P2 % SK_ROWCH) ^ (r & 15);
-      src[j] = p.A + (size_t)min(r, p.M - 1) * K + ch * 8;
+      int ar = row_base + min(r, M - 1);
+      if constexpr (GATHER) ar = p.a_rows[ar] / p.a_div;
+      src[j] = p.A + (size_t)ar * K + ch * 8;
     }
   }
   auto issue = [&](int slot, int k0) {
@@ -492,8 +506,9 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmArgs p) {
   for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = mi * 16 + 4 * (lane >> 4) + r;
-      if (row >= p.M) continue;
+      const int lr = mi * 16 + 4 * (lane >> 4) + r;
+      if (lr >= M) continue;
+      const int row = row_base + lr;
       if constexpr (KIND == K_SILU) {
         const float g = bf2f(f2bf(acc[0][mi][r]));
         const float u = bf2f(f2bf(acc[1][mi][r]));
@@ -609,10 +624,18 @@ hipError_t launch_gemm_splitk(const void* A, const void* W, void* C, int M, int 
   return hipGetLastError();
 }
 
+template <int KIND, bool GATHER>
+static void launch_skinny_grouped(const GemmArgs& a, dim3 grid, int mt, hipStream_t s) {
+  if (mt == 1) hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 1, GATHER, true>), grid, dim3(64), 0, s, a);
+  else if (mt == 2) hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 2, GATHER, true>), grid, dim3(64), 0, s, a);
+  else if (mt <= 4) hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 4, GATHER, true>), grid, dim3(64), 0, s, a);
+  else hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 8, GATHER, true>), grid, dim3(64), 0, s, a);
+}
+
 hipError_t launch_gemm_grouped(const void* A, const int32_t* a_rows, int a_div, const void* W,
                                size_t w_group_stride, void* C, const int32_t* gtiles,
-                               const int32_t* n_gtiles, int max_mtiles, int N, int K, int epi,
-                               hipStream_t s) {
+                               const int32_t* n_gtiles, int max_mtiles, int max_rows, int N, int K,
+                               int epi, hipStream_t s) {
   if (max_mtiles == 0) return hipSuccess;
   GemmArgs a{};
   a.A = (const bf16_t*)A;
@@ -628,8 +651,22 @@ hipError_t launch_gemm_grouped(const void* A, const int32_t* a_rows, int a_div, 
   a.gtiles = gtiles;
   a.n_gtiles = n_gtiles;
   a.w_group_stride = w_group_stride;
-  const int grid = (a.tiles_m * a.tiles_n + 7) / 8 * 8;
   const bool g = a_rows != nullptr;
+  if (max_rows <= SKINNY_MAX_M && K % SK_KC == 0 && (epi == EPI_SILU || epi == EPI_BF16)) {
+    // no group has more than SKINNY_MAX_M rows (few tokens): one wave per 16 columns
+    // per group, covering the group's rows in ceil(max_rows / 16) row blocks
+    const dim3 grid((epi == EPI_SILU ? N / 2 : N) / 16, max_mtiles);
+    const int mt = (max_rows + 15) / 16;
+    if (epi == EPI_SILU) {
+      if (g) launch_skinny_grouped<K_SILU, true>(a, grid, mt, s);
+      else launch_skinny_grouped<K_SILU, false>(a, grid, mt, s);
+    } else {
+      if (g) launch_skinny_grouped<K_BF16, true>(a, grid, mt, s);
+      else launch_skinny_grouped<K_BF16, false>(a, grid, mt, s);
+    }
+    return hipGetLastError();
+  }
+  const int grid = (a.tiles_m * a.tiles_n + 7) / 8 * 8;
   if (epi == EPI_SILU) {
     if (g) hipLaunchKernelGGL((gemm_kernel<K_SILU, true, true>), dim3(grid), dim3(THREADS), 0, s, a);
     else hipLaunchKernelGGL((gemm_kernel<K_SILU, false, true>), dim3(grid), dim3(THREADS), 0, s, a);
@@ -659,15 +696,23 @@ hipError_t launch_lmhead_partials(const void* A, const int32_t* a_rows, const vo
   a.part_m = part_m;
   a.part_s = part_s;
   a.zid = zid;
-  if (M <= LM_SMALL_M) {
-    // a few scored rows (decode): 16-row tiles, 2 waves, so the weight stream is not
-    // accompanied by 240 duplicated A rows per tile
-    a.tiles_m = (M + LM_SMALL_M - 1) / LM_SMALL_M;
+  if (M <= LM_MID_M) {
+    // few scored rows (decode, small batches): 16- or 64-row tiles with 2 waves, so the
+    // weight stream is not accompanied by up to 255 duplicated A rows per tile
+    const int tbm = M <= LM_SMALL_M ? LM_SMALL_M : LM_MID_M / 2;
+    a.tiles_m = (M + tbm - 1) / tbm;
     const int grid = (a.tiles_m * a.tiles_n + 7) / 8 * 8;
-    if (a_rows)
-      hipLaunchKernelGGL((gemm_kernel<K_LMHEAD, true, false, LM_SMALL_M>), dim3(grid), dim3(NWN * 64), 0, s, a);
-    else
-      hipLaunchKernelGGL((gemm_kernel<K_LMHEAD, false, false, LM_SMALL_M>), dim3(grid), dim3(NWN * 64), 0, s, a);
+    if (tbm == LM_SMALL_M) {
+      if (a_rows)
+        hipLaunchKernelGGL((gemm_kernel<K_LMHEAD, true, false, LM_SMALL_M>), dim3(grid), dim3(NWN * 64), 0, s, a);
+      else
+        hipLaunchKernelGGL((gemm_kernel<K_LMHEAD, false, false, LM_SMALL_M>), dim3(grid), dim3(NWN * 64), 0, s, a);
+    } else {
+      if (a_rows)
+        hipLaunchKernelGGL((gemm_kernel<K_LMHEAD, true, false, LM_MID_M / 2>), dim3(grid), dim3(NWN * 64), 0, s, a);
+      else
+        hipLaunchKernelGGL((gemm_kernel<K_LMHEAD, false, false, LM_MID_M / 2>), dim3(grid), dim3(NWN * 64), 0, s, a);
+    }
     return hipGetLastError();
   }
   a.tiles_m = (M + BM - 1) / BM;

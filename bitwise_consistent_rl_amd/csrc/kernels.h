@@ -33,10 +33,11 @@ hipError_t launch_gemm_splitk(const void* A, const void* W, void* C, int M, int 
 // Grouped GEMM over a device tile list (see GemmArgs in gemm.hip): m-tile i covers
 // rows gtiles[3i+1] .. +gtiles[3i+2] of C with weight W + gtiles[3i] * w_group_stride;
 // A rows are a_rows[r] / a_div when a_rows is non-null, else r.
+// max_rows: an upper bound on the rows of any group (<= 16 selects the skinny schedule)
 hipError_t launch_gemm_grouped(const void* A, const int32_t* a_rows, int a_div, const void* W,
                                size_t w_group_stride, void* C, const int32_t* gtiles,
-                               const int32_t* n_gtiles, int max_mtiles, int N, int K, int epi,
-                               hipStream_t s);
+                               const int32_t* n_gtiles, int max_mtiles, int max_rows, int N, int K,
+                               int epi, hipStream_t s);
 // lm_head partials: for each row i < M and vocab chunk c (256 columns):
 // part_m[c * M + i] = max_j z_ij, part_s[c * M + i] = sum_j exp(z_ij - max),
 // and zid[i] = z[i, ids[i]].

@@ -216,7 +216,7 @@ def test_lmhead_rows_invariant_across_M(ctx, lm_inputs):
 
 
 def test_lmhead_ragged_vocab_and_normalisation(ctx):
-    """V = 4000 (last 128-column chunk partial): one hidden state scored against every
+    """V = 4000 (last 256-column chunk partial): one hidden state scored against every
     id gives the full distribution; sum exp(lp) = 1 and each lp matches the oracle."""
     H, V = 256, 4000
     hs = synth.normal_bf16((1, H), index=30)
