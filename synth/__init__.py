@@ -257,3 +257,30 @@ def fp8_attention_inputs(n_q: int, n_kv: int, head_dim: int, ctx: int, seed: int
     k = rng.standard_normal((ctx, n_kv, head_dim), dtype=np.float32)
     v = rng.standard_normal((ctx, n_kv, head_dim), dtype=np.float32)
     return to_bf16(q), to_bf16(k), to_bf16(v)
+
+
+def sparse_index_inputs(T: int, n_keys: int, heads: int = 64, dim: int = 128,
+                        exact: bool = True, seed: int = SEED_INPUTS, index: int = 9
+                        ) -> Tuple[torch.Tensor, np.ndarray, torch.Tensor]:
+    """Inputs of the sparse-attention indexer: index queries q_idx [T, heads, dim] bf16,
+    head weights w [T, heads] fp32 and index keys k_idx [n_keys, dim] bf16.
+
+    exact=True draws small integers so that every score is an exactly representable
+    fp32 value whatever the summation order (ties are frequent): q_idx in [-2, 2],
+    k_idx in [-7, 7] with one entry of each row set to +-7 (its FP8 scale is then
+    7/448 = 2^-6 and the codes are exact), w = +-2^j with j in [-2, 1].
+    exact=False draws N(0, 1) queries and keys and N(0, 1)/sqrt(heads) weights."""
+    rng = _rng(seed, index)
+    if exact:
+        q = rng.integers(-2, 3, size=(T, heads, dim)).astype(np.float32)
+        k = rng.integers(-7, 8, size=(n_keys, dim)).astype(np.float32)
+        if n_keys:
+            col = rng.integers(0, dim, size=n_keys)
+            k[np.arange(n_keys), col] = np.where(rng.random(n_keys) < 0.5, -7.0, 7.0)
+        w = (np.ldexp(1.0, rng.integers(-2, 2, size=(T, heads)))
+             * np.where(rng.random((T, heads)) < 0.25, -1.0, 1.0)).astype(np.float32)
+    else:
+        q = rng.standard_normal((T, heads, dim), dtype=np.float32)
+        k = rng.standard_normal((n_keys, dim), dtype=np.float32)
+        w = rng.standard_normal((T, heads), dtype=np.float32) / np.float32(np.sqrt(heads))
+    return to_bf16(q), w, to_bf16(k)
