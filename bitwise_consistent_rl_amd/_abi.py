@@ -33,6 +33,8 @@ EXPORTS = [
     "bci_op_kv_gather_dequant", "bci_op_attention", "bci_op_gather_scored",
     "bci_op_lmhead_logprob", "bci_op_moe_topk", "bci_op_moe_forward", "bci_profile_begin",
     "bci_profile_end", "bci_forward_logprobs_graph", "bci_graph_count", "bci_graph_reset",
+    "bci_op_index_key_write", "bci_op_index_scores", "bci_op_sparse_topk",
+    "bci_op_sparse_attention",
 ]
 
 
@@ -98,6 +100,10 @@ def load() -> ctypes.CDLL:
         "bci_op_lmhead_logprob": (st, [vp, vp, vp, vp, i32, i32, i32, vp, vp]),
         "bci_op_moe_topk": (st, [vp, vp, i32, vp, vp, vp]),
         "bci_op_moe_forward": (st, [vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp]),
+        "bci_op_index_key_write": (st, [vp, vp, i32, vp, vp, i32, vp]),
+        "bci_op_index_scores": (st, [vp, vp, vp, i32, i32, vp, vp, i32, vp, ctypes.c_int64, i32, vp]),
+        "bci_op_sparse_topk": (st, [vp, vp, ctypes.c_int64, i32, vp, vp]),
+        "bci_op_sparse_attention": (st, [vp, vp, i32, vp, i32, vp, vp]),
         "bci_profile_begin": (st, [vp]),
         "bci_profile_end": (st, [vp, ctypes.POINTER(ctypes.c_double), _P32]),
     }
@@ -255,6 +261,30 @@ def bci_op_moe_topk(ctx: int, logits, T: int, ids, w, stream=None) -> None:
 def bci_op_moe_forward(ctx: int, h, ids, w, T: int, wgu, wd, swgu, swd, out, stream=None) -> None:
     _check(ctx, load().bci_op_moe_forward(ctx, _ptr(h), _ptr(ids), _ptr(w), T, _ptr(wgu), _ptr(wd),
                                           _ptr(swgu), _ptr(swd), _ptr(out), _stream(stream)))
+
+
+def bci_op_index_key_write(ctx: int, kidx, index_dim: int, icodes, iscale, n_index_blocks: int,
+                           stream=None) -> None:
+    _check(ctx, load().bci_op_index_key_write(ctx, _ptr(kidx), index_dim, _ptr(icodes), _ptr(iscale),
+                                              n_index_blocks, _stream(stream)))
+
+
+def bci_op_index_scores(ctx: int, qidx, w, index_heads: int, index_dim: int, icodes, iscale,
+                        n_index_blocks: int, scores, score_stride: int, schedule: int = 0,
+                        stream=None) -> None:
+    _check(ctx, load().bci_op_index_scores(ctx, _ptr(qidx), _ptr(w), index_heads, index_dim,
+                                           _ptr(icodes), _ptr(iscale), n_index_blocks, _ptr(scores),
+                                           score_stride, schedule, _stream(stream)))
+
+
+def bci_op_sparse_topk(ctx: int, scores, score_stride: int, topk: int, sel, stream=None) -> None:
+    _check(ctx, load().bci_op_sparse_topk(ctx, _ptr(scores), score_stride, topk, _ptr(sel),
+                                          _stream(stream)))
+
+
+def bci_op_sparse_attention(ctx: int, q, layer: int, sel, topk: int, o, stream=None) -> None:
+    _check(ctx, load().bci_op_sparse_attention(ctx, _ptr(q), layer, _ptr(sel), topk, _ptr(o),
+                                               _stream(stream)))
 
 
 def bci_profile_begin(ctx: int) -> None:

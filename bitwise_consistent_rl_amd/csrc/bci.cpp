@@ -59,6 +59,8 @@ struct bci_ctx {
   size_t meta_words = 0;
   // metadata offsets (int32 words)
   size_t o_tok = 0, o_pos = 0, o_slot = 0, o_tiles = 0, o_btab = 0, o_srow = 0, o_sid = 0;
+  size_t o_tseq = 0, o_itiles = 0;  // token -> sequence; 4-token index-score tiles
+  int max_itiles = 0;
   // pinned staging for uploads (2 slots, each guarded by an event)
   int32_t* stage[2] = {nullptr, nullptr};
   hipEvent_t stage_ev[2] = {nullptr, nullptr};
@@ -75,6 +77,7 @@ struct bci_ctx {
   // current batch (host copy of what was uploaded)
   bool batch_valid = false;
   int n_seqs = 0, n_tokens = 0, n_scored = 0, n_tiles = 0, batch_seg = 1;
+  int n_itiles = 0, batch_max_pos = 0;
   std::vector<int32_t> h_cu, h_pos0, h_btab;  // h_btab with stride max_blocks
   // profiling of the gate_up GEMM launches (HIP events on the launch stream)
   bool prof_on = false;
@@ -184,7 +187,10 @@ bci_status bci_create(const bci_model_config* cfg_in, int32_t device, bci_ctx** 
   c->o_btab = c->o_tiles + 4 * (size_t)c->max_tiles;
   c->o_srow = c->o_btab + (size_t)g.max_seqs_per_call * c->max_blocks;
   c->o_sid = c->o_srow + R;
-  c->meta_words = c->o_sid + R;
+  c->max_itiles = (int)(T / IDX_TILE_TOKENS) + g.max_seqs_per_call;
+  c->o_tseq = c->o_sid + R;
+  c->o_itiles = c->o_tseq + T;
+  c->meta_words = c->o_itiles + 4 * (size_t)c->max_itiles;
 
   struct Part {
     void** dst;
@@ -416,11 +422,20 @@ bci_status bci_set_batch(bci_ctx* c, const bci_batch* b, void* stream) {
       c->h_btab[(size_t)i * c->max_blocks + j] = b->block_table[(size_t)i * b->max_blocks_per_seq + j];
   }
   std::memcpy(h + c->o_btab, c->h_btab.data(), c->h_btab.size() * sizeof(int32_t));
-  int tix = 0;
+  int tix = 0, iix = 0, max_pos = 0;
   for (int i = 0; i < b->n_seqs; ++i) {
     const int q0 = b->cu_q[i], ql = b->cu_q[i + 1] - q0, p0 = b->pos0[i];
+    max_pos = std::max(max_pos, p0 + ql - 1);
+    for (int t0 = 0; t0 < ql; t0 += IDX_TILE_TOKENS) {
+      int32_t* tl = h + c->o_itiles + 4 * (size_t)iix++;
+      tl[0] = i;
+      tl[1] = q0 + t0;
+      tl[2] = std::min(IDX_TILE_TOKENS, ql - t0);
+      tl[3] = p0 + t0;
+    }
     for (int t = 0; t < ql; ++t) {
       const int p = p0 + t;
+      h[c->o_tseq + q0 + t] = i;
       h[c->o_pos + q0 + t] = p;
       h[c->o_slot + q0 + t] = c->h_btab[(size_t)i * c->max_blocks + p / KV_BLOCK] * KV_BLOCK + p % KV_BLOCK;
     }
@@ -445,6 +460,8 @@ bci_status bci_set_batch(bci_ctx* c, const bci_batch* b, void* stream) {
   c->n_scored = b->n_scored;
   c->n_tiles = n_tiles;
   c->batch_seg = bseg;
+  c->n_itiles = iix;
+  c->batch_max_pos = max_pos;
   c->batch_valid = true;
   return BCI_OK;
 }
@@ -592,6 +609,122 @@ bci_status bci_op_attention(bci_ctx* c, const void* q, int32_t layer, void* o, v
   if (!q || !o || layer < 0 || layer >= c->cfg.n_layers)
     return fail(c, BCI_E_INVALID, "op_attention: null pointer or layer %d", layer);
   return op_attn(c, q, o, layer, S(stream));
+}
+
+// ------------------------------------------------------- sparse attention
+
+static bci_status check_index_cache(bci_ctx* c, const char* who, int dim, const void* codes,
+                                    const float* scales, int32_t n_index_blocks) {
+  if (dim != 64 && dim != 128) return fail(c, BCI_E_INVALID, "%s: index_dim %d is not 64 or 128", who, dim);
+  if (!codes || !scales) return fail(c, BCI_E_INVALID, "%s: null index cache", who);
+  if (!aligned16(codes) || !aligned16(scales))
+    return fail(c, BCI_E_INVALID, "%s: index cache buffers must be 16-byte aligned", who);
+  if (n_index_blocks < c->n_blocks)
+    return fail(c, BCI_E_INVALID, "%s: index cache has %d blocks, the bound KV cache %d", who,
+                n_index_blocks, c->n_blocks);
+  return BCI_OK;
+}
+
+bci_status bci_op_index_key_write(bci_ctx* c, const void* kidx, int32_t index_dim, void* icodes,
+                                  float* iscale, int32_t n_index_blocks, void* stream) {
+  if (!c) return BCI_E_INVALID;
+  if (bci_status st = need_batch(c, "op_index_key_write")) return st;
+  if (bci_status st = check_index_cache(c, "op_index_key_write", index_dim, icodes, iscale, n_index_blocks))
+    return st;
+  if (!kidx || !aligned16(kidx)) return fail(c, BCI_E_INVALID, "op_index_key_write: kidx null or unaligned");
+  HIP_TRY(c, launch_index_key_write(kidx, c->meta + c->o_slot, icodes, iscale, c->n_tokens, index_dim,
+                                    S(stream)));
+  return BCI_OK;
+}
+
+bci_status bci_op_index_scores(bci_ctx* c, const void* qidx, const float* w, int32_t index_heads,
+                               int32_t index_dim, const void* icodes, const float* iscale,
+                               int32_t n_index_blocks, float* scores, int64_t score_stride,
+                               int32_t schedule, void* stream) {
+  if (!c) return BCI_E_INVALID;
+  if (bci_status st = need_batch(c, "op_index_scores")) return st;
+  if (bci_status st = check_index_cache(c, "op_index_scores", index_dim, icodes, iscale, n_index_blocks))
+    return st;
+  if (index_heads != 16 && index_heads != 32 && index_heads != 64)
+    return fail(c, BCI_E_INVALID, "op_index_scores: index_heads %d is not 16, 32 or 64", index_heads);
+  if (!qidx || !w || !scores || !aligned16(qidx) || !aligned16(scores))
+    return fail(c, BCI_E_INVALID, "op_index_scores: null or unaligned qidx/w/scores");
+  if (score_stride < (int64_t)c->batch_max_pos + 1 || score_stride % 4)
+    return fail(c, BCI_E_INVALID, "op_index_scores: score_stride %lld must be a multiple of 4 and >= %d",
+                (long long)score_stride, c->batch_max_pos + 1);
+  if (schedule < 0 || schedule > 2) return fail(c, BCI_E_INVALID, "op_index_scores: schedule %d", schedule);
+  IdxArgs a{};
+  a.q = static_cast<const uint16_t*>(qidx);
+  a.w = w;
+  a.codes = static_cast<const uint8_t*>(icodes);
+  a.scales = iscale;
+  a.block_table = c->meta + c->o_btab;
+  a.tok_pos = c->meta + c->o_pos;
+  a.tok_seq = c->meta + c->o_tseq;
+  a.tiles = c->meta + c->o_itiles;
+  a.scores = scores;
+  a.stride = (size_t)score_stride;
+  a.T = c->n_tokens;
+  a.heads = index_heads;
+  a.dim = index_dim;
+  a.max_blocks = c->max_blocks;
+  a.n_tiles = c->n_itiles;
+  a.max_pos = c->batch_max_pos;
+  // the two schedules compute the same chain per (token, key); staging pays off when
+  // several query tokens of a sequence share each key block
+  const bool staged = schedule == 2 || (schedule == 0 && c->n_tokens >= 2 * c->n_seqs);
+  HIP_TRY(c, launch_index_scores(a, staged, S(stream)));
+  return BCI_OK;
+}
+
+bci_status bci_op_sparse_topk(bci_ctx* c, const float* scores, int64_t score_stride, int32_t topk,
+                              int32_t* sel, void* stream) {
+  if (!c) return BCI_E_INVALID;
+  if (bci_status st = need_batch(c, "op_sparse_topk")) return st;
+  if (!scores || !sel || !aligned16(scores))
+    return fail(c, BCI_E_INVALID, "op_sparse_topk: null or unaligned scores/sel");
+  if (topk < 1) return fail(c, BCI_E_INVALID, "op_sparse_topk: topk %d < 1", topk);
+  if (score_stride < (int64_t)c->batch_max_pos + 1 || score_stride % 4)
+    return fail(c, BCI_E_INVALID, "op_sparse_topk: score_stride %lld must be a multiple of 4 and >= %d",
+                (long long)score_stride, c->batch_max_pos + 1);
+  HIP_TRY(c, launch_sparse_topk(scores, (size_t)score_stride, c->meta + c->o_pos, c->n_tokens, topk, sel,
+                                S(stream)));
+  return BCI_OK;
+}
+
+bci_status bci_op_sparse_attention(bci_ctx* c, const void* q, int32_t layer, const int32_t* sel,
+                                   int32_t topk, void* o, void* stream) {
+  if (!c) return BCI_E_INVALID;
+  if (bci_status st = need_batch(c, "op_sparse_attention")) return st;
+  const auto& g = c->cfg;
+  if (!q || !o || !sel || layer < 0 || layer >= g.n_layers)
+    return fail(c, BCI_E_INVALID, "op_sparse_attention: null pointer or layer %d", layer);
+  if (!aligned16(q) || !aligned16(o))
+    return fail(c, BCI_E_INVALID, "op_sparse_attention: q and o must be 16-byte aligned");
+  if (g.kv_dtype != BCI_KV_FP8_E4M3)
+    return fail(c, BCI_E_UNSUPPORTED, "op_sparse_attention: needs an FP8 KV cache");
+  if (c->group > 16)
+    return fail(c, BCI_E_UNSUPPORTED, "op_sparse_attention: GQA group %d > 16", c->group);
+  if (topk < 64 || topk > SPARSE_MAX_K || topk % 64)
+    return fail(c, BCI_E_INVALID, "op_sparse_attention: topk %d must be a multiple of 64 in [64, %d]", topk,
+                SPARSE_MAX_K);
+  SparseAttnArgs a{};
+  a.q = q;
+  a.o = o;
+  a.kv = kv_layer(c, layer);
+  a.sel = sel;
+  a.block_table = c->meta + c->o_btab;
+  a.tok_pos = c->meta + c->o_pos;
+  a.tok_seq = c->meta + c->o_tseq;
+  a.T = c->n_tokens;
+  a.K = topk;
+  a.max_blocks = c->max_blocks;
+  a.nq = g.n_q_heads;
+  a.nkv = g.n_kv_heads;
+  a.d = g.head_dim;
+  a.scale_log2 = (float)(1.0 / std::sqrt((double)g.head_dim) * 1.4426950408889634);
+  HIP_TRY(c, launch_sparse_attention(a, S(stream)));
+  return BCI_OK;
 }
 
 bci_status bci_op_gather_scored(bci_ctx* c, const void* src, int32_t cols, void* out, void* stream) {

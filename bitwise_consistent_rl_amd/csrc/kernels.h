@@ -86,6 +86,42 @@ struct AttnArgs {
 constexpr int ATTN_ROWS = 64;  // query rows (token x head-in-group) per tile
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 
+// ---- sparse.hip (sparse attention over a Top-K selected key set)
+// index keys [T, DI] bf16 -> paged FP8 index cache (codes [n_blocks*64, DI], scales
+// [n_blocks*64]) at each token's cache slot
+hipError_t launch_index_key_write(const void* kidx, const int32_t* tok_slot, void* codes,
+                                  float* scales, int T, int DI, hipStream_t s);
+struct IdxArgs {
+  const uint16_t* q;           // [T, heads, dim] bf16 index queries
+  const float* w;              // [T, heads] head weights
+  const uint8_t* codes;        // [n_blocks * 64, dim] e4m3 index keys
+  const float* scales;         // [n_blocks * 64]
+  const int32_t* block_table;  // [n_seqs, max_blocks]
+  const int32_t* tok_pos;      // [T]
+  const int32_t* tok_seq;      // [T]
+  const int32_t* tiles;        // [n_tiles, 4] (seq, tok_begin, n_tok, pos_begin), <= 4 tokens
+  float* scores;               // [T, stride]
+  size_t stride;
+  int T, heads, dim, max_blocks, n_tiles, max_pos;
+};
+constexpr int IDX_TILE_TOKENS = 4;
+hipError_t launch_index_scores(const IdxArgs& a, bool staged, hipStream_t s);
+hipError_t launch_sparse_topk(const float* scores, size_t stride, const int32_t* tok_pos, int T,
+                              int K, int32_t* sel, hipStream_t s);
+struct SparseAttnArgs {
+  const void* q;               // [T, nq*d] bf16
+  void* o;                     // [T, nq*d] bf16
+  KvLayer kv;                  // FP8 cache layer
+  const int32_t* sel;          // [T, K] selected positions
+  const int32_t* block_table;
+  const int32_t* tok_pos;
+  const int32_t* tok_seq;
+  int T, K, max_blocks, nq, nkv, d;
+  float scale_log2;
+};
+constexpr int SPARSE_MAX_K = 2048;
+hipError_t launch_sparse_attention(const SparseAttnArgs& a, hipStream_t s);
+
 // ---- moe.hip
 constexpr int MOE_MAX_K = 8;
 hipError_t launch_moe_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,

@@ -241,6 +241,64 @@ bci_status bci_op_kv_gather_dequant(bci_ctx* ctx, int32_t seq, int32_t n_pos, in
  * "让训练前向使用推理的数值"). */
 bci_status bci_op_attention(bci_ctx* ctx, const void* q, int32_t layer, void* o, void* stream);
 
+/* ---- sparse attention over a Top-K selected key set --------------------------
+ * The DeepSeek-V4-Flash recipe runs sparse attention whose Top-K breaks ties by a
+ * fixed rule and lists the selected set in fixed position order, and feeds every
+ * phase the FP8 cache gathered and dequantised to BF16 before one sparse attention
+ * operator (page "Finish RL Training Faster" digest, section "让训练前向使用推理的数值"
+ * and its figure caption).  The pages give no scoring function; these calls use the
+ * indexer of DeepSeek's sparse attention:
+ *   score(t, s) = sum_h w[t,h] * relu(q_idx[t,h,:] . k_idx[s,:]),  0 <= s <= pos(t),
+ * with the index keys in an FP8 index cache (one e4m3 row and one fp32 scale per
+ * token, the KV cache's quantisation rule) read back as bf(fp32(code) * scale).
+ * The index cache is paged like the KV cache and uses the same block ids:
+ *   icodes [n_index_blocks, 64, index_dim] uint8, iscale [n_index_blocks, 64] fp32,
+ * caller owned, 16-byte aligned, n_index_blocks >= the bound KV cache's n_blocks;
+ * one such pair per layer.  index_dim is 64 or 128; index_heads 16, 32 or 64.
+ * Every token's scores, selection and output are bitwise independent of the batch,
+ * of prefill / chunked prefill / decode and of the score schedule. */
+
+/* Quantises kidx [n_tokens, index_dim] bf16 (one index key per token of the current
+ * batch) into the index cache at each token's position. */
+bci_status bci_op_index_key_write(bci_ctx* ctx, const void* kidx, int32_t index_dim, void* icodes,
+                                  float* iscale, int32_t n_index_blocks, void* stream);
+
+/* scores[t * score_stride + s] = score(t, s) (fp32) for s = 0 .. pos(t); later
+ * entries of the row are not written.  qidx [n_tokens, index_heads, index_dim] bf16
+ * (16-byte aligned), w [n_tokens, index_heads] fp32, scores 16-byte aligned,
+ * score_stride a multiple of 4 and > every position of the batch.  Per (t, s): fp32
+ * MFMA dot products in ascending 32-wide steps of index_dim, then one fixed
+ * relu-weighted chain over the heads.  schedule: 0 chooses from the batch shape,
+ * 1 forces keys read per token, 2 forces keys staged for four tokens of a sequence
+ * (testing; the bits are the same). */
+bci_status bci_op_index_scores(bci_ctx* ctx, const void* qidx, const float* w, int32_t index_heads,
+                               int32_t index_dim, const void* icodes, const float* iscale,
+                               int32_t n_index_blocks, float* scores, int64_t score_stride,
+                               int32_t schedule, void* stream);
+
+/* Top-K selection per token of the current batch: the topk positions s <= pos(t)
+ * with the largest scores, ranked by (score descending, position ascending) -- an
+ * equal score goes to the earlier position; NaN ranks above every number and
+ * -0 equals +0 -- written to sel[t * topk ..] in ascending position order.  When
+ * pos(t) + 1 <= topk every position 0 .. pos(t) is selected and the row is padded
+ * with -1.  scores as written by bci_op_index_scores (same stride rules);
+ * sel [n_tokens, topk] int32. */
+bci_status bci_op_sparse_topk(bci_ctx* ctx, const float* scores, int64_t score_stride, int32_t topk,
+                              int32_t* sel, void* stream);
+
+/* Attention of q [n_tokens, nq * d] bf16 (rotated) over the keys listed in
+ * sel [n_tokens, topk] (positions; an entry outside [0, pos(t)], e.g. the -1
+ * padding, is skipped) of layer `layer` of the bound FP8 cache; o as q.  K and V
+ * rows are gathered by position and dequantised with the cache's one rule.  Per
+ * (token, kv head): the list is cut into segments of 256 entries, each walked in
+ * 64-entry chunks in list order with the online softmax of bci_op_attention, and
+ * the segments are merged in ascending order; with every position selected the
+ * bits equal bci_op_attention on a context with attn_segment_keys = 256.  topk a
+ * multiple of 64 in [64, 2048]; FP8 cache and a GQA group <= 16 only
+ * (BCI_E_UNSUPPORTED otherwise). */
+bci_status bci_op_sparse_attention(bci_ctx* ctx, const void* q, int32_t layer, const int32_t* sel,
+                                   int32_t topk, void* o, void* stream);
+
 /* out[r] = src[score_rows[r]] for the current batch: [n_scored, cols] bf16. */
 bci_status bci_op_gather_scored(bci_ctx* ctx, const void* src, int32_t cols, void* out,
                                 void* stream);
