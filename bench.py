@@ -378,6 +378,137 @@ def longctx(args):
         del k, v, ks, vs
 
 
+def sparse_bench(args):
+    """Sparse attention over a Top-K selected set on the FP8 path (32 q / 4 kv heads of
+    128, e4m3 cache; indexer of 64 heads x 128 with an e4m3 index cache; K = 2048).
+    Decode steps at B = 1, 16, 64 with sequence 0 at 57344 tokens and the others uniform
+    in [8192, 57344]; each kernel of the step timed alone with HIP events on the launch
+    stream.  Then a chunked prefill (chunk 2048) of the last 2048 positions of a 32768-token
+    sequence.  Algorithmic bytes / flops per unit:
+      index scores   per (query, key): 132 B of index-key codes + scale read (decode: every
+                     query has its own sequence; prefill: the chunk's queries share the
+                     keys, read once), 4 B score written; 2 x 64 x 128 = 16384 flop
+      top-K          per (query, key): 4 B score read; per query 4 x 2048 B written
+      sparse attn    per (query, selected key): 4 kv heads x 2 x (128 + 4) B of K/V codes
+                     and scales; 4 x 32 x 128 = 16384 flop; per query 16 KiB of q and o."""
+    import numpy as np
+    import torch
+    import synth
+    from bitwise_consistent_rl_amd import _abi as abi
+    NQ, NKV, D, HI, DI, K = 32, 4, 128, 64, 128, 2048
+    width = (NQ + 2 * NKV) * D
+    C = 57344
+    rng = np.random.default_rng(5678)
+    lengths = [C] + [int(x) for x in rng.integers(8192, C + 1, size=63)]
+    n_rows = 63 * 131 + C + 64
+    qkv = synth.normal_bf16((n_rows, width), index=60).cuda()
+    _, _, kidx = synth.sparse_index_inputs(0, n_rows, HI, DI, exact=False, index=61)
+    kidx = kidx.cuda()
+    qi_all, w_all, _ = synth.sparse_index_inputs(2048, 0, HI, DI, exact=False, index=62)
+    qi_all, w_all = qi_all.cuda(), torch.from_numpy(w_all).cuda()
+    mc = abi.ModelConfig()
+    for k, v in dict(n_layers=1, hidden=512, n_q_heads=NQ, n_kv_heads=NKV, head_dim=D,
+                     intermediate=512, vocab=128, rms_eps=1e-6, rope_theta=1e6,
+                     kv_dtype=abi.BCI_KV_FP8_E4M3, kv_block_tokens=64, attn_segment_keys=1024,
+                     max_tokens_per_call=8192, max_seqs_per_call=64, max_scored_per_call=1,
+                     max_position=C + 64).items():
+        setattr(mc, k, v)
+    ctx = abi.bci_create(mc, 0)
+    blocks, nxt = [], 0
+    for L in lengths:
+        blocks.append(list(range(nxt, nxt + (L + 63) // 64)))
+        nxt += (L + 63) // 64
+    shape = (1, nxt, NKV, 64, D)
+    kc = torch.empty(shape, dtype=torch.uint8, device="cuda")
+    vc = torch.empty_like(kc)
+    ks = torch.empty(shape[:-1], device="cuda")
+    vs = torch.empty_like(ks)
+    ic = torch.empty(nxt, 64, DI, dtype=torch.uint8, device="cuda")
+    isc = torch.empty(nxt, 64, device="cuda")
+    abi.bci_bind_kv_cache(ctx, kc, vc, ks, vs, nxt)
+    maxb = max(len(b) for b in blocks)
+    stride = C + 64
+
+    def batch(chunks):
+        T = sum(n for _, _, n in chunks)
+        cu = np.concatenate([[0], np.cumsum([n for _, _, n in chunks])]).astype(np.int32)
+        bt = np.array([blocks[s] + [0] * (maxb - len(blocks[s])) for s, _, _ in chunks], np.int32)
+        abi.bci_set_batch(ctx, np.zeros(T, np.int32), cu,
+                          np.array([p for _, p, _ in chunks], np.int32), bt, [], [])
+
+    qbuf = torch.empty(8192, NQ * D, dtype=torch.bfloat16, device="cuda")
+    for sq, L in enumerate(lengths):
+        for s0 in range(0, L - 1, 8192):
+            n = min(8192, L - 1 - s0)
+            batch([(sq, s0, n)])
+            r = slice(sq * 131 + s0, sq * 131 + s0 + n)
+            abi.bci_op_rope_kv_write(ctx, qkv[r].contiguous(), qbuf, 0)
+            abi.bci_op_index_key_write(ctx, kidx[r].contiguous(), DI, ic, isc, nxt)
+    torch.cuda.synchronize()
+    log("sparse: caches filled")
+    scores = torch.empty(2048, stride, device="cuda")
+    sel = torch.empty(2048, K, dtype=torch.int32, device="cuda")
+    q = torch.empty(2048, NQ * D, dtype=torch.bfloat16, device="cuda")
+    o = torch.empty_like(q)
+
+    def report(name, B, keys, us, flops, nbytes, extra=None):
+        t_f, t_b = flops / (PEAK_BF16_TFLOPS * 1e12), nbytes / (PEAK_HBM_GBS * 1e9)
+        bound = "mfma" if t_f > t_b else "hbm"
+        rec = {"workload": "sparse attention, FP8 KV, K = 2048", "kernel": name, "batch": B,
+               "keys_scored": keys, "us": round(us, 2), "bound": bound,
+               "achieved": round(flops / us / 1e6, 1) if bound == "mfma" else round(nbytes / us / 1e3, 1),
+               "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
+               "frac_of_roofline": round(max(t_f, t_b) / (us * 1e-6), 4)}
+        rec.update(extra or {})
+        print(json.dumps(rec), flush=True)
+
+    for B in (1, 16, 64):
+        seqs = list(range(B))
+        chunks = [(s, lengths[s] - 1, 1) for s in seqs]
+        batch(chunks)
+        rows = torch.cat([qkv[s * 131 + lengths[s] - 1: s * 131 + lengths[s]] for s in seqs]).contiguous()
+        krows = torch.cat([kidx[s * 131 + lengths[s] - 1: s * 131 + lengths[s]] for s in seqs]).contiguous()
+        qi, wi = qi_all[:B].contiguous(), w_all[:B].contiguous()
+        qB, oB, sB, selB = q[:B], o[:B], scores[:B], sel[:B]
+        keys = sum(lengths[s] for s in seqs)
+        t_rope = _time_ms(lambda: abi.bci_op_rope_kv_write(ctx, rows, qB, 0), reps=20) * 1e3
+        t_ikw = _time_ms(lambda: abi.bci_op_index_key_write(ctx, krows, DI, ic, isc, nxt), reps=20) * 1e3
+        t_sc = _time_ms(lambda: abi.bci_op_index_scores(ctx, qi, wi, HI, DI, ic, isc, nxt, sB, stride),
+                        reps=20) * 1e3
+        t_tk = _time_ms(lambda: abi.bci_op_sparse_topk(ctx, sB, stride, K, selB), reps=20) * 1e3
+        t_at = _time_ms(lambda: abi.bci_op_sparse_attention(ctx, qB, 0, selB, K, oB), reps=20) * 1e3
+        report("index_scores", B, keys, t_sc, 16384.0 * keys, 136.0 * keys + B * (HI * DI * 2 + HI * 4))
+        report("sparse_topk", B, keys, t_tk, 0.0, 4.0 * keys + 4.0 * K * B)
+        report("sparse_attention", B, keys, t_at, 16384.0 * K * B, NKV * 2 * (D + 4) * K * B + 16384.0 * B)
+        step = t_rope + t_ikw + t_sc + t_tk + t_at
+        print(json.dumps({"workload": "sparse attention decode step, FP8 KV, K = 2048", "batch": B,
+                          "context_tokens": keys, "us_per_step": round(step, 2),
+                          "us": {"rope_kv_write": round(t_rope, 2), "index_key_write": round(t_ikw, 2),
+                                 "index_scores": round(t_sc, 2), "sparse_topk": round(t_tk, 2),
+                                 "sparse_attention": round(t_at, 2)},
+                          "tokens_per_s": round(B / step * 1e6, 1)}), flush=True)
+
+    # chunked prefill: the last 2048 positions of a 32768-token context (sequence 1 of the
+    # fill is at least 8192 long; use sequence 0's cache, positions 30720 .. 32767)
+    P0, n = 32768 - 2048, 2048
+    batch([(0, P0, n)])
+    qi, wi = qi_all[:n].contiguous(), w_all[:n].contiguous()
+    r = slice(P0, P0 + n)
+    abi.bci_op_rope_kv_write(ctx, qkv[r].contiguous(), q, 0)
+    keys = sum(P0 + i + 1 for i in range(n))
+    t_sc = _time_ms(lambda: abi.bci_op_index_scores(ctx, qi, wi, HI, DI, ic, isc, nxt, scores, stride),
+                    reps=3, warm=1) * 1e3
+    t_tk = _time_ms(lambda: abi.bci_op_sparse_topk(ctx, scores, stride, K, sel), reps=3, warm=1) * 1e3
+    t_at = _time_ms(lambda: abi.bci_op_sparse_attention(ctx, q, 0, sel, K, o), reps=3, warm=1) * 1e3
+    # the chunk's queries share one sequence's index keys: read once, scores written per query
+    report("index_scores", n, keys, t_sc, 16384.0 * keys,
+           132.0 * (P0 + n) + 4.0 * keys + n * (HI * DI * 2 + HI * 4), {"phase": "chunked prefill"})
+    report("sparse_topk", n, keys, t_tk, 0.0, 4.0 * keys + 4.0 * K * n, {"phase": "chunked prefill"})
+    report("sparse_attention", n, keys, t_at, 16384.0 * K * n, NKV * 2 * (D + 4) * K * n + 16384.0 * n,
+           {"phase": "chunked prefill"})
+    abi.bci_destroy(ctx)
+
+
 def _time_ms(fn, reps=10, warm=3):
     import torch
     for _ in range(warm):
@@ -489,7 +620,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--micro", choices=["gate_up"], default=None,
                     help="time one kernel alone at the workload's shape (for counter runs)")
-    ap.add_argument("--workload", choices=["recompute", "longctx", "rollout", "lmhead", "moe"],
+    ap.add_argument("--workload", choices=["recompute", "longctx", "rollout", "lmhead", "moe", "sparse"],
                     default="recompute",
                     help="longctx: FP8-KV long-context attention (decode steps, chunked prefill); "
                          "rollout: continuous-batching decode, invariant vs non-invariant mode; "
@@ -518,6 +649,8 @@ def main():
         return rollout_bench(args, cfg)
     if args.workload == "lmhead":
         return lmhead_bench(args)
+    if args.workload == "sparse":
+        return sparse_bench(args)
     if args.workload == "moe":
         return moe_bench(args)
     log("generating weights and workload")

@@ -35,6 +35,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <algorithm>
+
 namespace bci {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -106,20 +108,22 @@ hipError_t launch_index_key_write(const void* kidx, const int32_t* tok_slot, voi
 // wave's token's index heads (A operand, rows) with 64 keys (B operand,
 // columns: key 16kt + lc of the block), relu, weighted head sum.  Lane group lg
 // returns the scores of keys 16 lg + lc.
-template <int NHT, int DI>
-__device__ __forceinline__ float index_chain(const bf16x8_t (&qa)[NHT][DI / 32],
-                                             const bf16x8_t (&kb)[4][DI / 32],
+template <int NHT, int DI, typename Fetch>
+__device__ __forceinline__ float index_chain(const bf16x8_t (&qa)[NHT][DI / 32], Fetch fetch,
                                              const float (&wv)[NHT][4], int lg) {
   float out = 0.0f;
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) {
+    bf16x8_t kb[DI / 32];
+#pragma unroll
+    for (int ks = 0; ks < DI / 32; ++ks) kb[ks] = fetch(kt, ks);
     float v = 0.0f;
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
       f32x4_t d = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < DI / 32; ++ks)
-        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ht][ks], kb[kt][ks], d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ht][ks], kb[ks], d, 0, 0, 0);
 #pragma unroll
       for (int r = 0; r < 4; ++r) v = __builtin_fmaf(wv[ht][r], fmaxf(d[r], 0.0f), v);
     }
@@ -155,36 +159,61 @@ __device__ __forceinline__ int iswz(int key, int ch) {
     return key * (DI / 8) + (ch ^ ((key >> 1) & 7));
 }
 
-// Decode-like schedule: one token per workgroup, each wave one 64-key block,
-// key codes read straight into the B operand and dequantised in registers.
+// Decode-like schedule: one token per workgroup row of the grid; wave w of
+// workgroup x takes key blocks x*4 + w, then + 4*gridDim.x, ... (64 keys each),
+// reading the codes straight into the B operand (dequantised in registers); the
+// next block's codes are in flight while the current one is multiplied.
+template <int DI>
+struct RawKeys {
+  u32x2_t c[4][DI / 32];
+  float sc[4];
+};
+
+template <int DI>
+__device__ __forceinline__ void raw_keys_load(const IdxArgs& a, const int* btab, int s0, int pos,
+                                              int lg, int lc, RawKeys<DI>& r) {
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    const int s = min(s0 + 16 * kt + lc, pos);
+    const size_t slot = (size_t)btab[s >> 6] * SCHUNK + (s & 63);
+    r.sc[kt] = a.scales[slot];
+    const uint8_t* crow = a.codes + slot * DI;
+#pragma unroll
+    for (int ks = 0; ks < DI / 32; ++ks)
+      r.c[kt][ks] = *reinterpret_cast<const u32x2_t*>(crow + 32 * ks + 8 * lg);
+  }
+}
+
 template <int NHT, int DI>
 __global__ __launch_bounds__(256) void index_scores_direct(IdxArgs a) {
   const int t = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int lg = lane >> 4, lc = lane & 15;
   const int pos = a.tok_pos[t];
-  const int s0 = (blockIdx.x * 4 + wave) * SCHUNK;
-  if (s0 > pos) return;
+  const int nblk = pos / SCHUNK + 1;
+  const int step = 4 * gridDim.x;
+  int b = blockIdx.x * 4 + wave;
+  if (b >= nblk) return;
   const int* btab = a.block_table + (size_t)a.tok_seq[t] * a.max_blocks;
 
-  bf16x8_t kb[4][DI / 32];
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-    const int s = min(s0 + 16 * kt + lc, pos);
-    const size_t slot = (size_t)btab[s >> 6] * SCHUNK + (s & 63);
-    const float sc = a.scales[slot];
-    const uint8_t* crow = a.codes + slot * DI;
-#pragma unroll
-    for (int ks = 0; ks < DI / 32; ++ks)
-      kb[kt][ks] = dequant8(*reinterpret_cast<const u32x2_t*>(crow + 32 * ks + 8 * lg), sc);
-  }
+  RawKeys<DI> cur, nxt;
+  raw_keys_load<DI>(a, btab, b * SCHUNK, pos, lg, lc, cur);
   bf16x8_t qa[NHT][DI / 32];
   float wv[NHT][4];
   index_load_query<NHT, DI>(a, t, true, lg, lc, qa, wv);
+  float* srow = a.scores + (size_t)t * a.stride;
 
-  const float v = index_chain<NHT, DI>(qa, kb, wv, lg);
-  const int s = s0 + 16 * lg + lc;
-  if (s <= pos) a.scores[(size_t)t * a.stride + s] = v;
+  while (true) {
+    const int bn = b + step;
+    if (bn < nblk) raw_keys_load<DI>(a, btab, bn * SCHUNK, pos, lg, lc, nxt);
+    const float v = index_chain<NHT, DI>(
+        qa, [&](int kt, int ks) { return dequant8(cur.c[kt][ks], cur.sc[kt]); }, wv, lg);
+    const int s = b * SCHUNK + 16 * lg + lc;
+    if (s <= pos) srow[s] = v;
+    if (bn >= nblk) break;
+    b = bn;
+    cur = nxt;
+  }
 }
 
 // Prefill-like schedule: a tile of up to four consecutive tokens of one
@@ -232,13 +261,12 @@ __global__ __launch_bounds__(256) void index_scores_staged(IdxArgs a) {
     }
     __syncthreads();
     if (ok && s0 <= pos) {
-      bf16x8_t kb[4][DI / 32];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int ks = 0; ks < DI / 32; ++ks)
-          kb[kt][ks] = __builtin_bit_cast(bf16x8_t, Ks[iswz<DI>(16 * kt + lc, 4 * ks + lg)]);
-      const float v = index_chain<NHT, DI>(qa, kb, wv, lg);
+      const float v = index_chain<NHT, DI>(
+          qa,
+          [&](int kt, int ks) {
+            return __builtin_bit_cast(bf16x8_t, Ks[iswz<DI>(16 * kt + lc, 4 * ks + lg)]);
+          },
+          wv, lg);
       const int s = s0 + 16 * lg + lc;
       if (s <= pos) a.scores[(size_t)t * a.stride + s] = v;
     }
@@ -251,9 +279,15 @@ static void launch_scores_t(const IdxArgs& a, bool staged, hipStream_t s) {
     hipLaunchKernelGGL((index_scores_staged<NHT, DI>),
                        dim3((a.max_pos + IDX_STAGE_KEYS) / IDX_STAGE_KEYS, a.n_tiles), dim3(256), 0,
                        s, a);
-  else
-    hipLaunchKernelGGL((index_scores_direct<NHT, DI>),
-                       dim3((a.max_pos + 4 * SCHUNK) / (4 * SCHUNK), a.T), dim3(256), 0, s, a);
+  else {
+    // blocks per wave: enough workgroups to fill the chip, then longer runs per wave
+    // so that the token's index query is loaded once per several key blocks
+    const int max_blk = a.max_pos / SCHUNK + 1;
+    const long long waves = (long long)a.T * max_blk;
+    const int per_wave = (int)std::min<long long>(8, std::max<long long>(1, waves / 8192));
+    const int gx = (max_blk + 4 * per_wave - 1) / (4 * per_wave);
+    hipLaunchKernelGGL((index_scores_direct<NHT, DI>), dim3(gx, a.T), dim3(256), 0, s, a);
+  }
 }
 
 hipError_t launch_index_scores(const IdxArgs& a, bool staged, hipStream_t s) {
@@ -292,6 +326,9 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 
 constexpr int TK_THREADS = 1024;
 constexpr int TK_WAVES = TK_THREADS / WAVE;
+constexpr int TK_EPT = 64;      // positions per thread held in registers: rows up to 65536
+constexpr int TK_BINS = 4096;   // first digit: up to 12 bits below the row's common prefix
+constexpr int TK_CAP = 4096;    // keys of the chosen first-digit bin kept in LDS
 
 // inclusive prefix sum over the 64 lanes of a wave
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
@@ -303,81 +340,264 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
   return v;
 }
 
-__global__ __launch_bounds__(TK_THREADS) void sparse_topk_kernel(const float* scores, size_t stride,
-                                                                 const int32_t* tok_pos, int K,
-                                                                 int32_t* sel) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t s_digit, s_above;
-  __shared__ uint32_t wgt[TK_WAVES], weq[TK_WAVES];
-  const int t = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = tok_pos[t] + 1;
-  int32_t* out = sel + (size_t)t * K;
-  if (n <= K) {
-    for (int i = tid; i < K; i += TK_THREADS) out[i] = i < n ? i : -1;
-    return;
-  }
-  const float* row = scores + (size_t)t * stride;
-  const int n4 = n & ~3;
+struct TopkShared {
+  uint32_t hist[TK_BINS + 1];  // + a spare bin that takes the placeholder keys' adds
+  uint32_t cand[TK_CAP];
+  uint32_t wg[TK_WAVES], we[TK_WAVES];
+  uint32_t digit, above, ncand, kmin, kmax;
+};
 
-  // radix select of the K-th largest key, eight bits at a time from the top
-  uint32_t prefix = 0, pmask = 0;
-  uint32_t kk = (uint32_t)K;  // rank still to find among keys matching the prefix
+// Exclusive prefix over the workgroup (thread order) of two counters; also
+// returns the totals.
+__device__ __forceinline__ void topk_block_scan(TopkShared& sh, uint32_t cg, uint32_t ce, int tid,
+                                                uint32_t& pg, uint32_t& pe, uint32_t& tg,
+                                                uint32_t& te) {
+  const int lane = tid & 63, wave = tid >> 6;
+  const uint32_t ig = wave_incl_scan(cg, lane), ie = wave_incl_scan(ce, lane);
+  if (lane == 63) {
+    sh.wg[wave] = ig;
+    sh.we[wave] = ie;
+  }
+  __syncthreads();
+  pg = ig - cg;
+  pe = ie - ce;
+  tg = 0;
+  te = 0;
+  for (int w = 0; w < TK_WAVES; ++w) {
+    const uint32_t a = sh.wg[w], b = sh.we[w];
+    if (w < wave) {
+      pg += a;
+      pe += b;
+    }
+    tg += a;
+    te += b;
+  }
+  __syncthreads();  // wg/we may be rewritten after this
+}
+
+// After a histogram of nb bins (all threads call): sh.digit = the bin holding the
+// kk-th largest counted key, sh.above = the count in higher bins.  Thread tid owns
+// bins nb-1-tid*bpt down to nb-(tid+1)*bpt (descending order = thread order).
+__device__ __forceinline__ void topk_pick(TopkShared& sh, int nb, uint32_t kk, int tid) {
+  const int bpt = nb > TK_THREADS ? nb / TK_THREADS : 1;
+  const int hi = nb - 1 - tid * bpt;
+  uint32_t c[TK_BINS / TK_THREADS], sum = 0;
+#pragma unroll
+  for (int j = 0; j < TK_BINS / TK_THREADS; ++j) {
+    c[j] = (j < bpt && hi - j >= 0) ? sh.hist[hi - j] : 0u;
+    sum += c[j];
+  }
+  uint32_t above, dummy, t0, t1;
+  topk_block_scan(sh, sum, 0u, tid, above, dummy, t0, t1);
+#pragma unroll
+  for (int j = 0; j < TK_BINS / TK_THREADS; ++j) {
+    if (above < kk && kk <= above + c[j]) {
+      sh.digit = (uint32_t)(hi - j);
+      sh.above = above;
+    }
+    above += c[j];
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ uint32_t wave_umin(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = min(v, (uint32_t)__shfl_xor(v, o, WAVE));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor(v, o, WAVE));
+  return v;
+}
+
+// Rows of up to TK_THREADS * TK_EPT positions.  Thread tid holds positions
+// [tid * ept, tid * ept + ept) as order keys in registers (the row is read once);
+// slots past the row hold 0, below every real key (the smallest, that of -inf, is
+// 0x007fffff).  The K-th largest key tau is found in up to three steps:
+//   1. the row's smallest and largest keys: the bits above their highest
+//      differing bit are common to every key;
+//   2. a histogram of the next (up to) 12 bits picks the bin holding the K-th
+//      largest key -- these bits vary across the row, so the LDS adds spread;
+//   3. the keys of that bin (usually few) are copied to LDS and the remaining
+//      bits are resolved there, 10 at a time; a bin too full for LDS is resolved
+//      in the registers instead, 8 bits at a time.
+// tau and kk (how many keys equal to tau are taken) are exact integer results,
+// independent of the order of the LDS adds.
+__device__ __forceinline__ void topk_registers(TopkShared& sh, const float* row, int n, int K,
+                                               int32_t* out, int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
+  const int ept = (((n + TK_THREADS - 1) / TK_THREADS) + 3) & ~3;  // workgroup-uniform
+  const int p0 = tid * ept;
+  const int nv = max(0, min(ept, n - p0));
+  // one 16-byte load per group of four; a group that starts inside the row may run
+  // past its end, but never past the row's stride (a multiple of 4): those slots,
+  // and whole groups past the row (read from the row start instead), become 0
+  uint32_t key[TK_EPT];
+#pragma unroll
+  for (int j = 0; j < TK_EPT / 4; ++j) {
+    if (4 * j >= ept) continue;
+    const int off = 4 * j < nv ? p0 + 4 * j : 0;
+    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(row + off);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) key[4 * j + c] = (4 * j + c < nv) ? order_key(v[c]) : 0u;
+  }
+  // 1. min and max over the real keys
+  uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+  for (int e = 0; e < TK_EPT; ++e) {
+    if (e >= ept) continue;
+    mn = min(mn, key[e] != 0u ? key[e] : 0xffffffffu);
+    mx = max(mx, key[e]);
+  }
+  mn = wave_umin(mn);
+  mx = wave_umax(mx);
+  if (lane == 0) {
+    sh.wg[wave] = mn;
+    sh.we[wave] = mx;
+  }
+  __syncthreads();
+  mn = 0xffffffffu;
+  mx = 0u;
+  for (int w = 0; w < TK_WAVES; ++w) {
+    mn = min(mn, sh.wg[w]);
+    mx = max(mx, sh.we[w]);
+  }
+  __syncthreads();
+  uint32_t tau, kk = (uint32_t)K;
+  if (mn == mx) {
+    tau = mn;  // every key equal: the first K positions
+  } else {
+    const int rb = 32 - __clz(mn ^ mx);            // bits below the common prefix
+    const uint32_t common = rb == 32 ? 0u : (mx >> rb) << rb;
+    const int wa = min(rb, 12), sha = rb - wa;
+    const int nba = 1 << wa;
+    // 2. first digit
+    for (int i = tid; i <= TK_BINS; i += TK_THREADS) sh.hist[i] = 0;
+    if (tid == 0) sh.ncand = 0;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < TK_EPT; ++e) {
+      if (e >= ept) continue;
+      const uint32_t bin = key[e] >= mn ? (key[e] >> sha) & (uint32_t)(nba - 1) : (uint32_t)TK_BINS;
+      atomicAdd(&sh.hist[bin], 1u);
+    }
+    __syncthreads();
+    topk_pick(sh, nba, kk, tid);
+    const uint32_t da = sh.digit;
+    kk -= sh.above;
+    const uint32_t c_eq = sh.hist[da];
+    __syncthreads();  // every thread has read the bin count before hist is cleared again
+    uint32_t prefix = common | (da << sha);
+    if (sha == 0) {
+      tau = prefix;
+    } else if (c_eq <= (uint32_t)TK_CAP) {
+      // 3a. the bin's keys into LDS (their low bits), resolved there
+      const uint32_t low_mask = (1u << sha) - 1u;
+#pragma unroll
+      for (int e = 0; e < TK_EPT; ++e) {
+        if (e >= ept) continue;
+        if (key[e] >= mn && (key[e] >> sha) == (prefix >> sha))
+          sh.cand[atomicAdd(&sh.ncand, 1u)] = key[e] & low_mask;
+      }
+      __syncthreads();
+      uint32_t low = 0;
+      int left = sha;
+      while (left > 0) {
+        const int w = min(10, left), shb = left - w;
+        for (int i = tid; i < (1 << w); i += TK_THREADS) sh.hist[i] = 0;
+        __syncthreads();
+        for (int i = tid; i < (int)c_eq; i += TK_THREADS) {
+          const uint32_t v = sh.cand[i];
+          if ((v >> left) == (low >> left)) atomicAdd(&sh.hist[(v >> shb) & ((1u << w) - 1u)], 1u);
+        }
+        __syncthreads();
+        topk_pick(sh, 1 << w, kk, tid);
+        low |= sh.digit << shb;
+        kk -= sh.above;
+        left = shb;
+      }
+      tau = prefix | low;
+    } else {
+      // 3b. a crowded bin: the remaining bits in the registers, 8 at a time
+      int left = sha;
+      while (left > 0) {
+        const int w = min(8, left), shb = left - w;
+        const uint32_t pm = ~((1u << left) - 1u);
+        for (int i = tid; i <= TK_BINS; i += TK_THREADS) sh.hist[i] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < TK_EPT; ++e) {
+          if (e >= ept) continue;
+          const bool m = key[e] >= mn && (key[e] & pm) == prefix;
+          atomicAdd(&sh.hist[m ? (key[e] >> shb) & ((1u << w) - 1u) : (uint32_t)TK_BINS], 1u);
+        }
+        __syncthreads();
+        topk_pick(sh, 1 << w, kk, tid);
+        prefix |= sh.digit << shb;
+        kk -= sh.above;
+        left = shb;
+      }
+      tau = prefix;
+    }
+  }
+  // the selection in position order: every key above tau, and the first kk keys
+  // equal to it (tau > 0, so placeholders never qualify)
+  uint32_t cg = 0, ce = 0;
+#pragma unroll
+  for (int e = 0; e < TK_EPT; ++e) {
+    if (e >= ept) continue;
+    cg += key[e] > tau ? 1u : 0u;
+    ce += key[e] == tau ? 1u : 0u;
+  }
+  uint32_t gb, eb, tg, te;
+  topk_block_scan(sh, cg, ce, tid, gb, eb, tg, te);
+#pragma unroll
+  for (int e = 0; e < TK_EPT; ++e) {
+    if (e >= ept) continue;
+    const bool gt = key[e] > tau, eq = key[e] == tau;
+    const uint32_t slot = gb + min(eb, kk);  // < K by the selection invariant
+    if ((gt || (eq && eb < kk)) && slot < (uint32_t)K) out[slot] = p0 + e;
+    gb += gt ? 1u : 0u;
+    eb += eq ? 1u : 0u;
+  }
+}
+
+// Longer rows: radix select 8 bits at a time from the top, the row read from
+// memory in every pass.
+__device__ __forceinline__ void topk_streaming(TopkShared& sh, const float* row, int n, int K,
+                                               int32_t* out, int tid) {
+  const int n4 = n & ~3;
+  uint32_t prefix = 0, pmask = 0, kk = (uint32_t)K;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    if (tid < 256) hist[tid] = 0;
+    if (tid < 256) sh.hist[tid] = 0;
     __syncthreads();
     for (int i = 4 * tid; i < n4; i += 4 * TK_THREADS) {
       const f32x4_t v = *reinterpret_cast<const f32x4_t*>(row + i);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t u = order_key(v[j]);
-        if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+        if ((u & pmask) == prefix) atomicAdd(&sh.hist[(u >> shift) & 255u], 1u);
       }
     }
     for (int i = n4 + tid; i < n; i += TK_THREADS) {
       const uint32_t u = order_key(row[i]);
-      if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+      if ((u & pmask) == prefix) atomicAdd(&sh.hist[(u >> shift) & 255u], 1u);
     }
     __syncthreads();
-    if (wave == 0) {
-      // lane l holds bins 255-4l .. 252-4l, i.e. the bins in descending order
-      uint32_t c[4], sum = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        c[j] = hist[255 - 4 * lane - j];
-        sum += c[j];
-      }
-      uint32_t above = wave_incl_scan(sum, lane) - sum;  // keys in higher bins
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (above < kk && kk <= above + c[j]) {
-          s_digit = 255u - 4u * lane - j;
-          s_above = above;
-        }
-        above += c[j];
-      }
-    }
-    __syncthreads();
-    prefix |= s_digit << shift;
+    topk_pick(sh, 256, kk, tid);
+    prefix |= sh.digit << shift;
     pmask |= 255u << shift;
-    kk -= s_above;
+    kk -= sh.above;
   }
-  // prefix is the K-th largest key; the selection is every key above it and the
-  // first kk keys equal to it in position order.  Written in position order.
   const uint32_t tau = prefix;
   uint32_t base_gt = 0, base_eq = 0;
   for (int i0 = 0; i0 < n; i0 += 4 * TK_THREADS) {
     const int i = i0 + 4 * tid;
     uint32_t u[4];
-    if (i + 3 < n) {
-      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(row + i);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) u[j] = order_key(v[j]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) u[j] = (i + j < n) ? order_key(row[i + j]) : 0u;
-    }
+    for (int j = 0; j < 4; ++j) u[j] = (i + j < n) ? order_key(row[i + j]) : 0u;
     uint32_t cg = 0, ce = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -385,36 +605,44 @@ __global__ __launch_bounds__(TK_THREADS) void sparse_topk_kernel(const float* sc
       cg += (valid && u[j] > tau) ? 1u : 0u;
       ce += (valid && u[j] == tau) ? 1u : 0u;
     }
-    const uint32_t ig = wave_incl_scan(cg, lane), ie = wave_incl_scan(ce, lane);
-    if (lane == 63) {
-      wgt[wave] = ig;
-      weq[wave] = ie;
-    }
-    __syncthreads();
-    uint32_t pg = 0, pe = 0, tg = 0, te = 0;
-    for (int w = 0; w < TK_WAVES; ++w) {
-      const uint32_t a = wgt[w], b = weq[w];
-      if (w < wave) {
-        pg += a;
-        pe += b;
-      }
-      tg += a;
-      te += b;
-    }
-    uint32_t g_before = base_gt + pg + ig - cg, e_before = base_eq + pe + ie - ce;
+    uint32_t gb, eb, tg, te;
+    topk_block_scan(sh, cg, ce, tid, gb, eb, tg, te);
+    gb += base_gt;
+    eb += base_eq;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      if (i + j >= n) break;
-      const bool gt = u[j] > tau, eq = u[j] == tau;
-      const uint32_t slot = g_before + min(e_before, kk);  // < K by the radix invariant
-      if ((gt || (eq && e_before < kk)) && slot < (uint32_t)K) out[slot] = i + j;
-      g_before += gt ? 1u : 0u;
-      e_before += eq ? 1u : 0u;
+      if (i + j < n) {
+        const bool gt = u[j] > tau, eq = u[j] == tau;
+        const uint32_t slot = gb + min(eb, kk);  // < K by the selection invariant
+        if ((gt || (eq && eb < kk)) && slot < (uint32_t)K) out[slot] = i + j;
+        gb += gt ? 1u : 0u;
+        eb += eq ? 1u : 0u;
+      }
     }
     base_gt += tg;
     base_eq += te;
-    __syncthreads();  // wgt/weq are rewritten by the next tile
   }
+}
+
+// The K largest order keys of a row, ties to the lower position, written in
+// ascending position order.
+__global__ __launch_bounds__(TK_THREADS) void sparse_topk_kernel(const float* scores, size_t stride,
+                                                                 const int32_t* tok_pos, int K,
+                                                                 int32_t* sel) {
+  __shared__ TopkShared sh;
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int n = tok_pos[t] + 1;
+  int32_t* out = sel + (size_t)t * K;
+  if (n <= K) {
+    for (int i = tid; i < K; i += TK_THREADS) out[i] = i < n ? i : -1;
+    return;
+  }
+  const float* row = scores + (size_t)t * stride;
+  if (n <= TK_THREADS * TK_EPT)
+    topk_registers(sh, row, n, K, out, tid);
+  else
+    topk_streaming(sh, row, n, K, out, tid);
 }
 
 hipError_t launch_sparse_topk(const float* scores, size_t stride, const int32_t* tok_pos, int T,
@@ -471,12 +699,27 @@ __global__ __launch_bounds__(512, 1) void sparse_attention_kernel(SparseAttnArgs
   bool first = true;
   const size_t kvrow0 = (size_t)g * SCHUNK;  // head g's row offset inside a cache block
 
-  for (int c = 0; c < n_chunks; ++c) {
-    // entry e0 + lane: its cache row (kv head g), -1 when not a valid position
-    const int e = e_seg + c * SCHUNK + lane;
-    const int sp = srow[e];
-    const bool valid = sp >= 0 && sp <= pos;
-    const int slot = valid ? (btab[sp >> 6] * p.nkv * SCHUNK + (int)kvrow0 + (sp & 63)) : -1;
+  // the cache rows of all of this wave's entries first (entry e_seg + 64c + lane:
+  // row of kv head g, -1 when not a valid position), so each chunk then waits on
+  // one round of K/V loads only
+  constexpr int CPS = SSEG / SCHUNK;
+  int slots[CPS];
+  {
+    int sp[CPS];
+#pragma unroll
+    for (int c = 0; c < CPS; ++c) sp[c] = c < n_chunks ? srow[e_seg + c * SCHUNK + lane] : -1;
+#pragma unroll
+    for (int c = 0; c < CPS; ++c) {
+      const bool valid = sp[c] >= 0 && sp[c] <= pos;
+      slots[c] = valid ? (btab[sp[c] >> 6] * p.nkv * SCHUNK + (int)kvrow0 + (sp[c] & 63)) : -1;
+    }
+  }
+
+#pragma unroll
+  for (int c = 0; c < CPS; ++c) {
+    if (c >= n_chunks) break;
+    const int slot = slots[c];
+    const bool valid = slot >= 0;
     const uint64_t any = __ballot(valid);
     if (any == 0) continue;
     // K: the A operand rows, key 16kt + lc of the chunk, dims 32ks + 8lg .. +7

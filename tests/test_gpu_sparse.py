@@ -346,3 +346,57 @@ def test_full_size_decode_batch_sampled():
             check_token(ctx, oseq, lengths[s] - 1, 2048, sc64[j], sl64[j], o64[j])
     finally:
         ctx.close()
+
+
+# ------------------------------------------------ Top-K alone, on chosen score rows
+
+def _topk_rows():
+    """Score rows that exercise each path of the selection: equal keys, a crowded
+    first-digit bin (> 4096 keys), ties across the cut, signed zeros and negatives,
+    n just above K, spread values, and a row past 65536 positions."""
+    rng = np.random.default_rng(11)
+    rows = []
+    rows.append(np.full(9000, 1.5, np.float32))                                   # all equal
+    r = np.full(12000, 1.0, np.float32)                                            # crowded bin
+    r[rng.choice(12000, 300, replace=False)] = 2.0
+    rows.append(r)
+    rows.append((rng.integers(0, 40, 5000) * 0.25).astype(np.float32))             # coarse ties
+    r = rng.standard_normal(7000).astype(np.float32)
+    r[rng.choice(7000, 500, replace=False)] = 0.0
+    r[rng.choice(7000, 500, replace=False)] = -0.0
+    rows.append(r)                                                                 # signs, zeros
+    rows.append(-np.abs(rng.standard_normal(2049)).astype(np.float32))             # n = K + 1
+    rows.append((rng.standard_normal(60000) * 1e3).astype(np.float32))             # spread
+    r = np.full(30000, 3.0, np.float32)                                            # ties at the cut
+    r[:1000] = 5.0
+    rows.append(r)
+    rows.append(rng.standard_normal(70001).astype(np.float32))                     # > 65536
+    return rows
+
+
+def test_topk_rows_match_oracle():
+    a = abi()
+    rows = _topk_rows()
+    K = 2048
+    n_max = max(len(r) for r in rows)
+    ctx = SparseCtx([n_max] * len(rows), max_tokens=64, inputs=None)
+    try:
+        stride = ctx.stride
+        sc = np.zeros((len(rows), stride), np.float32)
+        for i, r in enumerate(rows):
+            sc[i, : len(r)] = r
+        chunks = [(i, len(r) - 1, 1) for i, r in enumerate(rows)]
+        bt = np.array([ctx.blocks[s] + [0] * (ctx.maxb - len(ctx.blocks[s])) for s, _, _ in chunks],
+                      np.int32)
+        a.bci_set_batch(ctx.h, np.zeros(len(rows), np.int32), np.arange(len(rows) + 1, dtype=np.int32),
+                        np.array([p for _, p, _ in chunks], np.int32), bt, [], [])
+        g_sc = torch.from_numpy(sc).cuda()
+        sel = torch.empty(len(rows), K, dtype=torch.int32, device="cuda")
+        a.bci_op_sparse_topk(ctx.h, g_sc, stride, K, sel)
+        torch.cuda.synchronize()
+        got = sel.cpu().numpy()
+        for i, r in enumerate(rows):
+            want = sparse.topk_select(r.astype(np.float64), K)
+            np.testing.assert_array_equal(got[i], want, err_msg=f"row {i} (n = {len(r)})")
+    finally:
+        ctx.close()
