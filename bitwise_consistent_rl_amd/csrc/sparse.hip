@@ -161,8 +161,9 @@ __device__ __forceinline__ int iswz(int key, int ch) {
 
 // Decode-like schedule: one token per workgroup row of the grid; wave w of
 // workgroup x takes key blocks x*4 + w, then + 4*gridDim.x, ... (64 keys each),
-// reading the codes straight into the B operand (dequantised in registers); the
-// next block's codes are in flight while the current one is multiplied.
+// reading the codes straight into the B operand (dequantised in registers).  A
+// prefetch of the next block's codes was measured slower (more registers, fewer
+// waves per SIMD) and is not used.
 template <int DI>
 struct RawKeys {
   u32x2_t c[4][DI / 32];
@@ -196,7 +197,7 @@ __global__ __launch_bounds__(256) void index_scores_direct(IdxArgs a) {
   if (b >= nblk) return;
   const int* btab = a.block_table + (size_t)a.tok_seq[t] * a.max_blocks;
 
-  RawKeys<DI> cur, nxt;
+  RawKeys<DI> cur;
   raw_keys_load<DI>(a, btab, b * SCHUNK, pos, lg, lc, cur);
   bf16x8_t qa[NHT][DI / 32];
   float wv[NHT][4];
@@ -205,14 +206,13 @@ __global__ __launch_bounds__(256) void index_scores_direct(IdxArgs a) {
 
   while (true) {
     const int bn = b + step;
-    if (bn < nblk) raw_keys_load<DI>(a, btab, bn * SCHUNK, pos, lg, lc, nxt);
     const float v = index_chain<NHT, DI>(
         qa, [&](int kt, int ks) { return dequant8(cur.c[kt][ks], cur.sc[kt]); }, wv, lg);
     const int s = b * SCHUNK + 16 * lg + lc;
     if (s <= pos) srow[s] = v;
     if (bn >= nblk) break;
     b = bn;
-    cur = nxt;
+    raw_keys_load<DI>(a, btab, bn * SCHUNK, pos, lg, lc, cur);
   }
 }
 

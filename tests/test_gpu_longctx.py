@@ -4,7 +4,8 @@ per-token-per-head scales, contexts 8K / 32K / 57K, batch 1..64 of mixed lengths
 Prefill, chunked prefill (chunk 2048) and decode all read the cache through the same
 gather + dequantise rule and run the same attention kernel; the output of a query is
 bitwise identical across the three phases and across batch sizes, and matches the
-oracle's attention over the GPU's own dequantised keys and values."""
+oracle's attention over its own rotated, FP8-round-tripped keys and values of the
+same seeded qkv rows."""
 import numpy as np
 import pytest
 import torch
@@ -121,11 +122,14 @@ def test_decode_invariant_across_batch_and_matches_oracle(qkv, C):
             assert same_bits(o1s, o1)
         finally:
             ctx_seq.close()
-        # parity: the oracle's attention over the GPU's dequantised K/V
-        K, V = ctx.gather(0, C)
-        ref = ops.causal_gqa_attention(f64(q1).reshape(1, NQ, D), f64(K), f64(V), [C - 1])
+        # parity: the oracle rotates and FP8-round-trips the same qkv rows itself
+        kv = f64(qkv[0:C, NQ * D:]).reshape(C, 2 * NKV, D)
+        K = ops.kv_roundtrip(ops.rope(kv[:, :NKV], np.arange(C), 1e6))
+        V = ops.kv_roundtrip(kv[:, NKV:])
+        qo = ops.rope(f64(qkv[C - 1: C, : NQ * D]).reshape(1, NQ, D), [C - 1], 1e6)
+        ref = ops.causal_gqa_attention(qo, K, V, [C - 1])
         got = f64(o1).reshape(1, NQ, D)
-        scale = np.max(np.abs(f64(V)))
+        scale = np.max(np.abs(V))
         assert np.max(np.abs(got - ref)) <= 1.5e-2 * scale
         assert np.mean(np.abs(got - ref)) <= 1.5e-3 * scale
     finally:

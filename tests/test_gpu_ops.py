@@ -392,10 +392,17 @@ def test_attention_parity(nq, nkv, d, seg, kv):
     calls = [[(i, 0, L) for i, L in enumerate(lengths)]]
     o, q, kvs = _attention_run(nq, nkv, d, kv, seg, lengths, qkv, calls)
     offs = np.concatenate([[0], np.cumsum(lengths)])
+    X = f64(qkv)
     for i, L in enumerate(lengths):
-        qi = f64(q[offs[i]:offs[i + 1]]).reshape(L, nq, d)
-        K, V = f64(kvs[i][0]), f64(kvs[i][1])
-        ref = ops.causal_gqa_attention(qi, K, V, np.arange(L))
+        # the oracle's own rotation (and FP8 round trip) of the same qkv rows
+        Xi = X[offs[i]:offs[i + 1]]
+        pos = np.arange(L)
+        qi = ops.rope(Xi[:, : nq * d].reshape(L, nq, d), pos, 1e6)
+        K = ops.rope(Xi[:, nq * d:(nq + nkv) * d].reshape(L, nkv, d), pos, 1e6)
+        V = Xi[:, (nq + nkv) * d:].reshape(L, nkv, d)
+        if kv == "fp8":
+            K, V = ops.kv_roundtrip(K), ops.kv_roundtrip(V)
+        ref = ops.causal_gqa_attention(qi, K, V, pos)
         got = f64(o[offs[i]:offs[i + 1]]).reshape(L, nq, d)
         err = np.abs(got - ref)
         scale = np.max(np.abs(V))
