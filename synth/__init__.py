@@ -284,3 +284,19 @@ def sparse_index_inputs(T: int, n_keys: int, heads: int = 64, dim: int = 128,
         k = rng.standard_normal((n_keys, dim), dtype=np.float32)
         w = rng.standard_normal((T, heads), dtype=np.float32) / np.float32(np.sqrt(heads))
     return to_bf16(q), w, to_bf16(k)
+
+
+def ssd_inputs(T: int, heads: int = 128, head_dim: int = 64, d_state: int = 128, groups: int = 8,
+               seed: int = SEED_INPUTS, index: int = 12) -> Dict[str, object]:
+    """Inputs of a Mamba-2-style state-space layer for T positions: x [T, heads, head_dim]
+    bf16 N(0, 1); dt [T, heads] fp32 log-uniform in [1e-3, 1e-1] (the step after its
+    softplus); A [heads] fp32 = -exp(U(0, ln 16)); B, C [T, groups, d_state] bf16 N(0, 1);
+    D [heads] fp32 = 1 + 0.1 N(0, 1)."""
+    rng = _rng(seed, index)
+    x = rng.standard_normal((T, heads, head_dim), dtype=np.float32)
+    dt = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), (T, heads))).astype(np.float32)
+    A = (-np.exp(rng.uniform(0.0, np.log(16.0), heads))).astype(np.float32)
+    B = rng.standard_normal((T, groups, d_state), dtype=np.float32)
+    C = rng.standard_normal((T, groups, d_state), dtype=np.float32)
+    D = (1.0 + 0.1 * rng.standard_normal(heads)).astype(np.float32)
+    return dict(x=to_bf16(x), dt=dt, A=A, B=to_bf16(B), C=to_bf16(C), D=D)
