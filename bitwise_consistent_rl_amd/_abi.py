@@ -34,7 +34,8 @@ EXPORTS = [
     "bci_op_lmhead_logprob", "bci_op_moe_topk", "bci_op_moe_forward", "bci_profile_begin",
     "bci_profile_end", "bci_forward_logprobs_graph", "bci_graph_count", "bci_graph_reset",
     "bci_op_index_key_write", "bci_op_index_scores", "bci_op_sparse_topk",
-    "bci_op_sparse_attention",
+    "bci_op_sparse_attention", "bci_ssd_create", "bci_ssd_destroy", "bci_ssd_last_error",
+    "bci_ssd_slot_bytes", "bci_ssd_set_batch", "bci_ssd_forward",
 ]
 
 
@@ -56,6 +57,12 @@ class ModelConfig(ctypes.Structure):
 
 
 _P32 = ctypes.POINTER(ctypes.c_int32)
+
+
+class SsdConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("n_heads", "head_dim", "d_state", "n_groups", "max_tokens_per_call",
+                 "max_seqs_per_call")]
 
 
 class Batch(ctypes.Structure):
@@ -104,6 +111,12 @@ def load() -> ctypes.CDLL:
         "bci_op_index_scores": (st, [vp, vp, vp, i32, i32, vp, vp, i32, vp, ctypes.c_int64, i32, vp]),
         "bci_op_sparse_topk": (st, [vp, vp, ctypes.c_int64, i32, vp, vp]),
         "bci_op_sparse_attention": (st, [vp, vp, i32, vp, i32, vp, vp]),
+        "bci_ssd_create": (st, [ctypes.POINTER(SsdConfig), i32, ctypes.POINTER(vp)]),
+        "bci_ssd_destroy": (None, [vp]),
+        "bci_ssd_last_error": (ctypes.c_char_p, [vp]),
+        "bci_ssd_slot_bytes": (ctypes.c_uint64, [vp, i32]),
+        "bci_ssd_set_batch": (st, [vp, i32, _P32, _P32, _P32, vp]),
+        "bci_ssd_forward": (st, [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp]),
         "bci_profile_begin": (st, [vp]),
         "bci_profile_end": (st, [vp, ctypes.POINTER(ctypes.c_double), _P32]),
     }
@@ -285,6 +298,47 @@ def bci_op_sparse_topk(ctx: int, scores, score_stride: int, topk: int, sel, stre
 def bci_op_sparse_attention(ctx: int, q, layer: int, sel, topk: int, o, stream=None) -> None:
     _check(ctx, load().bci_op_sparse_attention(ctx, _ptr(q), layer, _ptr(sel), topk, _ptr(o),
                                                _stream(stream)))
+
+
+def _ssd_check(ctx, status: int):
+    if status != BCI_OK:
+        msg = load().bci_ssd_last_error(ctx).decode() if ctx else ""
+        raise BciError(status, msg)
+
+
+def bci_ssd_create(cfg: SsdConfig, device: int = 0) -> int:
+    h = ctypes.c_void_p()
+    st = load().bci_ssd_create(ctypes.byref(cfg), device, ctypes.byref(h))
+    if st != BCI_OK:
+        raise BciError(st, "bci_ssd_create rejected the configuration or could not allocate")
+    return h.value
+
+
+def bci_ssd_destroy(ctx: int) -> None:
+    load().bci_ssd_destroy(ctx)
+
+
+def bci_ssd_last_error(ctx: int) -> str:
+    return load().bci_ssd_last_error(ctx).decode()
+
+
+def bci_ssd_slot_bytes(ctx: int, which: int) -> int:
+    return int(load().bci_ssd_slot_bytes(ctx, which))
+
+
+def bci_ssd_set_batch(ctx: int, cu_q, pos0, slot, stream=None) -> None:
+    """Host arrays: cu_q [n_seqs + 1], pos0 [n_seqs], slot [n_seqs]."""
+    keep = [_i32(cu_q), _i32(pos0), _i32(slot)]
+    n = len(keep[1])
+    _ssd_check(ctx, load().bci_ssd_set_batch(ctx, n, *[a.ctypes.data_as(_P32) for a in keep],
+                                             _stream(stream)))
+
+
+def bci_ssd_forward(ctx: int, x, dt, A, B, C, D, state, chunk_buf, n_slots: int, y,
+                    stream=None) -> None:
+    _ssd_check(ctx, load().bci_ssd_forward(ctx, _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                                           _ptr(D), _ptr(state), _ptr(chunk_buf), n_slots, _ptr(y),
+                                           _stream(stream)))
 
 
 def bci_profile_begin(ctx: int) -> None:

@@ -22,8 +22,8 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libbci.so")
 OBJ_DIR = os.path.join(ROOT, "_build", "obj")
 
-SOURCES = ["norm.hip", "gemm.hip", "rope_kv.hip", "attention.hip", "moe.hip", "sparse.hip",
-           "bci.cpp"]
+SOURCES = ["norm.hip", "gemm.hip", "rope_kv.hip", "attention.hip", "moe.hip", "sparse.hip", "ssd.hip",
+           "bci.cpp", "ssd_api.cpp"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

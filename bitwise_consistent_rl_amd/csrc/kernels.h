@@ -122,6 +122,23 @@ struct SparseAttnArgs {
 constexpr int SPARSE_MAX_K = 2048;
 hipError_t launch_sparse_attention(const SparseAttnArgs& a, hipStream_t s);
 
+// ---- ssd.hip (state-space layer, chunked; decode replays prefill's chunks)
+struct SsdArgs {
+  const uint16_t *x, *B, *C;   // call inputs: x [T, heads, 64], B/C [T, groups, N] bf16
+  const float *dt, *A, *D;     // dt [T, heads]; A, D [heads]
+  uint16_t* y;                 // [T, heads, 64] bf16
+  uint16_t *xb, *Bb;           // chunk buffers [slots][64][heads][64], [slots][64][groups][N]
+  float* dtb;                  // [slots][64][heads]
+  float* state;                // [slots][heads][64][N] fp32
+  float* cstate;               // [max_done][heads][64][N] fp32 workspace
+  float* lend;                 // [max_done][heads]
+  const int32_t* seqs;         // [n_seqs][6]: cu, pos0, q_len, slot, first done index, n done
+  const int32_t* inst;         // [n_inst][6]: seq, chunk, first pos, last pos, done index or -1, 0
+  const int32_t* done;         // [n_done]: instance of each completed chunk
+  int heads, groups, N, n_seqs, n_inst, n_done;
+};
+hipError_t launch_ssd(const SsdArgs& a, hipStream_t s);
+
 // ---- moe.hip
 constexpr int MOE_MAX_K = 8;
 hipError_t launch_moe_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,

@@ -338,6 +338,67 @@ bci_status bci_op_moe_forward(bci_ctx* ctx, const void* h, const int32_t* ids, c
                               int32_t T, const void* wgu, const void* wd, const void* swgu,
                               const void* swd, void* out, void* stream);
 
+/* ---- state-space layer (Mamba-2-style), chunked ---------------------------------
+ * Porting the method to Nemotron-3.5 meant recursive arithmetic in which decode
+ * replays prefill's chunked computation order and training reuses the same operator
+ * (page "Finish RL Training Faster" digest, sections "一致性有多个层面，修好一处还不能验收"
+ * and "两组结果，要连同分母一起读").  The pages give no formula; the layer computed is
+ * the Mamba-2 selective state-space recurrence, per head h (B, C shared by the heads of
+ * a group g = h / (n_heads / n_groups)), from a zero state at position 0:
+ *   h_t = exp(A[h] dt[t,h]) h_{t-1} + dt[t,h] B[t,g] (outer) x[t,h]
+ *   y[t,h] = bf( C[t,g] . h_t + D[h] x[t,h] )
+ * evaluated in chunks of 64 positions at fixed absolute positions.  The state is kept
+ * only at chunk ends; every position's output is computed from the state before its
+ * chunk and the chunk's inputs up to it by one routine, so a token's output bits do
+ * not depend on the batch, on how its sequence was split into calls (prefill, chunked
+ * prefill, decode) or on the call.  The context is separate from bci_ctx: a layer of
+ * this kind holds no KV cache.
+ *
+ * Per-slot memory is the caller's (one slot per sequence in flight):
+ *   state     [n_slots, n_heads, 64 (head dim), d_state] fp32 -- the state at the last
+ *             chunk end of the slot's sequence (never read for chunk 0, so a new
+ *             sequence needs no clearing);
+ *   chunk_buf [x: n_slots, 64, n_heads, 64 bf16][B: n_slots, 64, n_groups, d_state bf16]
+ *             [dt: n_slots, 64, n_heads fp32] -- the inputs of the slot's unfinished
+ *             chunk.  bci_ssd_slot_bytes(which = 0 / 1) gives one slot's size of each.
+ * A slot's pos0 in a call must equal the number of positions its sequence has already
+ * run through this layer (0 for a new sequence); calls that overlap on a slot race. */
+typedef struct bci_ssd bci_ssd;
+typedef struct {
+  int32_t n_heads;     /* multiple of n_groups */
+  int32_t head_dim;    /* 64 */
+  int32_t d_state;     /* 64 or 128 */
+  int32_t n_groups;
+  int32_t max_tokens_per_call;
+  int32_t max_seqs_per_call;
+} bci_ssd_config;
+
+/* Validates the configuration and allocates the workspace (chunk states of up to
+ * max_tokens_per_call / 64 + max_seqs_per_call chunks, and the call tables). */
+bci_status bci_ssd_create(const bci_ssd_config* cfg, int32_t device, bci_ssd** out);
+void bci_ssd_destroy(bci_ssd* ctx);
+const char* bci_ssd_last_error(const bci_ssd* ctx);
+/* Bytes of one slot: which = 0 the state, 1 the chunk buffer (0 for other values). */
+uint64_t bci_ssd_slot_bytes(const bci_ssd* ctx, int32_t which);
+
+/* The next call's layout (host arrays): sequence i owns tokens [cu_q[i], cu_q[i+1])
+ * (at least one) at positions pos0[i] .. and uses slot[i] (distinct within a call).
+ * Uploads the chunk tables on `stream`; errors leave nothing enqueued. */
+bci_status bci_ssd_set_batch(bci_ssd* ctx, int32_t n_seqs, const int32_t* cu_q, const int32_t* pos0,
+                             const int32_t* slot, void* stream);
+
+/* One layer over the current batch.  x [T, n_heads, 64] bf16, dt [T, n_heads] fp32 (the
+ * step after its softplus), A [n_heads] fp32 (< 0), B and C [T, n_groups, d_state] bf16,
+ * D [n_heads] fp32 (device pointers; x, dt, B, C, state, chunk_buf and y 16-byte
+ * aligned); y [T, n_heads, 64] bf16.  Updates the slots' state and chunk buffer.  Per
+ * head, with a_j = fp32(A log2 e) dt_j and L_t their inclusive prefix over the chunk:
+ *   y_t = bf((2^L_t (C_t . bf(H)) + sum_{j<=t} bf((C_t . B_j) 2^(L_t - L_j) dt_j) x_j) + D x_t),
+ *   H <- 2^L_63 H + sum_j x_j (outer) bf(B_j 2^(L_63 - L_j) dt_j)  at each chunk end,
+ * dot products on fp32-accumulating MFMA in ascending 32-wide steps. */
+bci_status bci_ssd_forward(bci_ssd* ctx, const void* x, const float* dt, const float* A, const void* B,
+                           const void* C, const float* D, float* state, void* chunk_buf, int32_t n_slots,
+                           void* y, void* stream);
+
 /* ---- instrumentation ----------------------------------------------------- */
 
 /* While enabled, bci_forward_logprobs records a HIP event pair on its stream
