@@ -509,6 +509,74 @@ def sparse_bench(args):
     abi.bci_destroy(ctx)
 
 
+def ssd_bench(args):
+    """Chunked state-space layer (Mamba-2-style; 128 heads x 64, 8 groups, state 128, chunks
+    of 64): a prefill call of 4 sequences x 4096 positions, and decode steps at B = 1, 16,
+    64 with every sequence 1000 positions in (the state, and a partly filled chunk, read
+    back).  Algorithmic work per (token, head): 2 x 64 x 128 (inter) + 2 x 64 x 128 (the
+    scores against the chunk) + 2 x 64 x 64 (their product with x) + 2 x 64 x 128 (the
+    chunk state, per position) = 57344 FLOP; bytes per token: x 16 KiB + B and C 4 KiB + dt
+    512 B read, y 16 KiB written; decode also reads each (sequence, head) state once
+    (32 KiB fp32)."""
+    import numpy as np
+    import torch
+    import synth
+    from bitwise_consistent_rl_amd import _abi as abi
+    H, G, N, P = 128, 8, 128, 64
+    cfg = abi.SsdConfig()
+    for k, v in dict(n_heads=H, head_dim=P, d_state=N, n_groups=G, max_tokens_per_call=16384,
+                     max_seqs_per_call=64).items():
+        setattr(cfg, k, v)
+    ctx = abi.bci_ssd_create(cfg, 0)
+    n_slots = 64
+    state = torch.zeros(n_slots, H, P, N, device="cuda")
+    cbuf = torch.zeros(abi.bci_ssd_slot_bytes(ctx, 1) * n_slots, dtype=torch.uint8, device="cuda")
+    d = synth.ssd_inputs(16384, H, P, N, G, index=30)
+    x, B, C = d["x"].cuda(), d["B"].cuda(), d["C"].cuda()
+    dt = torch.from_numpy(d["dt"]).cuda()
+    A, D = torch.from_numpy(d["A"]).cuda(), torch.from_numpy(d["D"]).cuda()
+    y = torch.empty_like(x)
+    flop_tok, byte_tok = 57344.0 * H, 16384 + 4096 + 512 + 16384
+
+    def report(name, T, us, extra_bytes=0.0):
+        flops, nbytes = flop_tok * T, byte_tok * T + extra_bytes
+        t_f, t_b = flops / (PEAK_BF16_TFLOPS * 1e12), nbytes / (PEAK_HBM_GBS * 1e9)
+        bound = "mfma" if t_f > t_b else "hbm"
+        print(json.dumps({"workload": "state-space layer, 128 heads x 64, state 128, chunk 64",
+                          "phase": name, "tokens": T, "us": round(us, 2),
+                          "tokens_per_s": round(T / us * 1e6, 1), "bound": bound,
+                          "achieved": round(flops / us / 1e6, 1) if bound == "mfma"
+                          else round(nbytes / us / 1e3, 1),
+                          "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
+                          "frac_of_roofline": round(max(t_f, t_b) / (us * 1e-6), 4)}), flush=True)
+
+    # prefill: 4 sequences x 4096 positions in one call (slots 0..3)
+    cu = np.arange(0, 16385, 4096, dtype=np.int32)
+
+    def prefill():
+        abi.bci_ssd_set_batch(ctx, cu, [0, 0, 0, 0], [0, 1, 2, 3])
+        abi.bci_ssd_forward(ctx, x, dt, A, B, C, D, state, cbuf, n_slots, y)
+    report("prefill 4 x 4096", 16384, _time_ms(prefill, reps=5, warm=2) * 1e3)
+    # decode: every slot holds 1000 positions (prefilled in calls of 16 sequences)
+    for s0 in range(0, 64, 16):
+        abi.bci_ssd_set_batch(ctx, np.arange(0, 16 * 1000 + 1, 1000, dtype=np.int32), [0] * 16,
+                              list(range(s0, s0 + 16)))
+        abi.bci_ssd_forward(ctx, x, dt, A, B, C, D, state, cbuf, n_slots, y)
+    torch.cuda.synchronize()
+    for Bn in (1, 16, 64):
+        cud = np.arange(Bn + 1, dtype=np.int32)
+        xs, dts, Bs, Cs = x[:Bn].contiguous(), dt[:Bn].contiguous(), B[:Bn].contiguous(), C[:Bn].contiguous()
+        ys = y[:Bn]
+
+        def step():
+            # position 1000 again each time: the same work per step (the chunk is not
+            # completed, so the slots' states are not changed)
+            abi.bci_ssd_set_batch(ctx, cud, [1000] * Bn, list(range(Bn)))
+            abi.bci_ssd_forward(ctx, xs, dts, A, Bs, Cs, D, state, cbuf, n_slots, ys)
+        report(f"decode B = {Bn}", Bn, _time_ms(step, reps=20) * 1e3, extra_bytes=Bn * H * P * N * 4.0)
+    abi.bci_ssd_destroy(ctx)
+
+
 def _time_ms(fn, reps=10, warm=3):
     import torch
     for _ in range(warm):
@@ -620,7 +688,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--micro", choices=["gate_up"], default=None,
                     help="time one kernel alone at the workload's shape (for counter runs)")
-    ap.add_argument("--workload", choices=["recompute", "longctx", "rollout", "lmhead", "moe", "sparse"],
+    ap.add_argument("--workload", choices=["recompute", "longctx", "rollout", "lmhead", "moe", "sparse", "ssd"],
                     default="recompute",
                     help="longctx: FP8-KV long-context attention (decode steps, chunked prefill); "
                          "rollout: continuous-batching decode, invariant vs non-invariant mode; "
@@ -651,6 +719,8 @@ def main():
         return lmhead_bench(args)
     if args.workload == "sparse":
         return sparse_bench(args)
+    if args.workload == "ssd":
+        return ssd_bench(args)
     if args.workload == "moe":
         return moe_bench(args)
     log("generating weights and workload")

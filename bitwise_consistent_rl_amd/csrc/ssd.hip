@@ -22,7 +22,9 @@
 // one new position -- gives the prefill's bits.
 //
 // Per call: chunk_state (chunks that complete in the call), state_pass (per
-// sequence and head, chunk order), chunk_out (every position of the call), and
+// sequence and head, chunk order; hands chunk_out each chunk's state-before in bf16,
+// exactly the rounding chunk_out applies to the slot's fp32 state), chunk_out
+// (every position of the call), and
 // chunk_append (the positions of an unfinished last chunk into the slot's chunk
 // buffer, which the next call reads back).
 #include "common.h"
@@ -139,10 +141,13 @@ __global__ __launch_bounds__(256) void ssd_chunk_state_kernel(SsdArgs a) {
 }
 
 // ------------------------------------------------------------- state pass
-// Per (sequence, head): walk the call's completed chunks in order; each chunk's
-// slot in cstate is replaced by the state before the chunk (what chunk_out reads)
-// and the running state becomes 2^{L_63} H + S.  The final state goes back to the
-// slot.  A sequence whose first chunk of the call is chunk 0 starts from zero.
+// Per (sequence, head, 1024-element block of the state): walk the call's completed
+// chunks in order; each chunk's state-before goes to hprev (rounded to bf16, the
+// form chunk_out multiplies with) and the running state becomes 2^{L_63} H + S.  The
+// final state goes back to the slot.  A sequence whose first chunk of the call is
+// chunk 0 starts from zero.  The chunk states of the next four chunks are loaded
+// before the chain uses them (they do not depend on it).
+constexpr int SP_EPB = 1024;  // state elements per workgroup (256 threads x 4)
 __global__ __launch_bounds__(256) void ssd_state_pass_kernel(SsdArgs a) {
   const int s = blockIdx.x, h = blockIdx.y;
   const int* sq = a.seqs + 6 * s;
@@ -150,17 +155,30 @@ __global__ __launch_bounds__(256) void ssd_state_pass_kernel(SsdArgs a) {
   if (nd == 0) return;
   const int c_first = a.inst[6 * a.done[k0] + 1];
   const size_t per = (size_t)SP * a.N;
-  float* st = a.state + ((size_t)slot * a.heads + h) * per;
-  for (size_t e = threadIdx.x; e < per; e += 256) {
-    float H = c_first == 0 ? 0.0f : st[e];
-    for (int k = k0; k < k0 + nd; ++k) {
-      float* cs = a.cstate + ((size_t)k * a.heads + h) * per;
-      const float S = cs[e];
-      cs[e] = H;
-      H = fexp2(a.lend[(size_t)k * a.heads + h]) * H + S;
+  const size_t e = (size_t)blockIdx.z * SP_EPB + 4 * threadIdx.x;
+  f32x4_t* st = reinterpret_cast<f32x4_t*>(a.state + ((size_t)slot * a.heads + h) * per + e);
+  f32x4_t H = c_first == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : *st;
+  for (int k = k0; k < k0 + nd; k += 4) {
+    f32x4_t S[4];
+    float ek[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (k + i < k0 + nd) {
+        S[i] = *reinterpret_cast<const f32x4_t*>(a.cstate + ((size_t)(k + i) * a.heads + h) * per + e);
+        ek[i] = fexp2(a.lend[(size_t)(k + i) * a.heads + h]);
+      }
     }
-    st[e] = H;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (k + i < k0 + nd) {
+        *reinterpret_cast<u32x2_t*>(a.hprev + ((size_t)(k + i) * a.heads + h) * per + e) =
+            u32x2_t{pack_f2bf2(H[0], H[1]), pack_f2bf2(H[2], H[3])};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) H[j] = ek[i] * H[j] + S[i][j];
+      }
+    }
   }
+  *st = H;
 }
 
 // ------------------------------------------------------------- chunk outputs
@@ -206,16 +224,22 @@ __global__ __launch_bounds__(256) void ssd_chunk_out_kernel(SsdArgs a) {
     for (int i = 0; i < 8; ++i) Xt[(8 * pc + i) * XT_STRIDE + j] = e[i];
   }
   // the state before the chunk, rounded to bf16: zero for chunk 0, the state pass's
-  // copy for a chunk completed in this call, the slot's state otherwise
+  // bf16 copy for a chunk completed in this call, the slot's state otherwise
   {
     const float* src = nullptr;
-    if (c > 0)
-      src = k >= 0 ? a.cstate + (((size_t)k * a.heads + h) * SP) * N
-                   : a.state + (((size_t)slot * a.heads + h) * SP) * N;
+    const bf16_t* srcb = nullptr;
+    if (c > 0) {
+      if (k >= 0)
+        srcb = a.hprev + (((size_t)k * a.heads + h) * SP) * N;
+      else
+        src = a.state + (((size_t)slot * a.heads + h) * SP) * N;
+    }
     for (int u = tid; u < SP * (N / 8); u += 256) {
       const int p = u / (N / 8), pc = u % (N / 8);
       u32x4_t v = u32x4_t{0, 0, 0, 0};
-      if (src) {
+      if (srcb) {
+        v = *reinterpret_cast<const u32x4_t*>(srcb + (size_t)p * N + 8 * pc);
+      } else if (src) {
         const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(src + (size_t)p * N + 8 * pc);
         const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(src + (size_t)p * N + 8 * pc + 4);
         v = u32x4_t{pack_f2bf2(lo[0], lo[1]), pack_f2bf2(lo[2], lo[3]), pack_f2bf2(hi[0], hi[1]),
@@ -336,7 +360,8 @@ template <int N>
 static void launch_ssd_t(const SsdArgs& a, hipStream_t st) {
   if (a.n_done > 0) {
     hipLaunchKernelGGL((ssd_chunk_state_kernel<N>), dim3(a.n_done, a.heads), dim3(256), 0, st, a);
-    hipLaunchKernelGGL(ssd_state_pass_kernel, dim3(a.n_seqs, a.heads), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(ssd_state_pass_kernel, dim3(a.n_seqs, a.heads, SP * N / SP_EPB), dim3(256), 0,
+                       st, a);
   }
   hipLaunchKernelGGL((ssd_chunk_out_kernel<N>), dim3(a.n_inst, a.heads), dim3(256), 0, st, a);
   hipLaunchKernelGGL(ssd_chunk_append_kernel, dim3(a.n_seqs, SQ), dim3(256), 0, st, a);
