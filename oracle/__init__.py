@@ -15,6 +15,8 @@ Contents
   sparse  -- index scores, Top-K with a fixed tie rule in position order,
              attention over the selected keys
   ssd     -- the Mamba-2-style selective state-space recurrence
+  backward -- gradients of add+RMSNorm, the SiLU-gated MLP, linear layers and
+             the lm_head logprob (roundings straight-through)
 
 Every function is pinned by a CPU test (tests/test_oracle_*.py) against
 something other than itself: library routines, closed forms, brute force or
@@ -22,4 +24,4 @@ invariants.  The full-model forward is pinned only through its parts plus
 invariants (causality, per-sequence independence, prefill == chunked ==
 token-by-token decode); the pages print no logprob values to compare with.
 """
-from . import codecs, ops, model, sparse, ssd  # noqa: F401
+from . import backward, codecs, ops, model, sparse, ssd  # noqa: F401

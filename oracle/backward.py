@@ -1,0 +1,85 @@
+"""Gradients of the forward's operators, in fp64 on the CPU.
+
+Test infrastructure only.  Nothing on the product path imports this.
+
+The trainer calls the inference kernels for its forward and adds its own backward;
+forward agreement does not prove the gradients right, so they are checked against an
+independent reference (page "Finish RL Training Faster" digest, section
+"让训练前向使用推理的数值").  Reading: the backward is evaluated at the forward's
+stored values (the bf16-rounded residual, gate/up outputs, activations and hidden
+states) and treats every rounding of the forward as the identity (straight-through);
+everything here is the exact derivative of the unrounded operator at those values.
+Each function writes the derivative out; the pins compare it with finite differences
+and with torch's autograd.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .ops import silu
+
+
+def rmsnorm_backward(r, g, dh, eps: float, dr_in=None):
+    """h = r * s * g with s = (mean(r^2) + eps)^(-1/2) per row.
+
+    dL/dr = g*dh*s - r * s^3 * sum_k(g_k dh_k r_k) / H (+ dr_in, the gradient that
+    reaches r through the residual stream); dL/dg = sum over rows of dh * r * s.
+    r, dh, dr_in: [rows, H]; g: [H].  Returns (dr, dg)."""
+    r = np.asarray(r, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    dh = np.asarray(dh, dtype=np.float64)
+    H = r.shape[-1]
+    s = 1.0 / np.sqrt(np.mean(r * r, axis=-1, keepdims=True) + eps)
+    dot = np.sum(g * dh * r, axis=-1, keepdims=True)
+    dr = g * dh * s - r * s ** 3 * dot / H
+    if dr_in is not None:
+        dr = dr + np.asarray(dr_in, dtype=np.float64)
+    dg = np.sum(dh * r * s, axis=0)
+    return dr, dg
+
+
+def silu_mul_backward(gate, up, dact):
+    """act = silu(gate) * up.  d gate = dact * up * silu'(gate), d up = dact * silu(gate),
+    silu'(x) = sig(x) * (1 + x * (1 - sig(x)))."""
+    gate = np.asarray(gate, dtype=np.float64)
+    up = np.asarray(up, dtype=np.float64)
+    dact = np.asarray(dact, dtype=np.float64)
+    sig = 1.0 / (1.0 + np.exp(-gate))
+    return dact * up * sig * (1.0 + gate * (1.0 - sig)), dact * silu(gate)
+
+
+def linear_backward(x, w, dy):
+    """y = x . w^T.  dx = dy . w, dw = dy^T . x."""
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    return dy @ w, dy.T @ x
+
+
+def mlp_backward(h, wgu, wd, dout, inter: int, gu, act):
+    """The SiLU-gated MLP out = act . wd^T, act = silu(g) u, [g u] = h . wgu^T.
+
+    gu, act: the forward's stored gate/up outputs and activation (bf16 values).
+    Returns (dh, dwgu, dwd)."""
+    dact, dwd = linear_backward(act, wd, dout)
+    dg, du = silu_mul_backward(gu[:, :inter], gu[:, inter:], dact)
+    dgu = np.concatenate([dg, du], axis=1)
+    dh, dwgu = linear_backward(h, wgu, dgu)
+    return dh, dwgu, dwd
+
+
+def logprob_backward(hf, emb, ids, gout):
+    """lp_i = z[i, ids_i] - logsumexp(z_i), z = hf . E^T; L = sum_i gout_i lp_i.
+
+    dz = gout_i (onehot(ids_i) - softmax(z_i)); dhf = dz . E; dE = dz^T . hf.
+    hf [M, H] and emb [V, H] as float64 values.  Returns (dhf, dE, dz)."""
+    hf = np.asarray(hf, dtype=np.float64)
+    emb = np.asarray(emb, dtype=np.float64)
+    gout = np.asarray(gout, dtype=np.float64)
+    z = hf @ emb.T
+    z = z - z.max(axis=1, keepdims=True)
+    p = np.exp(z)
+    p /= p.sum(axis=1, keepdims=True)
+    dz = -gout[:, None] * p
+    dz[np.arange(len(ids)), np.asarray(ids)] += gout
+    return dz @ emb, dz.T @ hf, dz

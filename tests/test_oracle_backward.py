@@ -1,0 +1,116 @@
+"""Pins of the gradient oracle (CPU only): every derivative it writes out is compared
+with central finite differences of the forward written in numpy, and with torch's
+autograd in fp64 (a library routine, independent of the explicit formulas).  A sign
+slip, a missing s^3 term, silu' written as sig(x) alone, or a transposed weight
+gradient fails these."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import backward as bw
+from oracle.ops import silu
+
+
+def fd(f, x, eps=1e-6):
+    """Central differences of the scalar f at x (float64 array), same shape as x."""
+    x = np.array(x, dtype=np.float64)
+    g = np.zeros_like(x)
+    it = np.nditer(x, flags=["multi_index"])
+    for _ in it:
+        i = it.multi_index
+        old = x[i]
+        x[i] = old + eps
+        fp = f(x)
+        x[i] = old - eps
+        fm = f(x)
+        x[i] = old
+        g[i] = (fp - fm) / (2 * eps)
+    return g
+
+
+def test_rmsnorm_backward_against_finite_differences_and_autograd():
+    rng = np.random.default_rng(0)
+    rows, H, eps = 3, 8, 1e-6
+    r = rng.standard_normal((rows, H))
+    g = 1 + 0.1 * rng.standard_normal(H)
+    dh = rng.standard_normal((rows, H))
+    dr_in = rng.standard_normal((rows, H))
+    dr, dg = bw.rmsnorm_backward(r, g, dh, eps, dr_in)
+
+    def h_of(rr, gg):
+        return rr / np.sqrt(np.mean(rr * rr, axis=-1, keepdims=True) + eps) * gg
+    np.testing.assert_allclose(dr - dr_in, fd(lambda rr: np.sum(h_of(rr, g) * dh), r), rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(dg, fd(lambda gg: np.sum(h_of(r, gg) * dh), g), rtol=1e-6, atol=1e-8)
+    rt = torch.tensor(r, requires_grad=True)
+    gt = torch.tensor(g, requires_grad=True)
+    (torch.nn.functional.rms_norm(rt, (H,), gt, eps) * torch.tensor(dh)).sum().backward()
+    np.testing.assert_allclose(dr - dr_in, rt.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dg, gt.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_silu_mul_backward():
+    rng = np.random.default_rng(1)
+    gate, up, dact = (rng.standard_normal((4, 6)) * 3 for _ in range(3))
+    dg, du = bw.silu_mul_backward(gate, up, dact)
+    np.testing.assert_allclose(dg, fd(lambda x: np.sum(silu(x) * up * dact), gate), rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(du, fd(lambda x: np.sum(silu(gate) * x * dact), up), rtol=1e-6, atol=1e-8)
+    # silu'(0) = 1/2; silu' -> 1 for large x, -> 0 for very negative x
+    d0, _ = bw.silu_mul_backward(np.array([0.0, 40.0, -40.0]), np.ones(3), np.ones(3))
+    np.testing.assert_allclose(d0, [0.5, 1.0, 0.0], atol=1e-12)
+
+
+def test_linear_and_mlp_backward_against_autograd():
+    rng = np.random.default_rng(2)
+    M, H, inter = 5, 8, 6
+    h = rng.standard_normal((M, H))
+    wgu = rng.standard_normal((2 * inter, H)) * 0.3
+    wd = rng.standard_normal((H, inter)) * 0.3
+    dout = rng.standard_normal((M, H))
+    gu = h @ wgu.T
+    act = silu(gu[:, :inter]) * gu[:, inter:]
+    dh, dwgu, dwd = bw.mlp_backward(h, wgu, wd, dout, inter, gu, act)
+    ht = torch.tensor(h, requires_grad=True)
+    wgut = torch.tensor(wgu, requires_grad=True)
+    wdt = torch.tensor(wd, requires_grad=True)
+    g = ht @ wgut.T
+    out = (torch.nn.functional.silu(g[:, :inter]) * g[:, inter:]) @ wdt.T
+    (out * torch.tensor(dout)).sum().backward()
+    for mine, ref in ((dh, ht.grad), (dwgu, wgut.grad), (dwd, wdt.grad)):
+        np.testing.assert_allclose(mine, ref.numpy(), rtol=1e-12, atol=1e-12)
+    # finite differences on one weight entry of each matrix
+    def loss(wgu_, wd_):
+        gg = h @ wgu_.T
+        return np.sum((silu(gg[:, :inter]) * gg[:, inter:]) @ wd_.T * dout)
+    e = 1e-6
+    for (i, j) in ((0, 0), (7, 3)):
+        wp, wm = wgu.copy(), wgu.copy()
+        wp[i, j] += e
+        wm[i, j] -= e
+        assert abs((loss(wp, wd) - loss(wm, wd)) / (2 * e) - dwgu[i, j]) < 1e-6
+    wp, wm = wd.copy(), wd.copy()
+    wp[2, 4] += e
+    wm[2, 4] -= e
+    assert abs((loss(wgu, wp) - loss(wgu, wm)) / (2 * e) - dwd[2, 4]) < 1e-6
+
+
+def test_logprob_backward():
+    rng = np.random.default_rng(3)
+    M, H, V = 4, 6, 11
+    hf = rng.standard_normal((M, H))
+    emb = rng.standard_normal((V, H)) * 0.5
+    ids = np.array([0, 3, 10, 3])
+    gout = rng.standard_normal(M)
+
+    def L(hf_, emb_):
+        z = hf_ @ emb_.T
+        m = z.max(axis=1, keepdims=True)
+        lse = m[:, 0] + np.log(np.exp(z - m).sum(axis=1))
+        return np.sum(gout * (z[np.arange(M), ids] - lse))
+    dhf, dE, dz = bw.logprob_backward(hf, emb, ids, gout)
+    np.testing.assert_allclose(dhf, fd(lambda x: L(x, emb), hf), rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(dE, fd(lambda x: L(hf, x), emb), rtol=1e-6, atol=1e-8)
+    # each row of dz sums to zero (softmax gradient) and only the sampled column is positive
+    np.testing.assert_allclose(dz.sum(axis=1), 0.0, atol=1e-12)
+    # a zero upstream gradient gives zero gradients
+    z0 = bw.logprob_backward(hf, emb, ids, np.zeros(M))
+    assert not any(np.any(t) for t in z0)
