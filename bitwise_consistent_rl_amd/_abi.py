@@ -35,7 +35,8 @@ EXPORTS = [
     "bci_profile_end", "bci_forward_logprobs_graph", "bci_graph_count", "bci_graph_reset",
     "bci_op_index_key_write", "bci_op_index_scores", "bci_op_sparse_topk",
     "bci_op_sparse_attention", "bci_ssd_create", "bci_ssd_destroy", "bci_ssd_last_error",
-    "bci_ssd_slot_bytes", "bci_ssd_set_batch", "bci_ssd_forward",
+    "bci_ssd_slot_bytes", "bci_ssd_set_batch", "bci_ssd_forward", "bci_op_transpose_bf16",
+    "bci_op_add_rmsnorm_backward", "bci_op_silu_mul_backward", "bci_op_logprob_backward_dz",
 ]
 
 
@@ -111,6 +112,10 @@ def load() -> ctypes.CDLL:
         "bci_op_index_scores": (st, [vp, vp, vp, i32, i32, vp, vp, i32, vp, ctypes.c_int64, i32, vp]),
         "bci_op_sparse_topk": (st, [vp, vp, ctypes.c_int64, i32, vp, vp]),
         "bci_op_sparse_attention": (st, [vp, vp, i32, vp, i32, vp, vp]),
+        "bci_op_transpose_bf16": (st, [vp, vp, vp, i32, i32, i32, vp]),
+        "bci_op_add_rmsnorm_backward": (st, [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, ctypes.c_float, vp]),
+        "bci_op_silu_mul_backward": (st, [vp, vp, vp, vp, i32, i32, vp]),
+        "bci_op_logprob_backward_dz": (st, [vp, vp, vp, vp, i32, i32, vp, vp]),
         "bci_ssd_create": (st, [ctypes.POINTER(SsdConfig), i32, ctypes.POINTER(vp)]),
         "bci_ssd_destroy": (None, [vp]),
         "bci_ssd_last_error": (ctypes.c_char_p, [vp]),
@@ -298,6 +303,27 @@ def bci_op_sparse_topk(ctx: int, scores, score_stride: int, topk: int, sel, stre
 def bci_op_sparse_attention(ctx: int, q, layer: int, sel, topk: int, o, stream=None) -> None:
     _check(ctx, load().bci_op_sparse_attention(ctx, _ptr(q), layer, _ptr(sel), topk, _ptr(o),
                                                _stream(stream)))
+
+
+def bci_op_transpose_bf16(ctx: int, src, dst, R: int, C: int, ld_dst: int, stream=None) -> None:
+    _check(ctx, load().bci_op_transpose_bf16(ctx, _ptr(src), _ptr(dst), R, C, ld_dst, _stream(stream)))
+
+
+def bci_op_add_rmsnorm_backward(ctx: int, r, g, dh, dr_in, dr, rstd, dg, rows: int, cols: int,
+                                eps: float, stream=None) -> None:
+    _check(ctx, load().bci_op_add_rmsnorm_backward(ctx, _ptr(r), _ptr(g), _ptr(dh), _ptr(dr_in),
+                                                   _ptr(dr), _ptr(rstd), _ptr(dg), rows, cols, eps,
+                                                   _stream(stream)))
+
+
+def bci_op_silu_mul_backward(ctx: int, gu, dact, dgu, rows: int, inter: int, stream=None) -> None:
+    _check(ctx, load().bci_op_silu_mul_backward(ctx, _ptr(gu), _ptr(dact), _ptr(dgu), rows, inter,
+                                                _stream(stream)))
+
+
+def bci_op_logprob_backward_dz(ctx: int, z, ids, gout, M: int, V: int, dz, stream=None) -> None:
+    _check(ctx, load().bci_op_logprob_backward_dz(ctx, _ptr(z), _ptr(ids), _ptr(gout), M, V,
+                                                  _ptr(dz), _stream(stream)))
 
 
 def _ssd_check(ctx, status: int):

@@ -52,6 +52,8 @@ struct bci_ctx {
   // split-attention partials: [max_seg][split_tokens][nq][d] and [..][2]
   float *attn_part_acc = nullptr, *attn_part_ml = nullptr;
   int max_seg = 1, split_tokens = 0;
+  // backward: partial sums of the RMSNorm gain gradient [max_tokens / 256][8192] fp32
+  float* bw_part = nullptr;
   // non-invariant mode: split-K accumulation buffer [FAST_SPLITK_MAX_M, max_n] fp32
   float* splitk_ws = nullptr;
   int splitk_max_n = 0;
@@ -211,6 +213,7 @@ bci_status bci_create(const bci_model_config* cfg_in, int32_t device, bci_ctx** 
       {(void**)&c->rope_cos, (size_t)g.max_position * (g.head_dim / 2) * 4},
       {(void**)&c->rope_sin, (size_t)g.max_position * (g.head_dim / 2) * 4},
       {(void**)&c->meta, c->meta_words * 4},
+      {(void**)&c->bw_part, (T + BW_DG_ROWS - 1) / BW_DG_ROWS * (size_t)8192 * 4},
   };
   c->max_seg = (g.max_position + g.attn_segment_keys - 1) / g.attn_segment_keys;
   if (g.mode == BCI_MODE_FAST) {
@@ -609,6 +612,49 @@ bci_status bci_op_attention(bci_ctx* c, const void* q, int32_t layer, void* o, v
   if (!q || !o || layer < 0 || layer >= c->cfg.n_layers)
     return fail(c, BCI_E_INVALID, "op_attention: null pointer or layer %d", layer);
   return op_attn(c, q, o, layer, S(stream));
+}
+
+// ------------------------------------------------------- backward pieces
+
+bci_status bci_op_transpose_bf16(bci_ctx* c, const void* src, void* dst, int32_t R, int32_t C, int32_t ld_dst,
+                                 void* stream) {
+  if (!c) return BCI_E_INVALID;
+  if (!src || !dst || R < 0 || C < 0 || C % 8 || ld_dst < R || ld_dst % 8 || !aligned16(src) || !aligned16(dst))
+    return fail(c, BCI_E_INVALID, "op_transpose_bf16: bad pointer or shape (C and ld_dst multiples of 8, "
+                                  "ld_dst >= R, 16-byte aligned)");
+  HIP_TRY(c, launch_transpose_bf16(src, dst, R, C, ld_dst, S(stream)));
+  return BCI_OK;
+}
+
+bci_status bci_op_add_rmsnorm_backward(bci_ctx* c, const void* r, const void* g, const void* dh,
+                                       const void* dr_in, void* dr, float* rstd, float* dg, int32_t rows,
+                                       int32_t cols, float eps, void* stream) {
+  if (!c) return BCI_E_INVALID;
+  if (!r || !g || !dh || !dr || !rstd || !dg || rows < 0 || cols < 8 || cols > 8192 || cols % 8)
+    return fail(c, BCI_E_INVALID, "op_add_rmsnorm_backward: bad pointer or shape");
+  if (rows > c->cfg.max_tokens_per_call)
+    return fail(c, BCI_E_WORKSPACE, "op_add_rmsnorm_backward: rows %d > max_tokens_per_call %d", rows,
+                c->cfg.max_tokens_per_call);
+  HIP_TRY(c, launch_rmsnorm_backward(r, g, dh, dr_in, dr, rstd, dg, c->bw_part, rows, cols, eps, S(stream)));
+  return BCI_OK;
+}
+
+bci_status bci_op_silu_mul_backward(bci_ctx* c, const void* gu, const void* dact, void* dgu, int32_t rows,
+                                    int32_t inter, void* stream) {
+  if (!c) return BCI_E_INVALID;
+  if (!gu || !dact || !dgu || rows < 0 || inter < 1)
+    return fail(c, BCI_E_INVALID, "op_silu_mul_backward: bad pointer or shape");
+  HIP_TRY(c, launch_silu_mul_backward(gu, dact, dgu, rows, inter, S(stream)));
+  return BCI_OK;
+}
+
+bci_status bci_op_logprob_backward_dz(bci_ctx* c, const float* z, const int32_t* ids, const float* gout,
+                                      int32_t M, int32_t V, void* dz, void* stream) {
+  if (!c) return BCI_E_INVALID;
+  if (!z || !ids || !gout || !dz || M < 0 || V < 1)
+    return fail(c, BCI_E_INVALID, "op_logprob_backward_dz: bad pointer or shape");
+  HIP_TRY(c, launch_logprob_dz(z, ids, gout, dz, M, V, S(stream)));
+  return BCI_OK;
 }
 
 // ------------------------------------------------------- sparse attention

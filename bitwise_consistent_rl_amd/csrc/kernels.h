@@ -140,6 +140,17 @@ struct SsdArgs {
 };
 hipError_t launch_ssd(const SsdArgs& a, hipStream_t s);
 
+// ---- backward.hip
+hipError_t launch_transpose_bf16(const void* src, void* dst, int R, int C, int ldd, hipStream_t s);
+constexpr int BW_DG_ROWS = 256;  // rows per partial sum of the gain gradient
+hipError_t launch_rmsnorm_backward(const void* r, const void* g, const void* dh, const void* dr_in,
+                                   void* dr, float* rstd, float* dg, float* part, int rows, int cols,
+                                   float eps, hipStream_t s);
+hipError_t launch_silu_mul_backward(const void* gu, const void* dact, void* dgu, int rows, int inter,
+                                    hipStream_t s);
+hipError_t launch_logprob_dz(const float* z, const int32_t* ids, const float* gout, void* dz, int M, int V,
+                             hipStream_t s);
+
 // ---- moe.hip
 constexpr int MOE_MAX_K = 8;
 hipError_t launch_moe_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,

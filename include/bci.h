@@ -338,6 +338,50 @@ bci_status bci_op_moe_forward(bci_ctx* ctx, const void* h, const int32_t* ids, c
                               int32_t T, const void* wgu, const void* wd, const void* swgu,
                               const void* swd, void* out, void* stream);
 
+/* ---- backward pieces ---------------------------------------------------------
+ * The trainer keeps the inference forward and adds its own backward, whose gradients
+ * are checked against an independent reference (page "Finish RL Training Faster"
+ * digest, section "让训练前向使用推理的数值").  The backward's GEMMs are
+ * bci_op_gemm_bf16 on transposed operands (dX = dY . W as dY . (W^T)^T; dW = dY^T . X
+ * as (dY^T) . (X^T)^T with the token dimension padded to 64 by zeros), so every element
+ * is one ascending fp32 MFMA chain; the calls below are the pieces around them.  The
+ * forward's roundings are taken as the identity (straight-through) and the backward
+ * is evaluated at the forward's stored bf16 values.  Activation gradients are bf16,
+ * weight and gain gradients fp32. */
+
+/* dst[c * ld_dst + r] = src[r * C + c] for r < R, c < C; 0 for R <= r < ld_dst (bf16).
+ * C and ld_dst multiples of 8, ld_dst >= R, both pointers 16-byte aligned. */
+bci_status bci_op_transpose_bf16(bci_ctx* ctx, const void* src, void* dst, int32_t R, int32_t C,
+                                 int32_t ld_dst, void* stream);
+
+/* Backward of h = bf(r * s * g), s = 1 / sqrt(mean(r^2) + eps) (the forward's
+ * expression), per row of r [rows, cols] (the forward's rounded residual):
+ *   dr = bf((g dh) s - r (s^3 sum_k g_k dh_k r_k / cols) + dr_in)   (dr_in may be NULL:
+ *        the gradient reaching r through the residual stream; dr is then also the
+ *        gradient of both inputs of the forward's add),
+ *   rstd[row] = s (fp32), dg[k] = sum over rows in ascending order (partial sums over
+ *   blocks of 256 rows, then the blocks in order) of dh r s (fp32).
+ * g [cols] bf16; dh, dr_in, dr [rows, cols] bf16.  cols % 8 == 0, cols <= 8192,
+ * rows <= max_tokens_per_call. */
+bci_status bci_op_add_rmsnorm_backward(bci_ctx* ctx, const void* r, const void* g, const void* dh,
+                                       const void* dr_in, void* dr, float* rstd, float* dg,
+                                       int32_t rows, int32_t cols, float eps, void* stream);
+
+/* Backward of act = bf(silu(gate) * up): gu [rows, 2 I] (gate columns then up columns,
+ * the gate_up GEMM's bf16 output), dact [rows, I] bf16 -> dgu [rows, 2 I] bf16 =
+ * [bf(dact up silu'(gate)), bf(dact silu(gate))], silu'(x) = sig(x)(1 + x(1 - sig(x))). */
+bci_status bci_op_silu_mul_backward(bci_ctx* ctx, const void* gu, const void* dact, void* dgu,
+                                    int32_t rows, int32_t inter, void* stream);
+
+/* The logprob's gradient with respect to the logits: z [M, V] fp32 (the lm_head GEMM
+ * with the fp32 epilogue), ids [M] int32, gout [M] fp32 (dL/dlp) -> dz [M, V] bf16 =
+ * bf(gout_i ((j == ids_i) - exp(z_ij - m_i) / S_i)), (m_i, S_i) the row's max and sum of
+ * exp(z - m) by a fixed tree (an id outside [0, V) gives a NaN row).  dhf = dz . E and
+ * dE = dz^T . hf follow as GEMMs. */
+bci_status bci_op_logprob_backward_dz(bci_ctx* ctx, const float* z, const int32_t* ids,
+                                      const float* gout, int32_t M, int32_t V, void* dz,
+                                      void* stream);
+
 /* ---- state-space layer (Mamba-2-style), chunked ---------------------------------
  * Porting the method to Nemotron-3.5 meant recursive arithmetic in which decode
  * replays prefill's chunked computation order and training reuses the same operator

@@ -1,0 +1,153 @@
+"""Backward pieces of the invariant forward against the fp64 gradient oracle, and their
+determinism: transpose (exact), add+RMSNorm, SiLU*up, linear / SiLU-gated MLP and the
+lm_head logprob (config 3's vocabulary), at the Qwen3-shaped widths.
+
+Tolerances.  A kernel that rounds its own fp32 result to bf16 is held to the bf16
+grid (1-2 ulp plus the fp32 cancellation bound).  Composite gradients pass through
+bf16 intermediates the oracle does not round (dact, dgu, dz -- 2^-9 relative each) and
+fp32 GEMM accumulation: they are held to a relative Frobenius error of 1e-2 and
+elementwise to 1.5e-2 of the tensor's largest magnitude (measured: 0.9-2.9e-3 and
+up to 4.0e-3)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import BF, assert_bf16_close, f64, same_bits
+from oracle import backward as ob
+from oracle import ops
+from test_gpu_ops import abi, make_ctx
+
+pytestmark = pytest.mark.gpu
+
+REL_FRO, MAX_FRAC = 1e-2, 1.5e-2
+
+
+def bwd():
+    from bitwise_consistent_rl_amd import backward
+    return backward
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    h = make_ctx(max_tokens=4096, max_scored=512)
+    yield h
+    torch.cuda.synchronize()
+    abi().bci_destroy(h)
+
+
+def close(got, ref, what):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    fro = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300)
+    mx = np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-300)
+    print(f"{what}: relative Frobenius {fro:.2e}, max/max {mx:.2e}", flush=True)
+    assert fro <= REL_FRO and mx <= MAX_FRAC, (what, fro, mx)
+
+
+@pytest.mark.parametrize("R,C,ld", [(1, 8, 8), (37, 64, 64), (300, 2048, 320), (4096, 72, 4096)])
+def test_transpose_exact(ctx, R, C, ld):
+    x = synth.normal_bf16((R, C), index=R + C).cuda()
+    out = torch.full((C, ld), float("nan"), dtype=BF, device="cuda")
+    abi().bci_op_transpose_bf16(ctx, x, out, R, C, ld)
+    torch.cuda.synchronize()
+    want = torch.zeros(C, ld, dtype=BF)
+    want[:, :R] = x.cpu().T
+    assert same_bits(out, want)
+
+
+@pytest.mark.parametrize("rows,H", [(1, 256), (77, 2048), (600, 4096)])
+def test_add_rmsnorm_backward(ctx, rows, H):
+    r = synth.normal_bf16((rows, H), index=60).cuda()
+    g = synth.normal_bf16((H,), index=61, scale=0.1).cuda()
+    g = (g.float() + 1.0).to(BF)
+    dh = synth.normal_bf16((rows, H), index=62).cuda()
+    dr_in = synth.normal_bf16((rows, H), index=63).cuda()
+    dr, dg, rstd = bwd().add_rmsnorm_backward(ctx, r, g, dh, 1e-6, dr_in)
+    torch.cuda.synchronize()
+    R, G, DH, DRI = f64(r), f64(g), f64(dh), f64(dr_in)
+    ref_dr, ref_dg = ob.rmsnorm_backward(R, G, DH, 1e-6, DRI)
+    s = 1.0 / np.sqrt(np.mean(R * R, axis=1, keepdims=True) + 1e-6)
+    cancel = 2.0 ** -20 * (np.abs(G * DH) * s + np.abs(R) * s ** 3 * np.sum(np.abs(G * DH * R), axis=1,
+                                                                             keepdims=True) / H + np.abs(DRI))
+    assert_bf16_close(f64(dr), ref_dr, abs_bound=cancel, max_ulp=1, frac_exact=0.99, what="dr")
+    np.testing.assert_allclose(rstd.cpu().numpy(), s[:, 0], rtol=1e-6)
+    bound = 1e-5 * np.sum(np.abs(DH * R) * s, axis=0) + 1e-30
+    assert np.all(np.abs(dg.cpu().numpy() - ref_dg) <= bound)
+    # deterministic, and each row of dr independent of the other rows
+    dr2, dg2, _ = bwd().add_rmsnorm_backward(ctx, r, g, dh, 1e-6, dr_in)
+    assert same_bits(dr2, dr) and same_bits(dg2, dg)
+    if rows > 1:
+        sub = slice(rows // 3, rows // 3 + 5)
+        dr3, _, _ = bwd().add_rmsnorm_backward(ctx, r[sub].contiguous(), g, dh[sub].contiguous(), 1e-6,
+                                               dr_in[sub].contiguous())
+        assert same_bits(dr3, dr[sub])
+
+
+def test_silu_mul_backward(ctx):
+    rows, inter = 129, 768
+    gu = synth.normal_bf16((rows, 2 * inter), index=64, scale=3.0).cuda()
+    dact = synth.normal_bf16((rows, inter), index=65).cuda()
+    dgu = torch.empty_like(gu)
+    abi().bci_op_silu_mul_backward(ctx, gu, dact, dgu, rows, inter)
+    torch.cuda.synchronize()
+    G, D = f64(gu), f64(dact)
+    rg, ru = ob.silu_mul_backward(G[:, :inter], G[:, inter:], D)
+    got = f64(dgu)
+    assert_bf16_close(got[:, :inter], rg, abs_bound=2.0 ** -20 * np.abs(D * G[:, inter:]), max_ulp=2,
+                      what="d gate")
+    assert_bf16_close(got[:, inter:], ru, abs_bound=2.0 ** -20 * np.abs(D * G[:, :inter]), max_ulp=2,
+                      what="d up")
+
+
+@pytest.mark.parametrize("M,H,inter", [(37, 256, 768), (300, 2048, 6144)])
+def test_mlp_backward(ctx, M, H, inter):
+    h = synth.normal_bf16((M, H), index=66).cuda()
+    wgu = synth.normal_bf16((2 * inter, H), index=67, scale=0.02).cuda()
+    wd = synth.normal_bf16((H, inter), index=68, scale=0.02).cuda()
+    dout = synth.normal_bf16((M, H), index=69).cuda()
+    dh, dwgu, dwd, gu, act = bwd().mlp_backward(ctx, h, wgu, wd, dout, inter)
+    torch.cuda.synchronize()
+    # the forward values the oracle is evaluated at: its own forward of the same inputs
+    Hh, Wgu, Wd, Do = f64(h), f64(wgu), f64(wd), f64(dout)
+    Gu = ops.bf(ops.linear(Hh, Wgu))
+    Act = ops.silu_mul(Gu[:, :inter], Gu[:, inter:])
+    rdh, rdwgu, rdwd = ob.mlp_backward(Hh, Wgu, Wd, Do, inter, Gu, Act)
+    close(f64(dh), rdh, f"dh M={M}")
+    close(dwgu.cpu().numpy(), rdwgu, f"dwgu M={M}")
+    close(dwd.cpu().numpy(), rdwd, f"dwd M={M}")
+    # deterministic; rows of dh independent of the batch
+    dh2, dwgu2, dwd2, _, _ = bwd().mlp_backward(ctx, h, wgu, wd, dout, inter)
+    assert same_bits(dh2, dh) and same_bits(dwgu2, dwgu) and same_bits(dwd2, dwd)
+    sub = slice(M // 2, M // 2 + 3)
+    dh3, _, _, _, _ = bwd().mlp_backward(ctx, h[sub].contiguous(), wgu, wd, dout[sub].contiguous(), inter)
+    assert same_bits(dh3, dh[sub])
+
+
+@pytest.mark.parametrize("M,V", [(7, 4096), (64, 151936)])
+def test_logprob_backward(ctx, M, V):
+    H = 2048
+    hs, w, ids = synth.lmhead_inputs(M, hidden=H, vocab=V)
+    gout = np.random.default_rng(M).standard_normal(M).astype(np.float32)
+    hf, emb = hs.cuda(), w.cuda()
+    gids = torch.from_numpy(ids.astype(np.int32)).cuda()
+    gg = torch.from_numpy(gout).cuda()
+    dhf, dE = bwd().logprob_backward(ctx, hf, emb, gids, gg)
+    torch.cuda.synchronize()
+    HF, E = f64(hs), f64(w)
+    # oracle: dz in full, dhf in full, dE on the sampled rows and a random sample of others
+    z = HF @ E.T
+    z -= z.max(axis=1, keepdims=True)
+    p = np.exp(z)
+    p /= p.sum(axis=1, keepdims=True)
+    dz = -gout[:, None].astype(np.float64) * p
+    dz[np.arange(M), ids] += gout
+    close(f64(dhf), dz @ E, f"dhf M={M} V={V}")
+    rows = np.unique(np.concatenate([ids, np.random.default_rng(1).choice(V, 256, replace=False)]))
+    close(dE[torch.from_numpy(rows).cuda()].cpu().numpy(), dz[:, rows].T @ HF, f"dE rows M={M} V={V}")
+    # the oracle module's own function on the small vocabulary
+    if V <= 4096:
+        rdhf, rdE, _ = ob.logprob_backward(HF, E, ids, gout)
+        close(dE.cpu().numpy(), rdE, "dE full")
+    dhf2, dE2 = bwd().logprob_backward(ctx, hf, emb, gids, gg)
+    assert same_bits(dhf2, dhf) and same_bits(dE2, dE)
