@@ -577,6 +577,59 @@ def ssd_bench(args):
     abi.bci_ssd_destroy(ctx)
 
 
+def backward_bench(args):
+    """Backward pieces at the Qwen3-shaped widths: the SiLU-gated MLP (H 2048, I 6144) over
+    4096 tokens, add+RMSNorm over 4096 x 2048, and the lm_head logprob (V 151936) over 512
+    scored rows.  Algorithmic work: MLP 3 x 2 x (2 x M x H x 2I ... ) -- the forward
+    recompute of gate/up and the activation (2 GEMMs) plus four gradient GEMMs:
+    2 M H 2I (gu) + 2 M H 2I (act) + 2 M I H x 2 (dact, dwd) + 2 M 2I H x 2 (dh, dwgu);
+    lm_head: 2 M V H x 3 (z, dhf, dE); RMSNorm: 10 B per element (r, dh, dr_in read, dr
+    written, r and dh read again for dg)."""
+    import torch
+    import synth
+    from bitwise_consistent_rl_amd import _abi as abi
+    from bitwise_consistent_rl_amd import backward as bw
+    H, I, V = 2048, 6144, 151936
+    mc = abi.ModelConfig()
+    for k, v in dict(n_layers=1, hidden=H, n_q_heads=16, n_kv_heads=8, head_dim=128, intermediate=I,
+                     vocab=V, rms_eps=1e-6, rope_theta=1e6, kv_block_tokens=64, attn_segment_keys=2048,
+                     max_tokens_per_call=4096, max_seqs_per_call=1, max_scored_per_call=512,
+                     max_position=64).items():
+        setattr(mc, k, v)
+    ctx = abi.bci_create(mc, 0)
+
+    def report(name, ms, flops=0.0, nbytes=0.0):
+        t_f, t_b = flops / (PEAK_BF16_TFLOPS * 1e12), nbytes / (PEAK_HBM_GBS * 1e9)
+        bound = "mfma" if t_f > t_b else "hbm"
+        print(json.dumps({"workload": "backward pieces (Qwen3-shaped widths)", "op": name,
+                          "ms": round(ms, 3), "bound": bound,
+                          "achieved": round(flops / ms / 1e9, 1) if bound == "mfma"
+                          else round(nbytes / ms / 1e6, 1),
+                          "unit": "TFLOP/s" if bound == "mfma" else "GB/s",
+                          "frac_of_roofline": round(max(t_f, t_b) / (ms * 1e-3), 4)}), flush=True)
+
+    M = 4096
+    h = synth.normal_bf16((M, H), index=66).cuda()
+    wgu = synth.normal_bf16((2 * I, H), index=67, scale=0.02).cuda()
+    wd = synth.normal_bf16((H, I), index=68, scale=0.02).cuda()
+    dout = synth.normal_bf16((M, H), index=69).cuda()
+    ms = _time_ms(lambda: bw.mlp_backward(ctx, h, wgu, wd, dout, I), reps=5, warm=2)
+    report("SiLU-MLP backward, 4096 tokens", ms, flops=2.0 * M * H * 2 * I * 2 + 2.0 * M * I * H * 2
+           + 2.0 * M * 2 * I * H * 2)
+    g = (synth.normal_bf16((H,), index=61, scale=0.1).float() + 1.0).to(torch.bfloat16).cuda()
+    ms = _time_ms(lambda: bw.add_rmsnorm_backward(ctx, h, g, dout, 1e-6, dout), reps=10)
+    report("add+RMSNorm backward, 4096 x 2048", ms, nbytes=10.0 * M * H)
+    Ms = 512
+    hs, w, ids = synth.lmhead_inputs(Ms, hidden=H, vocab=V)
+    hf, emb = hs.cuda(), w.cuda()
+    gids = torch.from_numpy(ids.astype("int32")).cuda()
+    gg = torch.ones(Ms, device="cuda")
+    embT = bw.transpose(ctx, emb, ld=V)
+    ms = _time_ms(lambda: bw.logprob_backward(ctx, hf, emb, gids, gg, embT=embT), reps=3, warm=1)
+    report("lm_head logprob backward, 512 rows", ms, flops=2.0 * Ms * V * H * 3)
+    abi.bci_destroy(ctx)
+
+
 def _time_ms(fn, reps=10, warm=3):
     import torch
     for _ in range(warm):
@@ -688,7 +741,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--micro", choices=["gate_up"], default=None,
                     help="time one kernel alone at the workload's shape (for counter runs)")
-    ap.add_argument("--workload", choices=["recompute", "longctx", "rollout", "lmhead", "moe", "sparse", "ssd"],
+    ap.add_argument("--workload", choices=["recompute", "longctx", "rollout", "lmhead", "moe", "sparse", "ssd",
+                             "backward"],
                     default="recompute",
                     help="longctx: FP8-KV long-context attention (decode steps, chunked prefill); "
                          "rollout: continuous-batching decode, invariant vs non-invariant mode; "
@@ -721,6 +775,8 @@ def main():
         return sparse_bench(args)
     if args.workload == "ssd":
         return ssd_bench(args)
+    if args.workload == "backward":
+        return backward_bench(args)
     if args.workload == "moe":
         return moe_bench(args)
     log("generating weights and workload")

@@ -13,10 +13,10 @@
 //   rmsnorm_backward      per row: s = 1/sqrt(mean(r^2)+eps) (the forward's expression),
 //                         dr = (g dh) s - r (s^3 sum_k g_k dh_k r_k / H) + dr_in
 //   rmsnorm_dg            dg = sum over rows, ascending, of dh r s: partial sums over
-//                         blocks of 256 rows, then the partials in block order
+//                         blocks of 64 rows, then the partials in block order
 //   silu_mul_backward     d gate = dact u silu'(gate), d up = dact silu(gate)
-//   logprob_dz            per row: (m, S) = (max z, sum exp(z - m)) by a fixed tree;
-//                         dz = g ((j == id) - exp(z - m) / S)
+//   logprob_dz            per row: (m, S) = (max z, sum exp(z - m)) folded per thread and
+//                         merged by a fixed tree; dz = g ((j == id) - exp(z - m) / S)
 #include "common.h"
 #include "kernels.h"
 
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(BW_THREADS) void rmsnorm_backward_kernel(
 }
 
 constexpr int DG_ROWS = BW_DG_ROWS;
-// partial[b][k] = sum over rows 256b .. 256b+255 (ascending) of dh r s
+// partial[b][k] = sum over rows 64b .. 64b+63 (ascending) of dh r s
 __global__ __launch_bounds__(BW_THREADS) void rmsnorm_dg_partial_kernel(
     const bf16_t* __restrict__ r, const bf16_t* __restrict__ dh, const float* __restrict__ rstd,
     float* __restrict__ part, int rows, int cols) {
@@ -173,45 +173,79 @@ hipError_t launch_silu_mul_backward(const void* gu, const void* dact, void* dgu,
 
 // ------------------------------------------------------------- logprob backward
 
-__device__ __forceinline__ float block_max_fixed(float v, float* red) {
-  v = wave_max(v);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  float t = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < BW_THREADS / WAVE; ++w) t = fmaxf(t, red[w]);
-  __syncthreads();
-  return t;
+constexpr int LP_THREADS = 1024;
+
+// (m, s) <- (m, s) merged with (m2, s2): the running max and the sum of exp(x - max)
+__device__ __forceinline__ void ms_merge(float& m, float& s, float m2, float s2) {
+  const float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) return;
+  s = s * fexp(m - mn) + s2 * fexp(m2 - mn);
+  m = mn;
 }
 
-__global__ __launch_bounds__(BW_THREADS) void logprob_dz_kernel(const float* __restrict__ z,
+// One workgroup per row: each thread folds its columns (16-byte loads, strided by the
+// workgroup) into a running (max, sum exp) pair, the pairs are merged by a fixed xor
+// tree in each wave and then wave by wave in order; a second pass writes dz.
+__global__ __launch_bounds__(LP_THREADS) void logprob_dz_kernel(const float* __restrict__ z,
                                                                 const int32_t* __restrict__ ids,
                                                                 const float* __restrict__ gout,
                                                                 bf16_t* __restrict__ dz, int V) {
-  __shared__ float red[BW_THREADS / WAVE];
+  __shared__ float wm[LP_THREADS / WAVE], ws[LP_THREADS / WAVE];
   const size_t row = blockIdx.x;
   const float* zr = z + row * V;
-  float m = -INFINITY;
-  for (int j = threadIdx.x; j < V; j += BW_THREADS) m = fmaxf(m, zr[j]);
-  m = block_max_fixed(m, red);
-  float sum = 0.0f;
-  for (int j = threadIdx.x; j < V; j += BW_THREADS) sum = sum + fexp(zr[j] - m);
-  sum = block_sum_fixed(sum, red);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int V4 = (V & 3) == 0 ? V / 4 : 0;   // rows of a multiple of 4 columns: 16-byte loads
+  float m = -INFINITY, s = 0.0f;
+  if (V4) {
+    for (int j = tid; j < V4; j += LP_THREADS) {
+      const f32x4_t v = reinterpret_cast<const f32x4_t*>(zr)[j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ms_merge(m, s, v[i], 1.0f);
+    }
+  } else {
+    for (int j = tid; j < V; j += LP_THREADS) ms_merge(m, s, zr[j], 1.0f);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, WAVE), s2 = __shfl_xor(s, o, WAVE);
+    ms_merge(m, s, m2, s2);
+  }
+  if (lane == 0) {
+    wm[wave] = m;
+    ws[wave] = s;
+  }
+  __syncthreads();
+  m = wm[0];
+  s = ws[0];
+  for (int w = 1; w < LP_THREADS / WAVE; ++w) ms_merge(m, s, wm[w], ws[w]);
   const int id = ids[row];
   const float g = gout[row];
   const bool bad = id < 0 || id >= V;
-  for (int j = threadIdx.x; j < V; j += BW_THREADS) {
-    const float p = fexp(zr[j] - m) / sum;
-    const float v = bad ? __uint_as_float(0x7fc00000u) : g * ((j == id ? 1.0f : 0.0f) - p);
-    dz[row * V + j] = f2bf(v);
+  const float nan = __uint_as_float(0x7fc00000u);
+  bf16_t* dr = dz + row * V;
+  if (V4) {
+    for (int j = tid; j < V4; j += LP_THREADS) {
+      const f32x4_t v = reinterpret_cast<const f32x4_t*>(zr)[j];
+      float o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = fexp(v[i] - m) / s;
+        o[i] = bad ? nan : g * ((4 * j + i == id ? 1.0f : 0.0f) - p);
+      }
+      *reinterpret_cast<uint2*>(dr + 4 * j) = make_uint2(pack_f2bf2(o[0], o[1]), pack_f2bf2(o[2], o[3]));
+    }
+  } else {
+    for (int j = tid; j < V; j += LP_THREADS) {
+      const float p = fexp(zr[j] - m) / s;
+      dr[j] = f2bf(bad ? nan : g * ((j == id ? 1.0f : 0.0f) - p));
+    }
   }
 }
 
 hipError_t launch_logprob_dz(const float* z, const int32_t* ids, const float* gout, void* dz, int M, int V,
                              hipStream_t s) {
   if (M == 0) return hipSuccess;
-  hipLaunchKernelGGL(logprob_dz_kernel, dim3(M), dim3(BW_THREADS), 0, s, z, ids, gout, (bf16_t*)dz, V);
+  hipLaunchKernelGGL(logprob_dz_kernel, dim3(M), dim3(LP_THREADS), 0, s, z, ids, gout, (bf16_t*)dz, V);
   return hipGetLastError();
 }
 

@@ -52,7 +52,7 @@ struct bci_ctx {
   // split-attention partials: [max_seg][split_tokens][nq][d] and [..][2]
   float *attn_part_acc = nullptr, *attn_part_ml = nullptr;
   int max_seg = 1, split_tokens = 0;
-  // backward: partial sums of the RMSNorm gain gradient [max_tokens / 256][8192] fp32
+  // backward: partial sums of the RMSNorm gain gradient [max_tokens / 64][8192] fp32
   float* bw_part = nullptr;
   // non-invariant mode: split-K accumulation buffer [FAST_SPLITK_MAX_M, max_n] fp32
   float* splitk_ws = nullptr;

@@ -142,7 +142,7 @@ hipError_t launch_ssd(const SsdArgs& a, hipStream_t s);
 
 // ---- backward.hip
 hipError_t launch_transpose_bf16(const void* src, void* dst, int R, int C, int ldd, hipStream_t s);
-constexpr int BW_DG_ROWS = 256;  // rows per partial sum of the gain gradient
+constexpr int BW_DG_ROWS = 64;  // rows per partial sum of the gain gradient
 hipError_t launch_rmsnorm_backward(const void* r, const void* g, const void* dh, const void* dr_in,
                                    void* dr, float* rstd, float* dg, float* part, int rows, int cols,
                                    float eps, hipStream_t s);

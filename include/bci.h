@@ -360,7 +360,7 @@ bci_status bci_op_transpose_bf16(bci_ctx* ctx, const void* src, void* dst, int32
  *        the gradient reaching r through the residual stream; dr is then also the
  *        gradient of both inputs of the forward's add),
  *   rstd[row] = s (fp32), dg[k] = sum over rows in ascending order (partial sums over
- *   blocks of 256 rows, then the blocks in order) of dh r s (fp32).
+ *   blocks of 64 rows, then the blocks in order) of dh r s (fp32).
  * g [cols] bf16; dh, dr_in, dr [rows, cols] bf16.  cols % 8 == 0, cols <= 8192,
  * rows <= max_tokens_per_call. */
 bci_status bci_op_add_rmsnorm_backward(bci_ctx* ctx, const void* r, const void* g, const void* dh,
@@ -376,7 +376,8 @@ bci_status bci_op_silu_mul_backward(bci_ctx* ctx, const void* gu, const void* da
 /* The logprob's gradient with respect to the logits: z [M, V] fp32 (the lm_head GEMM
  * with the fp32 epilogue), ids [M] int32, gout [M] fp32 (dL/dlp) -> dz [M, V] bf16 =
  * bf(gout_i ((j == ids_i) - exp(z_ij - m_i) / S_i)), (m_i, S_i) the row's max and sum of
- * exp(z - m) by a fixed tree (an id outside [0, V) gives a NaN row).  dhf = dz . E and
+ * exp(z - m), folded per thread and merged by a fixed tree (an id outside [0, V) gives
+ * a NaN row).  V % 4 == 0 uses 16-byte loads; z and dz then 16- and 8-byte aligned.  dhf = dz . E and
  * dE = dz^T . hf follow as GEMMs. */
 bci_status bci_op_logprob_backward_dz(bci_ctx* ctx, const float* z, const int32_t* ids,
                                       const float* gout, int32_t M, int32_t V, void* dz,

@@ -135,19 +135,12 @@ def test_logprob_backward(ctx, M, V):
     dhf, dE = bwd().logprob_backward(ctx, hf, emb, gids, gg)
     torch.cuda.synchronize()
     HF, E = f64(hs), f64(w)
-    # oracle: dz in full, dhf in full, dE on the sampled rows and a random sample of others
-    z = HF @ E.T
-    z -= z.max(axis=1, keepdims=True)
-    p = np.exp(z)
-    p /= p.sum(axis=1, keepdims=True)
-    dz = -gout[:, None].astype(np.float64) * p
-    dz[np.arange(M), ids] += gout
-    close(f64(dhf), dz @ E, f"dhf M={M} V={V}")
-    rows = np.unique(np.concatenate([ids, np.random.default_rng(1).choice(V, 256, replace=False)]))
-    close(dE[torch.from_numpy(rows).cuda()].cpu().numpy(), dz[:, rows].T @ HF, f"dE rows M={M} V={V}")
-    # the oracle module's own function on the small vocabulary
+    rdhf, rdE, _ = ob.logprob_backward(HF, E, ids, gout)
+    close(f64(dhf), rdhf, f"dhf M={M} V={V}")
     if V <= 4096:
-        rdhf, rdE, _ = ob.logprob_backward(HF, E, ids, gout)
-        close(dE.cpu().numpy(), rdE, "dE full")
+        close(dE.cpu().numpy(), rdE, f"dE M={M} V={V}")
+    else:   # the sampled rows and 256 others (a 151936 x 2048 comparison is not needed)
+        rows = np.unique(np.concatenate([ids, np.random.default_rng(1).choice(V, 256, replace=False)]))
+        close(dE[torch.from_numpy(rows).cuda()].cpu().numpy(), rdE[rows], f"dE rows M={M} V={V}")
     dhf2, dE2 = bwd().logprob_backward(ctx, hf, emb, gids, gg)
     assert same_bits(dhf2, dhf) and same_bits(dE2, dE)
