@@ -83,3 +83,52 @@ def logprob_backward(hf, emb, ids, gout):
     dz = -gout[:, None] * p
     dz[np.arange(len(ids)), np.asarray(ids)] += gout
     return dz @ emb, dz.T @ hf, dz
+
+
+def attention_backward(q, k, v, o, do):
+    """Causal GQA attention of one sequence (positions 0..T-1): o = softmax(q k^T / sqrt(d)) v.
+
+    q, o, do: [T, nq, d]; k, v: [T, nkv, d] (the keys and values the forward attended
+    to -- for an FP8 cache the dequantised ones; the quantiser's gradient is taken as
+    the identity, so dk and dv are also the gradients of the keys and values before
+    quantisation).  With P the attention weights, D_i = sum_d do_i o_i (o as stored):
+        dv_j = sum_i P_ij do_i,  dP_ij = do_i . v_j,  dS = P * (dP - D),
+        dq_i = sum_j dS_ij k_j / sqrt(d),  dk_j = sum_i dS_ij q_i / sqrt(d),
+    summed over the query heads that read each kv head.  Returns (dq, dk, dv)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    o = np.asarray(o, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    T, nq, d = q.shape
+    nkv = k.shape[1]
+    grp = nq // nkv
+    mask = np.tril(np.ones((T, T), dtype=bool))
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for h in range(nq):
+        g = h // grp
+        s = q[:, h] @ k[:, g].T / np.sqrt(d)
+        s = np.where(mask, s, -np.inf)
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        D = np.sum(do[:, h] * o[:, h], axis=1, keepdims=True)
+        dP = do[:, h] @ v[:, g].T
+        dS = p * (dP - D)
+        dv[:, g] += p.T @ do[:, h]
+        dq[:, h] = dS @ k[:, g] / np.sqrt(d)
+        dk[:, g] += dS.T @ q[:, h] / np.sqrt(d)
+    return dq, dk, dv
+
+
+def rope_backward(dx_rot, positions, theta: float):
+    """The rotation's transpose: x_rot = (x1 c - x2 s, x2 c + x1 s) per pair (i, i + d/2),
+    so dx1 = dr1 c + dr2 s, dx2 = dr2 c - dr1 s.  dx_rot: [T, heads, d]."""
+    from .ops import rope_tables
+    dx_rot = np.asarray(dx_rot, dtype=np.float64)
+    d = dx_rot.shape[-1]
+    c, s = rope_tables(positions, d, theta)
+    c, s = c[:, None, :], s[:, None, :]
+    r1, r2 = dx_rot[..., : d // 2], dx_rot[..., d // 2:]
+    return np.concatenate([r1 * c + r2 * s, r2 * c - r1 * s], axis=-1)

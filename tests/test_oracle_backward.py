@@ -114,3 +114,51 @@ def test_logprob_backward():
     # a zero upstream gradient gives zero gradients
     z0 = bw.logprob_backward(hf, emb, ids, np.zeros(M))
     assert not any(np.any(t) for t in z0)
+
+
+def test_attention_backward_against_autograd_and_finite_differences():
+    rng = np.random.default_rng(4)
+    T, nq, nkv, d = 7, 4, 2, 8
+    q, k, v, do = (rng.standard_normal(s) for s in ((T, nq, d), (T, nkv, d), (T, nkv, d), (T, nq, d)))
+
+    def fwd(q_, k_, v_):
+        out = np.empty((T, nq, d))
+        for h in range(nq):
+            g = h // (nq // nkv)
+            s = q_[:, h] @ k_[:, g].T / np.sqrt(d)
+            s = np.where(np.tril(np.ones((T, T), bool)), s, -np.inf)
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            out[:, h] = (p / p.sum(axis=1, keepdims=True)) @ v_[:, g]
+        return out
+    o = fwd(q, k, v)
+    dq, dk, dv = bw.attention_backward(q, k, v, o, do)
+    np.testing.assert_allclose(dq, fd(lambda x: np.sum(fwd(x, k, v) * do), q), rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(dk, fd(lambda x: np.sum(fwd(q, x, v) * do), k), rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(dv, fd(lambda x: np.sum(fwd(q, k, x) * do), v), rtol=1e-6, atol=1e-8)
+    qt, kt, vt = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    ke = kt.repeat_interleave(nq // nkv, dim=1)
+    ve = vt.repeat_interleave(nq // nkv, dim=1)
+    s = torch.einsum("thd,shd->hts", qt, ke) / np.sqrt(d)
+    s = s.masked_fill(~torch.tril(torch.ones(T, T, dtype=torch.bool)), float("-inf"))
+    out = torch.einsum("hts,shd->thd", torch.softmax(s, dim=-1), ve)
+    (out * torch.tensor(do)).sum().backward()
+    for mine, ref in ((dq, qt.grad), (dk, kt.grad), (dv, vt.grad)):
+        np.testing.assert_allclose(mine, ref.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_rope_backward_is_the_inverse_rotation():
+    from oracle import ops
+    rng = np.random.default_rng(5)
+    T, H, d = 6, 3, 16
+    x = rng.standard_normal((T, H, d))
+    pos = np.arange(10, 10 + T)
+    dy = rng.standard_normal((T, H, d))
+    # <R x, dy> = <x, R^T dy> for the rotation R, computed without rounding
+    c, s = ops.rope_tables(pos, d, 1e4)
+    c, s = c[:, None, :], s[:, None, :]
+    x1, x2 = x[..., : d // 2], x[..., d // 2:]
+    rx = np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+    np.testing.assert_allclose(np.sum(rx * dy), np.sum(x * bw.rope_backward(dy, pos, 1e4)), rtol=1e-12)
+    # the transpose of a rotation is its inverse (up to the fp32 rounding of the table)
+    back = bw.rope_backward(rx, pos, 1e4)
+    np.testing.assert_allclose(back, x, rtol=1e-6, atol=1e-6)
