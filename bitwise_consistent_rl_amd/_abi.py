@@ -37,6 +37,7 @@ EXPORTS = [
     "bci_op_sparse_attention", "bci_ssd_create", "bci_ssd_destroy", "bci_ssd_last_error",
     "bci_ssd_slot_bytes", "bci_ssd_set_batch", "bci_ssd_forward", "bci_op_transpose_bf16",
     "bci_op_add_rmsnorm_backward", "bci_op_silu_mul_backward", "bci_op_logprob_backward_dz",
+    "bci_op_attention_backward",
 ]
 
 
@@ -116,6 +117,7 @@ def load() -> ctypes.CDLL:
         "bci_op_add_rmsnorm_backward": (st, [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, ctypes.c_float, vp]),
         "bci_op_silu_mul_backward": (st, [vp, vp, vp, vp, i32, i32, vp]),
         "bci_op_logprob_backward_dz": (st, [vp, vp, vp, vp, i32, i32, vp, vp]),
+        "bci_op_attention_backward": (st, [vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp]),
         "bci_ssd_create": (st, [ctypes.POINTER(SsdConfig), i32, ctypes.POINTER(vp)]),
         "bci_ssd_destroy": (None, [vp]),
         "bci_ssd_last_error": (ctypes.c_char_p, [vp]),
@@ -324,6 +326,11 @@ def bci_op_silu_mul_backward(ctx: int, gu, dact, dgu, rows: int, inter: int, str
 def bci_op_logprob_backward_dz(ctx: int, z, ids, gout, M: int, V: int, dz, stream=None) -> None:
     _check(ctx, load().bci_op_logprob_backward_dz(ctx, _ptr(z), _ptr(ids), _ptr(gout), M, V,
                                                   _ptr(dz), _stream(stream)))
+
+
+def bci_op_attention_backward(ctx: int, q, k, v, o, dout, L: int, dq, dk, dv, stream=None) -> None:
+    _check(ctx, load().bci_op_attention_backward(ctx, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), L,
+                                                 _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream)))
 
 
 def _ssd_check(ctx, status: int):

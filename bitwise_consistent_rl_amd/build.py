@@ -23,6 +23,7 @@ LIB = os.path.join(HERE, "libbci.so")
 OBJ_DIR = os.path.join(ROOT, "_build", "obj")
 
 SOURCES = ["norm.hip", "gemm.hip", "rope_kv.hip", "attention.hip", "moe.hip", "sparse.hip", "ssd.hip", "backward.hip",
+           "attn_backward.hip",
            "bci.cpp", "ssd_api.cpp"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", f"--offload-arch={ARCH}",

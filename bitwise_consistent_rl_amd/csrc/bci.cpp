@@ -52,8 +52,10 @@ struct bci_ctx {
   // split-attention partials: [max_seg][split_tokens][nq][d] and [..][2]
   float *attn_part_acc = nullptr, *attn_part_ml = nullptr;
   int max_seg = 1, split_tokens = 0;
-  // backward: partial sums of the RMSNorm gain gradient [max_tokens / 64][8192] fp32
+  // backward: partial sums of the RMSNorm gain gradient [max_tokens / 64][8192] fp32,
+  // and the attention backward's per-row statistics [max_tokens][nq] fp32 (x2)
   float* bw_part = nullptr;
+  float *ab_lse = nullptr, *ab_dsum = nullptr;
   // non-invariant mode: split-K accumulation buffer [FAST_SPLITK_MAX_M, max_n] fp32
   float* splitk_ws = nullptr;
   int splitk_max_n = 0;
@@ -214,6 +216,8 @@ bci_status bci_create(const bci_model_config* cfg_in, int32_t device, bci_ctx** 
       {(void**)&c->rope_sin, (size_t)g.max_position * (g.head_dim / 2) * 4},
       {(void**)&c->meta, c->meta_words * 4},
       {(void**)&c->bw_part, (T + BW_DG_ROWS - 1) / BW_DG_ROWS * (size_t)8192 * 4},
+      {(void**)&c->ab_lse, T * (size_t)g.n_q_heads * 4},
+      {(void**)&c->ab_dsum, T * (size_t)g.n_q_heads * 4},
   };
   c->max_seg = (g.max_position + g.attn_segment_keys - 1) / g.attn_segment_keys;
   if (g.mode == BCI_MODE_FAST) {
@@ -654,6 +658,39 @@ bci_status bci_op_logprob_backward_dz(bci_ctx* c, const float* z, const int32_t*
   if (!z || !ids || !gout || !dz || M < 0 || V < 1)
     return fail(c, BCI_E_INVALID, "op_logprob_backward_dz: bad pointer or shape");
   HIP_TRY(c, launch_logprob_dz(z, ids, gout, dz, M, V, S(stream)));
+  return BCI_OK;
+}
+
+bci_status bci_op_attention_backward(bci_ctx* c, const void* q, const void* k, const void* v,
+                                     const void* o, const void* dout, int32_t L, void* dq, void* dk,
+                                     void* dv, void* stream) {
+  if (!c) return BCI_E_INVALID;
+  const auto& g = c->cfg;
+  if (!q || !k || !v || !o || !dout || !dq || !dk || !dv || L < 0)
+    return fail(c, BCI_E_INVALID, "op_attention_backward: bad pointer or length");
+  for (const void* p : {q, k, v, o, dout, (const void*)dq, (const void*)dk, (const void*)dv})
+    if (!aligned16(p)) return fail(c, BCI_E_INVALID, "op_attention_backward: tensors must be 16-byte aligned");
+  if (L > g.max_tokens_per_call)
+    return fail(c, BCI_E_WORKSPACE, "op_attention_backward: L %d > max_tokens_per_call %d", L,
+                g.max_tokens_per_call);
+  AttnBwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<const uint16_t*>(o);
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.dq = static_cast<uint16_t*>(dq);
+  a.dk = static_cast<uint16_t*>(dk);
+  a.dv = static_cast<uint16_t*>(dv);
+  a.lse = c->ab_lse;
+  a.dsum = c->ab_dsum;
+  a.L = L;
+  a.nq = g.n_q_heads;
+  a.nkv = g.n_kv_heads;
+  a.d = g.head_dim;
+  a.scale = (float)(1.0 / std::sqrt((double)g.head_dim));
+  a.scale_log2 = (float)(1.0 / std::sqrt((double)g.head_dim) * 1.4426950408889634);
+  HIP_TRY(c, launch_attention_backward(a, S(stream)));
   return BCI_OK;
 }
 

@@ -151,6 +151,16 @@ hipError_t launch_silu_mul_backward(const void* gu, const void* dact, void* dgu,
 hipError_t launch_logprob_dz(const float* z, const int32_t* ids, const float* gout, void* dz, int M, int V,
                              hipStream_t s);
 
+// ---- attn_backward.hip (one sequence at positions 0..L-1)
+struct AttnBwdArgs {
+  const uint16_t *q, *k, *v, *o, *dout;  // q, o, dout [L, nq, d]; k, v [L, nkv, d] bf16
+  uint16_t *dq, *dk, *dv;                // bf16, same shapes
+  float *lse, *dsum;                     // workspace [L, nq]: log2-sum-exp2, sum dO o
+  int L, nq, nkv, d;
+  float scale, scale_log2;               // 1/sqrt(d), log2(e)/sqrt(d)
+};
+hipError_t launch_attention_backward(const AttnBwdArgs& a, hipStream_t s);
+
 // ---- moe.hip
 constexpr int MOE_MAX_K = 8;
 hipError_t launch_moe_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,

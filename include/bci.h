@@ -383,6 +383,22 @@ bci_status bci_op_logprob_backward_dz(bci_ctx* ctx, const float* z, const int32_
                                       const float* gout, int32_t M, int32_t V, void* dz,
                                       void* stream);
 
+/* Backward of the causal GQA attention of one sequence at positions 0..L-1 (the
+ * context's heads and head_dim): q, o, dout [L, nq, d], k, v [L, nkv, d] bf16 -- k and v
+ * the keys and values the forward attended to (for an FP8 cache the dequantised ones:
+ * the quantiser's gradient is taken as the identity, so dk and dv are also the
+ * gradients of the keys and values before quantisation, the straight-through of the
+ * digest's section "让训练前向使用推理的数值").  With P the weights and D = sum dO o:
+ *   dq = dS k / sqrt(d),  dk = dS^T q / sqrt(d),  dv = P^T dO,  dS = P (dO v^T - D),
+ * summed over the query heads of each kv head; dq, dk, dv bf16, same shapes.  Each
+ * element accumulates in one fixed order (dq over 64-key chunks ascending, dk and dv
+ * over 64-row chunks ascending; no atomics), so the result is deterministic.  The row
+ * statistics (log-sum-exp, D) are recomputed into the workspace.  L <= max_tokens_per_call;
+ * all tensors 16-byte aligned. */
+bci_status bci_op_attention_backward(bci_ctx* ctx, const void* q, const void* k, const void* v,
+                                     const void* o, const void* dout, int32_t L, void* dq, void* dk,
+                                     void* dv, void* stream);
+
 /* ---- state-space layer (Mamba-2-style), chunked ---------------------------------
  * Porting the method to Nemotron-3.5 meant recursive arithmetic in which decode
  * replays prefill's chunked computation order and training reuses the same operator

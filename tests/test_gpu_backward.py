@@ -144,3 +144,44 @@ def test_logprob_backward(ctx, M, V):
         close(dE[torch.from_numpy(rows).cuda()].cpu().numpy(), rdE[rows], f"dE rows M={M} V={V}")
     dhf2, dE2 = bwd().logprob_backward(ctx, hf, emb, gids, gg)
     assert same_bits(dhf2, dhf) and same_bits(dE2, dE)
+
+
+@pytest.mark.parametrize("L,nq,nkv,d,kv", [(37, 4, 2, 64, "bf16"), (300, 16, 8, 128, "bf16"),
+                                           (200, 32, 4, 128, "fp8"), (129, 16, 8, 128, "fp8")])
+def test_attention_backward(L, nq, nkv, d, kv):
+    """The GPU's forward (RoPE + KV write, FP8 round trip for an FP8 cache, attention) then
+    the backward over the keys and values it attended to; the oracle rotates, round-trips,
+    attends and differentiates the same seeded rows itself."""
+    from test_gpu_ops import _attention_run
+    a = abi()
+    qkv = synth.normal_bf16((L, (nq + 2 * nkv) * d), index=70)
+    o, q, kvs = _attention_run(nq, nkv, d, kv, 2048, [L], qkv, [[(0, 0, L)]])
+    K, Vv = kvs[0]
+    dout = synth.normal_bf16((L, nq * d), index=71).cuda()
+    h = make_ctx(hidden=512, nq=nq, nkv=nkv, d=d, inter=512, vocab=4096, kv=kv, max_tokens=1024)
+    try:
+        outs = []
+        for _ in range(2):
+            dq = torch.empty(L, nq * d, dtype=BF, device="cuda")
+            dk = torch.empty(L, nkv * d, dtype=BF, device="cuda")
+            dv = torch.empty(L, nkv * d, dtype=BF, device="cuda")
+            a.bci_op_attention_backward(h, q, K, Vv, o, dout, L, dq, dk, dv)
+            torch.cuda.synchronize()
+            outs.append((dq, dk, dv))
+        assert all(same_bits(x, y) for x, y in zip(*outs))       # deterministic
+    finally:
+        torch.cuda.synchronize()
+        a.bci_destroy(h)
+    X = f64(qkv)
+    pos = np.arange(L)
+    qo = ops.rope(X[:, : nq * d].reshape(L, nq, d), pos, 1e6)
+    ko = ops.rope(X[:, nq * d:(nq + nkv) * d].reshape(L, nkv, d), pos, 1e6)
+    vo = X[:, (nq + nkv) * d:].reshape(L, nkv, d)
+    if kv == "fp8":
+        ko, vo = ops.kv_roundtrip(ko), ops.kv_roundtrip(vo)
+    oo = ops.causal_gqa_attention(qo, ko, vo, pos)
+    rdq, rdk, rdv = ob.attention_backward(qo, ko, vo, oo, f64(dout).reshape(L, nq, d))
+    dq, dk, dv = outs[0]
+    close(f64(dq).reshape(L, nq, d), rdq, f"dq L={L} {kv}")
+    close(f64(dk).reshape(L, nkv, d), rdk, f"dk L={L} {kv}")
+    close(f64(dv).reshape(L, nkv, d), rdv, f"dv L={L} {kv}")
