@@ -627,6 +627,17 @@ def backward_bench(args):
     embT = bw.transpose(ctx, emb, ld=V)
     ms = _time_ms(lambda: bw.logprob_backward(ctx, hf, emb, gids, gg, embT=embT), reps=3, warm=1)
     report("lm_head logprob backward, 512 rows", ms, flops=2.0 * Ms * V * H * 3)
+    # attention backward, one 4096-token sequence, 16 q / 8 kv heads of 128: five products
+    # of the causal half (S, dP, dV, dQ, dK) = 5 x 2 x nq x d x L^2 / 2 FLOP
+    L, NQ, NKV, D = 4096, 16, 8, 128
+    q = synth.normal_bf16((L, NQ * D), index=72).cuda()
+    kk = synth.normal_bf16((L, NKV * D), index=73).cuda()
+    vv = synth.normal_bf16((L, NKV * D), index=74).cuda()
+    o = synth.normal_bf16((L, NQ * D), index=75).cuda()
+    do = synth.normal_bf16((L, NQ * D), index=76).cuda()
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(kk), torch.empty_like(vv)
+    ms = _time_ms(lambda: abi.bci_op_attention_backward(ctx, q, kk, vv, o, do, L, dq, dk, dv), reps=5)
+    report("attention backward, 4096 tokens, 16/8 heads of 128", ms, flops=5.0 * NQ * D * L * L)
     abi.bci_destroy(ctx)
 
 
