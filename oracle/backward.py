@@ -132,3 +132,45 @@ def rope_backward(dx_rot, positions, theta: float):
     c, s = c[:, None, :], s[:, None, :]
     r1, r2 = dx_rot[..., : d // 2], dx_rot[..., d // 2:]
     return np.concatenate([r1 * c + r2 * s, r2 * c - r1 * s], axis=-1)
+
+
+def decoder_layer_backward(cfg, W, li: int, fwd: dict, d_r, d_m):
+    """Gradient of one pre-norm decoder layer of one sequence at positions 0..n-1 (the
+    layer of ``oracle.model.decoder_layer``, one chunk, empty cache before it):
+
+        r1, h = AddNorm(m_prev, r_in, g_attn);  q, k, v = RoPE(split(h Wqkv^T))
+        a = Attn(q, k, v) Wo^T;  r2, h2 = AddNorm(a, r1, g_mlp);  m = MLP(h2)
+
+    ``fwd`` holds the forward's stored values (keys r_mid = r1, h, q, K, V, o, r = r2,
+    h2, as ``decoder_layer`` returns them); d_r and d_m are the gradients reaching the
+    layer's outputs r2 and m.  The chain runs the layer backwards, each step the exact
+    derivative evaluated at the stored values with every rounding (and an FP8 cache's
+    quantiser) taken as the identity:
+        dh2, dWgu, dWd = MLP backward;      dr2 = d_r + AddNorm backward of h2
+        do, dWo = dr2 through a = o Wo^T;   dq, dk, dv = attention backward
+        dqkv = [R^T dq, R^T dk, dv];        dh, dWqkv = dqkv through h Wqkv^T
+        dr1 = dr2 + AddNorm backward of h   (= d m_prev = d r_in, the add's two inputs)
+    Returns a dict of float64 arrays: d_r_in, attn_norm, wqkv, wo, mlp_norm, wgu, wd."""
+    from . import ops
+    nq, nkv, d, inter = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.intermediate
+    p = f"layers.{li}."
+    n = fwd["h"].shape[0]
+    pos = np.arange(n)
+    h2 = np.asarray(fwd["h2"], dtype=np.float64)
+    gu = fwd.get("gu")
+    if gu is None:
+        gu = ops.bf(ops.linear(h2, W(p + "wgu")))
+    act = fwd.get("act")
+    if act is None:
+        act = ops.silu_mul(gu[:, :inter], gu[:, inter:])
+    dh2, dwgu, dwd = mlp_backward(h2, W(p + "wgu"), W(p + "wd"), d_m, inter, gu, act)
+    dr2, dg2 = rmsnorm_backward(fwd["r"], W(p + "mlp_norm"), dh2, cfg.rms_eps, d_r)
+    o = np.asarray(fwd["o"], dtype=np.float64)
+    do, dwo = linear_backward(o.reshape(n, nq * d), W(p + "wo"), dr2)
+    dq, dk, dv = attention_backward(fwd["q"], fwd["K"], fwd["V"], o, do.reshape(n, nq, d))
+    dqkv = np.concatenate([rope_backward(dq, pos, cfg.rope_theta).reshape(n, nq * d),
+                           rope_backward(dk, pos, cfg.rope_theta).reshape(n, nkv * d),
+                           dv.reshape(n, nkv * d)], axis=1)
+    dh, dwqkv = linear_backward(fwd["h"], W(p + "wqkv"), dqkv)
+    dr1, dg1 = rmsnorm_backward(fwd["r_mid"], W(p + "attn_norm"), dh, cfg.rms_eps, dr2)
+    return dict(d_r_in=dr1, attn_norm=dg1, wqkv=dwqkv, wo=dwo, mlp_norm=dg2, wgu=dwgu, wd=dwd)

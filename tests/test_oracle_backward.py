@@ -162,3 +162,70 @@ def test_rope_backward_is_the_inverse_rotation():
     # the transpose of a rotation is its inverse (up to the fp32 rounding of the table)
     back = bw.rope_backward(rx, pos, 1e4)
     np.testing.assert_allclose(back, x, rtol=1e-6, atol=1e-6)
+
+
+def test_decoder_layer_backward_against_autograd_and_finite_differences():
+    """The layer composition (every piece, the residual paths into both norms, the RoPE
+    transpose, the split of dqkv) against torch's autograd of the same layer written
+    without roundings, fed with that forward's values; and central differences."""
+    from types import SimpleNamespace
+    from oracle import ops
+    rng = np.random.default_rng(6)
+    n, H, nq, nkv, d, inter = 6, 16, 4, 2, 8, 12
+    cfg = SimpleNamespace(n_q_heads=nq, n_kv_heads=nkv, head_dim=d, intermediate=inter, rms_eps=1e-6,
+                          rope_theta=1e4)
+    w = {"attn_norm": 1 + 0.1 * rng.standard_normal(H), "wqkv": rng.standard_normal(((nq + 2 * nkv) * d, H)) * 0.3,
+         "wo": rng.standard_normal((H, nq * d)) * 0.3, "mlp_norm": 1 + 0.1 * rng.standard_normal(H),
+         "wgu": rng.standard_normal((2 * inter, H)) * 0.3, "wd": rng.standard_normal((H, inter)) * 0.3}
+    m_prev, r_in, d_r, d_m = (rng.standard_normal((n, H)) for _ in range(4))
+    c, s = (torch.tensor(x) for x in ops.rope_tables(np.arange(n), d, cfg.rope_theta))
+    causal = torch.tril(torch.ones(n, n, dtype=torch.bool))
+
+    def layer(mp, ri, g1, wqkv, wo, g2, wgu, wd):
+        def norm(x, g):
+            return x / torch.sqrt((x * x).mean(dim=-1, keepdim=True) + cfg.rms_eps) * g
+
+        def rot(x):   # [n, heads, d], half-split pairs
+            x1, x2 = x[..., : d // 2], x[..., d // 2:]
+            return torch.cat([x1 * c[:, None] - x2 * s[:, None], x2 * c[:, None] + x1 * s[:, None]], dim=-1)
+        r1 = mp + ri
+        h = norm(r1, g1)
+        qkv = h @ wqkv.T
+        q = rot(qkv[:, : nq * d].reshape(n, nq, d))
+        k = rot(qkv[:, nq * d:(nq + nkv) * d].reshape(n, nkv, d))
+        v = qkv[:, (nq + nkv) * d:].reshape(n, nkv, d)
+        heads = []
+        for hq in range(nq):
+            g = hq // (nq // nkv)
+            sc = (q[:, hq] @ k[:, g].T / np.sqrt(d)).masked_fill(~causal, float("-inf"))
+            heads.append(torch.softmax(sc, dim=-1) @ v[:, g])
+        o = torch.stack(heads, dim=1)
+        r2 = r1 + o.reshape(n, nq * d) @ wo.T
+        h2 = norm(r2, g2)
+        gu = h2 @ wgu.T
+        act = torch.nn.functional.silu(gu[:, :inter]) * gu[:, inter:]
+        m = act @ wd.T
+        return dict(r_mid=r1, h=h, q=q, K=k, V=v, o=o, r=r2, h2=h2, gu=gu, act=act, m=m)
+
+    names = ["attn_norm", "wqkv", "wo", "mlp_norm", "wgu", "wd"]
+    ins = [torch.tensor(m_prev, requires_grad=True), torch.tensor(r_in, requires_grad=True)] + \
+          [torch.tensor(w[k], requires_grad=True) for k in names]
+    out = layer(*ins)
+    ((out["r"] * torch.tensor(d_r)).sum() + (out["m"] * torch.tensor(d_m)).sum()).backward()
+    fwd = {k: v.detach().numpy() for k, v in out.items()}
+    res = bw.decoder_layer_backward(cfg, lambda name: w[name.split(".")[-1]], 0, fwd, d_r, d_m)
+    np.testing.assert_allclose(res["d_r_in"], ins[0].grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(res["d_r_in"], ins[1].grad.numpy(), rtol=1e-10, atol=1e-12)
+    for k, t in zip(names, ins[2:]):
+        np.testing.assert_allclose(res[k], t.grad.numpy(), rtol=1e-10, atol=1e-12, err_msg=k)
+
+    def loss(i, j, e):
+        args = [x.detach().clone() for x in ins]
+        args[i][j] += e
+        o = layer(*args)
+        return float((o["r"] * torch.tensor(d_r)).sum() + (o["m"] * torch.tensor(d_m)).sum())
+    e = 1e-6
+    for i, j, want in ((1, (2, 3), res["d_r_in"][2, 3]), (3, (5, 7), res["wqkv"][5, 7]),
+                       (3, ((nq + nkv) * d + 1, 4), res["wqkv"][(nq + nkv) * d + 1, 4]),
+                       (4, (1, 2), res["wo"][1, 2]), (2, (9,), res["attn_norm"][9])):
+        assert abs((loss(i, j, e) - loss(i, j, -e)) / (2 * e) - want) < 1e-6 * max(1.0, abs(want))
