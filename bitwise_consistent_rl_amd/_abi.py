@@ -37,6 +37,7 @@ EXPORTS = [
     "bci_op_sparse_attention", "bci_ssd_create", "bci_ssd_destroy", "bci_ssd_last_error",
     "bci_ssd_slot_bytes", "bci_ssd_set_batch", "bci_ssd_forward", "bci_op_transpose_bf16",
     "bci_op_add_rmsnorm_backward", "bci_op_silu_mul_backward", "bci_op_logprob_backward_dz",
+    "bci_op_rope_backward",
     "bci_op_attention_backward",
 ]
 
@@ -117,6 +118,7 @@ def load() -> ctypes.CDLL:
         "bci_op_add_rmsnorm_backward": (st, [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, ctypes.c_float, vp]),
         "bci_op_silu_mul_backward": (st, [vp, vp, vp, vp, i32, i32, vp]),
         "bci_op_logprob_backward_dz": (st, [vp, vp, vp, vp, i32, i32, vp, vp]),
+        "bci_op_rope_backward": (st, [vp, vp, vp, vp, vp, vp]),
         "bci_op_attention_backward": (st, [vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp]),
         "bci_ssd_create": (st, [ctypes.POINTER(SsdConfig), i32, ctypes.POINTER(vp)]),
         "bci_ssd_destroy": (None, [vp]),
@@ -321,6 +323,10 @@ def bci_op_add_rmsnorm_backward(ctx: int, r, g, dh, dr_in, dr, rstd, dg, rows: i
 def bci_op_silu_mul_backward(ctx: int, gu, dact, dgu, rows: int, inter: int, stream=None) -> None:
     _check(ctx, load().bci_op_silu_mul_backward(ctx, _ptr(gu), _ptr(dact), _ptr(dgu), rows, inter,
                                                 _stream(stream)))
+
+
+def bci_op_rope_backward(ctx: int, dq, dk, dv, dqkv, stream=None) -> None:
+    _check(ctx, load().bci_op_rope_backward(ctx, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dqkv), _stream(stream)))
 
 
 def bci_op_logprob_backward_dz(ctx: int, z, ids, gout, M: int, V: int, dz, stream=None) -> None:

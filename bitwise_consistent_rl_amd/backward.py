@@ -92,3 +92,59 @@ def logprob_backward(ctx: int, hf: torch.Tensor, emb: torch.Tensor, ids: torch.T
     abi.bci_op_logprob_backward_dz(ctx, z, ids, gout, M, V, dz)
     del z
     return linear_backward(ctx, hf, emb, dz, wT=embT)
+
+
+def rope_backward(ctx: int, dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor) -> torch.Tensor:
+    """[R^T dq, R^T dk, dv] for the current batch, laid out as the forward's qkv rows."""
+    T = dq.shape[0]
+    dqkv = torch.empty(T, dq.shape[1] + dk.shape[1] + dv.shape[1], dtype=BF, device=dq.device)
+    abi.bci_op_rope_backward(ctx, dq, dk, dv, dqkv)
+    return dqkv
+
+
+def decoder_layer_forward(ctx: int, layer: int, w: dict, r_in: torch.Tensor, m_prev: torch.Tensor = None,
+                          *, nq: int, nkv: int, d: int, inter: int, eps: float) -> dict:
+    """One pre-norm decoder layer over the current batch (one sequence at positions
+    0..L-1, its cache bound), op by op with the forward's own entry points, keeping what
+    the backward needs:
+        r1, h = AddNorm(m_prev, r_in, attn_norm);  q, k, v = RoPE(split(h Wqkv^T)) -> cache
+        o = Attn(q, cache);  a = o Wo^T;  r2, h2 = AddNorm(a, r1, mlp_norm);  m = MLP(h2)
+    ``w``: attn_norm, wqkv, wo, mlp_norm, wgu, wd (bf16).  Returns the saved tensors and
+    the outputs r (= r2) and m."""
+    L, H = r_in.shape
+    r = r_in.clone()
+    h = torch.empty_like(r)
+    abi.bci_op_add_rmsnorm(ctx, m_prev, r, h, w["attn_norm"], L, H, eps)
+    r1 = r.clone()
+    qkv = gemm(ctx, h, w["wqkv"], abi.BCI_EPI_BF16)
+    q = torch.empty(L, nq * d, dtype=BF, device=r.device)
+    abi.bci_op_rope_kv_write(ctx, qkv, q, layer)
+    o = torch.empty_like(q)
+    abi.bci_op_attention(ctx, q, layer, o)
+    a = gemm(ctx, o, w["wo"], abi.BCI_EPI_BF16)
+    h2 = torch.empty_like(r)
+    abi.bci_op_add_rmsnorm(ctx, a, r, h2, w["mlp_norm"], L, H, eps)
+    act = gemm(ctx, h2, w["wgu"], abi.BCI_EPI_SILU_MUL, out_cols=inter)
+    m = gemm(ctx, act, w["wd"], abi.BCI_EPI_BF16)
+    k = torch.empty(L, nkv * d, dtype=BF, device=r.device)
+    v = torch.empty_like(k)
+    abi.bci_op_kv_gather_dequant(ctx, 0, L, layer, k, v)    # the keys and values attended to
+    return dict(r_mid=r1, h=h, q=q, K=k, V=v, o=o, r=r, h2=h2, m=m)
+
+
+def decoder_layer_backward(ctx: int, w: dict, saved: dict, d_r: torch.Tensor, d_m: torch.Tensor, *,
+                           inter: int, eps: float) -> dict:
+    """Gradient of ``decoder_layer_forward``'s layer, the current batch still set: the
+    layer run backwards, every rounding (and an FP8 cache's quantiser) taken as the
+    identity.  d_r, d_m: gradients reaching the outputs r2 and m.  Returns d_r_in (also
+    the gradient of m_prev) in bf16 and the weight gradients in fp32."""
+    L = d_r.shape[0]
+    dh2, dwgu, dwd, _, _ = mlp_backward(ctx, saved["h2"], w["wgu"], w["wd"], d_m, inter)
+    dr2, dg2, _ = add_rmsnorm_backward(ctx, saved["r"], w["mlp_norm"], dh2, eps, d_r)
+    do, dwo = linear_backward(ctx, saved["o"], w["wo"], dr2)
+    dq, dk, dv = torch.empty_like(saved["q"]), torch.empty_like(saved["K"]), torch.empty_like(saved["V"])
+    abi.bci_op_attention_backward(ctx, saved["q"], saved["K"], saved["V"], saved["o"], do, L, dq, dk, dv)
+    dqkv = rope_backward(ctx, dq, dk, dv)
+    dh, dwqkv = linear_backward(ctx, saved["h"], w["wqkv"], dqkv)
+    dr1, dg1, _ = add_rmsnorm_backward(ctx, saved["r_mid"], w["attn_norm"], dh, eps, dr2)
+    return dict(d_r_in=dr1, attn_norm=dg1, wqkv=dwqkv, wo=dwo, mlp_norm=dg2, wgu=dwgu, wd=dwd)

@@ -9,12 +9,12 @@
 //
 // One sequence at positions 0..L-1; rows are (token, query head of the kv head's
 // group) pairs as in the forward's tiles.  With t = (q . k) log2(e)/sqrt(d):
-//   pass 1 (per 64-row query tile, 4 waves x 16 rows):
+//   pass 1 (per 128-row query tile, 8 waves x 16 rows):
 //     lse2 = log2-sum-exp2 of t over keys <= the row's position (online, per 64-key
 //            chunk, the forward's expressions), D = sum_d dO o (fixed tree);
 //     P = 2^(t - lse2), dP = dO . v, dS = P (dP - D),
 //     dQ = (sum over 64-key chunks, ascending, of dS . K) / sqrt(d)
-//   pass 2 (per 64-key tile, one wave per 16 keys; rows ascending in 64-row chunks):
+//   pass 2 (per 128-key tile, one wave per 16 keys; rows ascending in 64-row chunks):
 //     dV = sum_rows P^T dO,  dK = (sum_rows dS^T Q) / sqrt(d)
 // Products on v_mfma_f32_16x16x32_bf16 with P and dS rounded to bf16 as operands (as P
 // in the forward).  Each output element accumulates in one fixed order, so the result
@@ -39,18 +39,26 @@ __device__ __forceinline__ int rswz(int row, int ch) {  // 16-byte chunk ch of a
 }
 
 // 64 rows of D bf16 (row i from src_row(i), or zeros) -> rows (swizzled) and/or the
-// transpose [D][AB_TS]
-template <int D, typename RowPtr>
+// transpose [D][AB_TS]; a unit is two consecutive rows x 8 columns, so the transpose
+// is written as 4-byte pairs
+template <int D, int NT, typename RowPtr>
 __device__ __forceinline__ void stage(RowPtr src_row, int n_valid, u32x4_t* rows, bf16_t* tr, int tid) {
-  for (int u = tid; u < AB_CH * (D / 8); u += 256) {
-    const int i = u / (D / 8), pc = u % (D / 8);
-    u32x4_t v = u32x4_t{0, 0, 0, 0};
-    if (i < n_valid) v = *reinterpret_cast<const u32x4_t*>(src_row(i) + 8 * pc);
-    if (rows) rows[rswz<D>(i, pc)] = v;
+  for (int u = tid; u < (AB_CH / 2) * (D / 8); u += NT) {
+    const int ip = u / (D / 8), pc = u % (D / 8);
+    const int i0 = 2 * ip;
+    u32x4_t va = u32x4_t{0, 0, 0, 0}, vb = va;
+    if (i0 < n_valid) va = *reinterpret_cast<const u32x4_t*>(src_row(i0) + 8 * pc);
+    if (i0 + 1 < n_valid) vb = *reinterpret_cast<const u32x4_t*>(src_row(i0 + 1) + 8 * pc);
+    if (rows) {
+      rows[rswz<D>(i0, pc)] = va;
+      rows[rswz<D>(i0 + 1, pc)] = vb;
+    }
     if (tr) {
-      const bf16_t* e = reinterpret_cast<const bf16_t*>(&v);
+      const bf16_t* ea = reinterpret_cast<const bf16_t*>(&va);
+      const bf16_t* eb = reinterpret_cast<const bf16_t*>(&vb);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) tr[(8 * pc + k) * AB_TS + i] = e[k];
+      for (int k = 0; k < 8; ++k)
+        *reinterpret_cast<uint32_t*>(tr + (8 * pc + k) * AB_TS + i0) = pack_bf2(ea[k], eb[k]);
     }
   }
 }
@@ -74,19 +82,23 @@ __device__ __forceinline__ bf16x8_t pack_frag(const float (&x)[4][4], int k2) {
 }
 
 // ------------------------------------------------------------- pass 1: stats, dQ
+constexpr int AB_WAVES = 8;                 // waves per workgroup (16 rows or keys each)
+constexpr int AB_THREADS = AB_WAVES * 64;
+constexpr int AB_TILE = AB_WAVES * 16;      // query rows (pass 1) or keys (pass 2) per workgroup
+
 template <int D>
-__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(AttnBwdArgs a) {
+__global__ __launch_bounds__(AB_THREADS) void attn_bwd_dq_kernel(AttnBwdArgs a) {
   __shared__ __attribute__((aligned(16))) u32x4_t Kr[AB_CH * D / 8];
   __shared__ __attribute__((aligned(16))) u32x4_t Vr[AB_CH * D / 8];
   __shared__ __attribute__((aligned(16))) bf16_t Kt[D * AB_TS];
-  const int tile = blockIdx.x, g = blockIdx.y;
+  const int tile = gridDim.x - 1 - blockIdx.x, g = blockIdx.y;  // longest (latest) tiles first
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lg = lane >> 4, lc = lane & 15;
   const int group = a.nq / a.nkv;
-  const int row = tile * 64 + wave * 16 + lc;
+  const int row = tile * AB_TILE + wave * 16 + lc;
   const int tk = row / group, hq = g * group + row % group;
   const bool row_ok = tk < a.L;
-  const int kmax = min(a.L - 1, (tile * 64 + 63) / group);  // last key any row of the tile needs
+  const int kmax = min(a.L - 1, (tile * AB_TILE + AB_TILE - 1) / group);  // last key any row needs
   const bf16_t* qrow = a.q + ((size_t)tk * a.nq + hq) * D;
   const bf16_t* dorow = a.dout + ((size_t)tk * a.nq + hq) * D;
   const bf16_t* orow = a.o + ((size_t)tk * a.nq + hq) * D;
@@ -119,7 +131,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(AttnBwdArgs a) {
   for (int c = 0; c < nchunks; ++c) {
     if (c > 0) __syncthreads();
     const int base = c * AB_CH;
-    stage<D>([&](int i) { return krow(base + i); }, min(AB_CH, a.L - base), Kr, nullptr, tid);
+    stage<D, AB_THREADS>([&](int i) { return krow(base + i); }, min(AB_CH, a.L - base), Kr, nullptr, tid);
     __syncthreads();
     float t[4][4], mloc = -INFINITY;
 #pragma unroll
@@ -162,8 +174,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(AttnBwdArgs a) {
     __syncthreads();
     const int base = c * AB_CH;
     const int nv = min(AB_CH, a.L - base);
-    stage<D>([&](int i) { return krow(base + i); }, nv, Kr, Kt, tid);
-    stage<D>([&](int i) { return vrow(base + i); }, nv, Vr, nullptr, tid);
+    stage<D, AB_THREADS>([&](int i) { return krow(base + i); }, nv, Kr, Kt, tid);
+    stage<D, AB_THREADS>([&](int i) { return vrow(base + i); }, nv, Vr, nullptr, tid);
     __syncthreads();
     float ds[4][4];
 #pragma unroll
@@ -204,7 +216,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(AttnBwdArgs a) {
 
 // ------------------------------------------------------------- pass 2: dK, dV
 template <int D>
-__global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
+__global__ __launch_bounds__(AB_THREADS) void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
   __shared__ __attribute__((aligned(16))) u32x4_t Qr[AB_CH * D / 8];
   __shared__ __attribute__((aligned(16))) u32x4_t Or[AB_CH * D / 8];   // dO rows
   __shared__ __attribute__((aligned(16))) bf16_t Qt[D * AB_TS];
@@ -215,7 +227,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lg = lane >> 4, lc = lane & 15;
   const int group = a.nq / a.nkv;
-  const int key = ktile * 64 + wave * 16 + lc;  // this lane's key (MFMA column)
+  const int key = ktile * AB_TILE + wave * 16 + lc;  // this lane's key (MFMA column)
   const bool key_ok = key < a.L;
 
   bf16x8_t kf[D / 32], vf[D / 32];
@@ -236,7 +248,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
     dv[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
   const int n_rows = a.L * group;
-  const int row0 = (ktile * 64) * group;  // the first row whose token can see this tile
+  const int row0 = (ktile * AB_TILE) * group;  // the first row whose token can see this tile
   for (int rb = row0; rb < n_rows; rb += AB_CH) {
     if (rb > row0) __syncthreads();
     const int nv = min(AB_CH, n_rows - rb);
@@ -248,8 +260,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
       const int R = rb + i;
       return a.dout + ((size_t)(R / group) * a.nq + g * group + R % group) * D;
     };
-    stage<D>(qrow, nv, Qr, Qt, tid);
-    stage<D>(drow, nv, Or, Ot, tid);
+    stage<D, AB_THREADS>(qrow, nv, Qr, Qt, tid);
+    stage<D, AB_THREADS>(drow, nv, Or, Ot, tid);
     if (tid < AB_CH) {
       const int R = rb + tid;
       const bool ok = tid < nv;
@@ -307,8 +319,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
 template <int D>
 static void launch_ab(const AttnBwdArgs& a, hipStream_t s) {
   const int group = a.nq / a.nkv;
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<D>), dim3((a.L * group + 63) / 64, a.nkv), dim3(256), 0, s, a);
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D>), dim3((a.L + 63) / 64, a.nkv), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<D>), dim3((a.L * group + AB_TILE - 1) / AB_TILE, a.nkv),
+                     dim3(AB_THREADS), 0, s, a);
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D>), dim3((a.L + AB_TILE - 1) / AB_TILE, a.nkv), dim3(AB_THREADS),
+                     0, s, a);
 }
 
 hipError_t launch_attention_backward(const AttnBwdArgs& a, hipStream_t s) {

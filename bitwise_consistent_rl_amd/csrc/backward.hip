@@ -249,4 +249,65 @@ hipError_t launch_logprob_dz(const float* z, const int32_t* ids, const float* go
   return hipGetLastError();
 }
 
+
+
+// ---------------------------------------------------------------- RoPE backward
+// The rotation's transpose at each token's position, with the forward's fp32 table:
+// for the pair (x1, x2) = (e, d/2 + e) of a q or k head,
+//   dx1 = dr1 c + dr2 s,  dx2 = dr2 c - dr1 s   (fp32, rounded to bf16 once),
+// and the v heads' gradient passes through.  Output row t is dqkv [t] laid out as
+// the forward's qkv row (q heads, k heads, v heads).  One workgroup per token; a
+// thread owns 8 consecutive pairs of one head (16-byte loads and stores).
+__global__ __launch_bounds__(256) void rope_backward_kernel(
+    const bf16_t* __restrict__ dq, const bf16_t* __restrict__ dk, const bf16_t* __restrict__ dv,
+    bf16_t* __restrict__ dqkv, const int32_t* __restrict__ tok_pos, const float* __restrict__ rcos,
+    const float* __restrict__ rsin, int nq, int nkv, int d) {
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  const int t = blockIdx.x;
+  const int half = d >> 1, upr = d >> 4;
+  const int pos = tok_pos[t];
+  const int n_heads = nq + 2 * nkv;
+  for (int u = threadIdx.x; u < n_heads * upr; u += blockDim.x) {
+    const int hd = u / upr, e0 = 8 * (u % upr);
+    const bf16_t* src;
+    if (hd < nq) src = dq + ((size_t)t * nq + hd) * d;
+    else if (hd < nq + nkv) src = dk + ((size_t)t * nkv + hd - nq) * d;
+    else src = dv + ((size_t)t * nkv + hd - nq - nkv) * d;
+    u32x4_t lo = *reinterpret_cast<const u32x4_t*>(src + e0);
+    u32x4_t hi = *reinterpret_cast<const u32x4_t*>(src + half + e0);
+    if (hd < nq + nkv) {
+      const bf16_t* rl = reinterpret_cast<const bf16_t*>(&lo);
+      const bf16_t* rh = reinterpret_cast<const bf16_t*>(&hi);
+      float y1[8], y2[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float c = rcos[(size_t)pos * half + e0 + i], sn = rsin[(size_t)pos * half + e0 + i];
+        const float r1 = bf2f(rl[i]), r2 = bf2f(rh[i]);
+        const float a1 = r1 * c, b1 = r2 * sn;
+        const float a2 = r2 * c, b2 = r1 * sn;
+        y1[i] = a1 + b1;
+        y2[i] = a2 - b2;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lo[i] = pack_f2bf2(y1[2 * i], y1[2 * i + 1]);
+        hi[i] = pack_f2bf2(y2[2 * i], y2[2 * i + 1]);
+      }
+    }
+    bf16_t* dst = dqkv + ((size_t)t * n_heads + hd) * d;
+    *reinterpret_cast<u32x4_t*>(dst + e0) = lo;
+    *reinterpret_cast<u32x4_t*>(dst + half + e0) = hi;
+  }
+}
+
+hipError_t launch_rope_backward(const void* dq, const void* dk, const void* dv, void* dqkv,
+                                const int32_t* tok_pos, const float* rcos, const float* rsin, int T, int nq,
+                                int nkv, int d, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(rope_backward_kernel, dim3(T), dim3(256), 0, s, static_cast<const bf16_t*>(dq),
+                     static_cast<const bf16_t*>(dk), static_cast<const bf16_t*>(dv), static_cast<bf16_t*>(dqkv),
+                     tok_pos, rcos, rsin, nq, nkv, d);
+  return hipGetLastError();
+}
+
 }  // namespace bci

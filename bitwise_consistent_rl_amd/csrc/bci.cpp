@@ -652,6 +652,19 @@ bci_status bci_op_silu_mul_backward(bci_ctx* c, const void* gu, const void* dact
   return BCI_OK;
 }
 
+bci_status bci_op_rope_backward(bci_ctx* c, const void* dq, const void* dk, const void* dv, void* dqkv,
+                                void* stream) {
+  if (!c) return BCI_E_INVALID;
+  if (bci_status st = need_batch(c, "op_rope_backward")) return st;
+  if (!dq || !dk || !dv || !dqkv) return fail(c, BCI_E_INVALID, "op_rope_backward: null pointer");
+  if (!aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(dqkv))
+    return fail(c, BCI_E_INVALID, "op_rope_backward: all tensors must be 16-byte aligned");
+  const auto& g = c->cfg;
+  HIP_TRY(c, launch_rope_backward(dq, dk, dv, dqkv, c->meta + c->o_pos, c->rope_cos, c->rope_sin, c->n_tokens,
+                                  g.n_q_heads, g.n_kv_heads, g.head_dim, S(stream)));
+  return BCI_OK;
+}
+
 bci_status bci_op_logprob_backward_dz(bci_ctx* c, const float* z, const int32_t* ids, const float* gout,
                                       int32_t M, int32_t V, void* dz, void* stream) {
   if (!c) return BCI_E_INVALID;

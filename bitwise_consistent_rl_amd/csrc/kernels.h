@@ -150,6 +150,9 @@ hipError_t launch_silu_mul_backward(const void* gu, const void* dact, void* dgu,
                                     hipStream_t s);
 hipError_t launch_logprob_dz(const float* z, const int32_t* ids, const float* gout, void* dz, int M, int V,
                              hipStream_t s);
+hipError_t launch_rope_backward(const void* dq, const void* dk, const void* dv, void* dqkv,
+                                const int32_t* tok_pos, const float* rcos, const float* rsin, int T, int nq,
+                                int nkv, int d, hipStream_t s);
 
 // ---- attn_backward.hip (one sequence at positions 0..L-1)
 struct AttnBwdArgs {

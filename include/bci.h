@@ -383,6 +383,19 @@ bci_status bci_op_logprob_backward_dz(bci_ctx* ctx, const float* z, const int32_
                                       const float* gout, int32_t M, int32_t V, void* dz,
                                       void* stream);
 
+/* Backward of bci_op_rope_kv_write's rotation for the current batch: dq [n_tokens, nq d],
+ * dk and dv [n_tokens, nkv d] bf16 (gradients with respect to the rotated q, the keys
+ * written to the cache and the values) -> dqkv [n_tokens, (nq + 2 nkv) d] bf16, laid out
+ * as the forward's qkv input.  Per rotation pair (e, d/2 + e) of a q or k head, at the
+ * token's position and with the forward's fp32 table (c, s):
+ *   dx1 = bf(dr1 c + dr2 s),  dx2 = bf(dr2 c - dr1 s)   (the rotation's transpose),
+ * and dv is copied.  The forward's bf16 roundings (and, for an FP8 cache, the key's
+ * quantiser) are taken as the identity, the straight-through of page "Finish RL
+ * Training Faster" digest, section "让训练前向使用推理的数值".  All tensors 16-byte
+ * aligned (BCI_E_INVALID otherwise); BCI_E_STATE without a batch. */
+bci_status bci_op_rope_backward(bci_ctx* ctx, const void* dq, const void* dk, const void* dv, void* dqkv,
+                                void* stream);
+
 /* Backward of the causal GQA attention of one sequence at positions 0..L-1 (the
  * context's heads and head_dim): q, o, dout [L, nq, d], k, v [L, nkv, d] bf16 -- k and v
  * the keys and values the forward attended to (for an FP8 cache the dequantised ones:

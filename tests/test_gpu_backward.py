@@ -185,3 +185,90 @@ def test_attention_backward(L, nq, nkv, d, kv):
     close(f64(dq).reshape(L, nq, d), rdq, f"dq L={L} {kv}")
     close(f64(dk).reshape(L, nkv, d), rdk, f"dk L={L} {kv}")
     close(f64(dv).reshape(L, nkv, d), rdv, f"dv L={L} {kv}")
+
+
+def _layer_ctx(L, H, nq, nkv, d, inter, kv, pos0=0):
+    from test_gpu_ops import _alloc_cache, _batch_for
+    a = abi()
+    h = make_ctx(hidden=H, nq=nq, nkv=nkv, d=d, inter=inter, vocab=4096, kv=kv, max_tokens=1024)
+    lengths = [L] if np.isscalar(L) else list(L)
+    p0 = [pos0] * len(lengths) if np.isscalar(pos0) else list(pos0)
+    cu, p0a, bt, nb = _batch_for(lengths, p0)
+    cache = _alloc_cache(1, nb, nkv, d, kv)
+    a.bci_bind_kv_cache(h, *cache, nb)
+    a.bci_set_batch(h, np.zeros(int(cu[-1]), np.int32), cu, p0a, bt, [], [])
+    return h, cache
+
+
+def test_rope_backward():
+    """The rotation's transpose at every token's own position (two sequences, the second
+    starting at position 100): q and k heads within one bf16 rounding of the exact
+    transpose applied with the forward's fp32 table, v heads copied bit for bit."""
+    nq, nkv, d = 16, 8, 128
+    lengths, p0 = [37, 90], [0, 100]
+    h, cache = _layer_ctx(lengths, 2048, nq, nkv, d, 6144, "bf16", p0)
+    try:
+        T = sum(lengths)
+        dq = synth.normal_bf16((T, nq * d), index=80).cuda()
+        dk = synth.normal_bf16((T, nkv * d), index=81).cuda()
+        dv = synth.normal_bf16((T, nkv * d), index=82).cuda()
+        got = f64(bwd().rope_backward(h, dq, dk, dv))
+        torch.cuda.synchronize()
+    finally:
+        abi().bci_destroy(h)
+    pos = np.concatenate([np.arange(p, p + L) for p, L in zip(p0, lengths)])
+    for lo, hi, x, nh in ((0, nq * d, dq, nq), (nq * d, (nq + nkv) * d, dk, nkv)):
+        X = f64(x).reshape(T, nh, d)
+        ref = ob.rope_backward(X, pos, 1e6).reshape(T, nh * d)
+        c, s = ops.rope_tables(pos, d, 1e6)
+        cs = np.concatenate([np.abs(c), np.abs(c)], axis=1)[:, None, :]
+        ss = np.concatenate([np.abs(s), np.abs(s)], axis=1)[:, None, :]
+        sw = np.concatenate([X[..., d // 2:], X[..., : d // 2]], axis=-1)
+        bound = (2.0 ** -22 * (np.abs(X) * cs + np.abs(sw) * ss)).reshape(T, nh * d)
+        assert_bf16_close(got[:, lo:hi], ref, abs_bound=bound, max_ulp=1, frac_exact=0.999, what="rope bwd")
+    assert np.array_equal(got[:, (nq + nkv) * d:], f64(dv))
+
+
+@pytest.mark.parametrize("L,H,nq,nkv,d,inter,kv", [(200, 512, 8, 4, 64, 768, "bf16"),
+                                                   (300, 2048, 16, 8, 128, 6144, "fp8")])
+def test_decoder_layer_backward(L, H, nq, nkv, d, inter, kv):
+    """A whole decoder layer: the GPU's forward (op by op, keeping its values) and the
+    backward composed from the library's entry points, against the oracle's forward of the
+    same seeded inputs and its layer gradient (pinned by autograd and finite differences);
+    then the same backward again, bit for bit."""
+    from types import SimpleNamespace
+    from oracle import model as om
+    names = ["attn_norm", "wqkv", "wo", "mlp_norm", "wgu", "wd"]
+    sc = 1.0 / np.sqrt(H)
+    w = {"attn_norm": (synth.normal_bf16((H,), index=90, scale=0.1).float() + 1.0).to(BF),
+         "wqkv": synth.normal_bf16(((nq + 2 * nkv) * d, H), index=91, scale=sc),
+         "wo": synth.normal_bf16((H, nq * d), index=92, scale=1.0 / np.sqrt(nq * d)),
+         "mlp_norm": (synth.normal_bf16((H,), index=93, scale=0.1).float() + 1.0).to(BF),
+         "wgu": synth.normal_bf16((2 * inter, H), index=94, scale=sc),
+         "wd": synth.normal_bf16((H, inter), index=95, scale=1.0 / np.sqrt(inter))}
+    r_in = synth.normal_bf16((L, H), index=96)
+    m_prev = synth.normal_bf16((L, H), index=97)
+    d_r = synth.normal_bf16((L, H), index=98)
+    d_m = synth.normal_bf16((L, H), index=99)
+    wg = {k: v.cuda() for k, v in w.items()}
+    h, cache = _layer_ctx(L, H, nq, nkv, d, inter, kv)
+    try:
+        dims = dict(nq=nq, nkv=nkv, d=d, inter=inter, eps=1e-6)
+        saved = bwd().decoder_layer_forward(h, 0, wg, r_in.cuda(), m_prev.cuda(), **dims)
+        g1 = bwd().decoder_layer_backward(h, wg, saved, d_r.cuda(), d_m.cuda(), inter=inter, eps=1e-6)
+        g2 = bwd().decoder_layer_backward(h, wg, saved, d_r.cuda(), d_m.cuda(), inter=inter, eps=1e-6)
+        torch.cuda.synchronize()
+        assert all(same_bits(g1[k], g2[k]) for k in g1)                       # deterministic
+        got = {k: (f64(v) if v.dtype == BF else v.cpu().numpy().astype(np.float64)) for k, v in g1.items()}
+    finally:
+        torch.cuda.synchronize()
+        abi().bci_destroy(h)
+    cfg = SimpleNamespace(n_q_heads=nq, n_kv_heads=nkv, head_dim=d, intermediate=inter, rms_eps=1e-6,
+                          rope_theta=1e6)
+    Wf = {k: f64(v) for k, v in w.items()}
+    W = lambda name: Wf[name.split(".")[-1]]
+    fwd = om.decoder_layer(cfg, W, 0, f64(m_prev), f64(r_in), np.arange(L), np.zeros((0, nkv, d)),
+                           np.zeros((0, nkv, d)), kv)
+    ref = ob.decoder_layer_backward(cfg, W, 0, fwd, f64(d_r), f64(d_m))
+    for k in ["d_r_in"] + names:
+        close(got[k], ref[k], f"layer {k} L={L} {kv}")
