@@ -16,6 +16,7 @@
 //       m' = max(m, max_j t_j); a = 2^(m - m'); p_j = 2^(t_j - m')
 //       l = l * a + sum_j p_j   [fixed tree];  acc = acc * a + P.V  [MFMA, P in bf16]
 //     merge (m, l, acc) into (M, L, ACC) with the same exp2 rule
+//   (every "x * a" above is mul_unless_one: x itself when a is exactly 1)
 //   o = bf(ACC / L)
 // A chunk or segment that lies wholly after the row's position is an exact
 // no-op (a = 2^0 = 1, p = 0, and keys past the tile's last position are
@@ -36,6 +37,7 @@
 #include "kernels.h"
 
 #include <climits>
+#include <type_traits>
 
 namespace bci {
 
@@ -308,7 +310,8 @@ __global__ __launch_bounds__(ATHREADS, SPLIT ? 4 : 2) void attention_kernel(Attn
     g = w / gridDim.x;
     tile = w % gridDim.x;
   }
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int lg = lane >> 4, lc = lane & 15;
   const int seq = p.tiles[tile * 4 + 0];
   const int tok_begin = p.tiles[tile * 4 + 1];
@@ -380,36 +383,71 @@ __global__ __launch_bounds__(ATHREADS, SPLIT ? 4 : 2) void attention_kernel(Attn
     const u32x4_t* Kb = Ks[b];
     const bf16_t* Vb = Vt[b];
 
-    // S^T = K . Q^T : 4 key blocks of 16, D/32 steps
+    // S^T = K . Q^T : 4 key blocks of 16, D/32 steps.  Each block's chain runs over the
+    // steps in ascending order; the four chains are interleaved, and the K fragments
+    // of step ks + 1 are read while step ks multiplies.
     f32x4_t sacc[4];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      sacc[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int kt = 0; kt < 4; ++kt) sacc[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    {
+      bf16x8_t kf[D / 32][4];
 #pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) {
-        const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, Kb[kswz<D>(kt * 16 + lc, ks * 4 + lg)]);
-        sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sacc[kt], 0, 0, 0);
+      for (int ks = 0; ks < D / 32; ++ks)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+          kf[ks][kt] = __builtin_bit_cast(bf16x8_t, Kb[kswz<D>(kt * 16 + lc, ks * 4 + lg)]);
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+          sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks][kt], qf[ks], sacc[kt], 0, 0, 0);
+      if constexpr (PIPE) {  // order: reads 0, reads 1, products 0, reads 2, products 1, ...
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+          if (ks + 1 < D / 32) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        }
       }
     }
     // Causal mask.  It changes nothing for a chunk whose last key is at or before
     // the first (smallest) position of this wave's valid rows, so such chunks
     // skip it; rows past the tile's tokens are never stored.
-    const bool need_mask = c * CHUNK + CHUNK - 1 > wave_qpos_min;
+    const bool need_mask = c * CHUNK + CHUNK - 1 > wave_qpos_min;  // wave-uniform
     float t[4][4];
     float mloc = -INFINITY;
+    if constexpr (PIPE) {  // the mask as its own pass, skipped by whole chunks
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+      for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float v = sacc[kt][r] * p.scale_log2;
-        if (need_mask) {
-          const int key = c * CHUNK + kt * 16 + 4 * lg + r;
-          t[kt][r] = key <= qpos ? v : -INFINITY;
-        } else {
-          t[kt][r] = v;
-        }
-        mloc = fmaxf(mloc, t[kt][r]);
+        for (int r = 0; r < 4; ++r) t[kt][r] = sacc[kt][r] * p.scale_log2;
+      if (need_mask) {
+        const int kl = qpos - (c * CHUNK + 4 * lg);  // keys 16 kt + r <= kl are visible
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (kt * 16 + r > kl) t[kt][r] = -INFINITY;
       }
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mloc = fmaxf(mloc, t[kt][r]);
+    } else {  // fused (fewer live registers)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float v = sacc[kt][r] * p.scale_log2;
+          if (need_mask) {
+            const int key = c * CHUNK + kt * 16 + 4 * lg + r;
+            t[kt][r] = key <= qpos ? v : -INFINITY;
+          } else {
+            t[kt][r] = v;
+          }
+          mloc = fmaxf(mloc, t[kt][r]);
+        }
+    }
     mloc = xrow_max(mloc);
     const float mn = fmaxf(m, mloc);
     const float mu = (mn == -INFINITY) ? 0.0f : mn;
@@ -423,42 +461,78 @@ __global__ __launch_bounds__(ATHREADS, SPLIT ? 4 : 2) void attention_kernel(Attn
         rs = rs + pr[kt][r];
       }
     rs = xrow_sum(rs);
-    if (seg_start) {
-      // (m, l, acc) = (-inf, 0, 0): alpha = 2^(-inf) = 0, so l * alpha + rs is rs
-      // and acc * alpha is +0, exactly what these shortcuts give
-      l = rs;
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    } else {
-      const float alpha = fexp2(m - mu);
-      l = l * alpha + rs;
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[dt][r] = acc[dt][r] * alpha;
-    }
-    m = mn;
 
-    // O^T += V^T . P^T over two 32-key steps
+    // O^T += V^T . P^T over two 32-key steps; from_zero: the first step accumulates
+    // onto a literal zero
+    auto pv = [&](auto from_zero) {
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-      u32x4_t pw;
-      pw[0] = pack_f2bf2(pr[2 * k2][0], pr[2 * k2][1]);
-      pw[1] = pack_f2bf2(pr[2 * k2][2], pr[2 * k2][3]);
-      pw[2] = pack_f2bf2(pr[2 * k2 + 1][0], pr[2 * k2 + 1][1]);
-      pw[3] = pack_f2bf2(pr[2 * k2 + 1][2], pr[2 * k2 + 1][3]);
-      const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pw);
-      const int ko = k2 * 32 + 4 * lg;
+      for (int k2 = 0; k2 < 2; ++k2) {
+        u32x4_t pw;
+        pw[0] = pack_f2bf2(pr[2 * k2][0], pr[2 * k2][1]);
+        pw[1] = pack_f2bf2(pr[2 * k2][2], pr[2 * k2][3]);
+        pw[2] = pack_f2bf2(pr[2 * k2 + 1][0], pr[2 * k2 + 1][1]);
+        pw[3] = pack_f2bf2(pr[2 * k2 + 1][2], pr[2 * k2 + 1][3]);
+        const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pw);
+        const int ko = k2 * 32 + 4 * lg;
+        u32x4_t vw[D / 16];  // all fragments of the step are read, then multiplied
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) {
-        const bf16_t* vr = Vb + (dt * 16 + lc) * VT_STRIDE;
-        const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vr + ko);
-        const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vr + ko + 16);
-        const u32x4_t vw = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vw), pf,
-                                                          acc[dt], 0, 0, 0);
+        for (int dt = 0; dt < D / 16; ++dt) {
+          const bf16_t* vr = Vb + (dt * 16 + lc) * VT_STRIDE;
+          const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vr + ko);
+          const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vr + ko + 16);
+          vw[dt] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+        }
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+          const f32x4_t c0 = (decltype(from_zero)::value && k2 == 0) ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc[dt];
+          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vw[dt]), pf, c0, 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, D / 16, 0);
+      }
+    };
+    // (m, l, acc) = (-inf, 0, 0) at a segment start: alpha = 2^(-inf) = 0, so
+    // l * alpha + rs is rs and acc * alpha is +0, exactly what these shortcuts give
+    if constexpr (PIPE) {
+      if (seg_start) {
+        l = rs;
+        pv(std::true_type{});
+      } else {
+        const float alpha = fexp2(m - mu);
+        l = mul_unless_one(l, alpha) + rs;
+        scale_unless_one(acc, alpha);
+        pv(std::false_type{});
+      }
+    } else {  // fewer registers: one copy of the products
+      if (seg_start) {
+        l = rs;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      } else {
+        const float alpha = fexp2(m - mu);
+        l = mul_unless_one(l, alpha) + rs;
+        scale_unless_one(acc, alpha);
+      }
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        u32x4_t pw;
+        pw[0] = pack_f2bf2(pr[2 * k2][0], pr[2 * k2][1]);
+        pw[1] = pack_f2bf2(pr[2 * k2][2], pr[2 * k2][3]);
+        pw[2] = pack_f2bf2(pr[2 * k2 + 1][0], pr[2 * k2 + 1][1]);
+        pw[3] = pack_f2bf2(pr[2 * k2 + 1][2], pr[2 * k2 + 1][3]);
+        const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pw);
+        const int ko = k2 * 32 + 4 * lg;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+          const bf16_t* vr = Vb + (dt * 16 + lc) * VT_STRIDE;
+          const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vr + ko);
+          const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vr + ko + 16);
+          const u32x4_t vw = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vw), pf, acc[dt], 0, 0, 0);
+        }
       }
     }
+    m = mn;
 
     if constexpr (!SPLIT) {
       if (c == c_stop || ((c + 1) % seg_chunks) == 0) {
@@ -466,11 +540,13 @@ __global__ __launch_bounds__(ATHREADS, SPLIT ? 4 : 2) void attention_kernel(Attn
         const float Mn = fmaxf(M, m);
         const float Mu = (Mn == -INFINITY) ? 0.0f : Mn;
         const float a = fexp2(M - Mu), bb = fexp2(m - Mu);
-        L = L * a + l * bb;
+        L = mul_unless_one(L, a) + mul_unless_one(l, bb);
+        scale_unless_one(ACC, a);
+        scale_unless_one(acc, bb);
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) ACC[dt][r] = ACC[dt][r] * a + acc[dt][r] * bb;
+          for (int r = 0; r < 4; ++r) ACC[dt][r] = ACC[dt][r] + acc[dt][r];
         M = Mn;
       }
     }
@@ -528,8 +604,8 @@ __global__ __launch_bounds__(256) void attention_merge_kernel(AttnArgs p) {
     const float Mn = fmaxf(M, m);
     const float Mu = (Mn == -INFINITY) ? 0.0f : Mn;
     const float a = fexp2(M - Mu), b = fexp2(m - Mu);
-    L = L * a + l * b;
-    ACC = ACC * a + a_ * b;
+    L = mul_unless_one(L, a) + mul_unless_one(l, b);
+    ACC = mul_unless_one(ACC, a) + mul_unless_one(a_, b);
     M = Mn;
   }
   reinterpret_cast<bf16_t*>(p.o)[((size_t)t * p.nq + h) * D + d] = f2bf(ACC / L);

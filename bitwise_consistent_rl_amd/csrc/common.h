@@ -129,6 +129,28 @@ __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(
 __device__ __forceinline__ float flog(float x) { return logf(x); }
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + fexp(-g)); }
 
+// ------------------------------------------------- online-softmax rescaling
+// x * f, except that a factor of exactly 1 returns x itself.  Every rescale and merge
+// of online-softmax states (m, l, acc) in this library goes through this rule, so a
+// kernel that skips a multiply by 1 for a whole wave and one that tests each value
+// give the same bits, including where a multiply would quiet a NaN or flush a
+// denormal.  In a merge max(M, m) is one of the two maxima, so one of the two
+// factors 2^(M - max), 2^(m - max) is exactly 2^0 = 1.
+__device__ __forceinline__ float mul_unless_one(float x, float f) { return f == 1.0f ? x : x * f; }
+
+// x[i][r] <- mul_unless_one(x[i][r], f) with f per lane, as a branch: lanes with f == 1
+// are masked off (their x untouched, no temporaries), and a wave in which no lane
+// needs the multiply skips it.
+template <int N>
+__device__ __forceinline__ void scale_unless_one(f32x4_t (&x)[N], float f) {
+  if (f != 1.0f) {
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[i][r] = x[i][r] * f;
+  }
+}
+
 // ------------------------------------------------------ wave reductions
 // Fixed xor butterflies over the 64 lanes (or a lane group).  For + the two
 // partners add the same two values in either order, which IEEE addition

@@ -804,11 +804,8 @@ __global__ __launch_bounds__(512, 1) void sparse_attention_kernel(SparseAttnArgs
       for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     } else {
       const float alpha = fexp2(m - mu);
-      l = l * alpha + rs;
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[dt][r] = acc[dt][r] * alpha;
+      l = mul_unless_one(l, alpha) + rs;
+      scale_unless_one(acc, alpha);
     }
     m = mn;
     first = false;
@@ -874,8 +871,8 @@ __global__ __launch_bounds__(512, 1) void sparse_attention_kernel(SparseAttnArgs
       const float Mn = fmaxf(M, mw);
       const float Mu = (Mn == -INFINITY) ? 0.0f : Mn;
       const float a = fexp2(M - Mu), b = fexp2(mw - Mu);
-      L = L * a + lw * b;
-      ACC = ACC * a + aw * b;
+      L = mul_unless_one(L, a) + mul_unless_one(lw, b);
+      ACC = mul_unless_one(ACC, a) + mul_unless_one(aw, b);
       M = Mn;
     }
     reinterpret_cast<bf16_t*>(p.o)[(size_t)t * qstride + (size_t)(g * group + h) * D + d] =
