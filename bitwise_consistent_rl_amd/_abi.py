@@ -31,7 +31,7 @@ EXPORTS = [
     "bci_weight_version", "bci_bind_kv_cache", "bci_set_batch", "bci_forward_logprobs",
     "bci_op_embed", "bci_op_add_rmsnorm", "bci_op_gemm_bf16", "bci_op_rope_kv_write",
     "bci_op_kv_gather_dequant", "bci_op_attention", "bci_op_gather_scored",
-    "bci_op_lmhead_logprob", "bci_op_moe_topk", "bci_op_moe_forward", "bci_profile_begin",
+    "bci_op_lmhead_logprob", "bci_op_moe_topk", "bci_op_gemm_bf16_ksplit", "bci_op_moe_forward", "bci_profile_begin",
     "bci_profile_end", "bci_forward_logprobs_graph", "bci_graph_count", "bci_graph_reset",
     "bci_op_index_key_write", "bci_op_index_scores", "bci_op_sparse_topk",
     "bci_op_sparse_attention", "bci_ssd_create", "bci_ssd_destroy", "bci_ssd_last_error",
@@ -103,6 +103,7 @@ def load() -> ctypes.CDLL:
         "bci_op_embed": (st, [vp, vp, vp, vp]),
         "bci_op_add_rmsnorm": (st, [vp, vp, vp, vp, vp, i32, i32, ctypes.c_float, vp]),
         "bci_op_gemm_bf16": (st, [vp, vp, vp, vp, i32, i32, i32, i32, vp]),
+        "bci_op_gemm_bf16_ksplit": (st, [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]),
         "bci_op_rope_kv_write": (st, [vp, vp, vp, i32, vp]),
         "bci_op_kv_gather_dequant": (st, [vp, i32, i32, i32, vp, vp, vp]),
         "bci_op_attention": (st, [vp, vp, i32, vp, vp]),
@@ -251,6 +252,12 @@ def bci_op_add_rmsnorm(ctx: int, a, r, h, g, rows: int, cols: int, eps: float, s
 def bci_op_gemm_bf16(ctx: int, A, W, C, M: int, N: int, K: int, epilogue: int, stream=None) -> None:
     _check(ctx, load().bci_op_gemm_bf16(ctx, _ptr(A), _ptr(W), _ptr(C), M, N, K, epilogue,
                                         _stream(stream)))
+
+
+def bci_op_gemm_bf16_ksplit(ctx: int, A, W, C, M: int, N: int, K: int, k_split: int, epilogue: int,
+                            workspace, stream=None) -> None:
+    _check(ctx, load().bci_op_gemm_bf16_ksplit(ctx, _ptr(A), _ptr(W), _ptr(C), M, N, K, k_split, epilogue,
+                                               _ptr(workspace), _stream(stream)))
 
 
 def bci_op_rope_kv_write(ctx: int, qkv, q_out, layer: int, stream=None) -> None:

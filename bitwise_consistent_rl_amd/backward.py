@@ -17,6 +17,7 @@ import torch
 from . import _abi as abi
 
 BF = torch.bfloat16
+VOCAB_SLICE = 4096   # contraction slice of the lm_head backward's dz . E
 
 
 def _pad64(n: int) -> int:
@@ -41,16 +42,33 @@ def gemm(ctx: int, a: torch.Tensor, w: torch.Tensor, epi: int, out_cols: int = N
     return c
 
 
-def linear_backward(ctx: int, x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, wT: torch.Tensor = None):
+def gemm_ksplit(ctx: int, a: torch.Tensor, w: torch.Tensor, epi: int, k_split: int) -> torch.Tensor:
+    """a . w^T with the contraction in fixed slices of k_split summed in slice order
+    (for few output tiles over a long contraction)."""
+    M, K = a.shape
+    N = w.shape[0]
+    dtype = torch.float32 if epi == abi.BCI_EPI_F32 else BF
+    c = torch.empty(M, N, dtype=dtype, device=a.device)
+    ws = torch.empty((K + k_split - 1) // k_split * M * N, dtype=torch.float32, device=a.device)
+    abi.bci_op_gemm_bf16_ksplit(ctx, a, w, c, M, N, K, k_split, epi, ws)
+    return c
+
+
+def linear_backward(ctx: int, x: torch.Tensor, w: torch.Tensor, dy: torch.Tensor, wT: torch.Tensor = None,
+                    dx_k_split: int = None):
     """y = x . w^T (x [M, K], w [N, K], dy [M, N] bf16; N % 64 == 0).
-    Returns dx [M, K] bf16 and dw [N, K] fp32."""
+    Returns dx [M, K] bf16 and dw [N, K] fp32.  dx_k_split: contraction slice of the dx
+    product (over N), for a long N with few output tiles."""
     M, K = x.shape
     N = w.shape[0]
     if N % 64:
         raise ValueError("the output width of the forward GEMM must be a multiple of 64")
     if wT is None:
         wT = transpose(ctx, w, ld=N)                     # [K, N]
-    dx = gemm(ctx, dy, wT, abi.BCI_EPI_BF16)             # [M, K], contraction over N
+    if dx_k_split:
+        dx = gemm_ksplit(ctx, dy, wT, abi.BCI_EPI_BF16, dx_k_split)   # [M, K], slices of N
+    else:
+        dx = gemm(ctx, dy, wT, abi.BCI_EPI_BF16)         # [M, K], contraction over N
     Mp = _pad64(M)
     dw = gemm(ctx, transpose(ctx, dy, Mp), transpose(ctx, x, Mp), abi.BCI_EPI_F32)   # [N, K]
     return dx, dw
@@ -84,14 +102,16 @@ def mlp_backward(ctx: int, h: torch.Tensor, wgu: torch.Tensor, wd: torch.Tensor,
 
 def logprob_backward(ctx: int, hf: torch.Tensor, emb: torch.Tensor, ids: torch.Tensor,
                      gout: torch.Tensor, embT: torch.Tensor = None):
-    """lp = z[id] - logsumexp(z), z = hf . E^T (fp32 logits).  Returns (dhf bf16, dE fp32)."""
+    """lp = z[id] - logsumexp(z), z = hf . E^T (fp32 logits).  Returns (dhf bf16, dE fp32).
+    dhf = dz . E contracts over the whole vocabulary onto few output tiles, so it runs in
+    fixed vocabulary slices of VOCAB_SLICE summed in slice order."""
     M = hf.shape[0]
     V = emb.shape[0]
     z = gemm(ctx, hf, emb, abi.BCI_EPI_F32)                        # [M, V] fp32
     dz = torch.empty(M, V, dtype=BF, device=hf.device)
     abi.bci_op_logprob_backward_dz(ctx, z, ids, gout, M, V, dz)
     del z
-    return linear_backward(ctx, hf, emb, dz, wT=embT)
+    return linear_backward(ctx, hf, emb, dz, wT=embT, dx_k_split=VOCAB_SLICE if V > VOCAB_SLICE else None)
 
 
 def rope_backward(ctx: int, dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor) -> torch.Tensor:

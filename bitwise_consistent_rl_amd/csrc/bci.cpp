@@ -584,6 +584,21 @@ bci_status bci_op_gemm_bf16(bci_ctx* c, const void* A, const void* W, void* C, i
   return gemm_checked(c, A, nullptr, W, C, M, N, K, epi, S(stream));
 }
 
+bci_status bci_op_gemm_bf16_ksplit(bci_ctx* c, const void* A, const void* W, void* C, int32_t M, int32_t N,
+                                   int32_t K, int32_t k_split, int32_t epi, float* workspace, void* stream) {
+  if (!c) return BCI_E_INVALID;
+  if (!A || !W || !C || !workspace || M < 0 || N < 1 || K < 1)
+    return fail(c, BCI_E_INVALID, "op_gemm_ksplit: bad pointer or shape");
+  if (K % GEMM_BK || k_split < GEMM_BK || k_split % GEMM_BK)
+    return fail(c, BCI_E_INVALID, "op_gemm_ksplit: K %d and k_split %d must be multiples of %d", K, k_split,
+                GEMM_BK);
+  if (epi != BCI_EPI_BF16 && epi != BCI_EPI_F32)
+    return fail(c, BCI_E_INVALID, "op_gemm_ksplit: epilogue %d (BF16 or F32 only)", epi);
+  if (!aligned16(A) || !aligned16(W)) return fail(c, BCI_E_INVALID, "op_gemm_ksplit: A and W must be 16-byte aligned");
+  HIP_TRY(c, launch_gemm_ksplit(A, W, C, M, N, K, k_split, epi, workspace, S(stream)));
+  return BCI_OK;
+}
+
 bci_status bci_op_rope_kv_write(bci_ctx* c, const void* qkv, void* q_out, int32_t layer, void* stream) {
   if (!c) return BCI_E_INVALID;
   if (bci_status st = need_batch(c, "op_rope_kv_write")) return st;

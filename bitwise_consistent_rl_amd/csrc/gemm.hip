@@ -45,7 +45,7 @@ constexpr int STAGE = (BM + BN) * KCH;   // 16-byte chunks per LDS buffer
 constexpr int LM_SMALL_M = 16;           // lm_head rows up to which 16-row tiles are used
 constexpr int LM_MID_M = 128;            // ... and up to which 64-row tiles are used
 
-enum { K_BF16 = 0, K_F32 = 1, K_SILU = 2, K_LMHEAD = 3, K_ATOMIC = 4 };
+enum { K_BF16 = 0, K_F32 = 1, K_SILU = 2, K_LMHEAD = 3, K_ATOMIC = 4, K_PART = 5 };
 
 struct GemmArgs {
   const bf16_t* A;
@@ -64,8 +64,9 @@ struct GemmArgs {
   const int32_t* gtiles;
   const int32_t* n_gtiles;
   size_t w_group_stride;
-  // split-K (K_ATOMIC, non-invariant mode only): workgroup y covers K range
-  // [y * k_split, (y + 1) * k_split) and atomically adds its fp32 partial to C
+  // split-K: workgroup y covers K range [y * k_split, min(K, (y + 1) * k_split)).
+  // K_ATOMIC (non-invariant mode only) atomically adds its fp32 partial to C; K_PART
+  // stores it to C + y * M * N (fixed slices, summed later in slice order)
   int k_split;
 };
 
@@ -232,9 +233,9 @@ __global__ __launch_bounds__((TBM >= 64 ? TBM / 64 : 1) * NWN * 64, 1) void gemm
 
   int nk = K / BK;
   int kb = 0;
-  if constexpr (KIND == K_ATOMIC) {
+  if constexpr (KIND == K_ATOMIC || KIND == K_PART) {
     kb = blockIdx.y * p.k_split;
-    nk = p.k_split / BK;
+    nk = min(p.k_split, K - kb) / BK;
   }
   issue(0, kb);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
@@ -275,7 +276,9 @@ __global__ __launch_bounds__((TBM >= 64 ? TBM / 64 : 1) * NWN * 64, 1) void gemm
           }
         }
       }
-  } else if constexpr (KIND == K_BF16 || KIND == K_F32) {
+  } else if constexpr (KIND == K_BF16 || KIND == K_F32 || KIND == K_PART) {
+    void* Cout = p.C;
+    if constexpr (KIND == K_PART) Cout = reinterpret_cast<float*>(p.C) + (size_t)blockIdx.y * p.M * p.N;
 #pragma unroll
     for (int mi = 0; mi < KMI; ++mi)
 #pragma unroll
@@ -287,9 +290,9 @@ __global__ __launch_bounds__((TBM >= 64 ? TBM / 64 : 1) * NWN * 64, 1) void gemm
             const int col = tn * BN + wn * WTN + ni * 16 + (lane & 15);
             if (col >= p.N) continue;
             if constexpr (KIND == K_BF16)
-              reinterpret_cast<bf16_t*>(p.C)[(size_t)row * p.N + col] = f2bf(acc[mi][ni][r]);
+              reinterpret_cast<bf16_t*>(Cout)[(size_t)row * p.N + col] = f2bf(acc[mi][ni][r]);
             else
-              reinterpret_cast<float*>(p.C)[(size_t)row * p.N + col] = acc[mi][ni][r];
+              reinterpret_cast<float*>(Cout)[(size_t)row * p.N + col] = acc[mi][ni][r];
           }
         }
       }
@@ -621,6 +624,43 @@ hipError_t launch_gemm_splitk(const void* A, const void* W, void* C, int M, int 
   hipLaunchKernelGGL((gemm_kernel<K_ATOMIC, false, false>), dim3(grid, n_split), dim3(THREADS), 0, s, a);
   const size_t outs = (epi == EPI_SILU) ? (size_t)M * (N / 2) : n;
   hipLaunchKernelGGL(splitk_epilogue_kernel, dim3((unsigned)((outs + 255) / 256)), dim3(256), 0, s, ws, C, M, N, epi);
+  return hipGetLastError();
+}
+
+// Deterministic split-K: fixed contraction slices of k_split (the last may be
+// shorter), each an fp32 partial of the tiled GEMM's per-element chain, then summed in
+// ascending slice order and rounded once.  Element (i, j) depends only on row i of A,
+// row j of W and k_split, so rows stay independent of M.
+__global__ __launch_bounds__(256) void ksplit_reduce_kernel(const float* __restrict__ ws, int S, size_t n,
+                                                            void* __restrict__ C, int epi) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    float acc = ws[i];
+    for (int sl = 1; sl < S; ++sl) acc = acc + ws[(size_t)sl * n + i];
+    if (epi == EPI_F32) reinterpret_cast<float*>(C)[i] = acc;
+    else reinterpret_cast<bf16_t*>(C)[i] = f2bf(acc);
+  }
+}
+
+hipError_t launch_gemm_ksplit(const void* A, const void* W, void* C, int M, int N, int K, int k_split, int epi,
+                              float* ws, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  GemmArgs a{};
+  a.A = (const bf16_t*)A;
+  a.a_div = 1;
+  a.W = (const bf16_t*)W;
+  a.C = ws;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.tiles_m = (M + BM - 1) / BM;
+  a.tiles_n = (N + BN - 1) / BN;
+  a.k_split = k_split;
+  const int S = (K + k_split - 1) / k_split;
+  const int grid = (a.tiles_m * a.tiles_n + 7) / 8 * 8;
+  hipLaunchKernelGGL((gemm_kernel<K_PART, false, false>), dim3(grid, S), dim3(THREADS), 0, s, a);
+  const size_t n = (size_t)M * N;
+  hipLaunchKernelGGL(ksplit_reduce_kernel, dim3((unsigned)std::min<size_t>((n + 255) / 256, 8192)), dim3(256), 0, s,
+                     ws, S, n, C, epi);
   return hipGetLastError();
 }
 

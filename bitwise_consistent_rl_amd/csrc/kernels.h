@@ -30,6 +30,10 @@ constexpr int SKINNY_MAX_M = 128;
 constexpr int FAST_SPLITK_MAX_M = 256;
 hipError_t launch_gemm_splitk(const void* A, const void* W, void* C, int M, int N, int K, int epi,
                               float* ws, hipStream_t s);
+// Deterministic split-K (any mode): ws holds ceil(K / k_split) * M * N fp32 partials,
+// summed in slice order.  k_split % GEMM_BK == 0; epi EPI_BF16 or EPI_F32.
+hipError_t launch_gemm_ksplit(const void* A, const void* W, void* C, int M, int N, int K, int k_split, int epi,
+                              float* ws, hipStream_t s);
 // Grouped GEMM over a device tile list (see GemmArgs in gemm.hip): m-tile i covers
 // rows gtiles[3i+1] .. +gtiles[3i+2] of C with weight W + gtiles[3i] * w_group_stride;
 // A rows are a_rows[r] / a_div when a_rows is non-null, else r.

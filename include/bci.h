@@ -216,6 +216,20 @@ bci_status bci_op_add_rmsnorm(bci_ctx* ctx, const void* a, void* r, void* h, con
 bci_status bci_op_gemm_bf16(bci_ctx* ctx, const void* A, const void* W, void* C, int32_t M,
                             int32_t N, int32_t K, int32_t epilogue, void* stream);
 
+/* C = A . W^T as bci_op_gemm_bf16, with the contraction cut into fixed slices of
+ * k_split (the last may be shorter) for products with few output tiles and a long
+ * contraction (the logits' gradient times the embedding in the lm_head backward):
+ * slice s's fp32 partial (the same ascending 32-wide MFMA chain from zero over the
+ * slice) goes to workspace + s * M * N, then C = bf16 or fp32 of the partials summed in
+ * ascending slice order.  Deterministic, and row i depends only on row i of A, W and
+ * k_split (never on M) -- the fixed reduction order of page "Finish RL Training Faster"
+ * digest, section "让训练前向使用推理的数值".  A [M, K], W [N, K] bf16, 16-byte aligned;
+ * K and k_split multiples of 64; epilogue BCI_EPI_BF16 or BCI_EPI_F32; workspace fp32
+ * [ceil(K / k_split) * M * N], owned by the caller. */
+bci_status bci_op_gemm_bf16_ksplit(bci_ctx* ctx, const void* A, const void* W, void* C, int32_t M, int32_t N,
+                                   int32_t K, int32_t k_split, int32_t epilogue, float* workspace,
+                                   void* stream);
+
 /* For the current batch and layer: rotates q and k of qkv [n_tokens, (nq + 2 nkv) d]
  * (half-split RoPE at each token's absolute position, fp32 table, bf16 result),
  * writes q' to q_out [n_tokens, nq * d] and k', v into the bound cache (bf16, or

@@ -64,6 +64,56 @@ def test_gemm_bf16_parity(ctx, M, N, K):
                       what=f"gemm {M}x{N}x{K}")
 
 
+def _ksplit(ctx, a, w, epi, k_split):
+    M, K = a.shape
+    N = w.shape[0]
+    C = torch.empty(M, N, dtype=torch.float32 if epi == abi().BCI_EPI_F32 else BF, device="cuda")
+    ws = torch.empty((K + k_split - 1) // k_split * M * N, dtype=torch.float32, device="cuda")
+    abi().bci_op_gemm_bf16_ksplit(ctx, a, w, C, M, N, K, k_split, epi, ws)
+    torch.cuda.synchronize()
+    return C
+
+
+@pytest.mark.parametrize("M,N,K,k_split", [(37, 300, 2368, 256), (300, 512, 4096, 1024), (5, 128, 64, 64)])
+def test_gemm_ksplit(ctx, M, N, K, k_split):
+    """Contraction in fixed slices (the last one shorter when K % k_split != 0): within
+    the fp32 bound of the oracle's product, equal bit for bit to the fp32 sum, in slice
+    order, of the single-slice GEMMs, rows independent of M, and repeatable."""
+    a, w = synth.gemm_inputs(M, N, K, index=M + N + K + k_split)
+    ga, gw = cuda(a), cuda(w)
+    c32 = _ksplit(ctx, ga, gw, abi().BCI_EPI_F32, k_split)
+    cbf = _ksplit(ctx, ga, gw, abi().BCI_EPI_BF16, k_split)
+    A, W = f64(a), f64(w)
+    ref = ops.linear(A, W)
+    mag = np.abs(A) @ np.abs(W).T
+    got = c32.cpu().numpy()
+    assert np.all(np.abs(got - ref) <= K * 2.0 ** -24 * mag + 1e-30)
+    assert_bf16_close(f64(cbf), ops.bf(ref), abs_bound=K * 2.0 ** -24 * mag, max_ulp=1, frac_exact=0.999,
+                      what=f"ksplit {M}x{N}x{K}/{k_split}")
+    # the slices' own GEMMs (contiguous copies of the column slices), summed in order in fp32
+    acc = None
+    for k0 in range(0, K, k_split):
+        k1 = min(K, k0 + k_split)
+        part = gemm(ctx, ga[:, k0:k1].contiguous(), gw[:, k0:k1].contiguous(), abi().BCI_EPI_F32,
+                    dtype=torch.float32).cpu().numpy()
+        acc = part if acc is None else (acc + part).astype(np.float32)
+    assert np.array_equal(got.view(np.int32), acc.view(np.int32))
+    assert same_bits(cbf, torch.from_numpy(acc).to(BF))
+    sub = slice(M // 3, M // 3 + min(3, M))
+    assert same_bits(_ksplit(ctx, ga[sub].contiguous(), gw, abi().BCI_EPI_F32, k_split), c32[sub])
+    assert same_bits(_ksplit(ctx, ga, gw, abi().BCI_EPI_F32, k_split), c32)
+
+
+def test_gemm_ksplit_rejects_bad_arguments(ctx):
+    a, w = synth.gemm_inputs(4, 64, 128, index=3)
+    ga, gw = cuda(a), cuda(w)
+    C = torch.empty(4, 64, dtype=BF, device="cuda")
+    ws = torch.empty(4 * 64 * 2, dtype=torch.float32, device="cuda")
+    for k_split, epi in ((96, abi().BCI_EPI_BF16), (0, abi().BCI_EPI_BF16), (64, abi().BCI_EPI_SILU_MUL)):
+        with pytest.raises(abi().BciError):
+            abi().bci_op_gemm_bf16_ksplit(ctx, ga, gw, C, 4, 64, 128, k_split, epi, ws)
+
+
 def test_gemm_f32_epilogue_parity(ctx):
     M, N, K = 129, 256, 2048
     a, w = synth.gemm_inputs(M, N, K, index=11)
