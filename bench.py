@@ -636,7 +636,8 @@ def backward_bench(args):
     o = synth.normal_bf16((L, NQ * D), index=75).cuda()
     do = synth.normal_bf16((L, NQ * D), index=76).cuda()
     dq, dk, dv = torch.empty_like(q), torch.empty_like(kk), torch.empty_like(vv)
-    ms = _time_ms(lambda: abi.bci_op_attention_backward(ctx, q, kk, vv, o, do, L, dq, dk, dv), reps=5)
+    ws = torch.empty(2 * 4 * kk.numel(), dtype=torch.float32, device="cuda")   # row parts of dK/dV
+    ms = _time_ms(lambda: abi.bci_op_attention_backward(ctx, q, kk, vv, o, do, L, dq, dk, dv, ws), reps=5)
     report("attention backward, 4096 tokens, 16/8 heads of 128", ms, flops=5.0 * NQ * D * L * L)
     abi.bci_destroy(ctx)
 

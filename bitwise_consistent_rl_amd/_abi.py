@@ -120,7 +120,7 @@ def load() -> ctypes.CDLL:
         "bci_op_silu_mul_backward": (st, [vp, vp, vp, vp, i32, i32, vp]),
         "bci_op_logprob_backward_dz": (st, [vp, vp, vp, vp, i32, i32, vp, vp]),
         "bci_op_rope_backward": (st, [vp, vp, vp, vp, vp, vp]),
-        "bci_op_attention_backward": (st, [vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp]),
+        "bci_op_attention_backward": (st, [vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp]),
         "bci_ssd_create": (st, [ctypes.POINTER(SsdConfig), i32, ctypes.POINTER(vp)]),
         "bci_ssd_destroy": (None, [vp]),
         "bci_ssd_last_error": (ctypes.c_char_p, [vp]),
@@ -341,9 +341,11 @@ def bci_op_logprob_backward_dz(ctx: int, z, ids, gout, M: int, V: int, dz, strea
                                                   _ptr(dz), _stream(stream)))
 
 
-def bci_op_attention_backward(ctx: int, q, k, v, o, dout, L: int, dq, dk, dv, stream=None) -> None:
+def bci_op_attention_backward(ctx: int, q, k, v, o, dout, L: int, dq, dk, dv, workspace=None,
+                              stream=None) -> None:
     _check(ctx, load().bci_op_attention_backward(ctx, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), L,
-                                                 _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream)))
+                                                 _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                                 _stream(stream)))
 
 
 def _ssd_check(ctx, status: int):

@@ -114,6 +114,18 @@ def logprob_backward(ctx: int, hf: torch.Tensor, emb: torch.Tensor, ids: torch.T
     return linear_backward(ctx, hf, emb, dz, wT=embT, dx_k_split=VOCAB_SLICE if V > VOCAB_SLICE else None)
 
 
+def attention_backward(ctx: int, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                       do: torch.Tensor, split: bool = True):
+    """Causal GQA attention backward of one sequence (positions 0..L-1): (dq, dk, dv) bf16.
+    split: give the library its part buffer (fp32 [2, 4, L, nkv * d]) so the dK/dV pass
+    can cut long sequences' rows into fixed parts summed in order."""
+    L = q.shape[0]
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(2 * 4 * k.numel(), dtype=torch.float32, device=q.device) if split else None
+    abi.bci_op_attention_backward(ctx, q, k, v, o, do, L, dq, dk, dv, ws)
+    return dq, dk, dv
+
+
 def rope_backward(ctx: int, dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor) -> torch.Tensor:
     """[R^T dq, R^T dk, dv] for the current batch, laid out as the forward's qkv rows."""
     T = dq.shape[0]
@@ -162,8 +174,7 @@ def decoder_layer_backward(ctx: int, w: dict, saved: dict, d_r: torch.Tensor, d_
     dh2, dwgu, dwd, _, _ = mlp_backward(ctx, saved["h2"], w["wgu"], w["wd"], d_m, inter)
     dr2, dg2, _ = add_rmsnorm_backward(ctx, saved["r"], w["mlp_norm"], dh2, eps, d_r)
     do, dwo = linear_backward(ctx, saved["o"], w["wo"], dr2)
-    dq, dk, dv = torch.empty_like(saved["q"]), torch.empty_like(saved["K"]), torch.empty_like(saved["V"])
-    abi.bci_op_attention_backward(ctx, saved["q"], saved["K"], saved["V"], saved["o"], do, L, dq, dk, dv)
+    dq, dk, dv = attention_backward(ctx, saved["q"], saved["K"], saved["V"], saved["o"], do)
     dqkv = rope_backward(ctx, dq, dk, dv)
     dh, dwqkv = linear_backward(ctx, saved["h"], w["wqkv"], dqkv)
     dr1, dg1, _ = add_rmsnorm_backward(ctx, saved["r_mid"], w["attn_norm"], dh, eps, dr2)

@@ -80,18 +80,12 @@ struct ChunkLoader {
   u32x4_t kr[FP8 ? (KPT > 0 ? KPT : 1) : KBF];
   float ksc[KPT > 0 ? KPT : 1];
 
-  // V unit u -> (key pair, column chunk).  bf16: 16 key pairs x 4 chunks per
-  // wave, fp8: 32 key pairs x 2 chunks per wave; either way the transposed
-  // 4-byte LDS writes of one instruction fall on distinct banks or two-way.
+  // V unit u -> (key pair, column chunk): consecutive lanes take consecutive key
+  // pairs (32 per chunk), so the transposed 4-byte LDS writes of one instruction fall
+  // on distinct banks.
   __device__ static void vunit(int u, int& kp, int& ch) {
-    if constexpr (FP8) {
-      kp = u % 32;
-      ch = u / 32;
-    } else {
-      const int rest = u / 16;
-      ch = rest % CH;
-      kp = (rest / CH) * 16 + u % 16;
-    }
+    kp = u % 32;
+    ch = u / 32;
   }
 
   __device__ void issue(const AttnArgs& p, int blk, int g, int tid) {
@@ -227,7 +221,7 @@ __device__ __forceinline__ void load_chunk_sync(const AttnArgs& p, int blk, int 
     // V: two consecutive keys per unit, written transposed as 4-byte pairs
 #pragma unroll
     for (int u = tid; u < (CHUNK / 2) * CH; u += ATHREADS) {
-      const int kp = u / CH, ch = u % CH;
+      const int kp = u % (CHUNK / 2), ch = u / (CHUNK / 2);  // lanes along key pairs (banks)
       const int k0 = 2 * kp;
       u32x4_t a = *reinterpret_cast<const u32x4_t*>(vg + k0 * D + ch * 8);
       u32x4_t b = *reinterpret_cast<const u32x4_t*>(vg + (k0 + 1) * D + ch * 8);
@@ -267,7 +261,7 @@ __device__ __forceinline__ void load_chunk_sync(const AttnArgs& p, int blk, int 
     }
 #pragma unroll
     for (int u = tid; u < (CHUNK / 2) * CH16; u += ATHREADS) {
-      const int kp = u / CH16, c16 = u % CH16;
+      const int kp = u % (CHUNK / 2), c16 = u / (CHUNK / 2);  // lanes along key pairs (banks)
       const int k0 = 2 * kp;
       const u32x4_t ra = *reinterpret_cast<const u32x4_t*>(vg + k0 * D + c16 * 16);
       const u32x4_t rb = *reinterpret_cast<const u32x4_t*>(vg + (k0 + 1) * D + c16 * 16);

@@ -16,11 +16,17 @@
 //     dQ = (sum over 64-key chunks, ascending, of dS . K) / sqrt(d)
 //   pass 2 (per 128-key tile, one wave per 16 keys; rows ascending in 64-row chunks):
 //     dV = sum_rows P^T dO,  dK = (sum_rows dS^T Q) / sqrt(d)
+//     With a part buffer and many rows, the rows are cut into P <= 4 fixed parts (by
+//     row index, the same for every key tile); a tile's part writes its fp32 sums and a
+//     third kernel adds the parts in ascending order, so the first key tiles (which see
+//     every row) no longer set the pass's length.  One part gives the unsplit bits.
 // Products on v_mfma_f32_16x16x32_bf16 with P and dS rounded to bf16 as operands (as P
 // in the forward).  Each output element accumulates in one fixed order, so the result
 // is deterministic; rows of dQ do not depend on other sequences.
 #include "common.h"
 #include "kernels.h"
+
+#include <algorithm>
 
 namespace bci {
 
@@ -40,11 +46,13 @@ __device__ __forceinline__ int rswz(int row, int ch) {  // 16-byte chunk ch of a
 
 // 64 rows of D bf16 (row i from src_row(i), or zeros) -> rows (swizzled) and/or the
 // transpose [D][AB_TS]; a unit is two consecutive rows x 8 columns, so the transpose
-// is written as 4-byte pairs
+// is written as 4-byte pairs.  Consecutive lanes take consecutive row pairs (32 per
+// column chunk): their transposed writes land on consecutive banks (lanes along a row's
+// chunks would put 8 of them on each bank, the stride of 8 columns being 288 dwords).
 template <int D, int NT, typename RowPtr>
 __device__ __forceinline__ void stage(RowPtr src_row, int n_valid, u32x4_t* rows, bf16_t* tr, int tid) {
   for (int u = tid; u < (AB_CH / 2) * (D / 8); u += NT) {
-    const int ip = u / (D / 8), pc = u % (D / 8);
+    const int ip = u % (AB_CH / 2), pc = u / (AB_CH / 2);
     const int i0 = 2 * ip;
     u32x4_t va = u32x4_t{0, 0, 0, 0}, vb = va;
     if (i0 < n_valid) va = *reinterpret_cast<const u32x4_t*>(src_row(i0) + 8 * pc);
@@ -216,14 +224,14 @@ __global__ __launch_bounds__(AB_THREADS) void attn_bwd_dq_kernel(AttnBwdArgs a) 
 
 // ------------------------------------------------------------- pass 2: dK, dV
 template <int D>
-__global__ __launch_bounds__(AB_THREADS) void attn_bwd_dkdv_kernel(AttnBwdArgs a) {
+__global__ __launch_bounds__(AB_THREADS) void attn_bwd_dkdv_kernel(AttnBwdArgs a, int n_parts, int part_rows) {
   __shared__ __attribute__((aligned(16))) u32x4_t Qr[AB_CH * D / 8];
   __shared__ __attribute__((aligned(16))) u32x4_t Or[AB_CH * D / 8];   // dO rows
   __shared__ __attribute__((aligned(16))) bf16_t Qt[D * AB_TS];
   __shared__ __attribute__((aligned(16))) bf16_t Ot[D * AB_TS];        // dO^T
   __shared__ float lse_s[AB_CH], dsum_s[AB_CH];
   __shared__ int tok_s[AB_CH];
-  const int ktile = blockIdx.x, g = blockIdx.y;
+  const int ktile = blockIdx.x / n_parts, part = blockIdx.x % n_parts, g = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lg = lane >> 4, lc = lane & 15;
   const int group = a.nq / a.nkv;
@@ -247,8 +255,11 @@ __global__ __launch_bounds__(AB_THREADS) void attn_bwd_dkdv_kernel(AttnBwdArgs a
     dk[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     dv[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  const int n_rows = a.L * group;
-  const int row0 = (ktile * AB_TILE) * group;  // the first row whose token can see this tile
+  const int n_rows_all = a.L * group;
+  // rows of this (tile, part): from the first row whose token can see the tile, within the part
+  const int row0 = max((ktile * AB_TILE) * group, part * part_rows);
+  const int n_rows = min(n_rows_all, (part + 1) * part_rows);
+  if (row0 >= n_rows) return;  // the whole workgroup: no row of this part sees the tile
   for (int rb = row0; rb < n_rows; rb += AB_CH) {
     if (rb > row0) __syncthreads();
     const int nv = min(AB_CH, n_rows - rb);
@@ -303,7 +314,15 @@ __global__ __launch_bounds__(AB_THREADS) void attn_bwd_dkdv_kernel(AttnBwdArgs a
       }
     }
   }
-  if (key_ok) {
+  if (key_ok && n_parts > 1) {  // fp32 sums of this part
+    float* pk = a.part + (((size_t)part * a.L + key) * a.nkv + g) * D;
+    float* pv = pk + (size_t)AB_MAX_PARTS * a.L * a.nkv * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      *reinterpret_cast<f32x4_t*>(pk + dt * 16 + 4 * lg) = dk[dt];
+      *reinterpret_cast<f32x4_t*>(pv + dt * 16 + 4 * lg) = dv[dt];
+    }
+  } else if (key_ok) {
     bf16_t* dkr = a.dk + ((size_t)key * a.nkv + g) * D;
     bf16_t* dvr = a.dv + ((size_t)key * a.nkv + g) * D;
 #pragma unroll
@@ -316,13 +335,53 @@ __global__ __launch_bounds__(AB_THREADS) void attn_bwd_dkdv_kernel(AttnBwdArgs a
   }
 }
 
+// dK, dV = the parts' fp32 sums in ascending part order (only the parts that saw the
+// key's tile), then bf16 (dK times 1/sqrt(d) first, as in the unsplit pass).  One thread
+// per 4 consecutive elements of a (key, kv head) row.
+__global__ __launch_bounds__(256) void attn_bwd_part_sum_kernel(AttnBwdArgs a, int n_parts, int part_rows) {
+  const int group = a.nq / a.nkv;
+  const size_t n4 = (size_t)a.L * a.nkv * a.d / 4;
+  const size_t pstride = (size_t)a.L * a.nkv * a.d;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
+    const size_t e = 4 * i;
+    const int key = (int)(e / ((size_t)a.nkv * a.d));
+    const int p0 = ((key / AB_TILE) * AB_TILE * group) / part_rows;
+    f32x4_t sk = *reinterpret_cast<const f32x4_t*>(a.part + p0 * pstride + e);
+    f32x4_t sv = *reinterpret_cast<const f32x4_t*>(a.part + (AB_MAX_PARTS + p0) * pstride + e);
+    for (int p = p0 + 1; p < n_parts; ++p) {
+      const f32x4_t xk = *reinterpret_cast<const f32x4_t*>(a.part + p * pstride + e);
+      const f32x4_t xv = *reinterpret_cast<const f32x4_t*>(a.part + (AB_MAX_PARTS + p) * pstride + e);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sk[r] = sk[r] + xk[r];
+        sv[r] = sv[r] + xv[r];
+      }
+    }
+    *reinterpret_cast<u32x2_t*>(a.dk + e) =
+        u32x2_t{pack_f2bf2(sk[0] * a.scale, sk[1] * a.scale), pack_f2bf2(sk[2] * a.scale, sk[3] * a.scale)};
+    *reinterpret_cast<u32x2_t*>(a.dv + e) = u32x2_t{pack_f2bf2(sv[0], sv[1]), pack_f2bf2(sv[2], sv[3])};
+  }
+}
+
 template <int D>
 static void launch_ab(const AttnBwdArgs& a, hipStream_t s) {
   const int group = a.nq / a.nkv;
+  const int n_rows = a.L * group;
+  int n_parts = 1, part_rows = n_rows;
+  if (a.part) {
+    n_parts = std::min(AB_MAX_PARTS, std::max(1, n_rows / AB_PART_MIN_ROWS));
+    part_rows = ((n_rows + n_parts - 1) / n_parts + AB_CH - 1) / AB_CH * AB_CH;
+    n_parts = (n_rows + part_rows - 1) / part_rows;
+  }
   hipLaunchKernelGGL((attn_bwd_dq_kernel<D>), dim3((a.L * group + AB_TILE - 1) / AB_TILE, a.nkv),
                      dim3(AB_THREADS), 0, s, a);
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D>), dim3((a.L + AB_TILE - 1) / AB_TILE, a.nkv), dim3(AB_THREADS),
-                     0, s, a);
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D>), dim3((a.L + AB_TILE - 1) / AB_TILE * n_parts, a.nkv),
+                     dim3(AB_THREADS), 0, s, a, n_parts, part_rows);
+  if (n_parts > 1) {
+    const size_t n4 = (size_t)a.L * a.nkv * a.d / 4;
+    hipLaunchKernelGGL(attn_bwd_part_sum_kernel, dim3((unsigned)std::min<size_t>((n4 + 255) / 256, 8192)),
+                       dim3(256), 0, s, a, n_parts, part_rows);
+  }
 }
 
 hipError_t launch_attention_backward(const AttnBwdArgs& a, hipStream_t s) {

@@ -691,7 +691,7 @@ bci_status bci_op_logprob_backward_dz(bci_ctx* c, const float* z, const int32_t*
 
 bci_status bci_op_attention_backward(bci_ctx* c, const void* q, const void* k, const void* v,
                                      const void* o, const void* dout, int32_t L, void* dq, void* dk,
-                                     void* dv, void* stream) {
+                                     void* dv, float* workspace, void* stream) {
   if (!c) return BCI_E_INVALID;
   const auto& g = c->cfg;
   if (!q || !k || !v || !o || !dout || !dq || !dk || !dv || L < 0)
@@ -712,6 +712,9 @@ bci_status bci_op_attention_backward(bci_ctx* c, const void* q, const void* k, c
   a.dv = static_cast<uint16_t*>(dv);
   a.lse = c->ab_lse;
   a.dsum = c->ab_dsum;
+  if (workspace && !aligned16(workspace))
+    return fail(c, BCI_E_INVALID, "op_attention_backward: workspace must be 16-byte aligned");
+  a.part = workspace;
   a.L = L;
   a.nq = g.n_q_heads;
   a.nkv = g.n_kv_heads;

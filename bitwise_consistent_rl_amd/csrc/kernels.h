@@ -163,9 +163,14 @@ struct AttnBwdArgs {
   const uint16_t *q, *k, *v, *o, *dout;  // q, o, dout [L, nq, d]; k, v [L, nkv, d] bf16
   uint16_t *dq, *dk, *dv;                // bf16, same shapes
   float *lse, *dsum;                     // workspace [L, nq]: log2-sum-exp2, sum dO o
+  float* part;                           // null, or fp32 [AB_MAX_PARTS][L][nkv][d] x 2 (dK, dV)
   int L, nq, nkv, d;
   float scale, scale_log2;               // 1/sqrt(d), log2(e)/sqrt(d)
 };
+// the dK/dV pass splits each key tile's rows into at most AB_MAX_PARTS fixed parts of
+// >= AB_PART_MIN_ROWS rows (when a part buffer is given), summed in part order
+constexpr int AB_MAX_PARTS = 4;
+constexpr int AB_PART_MIN_ROWS = 2048;
 hipError_t launch_attention_backward(const AttnBwdArgs& a, hipStream_t s);
 
 // ---- moe.hip

@@ -420,11 +420,15 @@ bci_status bci_op_rope_backward(bci_ctx* ctx, const void* dq, const void* dk, co
  * summed over the query heads of each kv head; dq, dk, dv bf16, same shapes.  Each
  * element accumulates in one fixed order (dq over 64-key chunks ascending, dk and dv
  * over 64-row chunks ascending; no atomics), so the result is deterministic.  The row
- * statistics (log-sum-exp, D) are recomputed into the workspace.  L <= max_tokens_per_call;
- * all tensors 16-byte aligned. */
+ * statistics (log-sum-exp, D) are recomputed into the context's workspace.  workspace:
+ * NULL, or fp32 [2 * 4 * L * nkv * d] owned by the caller, 16-byte aligned: with it and
+ * at least 4096 (token, query head) rows per kv head, the dK/dV pass cuts the rows into
+ * at most 4 fixed parts (by row index), sums each part in fp32 and adds the parts in
+ * ascending order -- deterministic, balanced across the causal key tiles; different bits
+ * from the unsplit order.  L <= max_tokens_per_call; all tensors 16-byte aligned. */
 bci_status bci_op_attention_backward(bci_ctx* ctx, const void* q, const void* k, const void* v,
                                      const void* o, const void* dout, int32_t L, void* dq, void* dk,
-                                     void* dv, void* stream);
+                                     void* dv, float* workspace, void* stream);
 
 /* ---- state-space layer (Mamba-2-style), chunked ---------------------------------
  * Porting the method to Nemotron-3.5 meant recursive arithmetic in which decode

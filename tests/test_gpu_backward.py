@@ -147,28 +147,36 @@ def test_logprob_backward(ctx, M, V):
 
 
 @pytest.mark.parametrize("L,nq,nkv,d,kv", [(37, 4, 2, 64, "bf16"), (300, 16, 8, 128, "bf16"),
-                                           (200, 32, 4, 128, "fp8"), (129, 16, 8, 128, "fp8")])
+                                           (200, 32, 4, 128, "fp8"), (129, 16, 8, 128, "fp8"),
+                                           (1100, 8, 2, 128, "bf16"), (1100, 4, 1, 64, "fp8")])
 def test_attention_backward(L, nq, nkv, d, kv):
     """The GPU's forward (RoPE + KV write, FP8 round trip for an FP8 cache, attention) then
     the backward over the keys and values it attended to; the oracle rotates, round-trips,
-    attends and differentiates the same seeded rows itself."""
+    attends and differentiates the same seeded rows itself.  With the part buffer given:
+    at L = 1100 (4400 rows per kv head) the dK/dV rows are cut into two parts, within the
+    same tolerance; below 4096 rows the part buffer changes no bit."""
     from test_gpu_ops import _attention_run
     a = abi()
     qkv = synth.normal_bf16((L, (nq + 2 * nkv) * d), index=70)
     o, q, kvs = _attention_run(nq, nkv, d, kv, 2048, [L], qkv, [[(0, 0, L)]])
     K, Vv = kvs[0]
     dout = synth.normal_bf16((L, nq * d), index=71).cuda()
-    h = make_ctx(hidden=512, nq=nq, nkv=nkv, d=d, inter=512, vocab=4096, kv=kv, max_tokens=1024)
+    h = make_ctx(hidden=512, nq=nq, nkv=nkv, d=d, inter=512, vocab=4096, kv=kv, max_tokens=2048)
     try:
         outs = []
-        for _ in range(2):
+        ws = torch.full((2 * 4 * L * nkv * d,), float("nan"), device="cuda")
+        for w in (ws, ws, None):
             dq = torch.empty(L, nq * d, dtype=BF, device="cuda")
             dk = torch.empty(L, nkv * d, dtype=BF, device="cuda")
             dv = torch.empty(L, nkv * d, dtype=BF, device="cuda")
-            a.bci_op_attention_backward(h, q, K, Vv, o, dout, L, dq, dk, dv)
+            a.bci_op_attention_backward(h, q, K, Vv, o, dout, L, dq, dk, dv, w)
             torch.cuda.synchronize()
             outs.append((dq, dk, dv))
-        assert all(same_bits(x, y) for x, y in zip(*outs))       # deterministic
+        assert all(same_bits(x, y) for x, y in zip(outs[0], outs[1]))       # deterministic
+        split = L * (nq // nkv) >= 4096
+        assert same_bits(outs[0][0], outs[2][0])                            # dq never split
+        if not split:
+            assert all(same_bits(x, y) for x, y in zip(outs[0], outs[2]))
     finally:
         torch.cuda.synchronize()
         a.bci_destroy(h)
@@ -181,10 +189,10 @@ def test_attention_backward(L, nq, nkv, d, kv):
         ko, vo = ops.kv_roundtrip(ko), ops.kv_roundtrip(vo)
     oo = ops.causal_gqa_attention(qo, ko, vo, pos)
     rdq, rdk, rdv = ob.attention_backward(qo, ko, vo, oo, f64(dout).reshape(L, nq, d))
-    dq, dk, dv = outs[0]
-    close(f64(dq).reshape(L, nq, d), rdq, f"dq L={L} {kv}")
-    close(f64(dk).reshape(L, nkv, d), rdk, f"dk L={L} {kv}")
-    close(f64(dv).reshape(L, nkv, d), rdv, f"dv L={L} {kv}")
+    for tag, (dq, dk, dv) in (("parts", outs[0]), ("unsplit", outs[2])):
+        close(f64(dq).reshape(L, nq, d), rdq, f"dq L={L} {kv} {tag}")
+        close(f64(dk).reshape(L, nkv, d), rdk, f"dk L={L} {kv} {tag}")
+        close(f64(dv).reshape(L, nkv, d), rdv, f"dv L={L} {kv} {tag}")
 
 
 def _layer_ctx(L, H, nq, nkv, d, inter, kv, pos0=0):
