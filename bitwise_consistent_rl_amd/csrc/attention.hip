@@ -46,7 +46,8 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int ATHREADS = 256;
 constexpr int CHUNK = 64;
-constexpr int VT_STRIDE = CHUNK + 8;  // bf16 elements per V^T row (pad: conflict-free reads)
+constexpr int VT_STRIDE = CHUNK + 4;  // bf16 per V^T row: 34 dwords, so the 8-byte fragment
+                                      // reads of 16 rows and the pair writes spread over the banks
 
 template <int D>
 __device__ __forceinline__ int kswz(int key, int ch) {

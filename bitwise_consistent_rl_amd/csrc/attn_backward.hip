@@ -34,7 +34,7 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int AB_CH = 64;             // keys per chunk / rows per chunk
-constexpr int AB_TS = AB_CH + 8;      // stride of transposed tiles (bf16)
+constexpr int AB_TS = AB_CH + 4;      // stride of transposed tiles (bf16): 34 dwords, few bank conflicts
 
 template <int D>
 __device__ __forceinline__ int rswz(int row, int ch) {  // 16-byte chunk ch of a D-wide row
