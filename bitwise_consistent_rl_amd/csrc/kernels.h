@@ -134,9 +134,7 @@ struct SsdArgs {
   uint16_t *xb, *Bb;           // chunk buffers [slots][64][heads][64], [slots][64][groups][N]
   float* dtb;                  // [slots][64][heads]
   float* state;                // [slots][heads][64][N] fp32
-  float* cstate;               // [max_done][heads][64][N] fp32 workspace (chunk states)
   uint16_t* hprev;             // [max_done][heads][64][N] bf16 (state before each chunk)
-  float* lend;                 // [max_done][heads]
   const int32_t* seqs;         // [n_seqs][6]: cu, pos0, q_len, slot, first done index, n done
   const int32_t* inst;         // [n_inst][6]: seq, chunk, first pos, last pos, done index or -1, 0
   const int32_t* done;         // [n_done]: instance of each completed chunk

@@ -21,10 +21,10 @@
 // depends only on its own row and column, so a decode step -- a tile holding the
 // one new position -- gives the prefill's bits.
 //
-// Per call: chunk_state (chunks that complete in the call), state_pass (per
-// sequence and head, chunk order; hands chunk_out each chunk's state-before in bf16,
-// exactly the rounding chunk_out applies to the slot's fp32 state), chunk_out
-// (every position of the call), and
+// Per call: state_walk (per sequence and head, the chunks that complete in the call
+// in order: each chunk's state S on MFMA, the running state updated in registers, and
+// each chunk's state-before handed to chunk_out in bf16, exactly the rounding chunk_out
+// applies to the slot's fp32 state), chunk_out (every position of the call), and
 // chunk_append (the positions of an unfinished last chunk into the slot's chunk
 // buffer, which the next call reads back).
 #include "common.h"
@@ -77,108 +77,118 @@ __device__ __forceinline__ int bswz(int row, int ch) {  // 16-byte chunks of an 
   return row * (N / 8) + (ch ^ (row & (N / 8 - 1)));
 }
 
-// ------------------------------------------------------------- chunk state
-// One workgroup (4 waves) per (completed chunk, head): S[p][n] = sum_j x_j[p] bw_j[n],
-// bw_j = bf(B_j 2^{L_63 - L_j} dt_j).  Also writes L_63 (the chunk's total decay).
+// ------------------------------------------------------------- state walk
+// One workgroup (4 waves) per (sequence, head) walks the call's completed chunks in
+// order, the state H held in registers in the MFMA accumulator layout (wave w, lane l:
+// H[16w + 4(l/16) + r][16 nt + l%16]).  For each chunk: S = sum_j x_j (outer) bw_j on
+// MFMA (x^T and the weighted B^T staged in LDS), hprev = bf(H) (the state before the
+// chunk, for chunk_out), then H = 2^{L_63} H + S in fp32; no chunk state crosses HBM.
+// The next chunk's dt, x and B rows are loaded into registers while the current chunk
+// multiplies.  The final H goes back to the slot.
 template <int N>
-__global__ __launch_bounds__(256) void ssd_chunk_state_kernel(SsdArgs a) {
+__global__ __launch_bounds__(256) void ssd_state_walk_kernel(SsdArgs a) {
+  // staging units: two consecutive positions x 8 columns (lanes along the position
+  // pairs, so the transposed 4-byte writes fall on consecutive banks)
+  constexpr int NX = (SQ / 2) * (SP / 8) / 256;  // x units per thread per chunk
+  constexpr int NB = (SQ / 2) * (N / 8) / 256;   // B units per thread per chunk
   __shared__ __attribute__((aligned(16))) bf16_t Xt[SP * XT_STRIDE];   // x^T [p][j]
   __shared__ __attribute__((aligned(16))) bf16_t Bt[N * XT_STRIDE];    // bw^T [n][j]
   __shared__ float wj[SQ];
-  const int k = blockIdx.x, h = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lg = lane >> 4, lc = lane & 15;
-  const int inst = a.done[k];
-  const int s = a.inst[6 * inst + 0], c = a.inst[6 * inst + 1];
-  const int g = h / (a.heads / a.groups);
-  const float A2 = a.A[h] * LOG2E;
-
-  if (wave == 0) {
-    const PosSrc r = pos_src(a, s, c * SQ + lane);
-    const float dtj = dt_of(a, r, h);
-    const float L = chunk_scan(A2 * dtj, lane);
-    const float Lend = __shfl(L, SQ - 1, WAVE);
-    wj[lane] = fexp2(Lend - L) * dtj;
-    if (lane == 0) a.lend[(size_t)k * a.heads + h] = Lend;
-  }
-  __syncthreads();
-  // x^T and bw^T into LDS: thread -> (position j, 8-wide column piece)
-  for (int u = tid; u < SQ * (SP / 8); u += 256) {
-    const int j = u / (SP / 8), pc = u % (SP / 8);
-    const PosSrc r = pos_src(a, s, c * SQ + j);
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(x_row(a, r, h) + 8 * pc);
-    const bf16_t* e = reinterpret_cast<const bf16_t*>(&v);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) Xt[(8 * pc + i) * XT_STRIDE + j] = e[i];
-  }
-  for (int u = tid; u < SQ * (N / 8); u += 256) {
-    const int j = u / (N / 8), pc = u % (N / 8);
-    const PosSrc r = pos_src(a, s, c * SQ + j);
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(b_row(a, r, g) + 8 * pc);
-    const bf16_t* e = reinterpret_cast<const bf16_t*>(&v);
-    const float w = wj[j];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) Bt[(8 * pc + i) * XT_STRIDE + j] = f2bf(bf2f(e[i]) * w);
-  }
-  __syncthreads();
-  // wave w: rows p = 16w .. 16w+15; all N columns; contraction over the 64 positions
-  float* out = a.cstate + (((size_t)k * a.heads + h) * SP) * N;
-  const bf16_t* xr = Xt + (16 * wave + lc) * XT_STRIDE;
-#pragma unroll
-  for (int nt = 0; nt < N / 16; ++nt) {
-    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const bf16_t* br = Bt + (16 * nt + lc) * XT_STRIDE;
-#pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-      const bf16x8_t af = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(xr + 32 * k2 + 8 * lg));
-      const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(br + 32 * k2 + 8 * lg));
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr, acc, 0, 0, 0);
-    }
-    // acc[r] = S[p = 16w + 4lg + r][n = 16nt + lc]
-#pragma unroll
-    for (int r = 0; r < 4; ++r) out[(size_t)(16 * wave + 4 * lg + r) * N + 16 * nt + lc] = acc[r];
-  }
-}
-
-// ------------------------------------------------------------- state pass
-// Per (sequence, head, 1024-element block of the state): walk the call's completed
-// chunks in order; each chunk's state-before goes to hprev (rounded to bf16, the
-// form chunk_out multiplies with) and the running state becomes 2^{L_63} H + S.  The
-// final state goes back to the slot.  A sequence whose first chunk of the call is
-// chunk 0 starts from zero.  The chunk states of the next four chunks are loaded
-// before the chain uses them (they do not depend on it).
-constexpr int SP_EPB = 1024;  // state elements per workgroup (256 threads x 4)
-__global__ __launch_bounds__(256) void ssd_state_pass_kernel(SsdArgs a) {
+  __shared__ float ek_s;
   const int s = blockIdx.x, h = blockIdx.y;
   const int* sq = a.seqs + 6 * s;
   const int slot = sq[3], k0 = sq[4], nd = sq[5];
-  if (nd == 0) return;
+  if (nd == 0) return;  // the whole workgroup
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lg = lane >> 4, lc = lane & 15;
+  const int g = h / (a.heads / a.groups);
+  const float A2 = a.A[h] * LOG2E;
+  const size_t per = (size_t)SP * N;
+  float* st = a.state + ((size_t)slot * a.heads + h) * per;
   const int c_first = a.inst[6 * a.done[k0] + 1];
-  const size_t per = (size_t)SP * a.N;
-  const size_t e = (size_t)blockIdx.z * SP_EPB + 4 * threadIdx.x;
-  f32x4_t* st = reinterpret_cast<f32x4_t*>(a.state + ((size_t)slot * a.heads + h) * per + e);
-  f32x4_t H = c_first == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : *st;
-  for (int k = k0; k < k0 + nd; k += 4) {
-    f32x4_t S[4];
-    float ek[4];
+  f32x4_t H[N / 16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (k + i < k0 + nd) {
-        S[i] = *reinterpret_cast<const f32x4_t*>(a.cstate + ((size_t)(k + i) * a.heads + h) * per + e);
-        ek[i] = fexp2(a.lend[(size_t)(k + i) * a.heads + h]);
-      }
+  for (int nt = 0; nt < N / 16; ++nt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      H[nt][r] = c_first == 0 ? 0.0f : st[(size_t)(16 * wave + 4 * lg + r) * N + 16 * nt + lc];
+
+  // a chunk's inputs in registers: dt of position `lane` (wave 0), x and B pieces
+  float rdt = 0.0f;
+  u32x4_t rx[NX][2], rb[NB][2];
+  auto load = [&](int c) {
+    if (wave == 0) rdt = dt_of(a, pos_src(a, s, c * SQ + lane), h);
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+      const int u = i * 256 + tid, j = 2 * (u % (SQ / 2)), pc = u / (SQ / 2);
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        rx[i][q] = *reinterpret_cast<const u32x4_t*>(x_row(a, pos_src(a, s, c * SQ + j + q), h) + 8 * pc);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (k + i < k0 + nd) {
-        *reinterpret_cast<u32x2_t*>(a.hprev + ((size_t)(k + i) * a.heads + h) * per + e) =
-            u32x2_t{pack_f2bf2(H[0], H[1]), pack_f2bf2(H[2], H[3])};
+    for (int i = 0; i < NB; ++i) {
+      const int u = i * 256 + tid, j = 2 * (u % (SQ / 2)), pc = u / (SQ / 2);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) H[j] = ek[i] * H[j] + S[i][j];
+      for (int q = 0; q < 2; ++q)
+        rb[i][q] = *reinterpret_cast<const u32x4_t*>(b_row(a, pos_src(a, s, c * SQ + j + q), g) + 8 * pc);
+    }
+  };
+  load(c_first);
+
+  for (int k = k0; k < k0 + nd; ++k) {
+    if (k > k0) __syncthreads();  // the previous chunk's LDS reads are done
+    if (wave == 0) {
+      const float L = chunk_scan(A2 * rdt, lane);
+      const float Lend = __shfl(L, SQ - 1, WAVE);
+      wj[lane] = fexp2(Lend - L) * rdt;
+      if (lane == 0) ek_s = fexp2(Lend);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+      const int u = i * 256 + tid, j = 2 * (u % (SQ / 2)), pc = u / (SQ / 2);
+      const bf16_t* ea = reinterpret_cast<const bf16_t*>(&rx[i][0]);
+      const bf16_t* eb = reinterpret_cast<const bf16_t*>(&rx[i][1]);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) *reinterpret_cast<uint32_t*>(Xt + (8 * pc + q) * XT_STRIDE + j) = pack_bf2(ea[q], eb[q]);
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int u = i * 256 + tid, j = 2 * (u % (SQ / 2)), pc = u / (SQ / 2);
+      const bf16_t* ea = reinterpret_cast<const bf16_t*>(&rb[i][0]);
+      const bf16_t* eb = reinterpret_cast<const bf16_t*>(&rb[i][1]);
+      const float wa = wj[j], wb = wj[j + 1];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        *reinterpret_cast<uint32_t*>(Bt + (8 * pc + q) * XT_STRIDE + j) =
+            pack_bf2(f2bf(bf2f(ea[q]) * wa), f2bf(bf2f(eb[q]) * wb));
+    }
+    __syncthreads();
+    if (k + 1 < k0 + nd) load(a.inst[6 * a.done[k + 1] + 1]);  // in flight during the products
+    const float ek = ek_s;
+    bf16_t* hp = a.hprev + ((size_t)k * a.heads + h) * per;
+    const bf16_t* xr = Xt + (16 * wave + lc) * XT_STRIDE;
+#pragma unroll
+    for (int nt = 0; nt < N / 16; ++nt) {
+      f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const bf16_t* br = Bt + (16 * nt + lc) * XT_STRIDE;
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const bf16x8_t af = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(xr + 32 * k2 + 8 * lg));
+        const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(br + 32 * k2 + 8 * lg));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr, acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        hp[(size_t)(16 * wave + 4 * lg + r) * N + 16 * nt + lc] = f2bf(H[nt][r]);
+        H[nt][r] = ek * H[nt][r] + acc[r];
       }
     }
   }
-  *st = H;
+#pragma unroll
+  for (int nt = 0; nt < N / 16; ++nt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) st[(size_t)(16 * wave + 4 * lg + r) * N + 16 * nt + lc] = H[nt][r];
 }
 
 // ------------------------------------------------------------- chunk outputs
@@ -215,13 +225,17 @@ __global__ __launch_bounds__(256) void ssd_chunk_out_kernel(SsdArgs a) {
     if (j < navail) v = *reinterpret_cast<const u32x4_t*>(b_row(a, pos_src(a, s, c * SQ + j), g) + 8 * pc);
     Bc[bswz<N>(j, pc)] = v;
   }
-  for (int u = tid; u < SQ * (SP / 8); u += 256) {
-    const int j = u / (SP / 8), pc = u % (SP / 8);
-    u32x4_t v = u32x4_t{0, 0, 0, 0};
-    if (j < navail) v = *reinterpret_cast<const u32x4_t*>(x_row(a, pos_src(a, s, c * SQ + j), h) + 8 * pc);
-    const bf16_t* e = reinterpret_cast<const bf16_t*>(&v);
+  // x^T: a unit is two consecutive positions x 8 columns, written as 4-byte pairs by
+  // lanes along the position pairs (consecutive banks)
+  for (int u = tid; u < (SQ / 2) * (SP / 8); u += 256) {
+    const int jp = u % (SQ / 2), pc = u / (SQ / 2), j = 2 * jp;
+    u32x4_t va = u32x4_t{0, 0, 0, 0}, vb = va;
+    if (j < navail) va = *reinterpret_cast<const u32x4_t*>(x_row(a, pos_src(a, s, c * SQ + j), h) + 8 * pc);
+    if (j + 1 < navail) vb = *reinterpret_cast<const u32x4_t*>(x_row(a, pos_src(a, s, c * SQ + j + 1), h) + 8 * pc);
+    const bf16_t* ea = reinterpret_cast<const bf16_t*>(&va);
+    const bf16_t* eb = reinterpret_cast<const bf16_t*>(&vb);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) Xt[(8 * pc + i) * XT_STRIDE + j] = e[i];
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<uint32_t*>(Xt + (8 * pc + i) * XT_STRIDE + j) = pack_bf2(ea[i], eb[i]);
   }
   // the state before the chunk, rounded to bf16: zero for chunk 0, the state pass's
   // bf16 copy for a chunk completed in this call, the slot's state otherwise
@@ -358,11 +372,8 @@ __global__ __launch_bounds__(256) void ssd_chunk_append_kernel(SsdArgs a) {
 
 template <int N>
 static void launch_ssd_t(const SsdArgs& a, hipStream_t st) {
-  if (a.n_done > 0) {
-    hipLaunchKernelGGL((ssd_chunk_state_kernel<N>), dim3(a.n_done, a.heads), dim3(256), 0, st, a);
-    hipLaunchKernelGGL(ssd_state_pass_kernel, dim3(a.n_seqs, a.heads, SP * N / SP_EPB), dim3(256), 0,
-                       st, a);
-  }
+  if (a.n_done > 0)
+    hipLaunchKernelGGL((ssd_state_walk_kernel<N>), dim3(a.n_seqs, a.heads), dim3(256), 0, st, a);
   hipLaunchKernelGGL((ssd_chunk_out_kernel<N>), dim3(a.n_inst, a.heads), dim3(256), 0, st, a);
   hipLaunchKernelGGL(ssd_chunk_append_kernel, dim3(a.n_seqs, SQ), dim3(256), 0, st, a);
 }

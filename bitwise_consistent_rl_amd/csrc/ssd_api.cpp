@@ -25,7 +25,6 @@ struct bci_ssd {
   std::string err;
   int max_inst = 0, max_done = 0;
   void* ws = nullptr;
-  float *cstate = nullptr, *lend = nullptr;
   uint16_t* hprev = nullptr;
   int32_t* meta = nullptr;
   size_t meta_words = 0, o_seq = 0, o_inst = 0, o_done = 0;
@@ -83,18 +82,14 @@ bci_status bci_ssd_create(const bci_ssd_config* cfg, int32_t device, bci_ssd** o
   c->o_inst = c->o_seq + 6 * (size_t)g.max_seqs_per_call;
   c->o_done = c->o_inst + 6 * (size_t)c->max_inst;
   c->meta_words = c->o_done + (size_t)c->max_done;
-  const size_t cs = (size_t)c->max_done * slot_state_bytes(g);
-  const size_t hp = cs / 2;
-  const size_t le = ((size_t)c->max_done * g.n_heads * 4 + 255) / 256 * 256;
+  const size_t hp = ((size_t)c->max_done * slot_state_bytes(g) / 2 + 255) / 256 * 256;  // bf16 states
   const size_t mw = (c->meta_words * 4 + 255) / 256 * 256;
-  if (hipMalloc(&c->ws, cs + hp + le + mw) != hipSuccess) {
+  if (hipMalloc(&c->ws, hp + mw) != hipSuccess) {
     delete c;
     return BCI_E_WORKSPACE;
   }
-  c->cstate = static_cast<float*>(c->ws);
-  c->hprev = reinterpret_cast<uint16_t*>(static_cast<char*>(c->ws) + cs);
-  c->lend = reinterpret_cast<float*>(static_cast<char*>(c->ws) + cs + hp);
-  c->meta = reinterpret_cast<int32_t*>(static_cast<char*>(c->ws) + cs + hp + le);
+  c->hprev = static_cast<uint16_t*>(c->ws);
+  c->meta = reinterpret_cast<int32_t*>(static_cast<char*>(c->ws) + hp);
   if (hipHostMalloc((void**)&c->stage, c->meta_words * 4, hipHostMallocDefault) != hipSuccess ||
       hipEventCreateWithFlags(&c->stage_ev, hipEventDisableTiming) != hipSuccess) {
     bci_ssd_destroy(c);
@@ -214,9 +209,7 @@ bci_status bci_ssd_forward(bci_ssd* c, const void* x, const float* dt, const flo
   a.dtb = reinterpret_cast<float*>(cb + (size_t)n_slots * SSD_CHUNK *
                                             ((size_t)g.n_heads * SSD_HEAD_DIM * 2 + (size_t)g.n_groups * g.d_state * 2));
   a.state = state;
-  a.cstate = c->cstate;
   a.hprev = c->hprev;
-  a.lend = c->lend;
   a.seqs = c->meta + c->o_seq;
   a.inst = c->meta + c->o_inst;
   a.done = c->meta + c->o_done;
