@@ -103,7 +103,11 @@ def cpu_baseline(cfg, weights, seqs, budget_s: float = 12.0):
 def micro(args, cfg):
     """The gate_up GEMM alone (M = 16384 tokens of one packed call, N = 2 x 6144,
     K = 2048, SiLU*up epilogue), then a plain 1 GiB device copy whose bytes are known,
-    for calibrating the HBM byte counters."""
+    for calibrating the HBM byte counters.  --micro-data zeros runs it on all-zero
+    operands (same instructions and cycles, far less switching power, so the clock
+    stays near its maximum); --micro gate_up_hipblaslt times the vendor library's GEMM
+    (torch.matmul, plain bf16 output, not batch-invariant) on the same operands as a
+    reference rate.  With many --steps the rate is the steady, power-limited one."""
     import torch
     import synth
     from bitwise_consistent_rl_amd import _abi as abi
@@ -118,16 +122,24 @@ def micro(args, cfg):
     ctx = abi.bci_create(mc, 0)
     a, w = synth.gemm_inputs(M, N, K, index=90)
     a, w = a.cuda(), w.cuda()
+    if args.micro_data == "zeros":
+        a.zero_()
+        w.zero_()
     c = torch.empty(M, N // 2, dtype=torch.bfloat16, device="cuda")
+    if args.micro == "gate_up_hipblaslt":
+        cf = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        run = lambda: torch.matmul(a, w.t(), out=cf)  # noqa: E731
+    else:
+        run = lambda: abi.bci_op_gemm_bf16(ctx, a, w, c, M, N, K, abi.BCI_EPI_SILU_MUL)  # noqa: E731
     src = torch.empty(1 << 29, dtype=torch.int16, device="cuda")   # 1 GiB
     dst = torch.empty_like(src)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for _ in range(2):
-        abi.bci_op_gemm_bf16(ctx, a, w, c, M, N, K, abi.BCI_EPI_SILU_MUL)
+        run()
     torch.cuda.synchronize()
     start.record()
     for _ in range(args.steps):
-        abi.bci_op_gemm_bf16(ctx, a, w, c, M, N, K, abi.BCI_EPI_SILU_MUL)
+        run()
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
@@ -136,11 +148,62 @@ def micro(args, cfg):
         dst.copy_(src)
     torch.cuda.synchronize()
     abi.bci_destroy(ctx)
-    print(json.dumps({"micro": "gate_up", "M": M, "N": N, "K": K, "avg_ms": round(ms, 4),
+    print(json.dumps({"micro": args.micro, "data": args.micro_data, "M": M, "N": N, "K": K,
+                      "avg_ms": round(ms, 4),
                       "tflops": round(flops / ms / 1e9, 1),
                       "frac": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
                       "algorithmic_bytes": (M * K + N * K + M * N // 2) * 2,
                       "copy_bytes": 2 * (1 << 30)}), flush=True)
+
+
+def decode_bench(args, cfg):
+    """Decode steps alone, for a kernel trace: sequences of the Qwen3-shaped workload are
+    prefilled to their response midpoint, then `--steps` decode steps (one new token and
+    its logprob per sequence) run at B = 1 and B = 64, each timed with HIP events."""
+    import numpy as np
+    import torch
+    import synth
+    from bitwise_consistent_rl_amd import _abi as abi
+    from bitwise_consistent_rl_amd import engine
+    weights = synth.make_weights(cfg)
+    seqs = synth.rl_sequences(cfg, n_prompts=8, n_responses=8)
+    m = engine.Model(cfg, weights, max_tokens=8192, max_seqs=128, max_scored=8192,
+                     max_position=1024, seg_keys=QWEN_SEG_KEYS)
+    cache = m.new_cache(64 * 11 + 16)
+    m.bind_cache(cache)
+    steps = {}
+    for B in (1, 64):
+        sub = seqs[:B]
+        mids = [s.prompt_len + s.n_scored // 2 for s in sub]
+        blocks = [list(range(i * 11, i * 11 + 11)) for i in range(B)]
+        for g0 in range(0, B, 16):                       # prefill, <= 16 sequences per call
+            g = range(g0, min(B, g0 + 16))
+            engine.run_call(m, engine.CallPlan(
+                np.concatenate([sub[i].tokens[:mids[i]] for i in g]).astype(np.int32),
+                np.concatenate([[0], np.cumsum([mids[i] for i in g])]).astype(np.int32),
+                np.zeros(len(g), np.int32), np.array([blocks[i] for i in g], np.int32),
+                np.zeros(0, np.int32), np.zeros(0, np.int32), []))
+        abi.bci_set_batch(m.ctx, np.array([s.tokens[mid] for s, mid in zip(sub, mids)], np.int32),
+                          np.arange(B + 1, dtype=np.int32), np.array(mids, np.int32),
+                          np.array(blocks, np.int32), np.arange(B, dtype=np.int32),
+                          np.array([s.tokens[mid + 1] for s, mid in zip(sub, mids)], np.int32))
+        out = torch.empty(B, dtype=torch.float32, device="cuda")
+        for _ in range(3):
+            abi.bci_forward_logprobs(m.ctx, out)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            abi.bci_forward_logprobs(m.ctx, out)
+        e1.record()
+        torch.cuda.synchronize()
+        steps[str(B)] = round(e0.elapsed_time(e1) / args.steps, 3)
+        log(f"decode B = {B}: {steps[str(B)]} ms per step")
+    m.close()
+    weight_bytes = sum(v.numel() for v in weights.values()) * 2
+    print(json.dumps({"workload": "qwen3-1.7b-shaped decode steps", "decode_step_ms": steps,
+                      "steps": args.steps,
+                      "weight_streaming_floor_ms": round(weight_bytes / (PEAK_HBM_GBS * 1e6), 3)}),
+          flush=True)
 
 
 def rollout_bench(args, cfg):
@@ -751,10 +814,11 @@ def main():
     ap.add_argument("--max-tokens", type=int, default=16384)
     ap.add_argument("--accept-seqs", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--micro", choices=["gate_up"], default=None,
+    ap.add_argument("--micro", choices=["gate_up", "gate_up_hipblaslt"], default=None,
                     help="time one kernel alone at the workload's shape (for counter runs)")
-    ap.add_argument("--workload", choices=["recompute", "longctx", "rollout", "lmhead", "moe", "sparse", "ssd",
-                             "backward"],
+    ap.add_argument("--micro-data", choices=["random", "zeros"], default="random")
+    ap.add_argument("--workload", choices=["recompute", "longctx", "rollout", "decode", "lmhead", "moe",
+                                           "sparse", "ssd", "backward"],
                     default="recompute",
                     help="longctx: FP8-KV long-context attention (decode steps, chunked prefill); "
                          "rollout: continuous-batching decode, invariant vs non-invariant mode; "
@@ -781,6 +845,8 @@ def main():
         return longctx(args)
     if args.workload == "rollout":
         return rollout_bench(args, cfg)
+    if args.workload == "decode":
+        return decode_bench(args, cfg)
     if args.workload == "lmhead":
         return lmhead_bench(args)
     if args.workload == "sparse":

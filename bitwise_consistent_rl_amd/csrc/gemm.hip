@@ -402,14 +402,14 @@ __global__ __launch_bounds__((TBM >= 64 ? TBM / 64 : 1) * NWN * 64, 1) void gemm
 // over ascending 32-wide K steps, the same epilogue -- with a different
 // assignment of output elements: a one-wave workgroup owns 16 output columns
 // (16 gate + 16 up for SiLU) and all ceil(M/16) row blocks, so N/16 waves
-// stream the weights instead of N/256 workgroups.  K is cut into 128-wide
-// stages; each stage's W rows and A rows are copied by global_load_lds into a
-// private LDS ring of D stages, so D stages of loads are in flight while the
-// MFMAs consume the oldest.  A single wave needs no barrier, only vmcnt.
-constexpr int SK_KC = 128;                  // K per stage
-constexpr int SK_ROWCH = SK_KC / 8;         // 16-byte chunks per row per stage
+// stream the weights instead of N/256 workgroups.  K is cut into stages of
+// SK_KC (512 for a single row block when K allows); each stage's W rows and A
+// rows are copied by global_load_lds into a private LDS ring of D stages, so D
+// stages of loads are in flight while the MFMAs consume the oldest.  A single
+// wave needs no barrier, only vmcnt.  The stage width and the A rows a stage
+// holds change which loads run, never the MFMA chain of an output element.
+constexpr int SK_KC = 128;                  // K per stage (default)
 
-__device__ __forceinline__ int skswz(int row, int ch) { return row * SK_ROWCH + (ch ^ (row & 15)); }
 
 // s_waitcnt immediate for "vmcnt <= v" (gfx9 encoding; lgkmcnt/expcnt unconstrained)
 template <int V>
@@ -421,16 +421,26 @@ __device__ __forceinline__ void wait_vmcnt() {
 // GROUPED (the MoE expert GEMMs with few rows per expert): blockIdx.y is an entry of
 // the device tile list (group, first row, rows <= 16), W is the group's slice, A rows
 // are gathered through a_rows when GATHER.
-template <int KIND, int MT, bool GATHER = false, bool GROUPED = false>
+// AR: A rows a stage holds.  16 * MT, or 4 when M <= 4 (decode): the MFMA's rows past
+// AR read row AR - 1 (their outputs are never stored), so a stage copies 4 A rows
+// instead of 16.  KC: K per stage (SK_KC, or 512 for one row block: each W row is then
+// read in 1 KiB runs rather than 256-byte ones).
+template <int KIND, int MT, bool GATHER = false, bool GROUPED = false, int AR = 16 * MT, int KC = SK_KC>
 __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmArgs p) {
+  static_assert(AR == 16 * MT || (MT == 1 && AR == 4), "A rows per stage");
+  constexpr int ROWCH = KC / 8;                         // 16-byte chunks per row per stage
   constexpr int NB = (KIND == K_SILU) ? 2 : 1;          // weight streams (gate, up)
-  constexpr int WCH = NB * 16 * SK_ROWCH;               // W chunks per stage
-  constexpr int SCH = WCH + MT * 16 * SK_ROWCH;         // chunks per stage
+  constexpr int WCH = NB * 16 * ROWCH;                  // W chunks per stage
+  constexpr int SCH = WCH + AR * ROWCH;                 // chunks per stage
   constexpr int LPS = SCH / 64;                         // wave loads per stage
+  static_assert(SCH % 64 == 0, "whole wave loads per stage");
   constexpr int D_LDS = (128 * 1024 / 16) / SCH;
   constexpr int D_VM = 1 + 63 / LPS;
   constexpr int D0 = D_LDS < D_VM ? D_LDS : D_VM;
-  constexpr int D = D0 > 8 ? 8 : D0;                    // ring depth (stages in flight)
+  constexpr int D = D0 > 16 ? 16 : D0;                  // ring depth (stages in flight)
+  // chunk c of row r of a stage sits at r * ROWCH + (c ^ (r & 15)): 16 lanes reading
+  // 16 rows at one chunk hit 16 distinct 4-bank groups
+  auto swz = [](int row, int ch) { return row * ROWCH + (ch ^ (row & 15)); };
   static_assert(D >= 2, "ring too shallow");
   __shared__ u32x4_t ring[D * SCH];
   const int lane = threadIdx.x;
@@ -452,13 +462,13 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmArgs p) {
   for (int j = 0; j < LPS; ++j) {
     const int P = j * 64 + lane;
     if (P < WCH) {
-      const int r = P / SK_ROWCH, ch = (P % SK_ROWCH) ^ (r & 15);
+      const int r = P / ROWCH, ch = (P % ROWCH) ^ (r & 15);
       int wr = min(cb * 16 + (r & 15), ncols - 1);
       if (NB == 2 && r >= 16) wr += ncols;               // up rows follow the gate rows
       src[j] = W + (size_t)wr * K + ch * 8;
     } else {
       const int P2 = P - WCH;
-      const int r = P2 / SK_ROWCH, ch = (P2 % SK_ROWCH) ^ (r & 15);
+      const int r = P2 / ROWCH, ch = (P2 % ROWCH) ^ (r & 15);
       int ar = row_base + min(r, M - 1);
       if constexpr (GATHER) ar = p.a_rows[ar] / p.a_div;
       src[j] = p.A + (size_t)ar * K + ch * 8;
@@ -476,23 +486,24 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmArgs p) {
   for (int b = 0; b < NB; ++b)
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi) acc[b][mi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int nst = K / SK_KC;
+  const int nst = K / KC;
 #pragma unroll
   for (int st = 0; st < D; ++st)
-    if (st < nst) issue(st, st * SK_KC);
+    if (st < nst) issue(st, st * KC);
   for (int c = 0; c < nst; ++c) {
     if (c + D - 1 < nst) wait_vmcnt<(D - 1) * LPS>();   // stage c has landed
     else wait_vmcnt<0>();
     const u32x4_t* stg = ring + (c % D) * SCH;
 #pragma unroll
-    for (int s = 0; s < SK_KC / 32; ++s) {
+    for (int s = 0; s < KC / 32; ++s) {
       const int ch = s * 4 + (lane >> 4);
       bf16x8_t bw[NB];
 #pragma unroll
-      for (int b = 0; b < NB; ++b) bw[b] = __builtin_bit_cast(bf16x8_t, stg[skswz(b * 16 + (lane & 15), ch)]);
+      for (int b = 0; b < NB; ++b) bw[b] = __builtin_bit_cast(bf16x8_t, stg[swz(b * 16 + (lane & 15), ch)]);
 #pragma unroll
       for (int mi = 0; mi < MT; ++mi) {
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, stg[WCH + skswz(mi * 16 + (lane & 15), ch)]);
+        const int ar = AR == 16 * MT ? mi * 16 + (lane & 15) : min(lane & 15, AR - 1);
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, stg[WCH + swz(ar, ch)]);
 #pragma unroll
         for (int b = 0; b < NB; ++b)
           acc[b][mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bw[b], acc[b][mi], 0, 0, 0);
@@ -500,7 +511,7 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmArgs p) {
     }
     if (c + D < nst) {
       __builtin_amdgcn_s_waitcnt(0x0070 | (0x3 << 14) | 0xF);   // lgkmcnt(0): this slot's reads are done
-      issue(c % D, (c + D) * SK_KC);
+      issue(c % D, (c + D) * KC);
     }
   }
   if (cb * 16 >= ncols) return;
@@ -529,7 +540,11 @@ static hipError_t dispatch_skinny(const GemmArgs& a, hipStream_t s) {
   const int ncols = (KIND == K_SILU) ? a.N / 2 : a.N;
   const int grid = ncols / 16;
   const int mt = (a.M + 15) / 16;
-  if (mt == 1) hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 1>), dim3(grid), dim3(64), 0, s, a);
+  const bool wide = a.K % 512 == 0;
+  if (a.M <= 4 && wide) hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 1, false, false, 4, 512>), dim3(grid), dim3(64), 0, s, a);
+  else if (a.M <= 4) hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 1, false, false, 4>), dim3(grid), dim3(64), 0, s, a);
+  else if (mt == 1 && wide) hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 1, false, false, 16, 512>), dim3(grid), dim3(64), 0, s, a);
+  else if (mt == 1) hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 1>), dim3(grid), dim3(64), 0, s, a);
   else if (mt == 2) hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 2>), dim3(grid), dim3(64), 0, s, a);
   else if (mt <= 4) hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 4>), dim3(grid), dim3(64), 0, s, a);
   else hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 8>), dim3(grid), dim3(64), 0, s, a);
