@@ -205,28 +205,40 @@ __global__ __launch_bounds__((TBM >= 64 ? TBM / 64 : 1) * NWN * 64, 1) void gemm
   // slab, which the barrier between the two has published.  That barrier also
   // frees the slab's LDS buffer (its last fragments are in registers), so the
   // DMA of the slab after next is issued right after it.
+  // The next step's A fragments are read after the MFMAs of the first column
+  // blocks, FPG per block, never ahead of the step's first MFMAs: then at most 12
+  // LDS reads are outstanding when an MFMA needs one of them, within what the LDS
+  // counter can count, so the wait before it covers only reads issued a block or
+  // more earlier instead of every read in flight.
+  constexpr int FPG = (KMI + NI / 2 - 1) / (NI / 2);
   bf16x8_t fa0[KMI], fa1[KMI], fb[NI];
   auto step_a = [&](int st) {
-#pragma unroll
-    for (int mi = 0; mi < KMI; ++mi) fa1[mi] = lda(st, 1, mi);
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
 #pragma unroll
       for (int mi = 0; mi < KMI; ++mi) acc[mi][ni] = mfma(fa0[mi], fb[ni], acc[mi][ni]);
       fb[ni] = ldb(st, 1, ni);
+#pragma unroll
+      for (int mi = 0; mi < KMI; ++mi)
+        if (mi / FPG == ni) fa1[mi] = lda(st, 1, mi);
+      __builtin_amdgcn_sched_group_barrier(0x008, KMI, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1 + FPG, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
   auto step_b = [&](int st, auto prefetch) {
-    if constexpr (decltype(prefetch)::value) {
-#pragma unroll
-      for (int mi = 0; mi < KMI; ++mi) fa0[mi] = lda(st ^ 1, 0, mi);
-    }
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
 #pragma unroll
       for (int mi = 0; mi < KMI; ++mi) acc[mi][ni] = mfma(fa1[mi], fb[ni], acc[mi][ni]);
-      if constexpr (decltype(prefetch)::value) fb[ni] = ldb(st ^ 1, 0, ni);
+      if constexpr (decltype(prefetch)::value) {
+        fb[ni] = ldb(st ^ 1, 0, ni);
+#pragma unroll
+        for (int mi = 0; mi < KMI; ++mi)
+          if (mi / FPG == ni) fa0[mi] = lda(st ^ 1, 0, mi);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, KMI, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1 + FPG, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
