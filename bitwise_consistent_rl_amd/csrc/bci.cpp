@@ -929,13 +929,26 @@ static bci_status forward_impl(bci_ctx* c, float* lp, hipStream_t s) {
   // layer 0 norm: residual = E[token] (exact copy), no add
   HIP_TRY(c, launch_add_rmsnorm(nullptr, nullptr, c->bufR, c->bufH, c->w[1], c->meta + c->o_tok, E, T, H,
                                 g.rms_eps, s));
+  // calls on the tiled GEMM schedule (more rows than the skinny one takes, and in the
+  // non-invariant mode more than its split-K range) fuse RoPE into the QKV epilogue
+  const bool fuse_rope = g.head_dim == 128 && c->qkv_w % GEMM_BN == 0 && T > SKINNY_MAX_M &&
+                         (g.mode != BCI_MODE_FAST || T > FAST_SPLITK_MAX_M);
   for (int l = 0; l < g.n_layers; ++l) {
     const void* const* lw = &c->w[1 + 6 * l];  // attn_norm, wqkv, wo, mlp_norm, wgu, wd
     if (l > 0)
       HIP_TRY(c, launch_add_rmsnorm(c->bufX, c->bufR, c->bufR, c->bufH, lw[0], nullptr, nullptr, T, H,
                                     g.rms_eps, s));
-    if (bci_status st = gemm_checked(c, c->bufH, nullptr, lw[1], c->bufQKV, T, c->qkv_w, H, EPI_BF16, s)) return st;
-    if (bci_status st = op_rope(c, c->bufQKV, c->bufQ, l, s)) return st;
+    if (fuse_rope) {
+      // tiled QKV GEMM with RoPE and the KV write in its epilogue: the same bits as the
+      // GEMM into bufQKV followed by op_rope (the op-by-op path), without bufQKV
+      HIP_TRY(c, launch_gemm_qkv_rope(c->bufH, lw[1], T, c->qkv_w, H, c->bufQ, c->meta + c->o_pos,
+                                      c->meta + c->o_slot, c->rope_cos, c->rope_sin, kv_layer(c, l),
+                                      g.n_q_heads, g.n_kv_heads, g.kv_dtype == BCI_KV_FP8_E4M3, s));
+    } else {
+      if (bci_status st = gemm_checked(c, c->bufH, nullptr, lw[1], c->bufQKV, T, c->qkv_w, H, EPI_BF16, s))
+        return st;
+      if (bci_status st = op_rope(c, c->bufQKV, c->bufQ, l, s)) return st;
+    }
     if (bci_status st = op_attn(c, c->bufQ, c->bufO, l, s)) return st;
     if (bci_status st = gemm_checked(c, c->bufO, nullptr, lw[2], c->bufX, T, H, c->qd, EPI_BF16, s)) return st;
     HIP_TRY(c, launch_add_rmsnorm(c->bufX, c->bufR, c->bufR, c->bufH, lw[3], nullptr, nullptr, T, H,

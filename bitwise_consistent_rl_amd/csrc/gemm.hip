@@ -45,7 +45,7 @@ constexpr int STAGE = (BM + BN) * KCH;   // 16-byte chunks per LDS buffer
 constexpr int LM_SMALL_M = 16;           // lm_head rows up to which 16-row tiles are used
 constexpr int LM_MID_M = 128;            // ... and up to which 64-row tiles are used
 
-enum { K_BF16 = 0, K_F32 = 1, K_SILU = 2, K_LMHEAD = 3, K_ATOMIC = 4, K_PART = 5 };
+enum { K_BF16 = 0, K_F32 = 1, K_SILU = 2, K_LMHEAD = 3, K_ATOMIC = 4, K_PART = 5, K_ROPE = 6 };
 
 struct GemmArgs {
   const bf16_t* A;
@@ -68,6 +68,15 @@ struct GemmArgs {
   // K_ATOMIC (non-invariant mode only) atomically adds its fp32 partial to C; K_PART
   // stores it to C + y * M * N (fixed slices, summed later in slice order)
   int k_split;
+  // K_ROPE: the QKV projection's epilogue rotates q and k at each token's position
+  // and writes q to q_out [M, nq * 128] and k, v to the token's paged-cache slot
+  bf16_t* q_out;
+  const int32_t* tok_pos;
+  const int32_t* tok_slot;
+  const float* rcos;
+  const float* rsin;
+  KvLayer kv;
+  int nq, nkv, fp8;
 };
 
 // Row r of an LDS tile holds 8 chunks of 16 bytes; chunk c is stored at
@@ -338,6 +347,79 @@ __global__ __launch_bounds__((TBM >= 64 ? TBM / 64 : 1) * NWN * 64, 1) void gemm
         }
       }
     }
+  } else if constexpr (KIND == K_ROPE) {
+    // Head dimension 128: wave wn of column tile tn holds head 2 tn + wn, and the
+    // rotation pair (e, e + 64) of a row sits in blocks ni and ni + 4 of the same
+    // lane.  Each value is first rounded to bf16 (what a qkv buffer would hold), then
+    // rotated, rounded, scaled and encoded with the expressions of the standalone
+    // RoPE/KV-write kernel, so both give the same bits.
+    const int hd = tn * 2 + wn;
+    const bool is_q = hd < p.nq, rot = hd < p.nq + p.nkv;
+    const bool is_k = !is_q && rot;
+    const int gk = is_q ? 0 : (is_k ? hd - p.nq : hd - p.nq - p.nkv);
+    const int lc = lane & 15;
+#pragma unroll
+    for (int mi = 0; mi < KMI; ++mi)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int lr = lrow0 + mi * 16 + r;
+        const bool ok = lr < row_cnt;            // the same for the 16 lanes of a row
+        const int t = row_base + (ok ? lr : 0);
+        float y1[NI / 2], y2[NI / 2];
+        if (rot) {
+          const int pos = p.tok_pos[t];
+#pragma unroll
+          for (int ni = 0; ni < NI / 2; ++ni) {
+            const int e = ni * 16 + lc;
+            const float c = p.rcos[(size_t)pos * 64 + e], sn = p.rsin[(size_t)pos * 64 + e];
+            const float x1 = bf2f(f2bf(acc[mi][ni][r])), x2 = bf2f(f2bf(acc[mi][ni + NI / 2][r]));
+            const float a1 = x1 * c, b1 = x2 * sn;
+            const float a2 = x2 * c, b2 = x1 * sn;
+            y1[ni] = bf2f(f2bf(a1 - b1));
+            y2[ni] = bf2f(f2bf(a2 + b2));
+          }
+        } else {
+#pragma unroll
+          for (int ni = 0; ni < NI / 2; ++ni) {
+            y1[ni] = bf2f(f2bf(acc[mi][ni][r]));
+            y2[ni] = bf2f(f2bf(acc[mi][ni + NI / 2][r]));
+          }
+        }
+        size_t crow = 0;  // cache row of (block, kv head, slot)
+        if (!is_q) {
+          const int slot = p.tok_slot[t];
+          crow = ((size_t)(slot >> 6) * p.nkv + gk) * 64 + (slot & 63);
+        }
+        if (is_q || !p.fp8) {
+          bf16_t* dst = is_q ? p.q_out + (size_t)t * p.nq * 128 + hd * 128
+                             : reinterpret_cast<bf16_t*>(is_k ? p.kv.k : p.kv.v) + crow * 128;
+          if (ok) {
+#pragma unroll
+            for (int ni = 0; ni < NI / 2; ++ni) {
+              dst[ni * 16 + lc] = f2bf(y1[ni]);
+              dst[64 + ni * 16 + lc] = f2bf(y2[ni]);
+            }
+          }
+        } else {
+          // scale from the head's amax over its 128 rounded values (an exact max,
+          // so the order does not matter): 8 per lane, then the row's 16 lanes
+          float amax = 0.0f;
+#pragma unroll
+          for (int ni = 0; ni < NI / 2; ++ni) amax = fmaxf(amax, fmaxf(fabsf(y1[ni]), fabsf(y2[ni])));
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, WAVE));
+          const float sc = kv_scale_from_amax(amax);
+          uint8_t* dst = reinterpret_cast<uint8_t*>(is_k ? p.kv.k : p.kv.v) + crow * 128;
+          if (ok) {
+#pragma unroll
+            for (int ni = 0; ni < NI / 2; ++ni) {
+              dst[ni * 16 + lc] = (uint8_t)kv_encode(y1[ni], sc);
+              dst[64 + ni * 16 + lc] = (uint8_t)kv_encode(y2[ni], sc);
+            }
+            if (lc == 0) (is_k ? p.kv.ks : p.kv.vs)[crow] = sc;
+          }
+        }
+      }
   } else {  // K_LMHEAD: per row, (max, sum exp) over this 256-column vocab chunk
     // Row lr's chunk max is max over the NWN waves of redm[w][lr]; its sum is
     // s_0 + s_1 (+ ...) over reds[w][lr] in wave order; within a wave the
@@ -745,6 +827,35 @@ hipError_t launch_gemm_grouped(const void* A, const int32_t* a_rows, int a_div, 
   } else {
     return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_qkv_rope(const void* A, const void* W, int M, int N, int K, void* q_out,
+                                const int32_t* tok_pos, const int32_t* tok_slot, const float* rope_cos,
+                                const float* rope_sin, KvLayer kv, int nq, int nkv, bool fp8,
+                                hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  if (N % BN != 0 || N != (nq + 2 * nkv) * 128 || K % BK != 0) return hipErrorInvalidValue;
+  GemmArgs a{};
+  a.A = (const bf16_t*)A;
+  a.a_div = 1;
+  a.W = (const bf16_t*)W;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.tiles_m = (M + BM - 1) / BM;
+  a.tiles_n = N / BN;
+  a.q_out = (bf16_t*)q_out;
+  a.tok_pos = tok_pos;
+  a.tok_slot = tok_slot;
+  a.rcos = rope_cos;
+  a.rsin = rope_sin;
+  a.kv = kv;
+  a.nq = nq;
+  a.nkv = nkv;
+  a.fp8 = fp8 ? 1 : 0;
+  const int grid = (a.tiles_m * a.tiles_n + 7) / 8 * 8;
+  hipLaunchKernelGGL((gemm_kernel<K_ROPE, false, false>), dim3(grid), dim3(THREADS), 0, s, a);
   return hipGetLastError();
 }
 

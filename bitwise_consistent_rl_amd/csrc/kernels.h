@@ -62,6 +62,13 @@ struct KvLayer {
   float* ks;       // [n_blocks, nkv, 64] (fp8 only)
   float* vs;
 };
+// QKV GEMM with RoPE and the KV write in its epilogue (tiled schedule, head_dim
+// 128, N % 256 == 0): the same bits as launch_gemm(EPI_BF16) into a qkv buffer
+// followed by launch_rope_kv_write, without the qkv buffer.
+hipError_t launch_gemm_qkv_rope(const void* A, const void* W, int M, int N, int K, void* q_out,
+                                const int32_t* tok_pos, const int32_t* tok_slot, const float* rope_cos,
+                                const float* rope_sin, KvLayer kv, int nq, int nkv, bool fp8,
+                                hipStream_t s);
 hipError_t launch_rope_kv_write(const void* qkv, void* q_out, const int32_t* tok_pos,
                                 const int32_t* tok_slot, const float* rope_cos,
                                 const float* rope_sin, KvLayer kv, int T, int nq, int nkv, int d,

@@ -267,3 +267,28 @@ def test_fast_mode_is_correct_but_not_invariant():
         print("fast mode rollout vs recompute:", eng().acceptance(rec, roll), flush=True)
     finally:
         m.close()
+
+
+# ------------------------------- RoPE fused into the QKV GEMM (head_dim 128)
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_qkv_rope_fusion_bitwise(kv):
+    """Calls on the tiled GEMM schedule (more than 128 tokens) rotate q and k and write
+    the KV cache in the QKV GEMM's epilogue; the op-by-op path runs the GEMM into a qkv
+    buffer and the standalone RoPE/KV-write kernel.  Logprobs and every byte of the
+    cache (codes and scales for FP8) must agree."""
+    cfg = synth.ModelConfig("qwen-width-2-layer", 2, 2048, 16, 8, 128, 6144, 4096)
+    seqs = synth.rl_sequences(cfg, n_prompts=2, n_responses=3)
+    r = Rig(cfg, seqs, kv, 64, gain_noise=True, max_tokens=2048, max_seqs=16, max_position=1024,
+            n_blocks=128)
+    try:
+        fused = eng().recompute(r.model, seqs, r.cache_rollout)
+        split = eng().recompute(r.model, seqs, r.cache_train, op_by_op=True)
+        torch.cuda.synchronize()
+        assert bits_equal(fused, split)
+        a, b = r.cache_rollout, r.cache_train
+        pairs = [(a.k, b.k), (a.v, b.v)] + ([(a.k_scale, b.k_scale), (a.v_scale, b.v_scale)] if kv == "fp8" else [])
+        for x, y in pairs:
+            assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+        assert sum(s.length - 1 for s in seqs) > 128     # the fused schedule ran
+    finally:
+        r.model.close()
