@@ -929,14 +929,26 @@ static bci_status forward_impl(bci_ctx* c, float* lp, hipStream_t s) {
   // layer 0 norm: residual = E[token] (exact copy), no add
   HIP_TRY(c, launch_add_rmsnorm(nullptr, nullptr, c->bufR, c->bufH, c->w[1], c->meta + c->o_tok, E, T, H,
                                 g.rms_eps, s));
-  // calls on the tiled GEMM schedule (more rows than the skinny one takes, and in the
-  // non-invariant mode more than its split-K range) fuse RoPE into the QKV epilogue
-  const bool fuse_rope = g.head_dim == 128 && c->qkv_w % GEMM_BN == 0 && T > SKINNY_MAX_M &&
-                         (g.mode != BCI_MODE_FAST || T > FAST_SPLITK_MAX_M);
+  // Calls on the tiled GEMM schedule (more rows than the skinny one takes, and in the
+  // non-invariant mode more than its split-K range) fuse RoPE and the KV write into the
+  // QKV epilogue and the residual add into the O and down epilogues (the norm after
+  // them then only normalises); the bits are those of the unfused op sequence.
+  const bool tiled = T > SKINNY_MAX_M && (g.mode != BCI_MODE_FAST || T > FAST_SPLITK_MAX_M);
+  const bool fuse_rope = tiled && g.head_dim == 128 && c->qkv_w % GEMM_BN == 0;
+  const bool fuse_add = tiled && H % GEMM_BN == 0;
+  // the O or down projection, into bufX or (fused) added into the residual bufR
+  auto project = [&](const void* A, const void* W, int K) -> bci_status {
+    if (fuse_add) {
+      HIP_TRY(c, launch_gemm(A, nullptr, W, c->bufR, T, H, K, EPI_ADD, s));
+      return BCI_OK;
+    }
+    return gemm_checked(c, A, nullptr, W, c->bufX, T, H, K, EPI_BF16, s);
+  };
+  const void* addend = fuse_add ? nullptr : c->bufX;  // what the norms still add
   for (int l = 0; l < g.n_layers; ++l) {
     const void* const* lw = &c->w[1 + 6 * l];  // attn_norm, wqkv, wo, mlp_norm, wgu, wd
     if (l > 0)
-      HIP_TRY(c, launch_add_rmsnorm(c->bufX, c->bufR, c->bufR, c->bufH, lw[0], nullptr, nullptr, T, H,
+      HIP_TRY(c, launch_add_rmsnorm(addend, c->bufR, c->bufR, c->bufH, lw[0], nullptr, nullptr, T, H,
                                     g.rms_eps, s));
     if (fuse_rope) {
       // tiled QKV GEMM with RoPE and the KV write in its epilogue: the same bits as the
@@ -950,8 +962,8 @@ static bci_status forward_impl(bci_ctx* c, float* lp, hipStream_t s) {
       if (bci_status st = op_rope(c, c->bufQKV, c->bufQ, l, s)) return st;
     }
     if (bci_status st = op_attn(c, c->bufQ, c->bufO, l, s)) return st;
-    if (bci_status st = gemm_checked(c, c->bufO, nullptr, lw[2], c->bufX, T, H, c->qd, EPI_BF16, s)) return st;
-    HIP_TRY(c, launch_add_rmsnorm(c->bufX, c->bufR, c->bufR, c->bufH, lw[3], nullptr, nullptr, T, H,
+    if (bci_status st = project(c->bufO, lw[2], c->qd)) return st;
+    HIP_TRY(c, launch_add_rmsnorm(addend, c->bufR, c->bufR, c->bufH, lw[3], nullptr, nullptr, T, H,
                                   g.rms_eps, s));
     const bool prof = c->prof_on && !c->graph_mode && c->prof_n < MAX_PROFILE;
     if (prof) HIP_TRY(c, hipEventRecord(c->prof_ev[2 * c->prof_n], s));
@@ -959,10 +971,9 @@ static bci_status forward_impl(bci_ctx* c, float* lp, hipStream_t s) {
                                      EPI_SILU, s))
       return st;
     if (prof) HIP_TRY(c, hipEventRecord(c->prof_ev[2 * c->prof_n++ + 1], s));
-    if (bci_status st = gemm_checked(c, c->bufACT, nullptr, lw[5], c->bufX, T, H, g.intermediate, EPI_BF16, s))
-      return st;
+    if (bci_status st = project(c->bufACT, lw[5], g.intermediate)) return st;
   }
-  HIP_TRY(c, launch_add_rmsnorm(c->bufX, c->bufR, c->bufR, c->bufH, c->w[1 + 6 * g.n_layers], nullptr, nullptr,
+  HIP_TRY(c, launch_add_rmsnorm(addend, c->bufR, c->bufR, c->bufH, c->w[1 + 6 * g.n_layers], nullptr, nullptr,
                                 T, H, g.rms_eps, s));
   if (c->n_scored) {
     HIP_TRY(c, launch_lmhead_partials(c->bufH, c->meta + c->o_srow, E, c->meta + c->o_sid, c->n_scored, g.vocab,

@@ -45,7 +45,7 @@ constexpr int STAGE = (BM + BN) * KCH;   // 16-byte chunks per LDS buffer
 constexpr int LM_SMALL_M = 16;           // lm_head rows up to which 16-row tiles are used
 constexpr int LM_MID_M = 128;            // ... and up to which 64-row tiles are used
 
-enum { K_BF16 = 0, K_F32 = 1, K_SILU = 2, K_LMHEAD = 3, K_ATOMIC = 4, K_PART = 5, K_ROPE = 6 };
+enum { K_BF16 = 0, K_F32 = 1, K_SILU = 2, K_LMHEAD = 3, K_ATOMIC = 4, K_PART = 5, K_ROPE = 6, K_ADD = 7 };
 
 struct GemmArgs {
   const bf16_t* A;
@@ -190,7 +190,7 @@ __global__ __launch_bounds__((TBM >= 64 ? TBM / 64 : 1) * NWN * 64, 1) void gemm
   // consecutive columns of a row (measured faster for plain bf16 C than the
   // 8-byte pattern).  Either way each output element is the same ascending
   // chain of the same 32-wide dot products.
-  constexpr bool SWAP = (KIND == K_SILU);
+  constexpr bool SWAP = (KIND == K_SILU || KIND == K_ADD);
   auto mfma = [&](const bf16x8_t& fa, const bf16x8_t& fb, f32x4_t c) {
     if constexpr (SWAP) return __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb, fa, c, 0, 0, 0);
     else return __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, c, 0, 0, 0);
@@ -297,6 +297,33 @@ __global__ __launch_bounds__((TBM >= 64 ? TBM / 64 : 1) * NWN * 64, 1) void gemm
           }
         }
       }
+  } else if constexpr (KIND == K_ADD) {
+    // Residual add in place (N % 256 == 0, C 8-byte aligned): with the swapped operand
+    // order a lane holds 4 consecutive columns of one row per block, so it reads the
+    // row's 8 residual words of a block row first, then rewrites them, each element
+    // with the add+RMSNorm kernel's expression bf(bf(x) + r)
+#pragma unroll
+    for (int mi = 0; mi < KMI; ++mi) {
+      const int lr = wm * KWTM + mi * 16 + (lane & 15);
+      if (lr < row_cnt) {
+        bf16_t* rowp = reinterpret_cast<bf16_t*>(p.C) + (size_t)(row_base + lr) * p.N +
+                       tn * BN + wn * WTN + 4 * (lane >> 4);
+        uint2 old[NI];
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) old[ni] = *reinterpret_cast<const uint2*>(rowp + ni * 16);
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          const bf16_t* o = reinterpret_cast<const bf16_t*>(&old[ni]);
+          bf16_t v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = f2bf(bf2f(f2bf(acc[mi][ni][r])) + bf2f(o[r]));
+          uint2 w;
+          w.x = pack_bf2(v[0], v[1]);
+          w.y = pack_bf2(v[2], v[3]);
+          *reinterpret_cast<uint2*>(rowp + ni * 16) = w;
+        }
+      }
+    }
   } else if constexpr (KIND == K_BF16 || KIND == K_F32 || KIND == K_PART) {
     void* Cout = p.C;
     if constexpr (KIND == K_PART) Cout = reinterpret_cast<float*>(p.C) + (size_t)blockIdx.y * p.M * p.N;
@@ -672,6 +699,9 @@ hipError_t launch_gemm(const void* A, const int32_t* a_rows, const void* W, void
   a.a_div = 1;
   a.tiles_m = (M + BM - 1) / BM;
   a.tiles_n = (epi == EPI_SILU) ? (N / 2) / (BN / 2) : (N + BN - 1) / BN;
+  if (epi == EPI_ADD)
+    return (a_rows || N % BN || (reinterpret_cast<uintptr_t>(C) & 7)) ? hipErrorInvalidValue
+                                                                       : dispatch<K_ADD>(a, false, s);
   // decode-sized M: the skinny schedule (same per-element arithmetic, more waves)
   if (!a_rows && M <= SKINNY_MAX_M && K % SK_KC == 0 && N % 16 == 0) {
     switch (epi) {

@@ -19,7 +19,9 @@ hipError_t launch_gather_rows(const void* src, const int32_t* rows, void* dst, i
                               int cols, hipStream_t s);
 
 // ---- gemm.hip
-enum GemmEpi { EPI_BF16 = 0, EPI_F32 = 1, EPI_SILU = 2 };
+// EPI_ADD (tiled schedule only): C is a bf16 residual [M, N] updated in place,
+// C = bf(bf(A W^T) + C) -- the residual add of the add+RMSNorm that follows.
+enum GemmEpi { EPI_BF16 = 0, EPI_F32 = 1, EPI_SILU = 2, EPI_ADD = 3 };
 // C = A . W^T.  A [M, K] (rows gathered through a_rows when non-null), W [N, K].
 hipError_t launch_gemm(const void* A, const int32_t* a_rows, const void* W, void* C, int M, int N,
                        int K, int epi, hipStream_t s);

@@ -269,13 +269,14 @@ def test_fast_mode_is_correct_but_not_invariant():
         m.close()
 
 
-# ------------------------------- RoPE fused into the QKV GEMM (head_dim 128)
+# ------------- RoPE fused into the QKV GEMM (head_dim 128), residual add into O / down
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
 def test_qkv_rope_fusion_bitwise(kv):
     """Calls on the tiled GEMM schedule (more than 128 tokens) rotate q and k and write
-    the KV cache in the QKV GEMM's epilogue; the op-by-op path runs the GEMM into a qkv
-    buffer and the standalone RoPE/KV-write kernel.  Logprobs and every byte of the
-    cache (codes and scales for FP8) must agree."""
+    the KV cache in the QKV GEMM's epilogue and add the O and down projections into the
+    residual in theirs; the op-by-op path runs the GEMMs into buffers, the standalone
+    RoPE/KV-write kernel and the add+RMSNorm kernel with its add.  Logprobs and every
+    byte of the cache (codes and scales for FP8) must agree."""
     cfg = synth.ModelConfig("qwen-width-2-layer", 2, 2048, 16, 8, 128, 6144, 4096)
     seqs = synth.rl_sequences(cfg, n_prompts=2, n_responses=3)
     r = Rig(cfg, seqs, kv, 64, gain_noise=True, max_tokens=2048, max_seqs=16, max_position=1024,
