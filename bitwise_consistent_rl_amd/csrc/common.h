@@ -127,7 +127,11 @@ __device__ __forceinline__ float fexp(float x) { return expf(x); }
 // exp2(-inf) = 0 exactly, which the attention's no-op chunks rely on.
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float flog(float x) { return logf(x); }
-__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + fexp(-g)); }
+// SiLU g * sigma(g) = g * rcp(1 + 2^(-g log2 e)) on v_exp_f32 and v_rcp_f32 (about 1 ulp
+// each), the activation of every forward schedule (tiled, skinny and split-K epilogues).
+__device__ __forceinline__ float silu_f32(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * LOG2E));
+}
 
 // ------------------------------------------------- online-softmax rescaling
 // x * f, except that a factor of exactly 1 returns x itself.  Every rescale and merge
