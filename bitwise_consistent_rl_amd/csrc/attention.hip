@@ -17,7 +17,7 @@
 //       l = l * a + sum_j p_j   [fixed tree];  acc = acc * a + P.V  [MFMA, P in bf16]
 //     merge (m, l, acc) into (M, L, ACC) with the same exp2 rule
 //   (every "x * a" above is mul_unless_one: x itself when a is exactly 1)
-//   o = bf(ACC / L)
+//   o = bf(ACC * rcp(L))
 // A chunk or segment that lies wholly after the row's position is an exact
 // no-op (a = 2^0 = 1, p = 0, and keys past the tile's last position are
 // zeroed on load, so no 0 * NaN from unwritten cache slots), so a row gives the
@@ -570,11 +570,12 @@ __global__ __launch_bounds__(ATHREADS, SPLIT ? 4 : 2) void attention_kernel(Attn
 
   if (row_ok) {
     bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + (size_t)(tok_begin + tk) * qstride + hq * D;
+    const float il = attn_inv_l(L);
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
       u32x2_t w;
-      w[0] = pack_f2bf2(ACC[dt][0] / L, ACC[dt][1] / L);
-      w[1] = pack_f2bf2(ACC[dt][2] / L, ACC[dt][3] / L);
+      w[0] = pack_f2bf2(ACC[dt][0] * il, ACC[dt][1] * il);
+      w[1] = pack_f2bf2(ACC[dt][2] * il, ACC[dt][3] * il);
       *reinterpret_cast<u32x2_t*>(orow + dt * 16 + 4 * lg) = w;
     }
   }
@@ -583,7 +584,7 @@ __global__ __launch_bounds__(ATHREADS, SPLIT ? 4 : 2) void attention_kernel(Attn
 // Split schedule, second pass: for each (token, head) row merge segments
 // 0 .. pos / S in ascending order with exactly the expressions of the
 // in-workgroup merge above (a later, fully masked segment of a deeper tile is
-// an exact no-op there), then o = bf(ACC / L).  One thread per output element.
+// an exact no-op there), then o = bf(ACC * rcp(L)).  One thread per output element.
 template <int D>
 __global__ __launch_bounds__(256) void attention_merge_kernel(AttnArgs p) {
   const int t = blockIdx.x;
@@ -603,7 +604,7 @@ __global__ __launch_bounds__(256) void attention_merge_kernel(AttnArgs p) {
     ACC = mul_unless_one(ACC, a) + mul_unless_one(a_, b);
     M = Mn;
   }
-  reinterpret_cast<bf16_t*>(p.o)[((size_t)t * p.nq + h) * D + d] = f2bf(ACC / L);
+  reinterpret_cast<bf16_t*>(p.o)[((size_t)t * p.nq + h) * D + d] = f2bf(ACC * attn_inv_l(L));
 }
 
 template <int D, bool FP8>

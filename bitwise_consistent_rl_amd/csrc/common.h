@@ -133,6 +133,12 @@ __device__ __forceinline__ float silu_f32(float g) {
   return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * LOG2E));
 }
 
+// Attention output o = bf(ACC / L) evaluated as ACC * rcp(L) (v_rcp_f32, about 1 ulp):
+// one reciprocal per row instead of a division per element, in every attention
+// schedule (tiled, split + merge, sparse) alike.  L >= 1: the row's largest score
+// contributes 2^0.
+__device__ __forceinline__ float attn_inv_l(float L) { return __builtin_amdgcn_rcpf(L); }
+
 // ------------------------------------------------- online-softmax rescaling
 // x * f, except that a factor of exactly 1 returns x itself.  Every rescale and merge
 // of online-softmax states (m, l, acc) in this library goes through this rule, so a

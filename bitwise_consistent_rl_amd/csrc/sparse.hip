@@ -876,7 +876,7 @@ __global__ __launch_bounds__(512, 1) void sparse_attention_kernel(SparseAttnArgs
       M = Mn;
     }
     reinterpret_cast<bf16_t*>(p.o)[(size_t)t * qstride + (size_t)(g * group + h) * D + d] =
-        f2bf(ACC / L);
+        f2bf(ACC * attn_inv_l(L));
   }
 }
 
