@@ -454,16 +454,26 @@ __global__ __launch_bounds__((TBM >= 64 ? TBM / 64 : 1) * NWN * 64, 1) void gemm
     const int V = p.N;
     float* redm = reinterpret_cast<float*>(smem);  // [NWN][KBM]; the loop ended on a barrier
     float* reds = redm + NWN * KBM;                  // [NWN][KBM]
+    if (tn * BN + BN > V) {
+      // the vocabulary's last, partial chunk: columns past V become -inf, which adds
+      // nothing to the max and exactly +0 (2^-inf) to the sum, so the passes below need
+      // no per-logit bound checks
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        if (tn * BN + wn * WTN + ni * 16 + (lane & 15) < V) continue;
+#pragma unroll
+        for (int mi = 0; mi < KMI; ++mi)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[mi][ni][r] = -INFINITY;
+      }
+    }
 #pragma unroll
     for (int mi = 0; mi < KMI; ++mi)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float mx = -INFINITY;
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni) {
-          const int col = tn * BN + wn * WTN + ni * 16 + (lane & 15);
-          mx = fmaxf(mx, col < V ? acc[mi][ni][r] : -INFINITY);
-        }
+        for (int ni = 0; ni < NI; ++ni) mx = fmaxf(mx, acc[mi][ni][r]);
 #pragma unroll
         for (int o = 1; o <= 8; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, WAVE));
         if ((lane & 15) == 0) redm[wn * KBM + lrow0 + mi * 16 + r] = mx;
@@ -478,14 +488,10 @@ __global__ __launch_bounds__((TBM >= 64 ? TBM / 64 : 1) * NWN * 64, 1) void gemm
 #pragma unroll
         for (int w2 = 1; w2 < NWN; ++w2) m = fmaxf(m, redm[w2 * KBM + lr]);
         float s = 0.0f;
+        // e^(z - m) as 2^((z - m) log2 e) on v_exp_f32: three instructions per logit
+        // instead of the library expf's dozen, in every lm_head schedule alike
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni) {
-          const int col = tn * BN + wn * WTN + ni * 16 + (lane & 15);
-          // e^(z - m) as 2^((z - m) log2 e) on v_exp_f32: three instructions per logit
-          // instead of the library expf's dozen, in every lm_head schedule alike
-          const float e = col < V ? fexp2((acc[mi][ni][r] - m) * LOG2E) : 0.0f;
-          s = s + e;
-        }
+        for (int ni = 0; ni < NI; ++ni) s = s + fexp2((acc[mi][ni][r] - m) * LOG2E);
 #pragma unroll
         for (int o = 1; o <= 8; o <<= 1) s = s + __shfl_xor(s, o, WAVE);
         if ((lane & 15) == 0) reds[wn * KBM + lr] = s;
