@@ -222,6 +222,7 @@ __global__ __launch_bounds__((TBM >= 64 ? TBM / 64 : 1) * NWN * 64, 1) void gemm
   constexpr int FPG = (KMI + NI / 2 - 1) / (NI / 2);
   bf16x8_t fa0[KMI], fa1[KMI], fb[NI];
   auto step_a = [&](int st) {
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
 #pragma unroll
@@ -234,8 +235,10 @@ __global__ __launch_bounds__((TBM >= 64 ? TBM / 64 : 1) * NWN * 64, 1) void gemm
       __builtin_amdgcn_sched_group_barrier(0x100, 1 + FPG, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
   auto step_b = [&](int st, auto prefetch) {
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
 #pragma unroll
@@ -250,6 +253,7 @@ __global__ __launch_bounds__((TBM >= 64 ? TBM / 64 : 1) * NWN * 64, 1) void gemm
       __builtin_amdgcn_sched_group_barrier(0x100, 1 + FPG, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   int nk = K / BK;
