@@ -814,6 +814,8 @@ def main():
     ap.add_argument("--max-tokens", type=int, default=16384)
     ap.add_argument("--accept-seqs", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fast", action="store_true",
+                    help="skip timing the non-invariant mode on the recompute's calls")
     ap.add_argument("--micro", choices=["gate_up", "gate_up_hipblaslt"], default=None,
                     help="time one kernel alone at the workload's shape (for counter runs)")
     ap.add_argument("--micro-data", choices=["random", "zeros"], default="random")
@@ -874,11 +876,12 @@ def main():
     stream = torch.cuda.current_stream()
     log(f"{len(seqs)} sequences, {processed} processed / {scored} scored tokens, {len(calls)} calls")
 
-    def step():
+    def step(m=None):
+        ctx = (m or model).ctx
         for (plan, _), o in zip(calls, offs[:-1]):
-            abi.bci_set_batch(model.ctx, plan.tokens, plan.cu_q, plan.pos0, plan.block_table,
+            abi.bci_set_batch(ctx, plan.tokens, plan.cu_q, plan.pos0, plan.block_table,
                               plan.score_rows, plan.score_ids, stream)
-            abi.bci_forward_logprobs(model.ctx, lp_all[o:o + len(plan.score_rows)], stream)
+            abi.bci_forward_logprobs(ctx, lp_all[o:o + len(plan.score_rows)], stream)
 
     for i in range(args.warmup):
         step()
@@ -925,6 +928,31 @@ def main():
                                        == lp_host[: sum(len(r) for r in rec)].tobytes())
     del roll_cache
 
+    # the non-invariant mode (per-call attention segments, split-K for 129..256-row GEMMs)
+    # on the same calls with the same harness: the overhead the invariance costs here
+    fast = None
+    if args.steps > 0 and not args.no_fast:
+        log("non-invariant mode on the same calls")
+        fm = engine.Model(cfg, weights, kv_dtype="bf16", max_tokens=args.max_tokens, max_seqs=64,
+                          max_scored=args.max_tokens, max_position=1024, seg_keys=QWEN_SEG_KEYS,
+                          mode="fast")
+        fcache = fm.new_cache(n_blocks)
+        fm.bind_cache(fcache)
+        step(fm)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(fm)
+        torch.cuda.synchronize()
+        fdt = time.perf_counter() - t0
+        fm.close()
+        del fcache
+        torch.cuda.empty_cache()
+        fast_value = scored / (fdt / args.steps)
+        fast = {"value": round(fast_value, 1), "unit": "scored tokens/s",
+                "ms_per_step": round(fdt * 1e3 / args.steps, 3),
+                "invariant_over_fast": round(scored / (dt / args.steps) / fast_value, 4)}
+
     tr = gate_up_traffic()
     traffic = tr["bytes_per_launch"] if tr else None
     out = {
@@ -954,6 +982,7 @@ def main():
                           "achieved_tflops": round(step_flops / (dt / args.steps) / 1e12, 1),
                           "frac_of_mfma_peak": round(step_flops / (dt / args.steps) / 1e12 / PEAK_BF16_TFLOPS, 4)},
         "acceptance": acc,
+        "fast_mode": fast,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
