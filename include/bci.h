@@ -166,9 +166,10 @@ bci_status bci_set_batch(bci_ctx* ctx, const bci_batch* batch, void* stream);
  * QKV GEMM, RoPE + KV write, attention, O GEMM, add+RMSNorm, gate_up GEMM with
  * SiLU*up, down GEMM], final add+RMSNorm, lm_head + fp32 log-softmax + gather.
  * Writes d_logprobs[n_scored] (fp32).  This is the "rollout" entry point.  Batches
- * of more than 128 tokens run RoPE + KV write inside the QKV GEMM's epilogue and the
- * residual adds inside the O and down GEMMs' epilogues; every logprob and cache byte
- * equals what the same sequence of bci_op_* calls produces. */
+ * of more than 128 tokens (256 in BCI_MODE_FAST) run RoPE + KV write inside the QKV
+ * GEMM's epilogue (head_dim 128) and the residual adds inside the O and down GEMMs'
+ * epilogues (hidden % 256 == 0); every logprob and cache byte equals what the same
+ * sequence of bci_op_* calls produces. */
 bci_status bci_forward_logprobs(bci_ctx* ctx, float* d_logprobs, void* stream);
 
 /* bci_forward_logprobs replayed from a HIP graph.  On the first call for a batch
