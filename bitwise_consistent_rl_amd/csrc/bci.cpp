@@ -934,7 +934,11 @@ static bci_status forward_impl(bci_ctx* c, float* lp, hipStream_t s) {
   // QKV epilogue and the residual add into the O and down epilogues (the norm after
   // them then only normalises); the bits are those of the unfused op sequence.
   const bool tiled = T > SKINNY_MAX_M && (g.mode != BCI_MODE_FAST || T > FAST_SPLITK_MAX_M);
-  const bool fuse_rope = tiled && g.head_dim == 128 && c->qkv_w % GEMM_BN == 0;
+  // calls of at most 4 tokens (latency-bound decode) fuse RoPE into the skinny QKV
+  // schedule too, for bf16 caches; above that its two weight streams per wave (half the
+  // waves of the plain skinny GEMM) cost more than the launch they save
+  const bool fuse_rope = g.head_dim == 128 && c->qkv_w % GEMM_BN == 0 &&
+                         (tiled || (T <= 4 && g.kv_dtype != BCI_KV_FP8_E4M3 && H % 512 == 0));
   const bool fuse_add = tiled && H % GEMM_BN == 0;
   // the O or down projection, into bufX or (fused) added into the residual bufR
   auto project = [&](const void* A, const void* W, int K) -> bci_status {

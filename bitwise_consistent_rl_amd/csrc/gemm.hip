@@ -562,7 +562,8 @@ template <int KIND, int MT, bool GATHER = false, bool GROUPED = false, int AR = 
 __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmArgs p) {
   static_assert(AR == 16 * MT || (MT == 1 && AR == 4), "A rows per stage");
   constexpr int ROWCH = KC / 8;                         // 16-byte chunks per row per stage
-  constexpr int NB = (KIND == K_SILU) ? 2 : 1;          // weight streams (gate, up)
+  // weight streams: (gate, up) rows for SiLU; for RoPE the rows e and e + 64 of a head
+  constexpr int NB = (KIND == K_SILU || KIND == K_ROPE) ? 2 : 1;
   constexpr int WCH = NB * 16 * ROWCH;                  // W chunks per stage
   constexpr int SCH = WCH + AR * ROWCH;                 // chunks per stage
   constexpr int LPS = SCH / 64;                         // wave loads per stage
@@ -578,9 +579,12 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmArgs p) {
   __shared__ u32x4_t ring[D * SCH];
   const int lane = threadIdx.x;
   const int K = p.K;
-  const int ncols = (KIND == K_SILU) ? p.N / 2 : p.N;
+  const int ncols = (KIND == K_SILU || KIND == K_ROPE) ? p.N / 2 : p.N;
   const int cb = blockIdx.x;
   const int col = cb * 16 + (lane & 15);
+  // K_ROPE (head_dim 128): wave cb holds rotation pairs e = 16 (cb % 4) + 0..15 of head
+  // cb / 4, i.e. QKV columns 128 h + e (stream 0) and 128 h + 64 + e (stream 1)
+  const int rh = cb >> 2, re0 = (cb & 3) * 16;
   int row_base = 0, M = p.M;
   const bf16_t* W = p.W;
   if constexpr (GROUPED) {
@@ -596,8 +600,13 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmArgs p) {
     const int P = j * 64 + lane;
     if (P < WCH) {
       const int r = P / ROWCH, ch = (P % ROWCH) ^ (r & 15);
-      int wr = min(cb * 16 + (r & 15), ncols - 1);
-      if (NB == 2 && r >= 16) wr += ncols;               // up rows follow the gate rows
+      int wr;
+      if constexpr (KIND == K_ROPE) {
+        wr = rh * 128 + re0 + (r & 15) + (r >= 16 ? 64 : 0);
+      } else {
+        wr = min(cb * 16 + (r & 15), ncols - 1);
+        if (NB == 2 && r >= 16) wr += ncols;             // up rows follow the gate rows
+      }
       src[j] = W + (size_t)wr * K + ch * 8;
     } else {
       const int P2 = P - WCH;
@@ -660,6 +669,31 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmArgs p) {
         const float g = bf2f(f2bf(acc[0][mi][r]));
         const float u = bf2f(f2bf(acc[1][mi][r]));
         reinterpret_cast<bf16_t*>(p.C)[(size_t)row * ncols + col] = f2bf(silu_f32(g) * u);
+      } else if constexpr (KIND == K_ROPE) {
+        // bf16 cache only: the expressions of the standalone RoPE/KV-write kernel
+        const int e = re0 + (lane & 15);
+        const float x1 = bf2f(f2bf(acc[0][mi][r])), x2 = bf2f(f2bf(acc[1][mi][r]));
+        float y1 = x1, y2 = x2;
+        if (rh < p.nq + p.nkv) {
+          const int pos = p.tok_pos[row];
+          const float c = p.rcos[(size_t)pos * 64 + e], sn = p.rsin[(size_t)pos * 64 + e];
+          const float a1 = x1 * c, b1 = x2 * sn;
+          const float a2 = x2 * c, b2 = x1 * sn;
+          y1 = bf2f(f2bf(a1 - b1));
+          y2 = bf2f(f2bf(a2 + b2));
+        }
+        bf16_t* dst;
+        if (rh < p.nq) {
+          dst = p.q_out + (size_t)row * p.nq * 128 + rh * 128;
+        } else {
+          const bool is_k = rh < p.nq + p.nkv;
+          const int gk = is_k ? rh - p.nq : rh - p.nq - p.nkv;
+          const int slot = p.tok_slot[row];
+          const size_t crow = ((size_t)(slot >> 6) * p.nkv + gk) * 64 + (slot & 63);
+          dst = reinterpret_cast<bf16_t*>(is_k ? p.kv.k : p.kv.v) + crow * 128;
+        }
+        dst[e] = f2bf(y1);
+        dst[64 + e] = f2bf(y2);
       } else if constexpr (KIND == K_BF16) {
         reinterpret_cast<bf16_t*>(p.C)[(size_t)row * p.N + col] = f2bf(acc[0][mi][r]);
       } else {
@@ -894,6 +928,20 @@ hipError_t launch_gemm_qkv_rope(const void* A, const void* W, int M, int N, int 
   a.nq = nq;
   a.nkv = nkv;
   a.fp8 = fp8 ? 1 : 0;
+  if (M <= SKINNY_MAX_M) {
+    // decode-sized calls, bf16 cache (an FP8 scale needs a head's 128 values, spread
+    // over 4 waves here): the skinny schedule, one wave per 16 rotation pairs
+    if (fp8 || K % SK_KC) return hipErrorInvalidValue;
+    const dim3 grid(N / 32);
+    const int mt = (M + 15) / 16;
+    if (M <= 4 && K % 512 == 0)
+      hipLaunchKernelGGL((gemm_skinny_kernel<K_ROPE, 1, false, false, 4, 512>), grid, dim3(64), 0, s, a);
+    else if (mt == 1) hipLaunchKernelGGL((gemm_skinny_kernel<K_ROPE, 1>), grid, dim3(64), 0, s, a);
+    else if (mt == 2) hipLaunchKernelGGL((gemm_skinny_kernel<K_ROPE, 2>), grid, dim3(64), 0, s, a);
+    else if (mt <= 4) hipLaunchKernelGGL((gemm_skinny_kernel<K_ROPE, 4>), grid, dim3(64), 0, s, a);
+    else hipLaunchKernelGGL((gemm_skinny_kernel<K_ROPE, 8>), grid, dim3(64), 0, s, a);
+    return hipGetLastError();
+  }
   const int grid = (a.tiles_m * a.tiles_n + 7) / 8 * 8;
   hipLaunchKernelGGL((gemm_kernel<K_ROPE, false, false>), dim3(grid), dim3(THREADS), 0, s, a);
   return hipGetLastError();

@@ -291,5 +291,10 @@ def test_qkv_rope_fusion_bitwise(kv):
         for x, y in pairs:
             assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
         assert sum(s.length - 1 for s in seqs) > 128     # the fused schedule ran
+        # decode-sized calls (<= 128 tokens): with a bf16 cache the skinny QKV schedule
+        # rotates and writes the cache in its epilogue too
+        c3 = r.model.new_cache(128)
+        roll = eng().rollout(r.model, seqs, c3, cap=3)
+        assert bits_equal(roll, split)
     finally:
         r.model.close()
