@@ -50,9 +50,10 @@ def gate_up_traffic():
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
-# attention segment (keys) of the Qwen3-shaped model's numeric contract: one 64-key
-# chunk per segment, so a decode query's KV walk splits over every chunk
-QWEN_SEG_KEYS = 64
+# attention segment (keys) of the Qwen3-shaped model's numeric contract: contexts of
+# this workload stay below 1024 tokens, so every row's KV walk is one segment (the plain
+# online softmax, no segment merges) in prefill, recompute and decode alike
+QWEN_SEG_KEYS = 1024
 
 
 def log(msg):
