@@ -894,21 +894,24 @@ def main():
         log(f"warmup step {i + 1}/{args.warmup} done")
     first = lp_all.clone()
     torch.cuda.synchronize()
-    abi.bci_profile_begin(model.ctx)
+    # one event pair per gate_up launch of the timed region: calls x layers x steps
+    expect_launches = len(calls) * cfg.n_layers * args.steps
+    abi.bci_profile_begin(model.ctx, expect_launches)
     t0 = time.perf_counter()
     for i in range(args.steps):
         step()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    gu_ms, gu_launches = abi.bci_profile_end(model.ctx)
+    gu_ms, gu_launches, gu_rows, gu_dropped = abi.bci_profile_end(model.ctx)
     log(f"timed {args.steps} steps: {dt:.3f} s")
     if args.mode == "invariant":
         assert torch.equal(first.view(torch.int32), lp_all.view(torch.int32)), "run-to-run bits differ"
+    assert gu_launches == expect_launches and gu_dropped == 0, (gu_launches, gu_dropped, expect_launches)
+    assert gu_rows == args.steps * cfg.n_layers * sum(len(p.tokens) for p, _ in calls), gu_rows
 
-    # gate_up GEMM: 2 * M * (2 I) * H flops per launch, M = tokens of the call
-    per_step_gu = sum(2.0 * len(p.tokens) * 2 * cfg.intermediate * cfg.hidden * cfg.n_layers
-                      for p, _ in calls)
-    gu_flops = per_step_gu * args.steps
+    # gate_up GEMM: 2 * M * (2 I) * H flops per launch, M = tokens of the call; counted
+    # over exactly the launches whose events were timed
+    gu_flops = 2.0 * gu_rows * 2 * cfg.intermediate * cfg.hidden
     achieved = gu_flops / (gu_ms * 1e-3) / 1e12 if gu_ms > 0 else 0.0
     ms_per_step = dt * 1e3 / args.steps
 

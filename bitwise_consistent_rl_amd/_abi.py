@@ -127,8 +127,8 @@ def load() -> ctypes.CDLL:
         "bci_ssd_slot_bytes": (ctypes.c_uint64, [vp, i32]),
         "bci_ssd_set_batch": (st, [vp, i32, _P32, _P32, _P32, vp]),
         "bci_ssd_forward": (st, [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp]),
-        "bci_profile_begin": (st, [vp]),
-        "bci_profile_end": (st, [vp, ctypes.POINTER(ctypes.c_double), _P32]),
+        "bci_profile_begin": (st, [vp, i32]),
+        "bci_profile_end": (st, [vp, ctypes.POINTER(ctypes.c_double), _P32, ctypes.POINTER(ctypes.c_int64), _P32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -389,12 +389,16 @@ def bci_ssd_forward(ctx: int, x, dt, A, B, C, D, state, chunk_buf, n_slots: int,
                                            _stream(stream)))
 
 
-def bci_profile_begin(ctx: int) -> None:
-    _check(ctx, load().bci_profile_begin(ctx))
+def bci_profile_begin(ctx: int, capacity: int = 0) -> None:
+    _check(ctx, load().bci_profile_begin(ctx, capacity))
 
 
 def bci_profile_end(ctx: int):
+    """(summed kernel ms, launches timed, sum of their M, launches not timed)."""
     ms = ctypes.c_double()
     n = ctypes.c_int32()
-    _check(ctx, load().bci_profile_end(ctx, ctypes.byref(ms), ctypes.byref(n)))
-    return float(ms.value), int(n.value)
+    rows = ctypes.c_int64()
+    dropped = ctypes.c_int32()
+    _check(ctx, load().bci_profile_end(ctx, ctypes.byref(ms), ctypes.byref(n), ctypes.byref(rows),
+                                       ctypes.byref(dropped)))
+    return float(ms.value), int(n.value), int(rows.value), int(dropped.value)

@@ -22,7 +22,7 @@ using namespace bci;
 namespace {
 
 constexpr int KV_BLOCK = 64;
-constexpr int MAX_PROFILE = 8192;
+constexpr int DEFAULT_PROFILE = 8192;
 
 struct DevBuf {
   void* p = nullptr;
@@ -83,10 +83,13 @@ struct bci_ctx {
   int n_seqs = 0, n_tokens = 0, n_scored = 0, n_tiles = 0, batch_seg = 1;
   int n_itiles = 0, batch_max_pos = 0;
   std::vector<int32_t> h_cu, h_pos0, h_btab;  // h_btab with stride max_blocks
-  // profiling of the gate_up GEMM launches (HIP events on the launch stream)
+  // profiling of the gate_up GEMM launches (HIP events on the launch stream): one event
+  // pair and the row count M per timed launch; launches past the capacity are counted
+  // in prof_dropped and not timed
   bool prof_on = false;
-  int prof_n = 0;
+  int prof_n = 0, prof_dropped = 0, prof_cap = 0;
   std::vector<hipEvent_t> prof_ev;
+  std::vector<int32_t> prof_rows;
   // captured forwards, keyed by batch shape; bind_epoch changes whenever a rebind
   // moves a weight or cache buffer, which invalidates every captured graph
   struct Graph {
@@ -286,7 +289,6 @@ bci_status bci_create(const bci_model_config* cfg_in, int32_t device, bci_ctx** 
       return BCI_E_HIP;
     }
   }
-  c->prof_ev.assign(2 * MAX_PROFILE, nullptr);
   *out = c;
   return BCI_OK;
 }
@@ -969,12 +971,16 @@ static bci_status forward_impl(bci_ctx* c, float* lp, hipStream_t s) {
     if (bci_status st = project(c->bufO, lw[2], c->qd)) return st;
     HIP_TRY(c, launch_add_rmsnorm(addend, c->bufR, c->bufR, c->bufH, lw[3], nullptr, nullptr, T, H,
                                   g.rms_eps, s));
-    const bool prof = c->prof_on && !c->graph_mode && c->prof_n < MAX_PROFILE;
+    const bool prof = c->prof_on && !c->graph_mode && c->prof_n < c->prof_cap;
+    if (c->prof_on && !c->graph_mode && !prof) ++c->prof_dropped;
     if (prof) HIP_TRY(c, hipEventRecord(c->prof_ev[2 * c->prof_n], s));
     if (bci_status st = gemm_checked(c, c->bufH, nullptr, lw[4], c->bufACT, T, 2 * g.intermediate, H,
                                      EPI_SILU, s))
       return st;
-    if (prof) HIP_TRY(c, hipEventRecord(c->prof_ev[2 * c->prof_n++ + 1], s));
+    if (prof) {
+      HIP_TRY(c, hipEventRecord(c->prof_ev[2 * c->prof_n + 1], s));
+      c->prof_rows[c->prof_n++] = T;
+    }
     if (bci_status st = project(c->bufACT, lw[5], g.intermediate)) return st;
   }
   HIP_TRY(c, launch_add_rmsnorm(addend, c->bufR, c->bufR, c->bufH, c->w[1 + 6 * g.n_layers], nullptr, nullptr,
@@ -1067,28 +1073,39 @@ bci_status bci_graph_reset(bci_ctx* c) {
 
 // ------------------------------------------------------------ profiling
 
-bci_status bci_profile_begin(bci_ctx* c) {
+bci_status bci_profile_begin(bci_ctx* c, int32_t capacity) {
   if (!c) return BCI_E_INVALID;
+  if (capacity < 0) return fail(c, BCI_E_INVALID, "profile_begin: capacity %d < 0", capacity);
+  if (capacity == 0) capacity = DEFAULT_PROFILE;
   HIP_TRY(c, hipSetDevice(c->device));
-  for (auto& e : c->prof_ev)
-    if (!e) HIP_TRY(c, hipEventCreate(&e));
+  // events are created here, outside any timed region; the ring only grows
+  if (c->prof_ev.size() < 2 * (size_t)capacity) c->prof_ev.resize(2 * (size_t)capacity, nullptr);
+  for (size_t i = 0; i < 2 * (size_t)capacity; ++i)
+    if (!c->prof_ev[i]) HIP_TRY(c, hipEventCreate(&c->prof_ev[i]));
+  c->prof_cap = capacity;
+  c->prof_rows.assign(capacity, 0);
   c->prof_on = true;
   c->prof_n = 0;
+  c->prof_dropped = 0;
   return BCI_OK;
 }
 
-bci_status bci_profile_end(bci_ctx* c, double* total_ms, int32_t* launches) {
-  if (!c || !total_ms || !launches) return BCI_E_INVALID;
+bci_status bci_profile_end(bci_ctx* c, double* total_ms, int32_t* launches, int64_t* rows, int32_t* dropped) {
+  if (!c || !total_ms || !launches || !rows || !dropped) return BCI_E_INVALID;
   c->prof_on = false;
   double tot = 0.0;
+  int64_t m = 0;
   for (int i = 0; i < c->prof_n; ++i) {
     HIP_TRY(c, hipEventSynchronize(c->prof_ev[2 * i + 1]));
     float ms = 0.0f;
     HIP_TRY(c, hipEventElapsedTime(&ms, c->prof_ev[2 * i], c->prof_ev[2 * i + 1]));
     tot += ms;
+    m += c->prof_rows[i];
   }
   *total_ms = tot;
   *launches = c->prof_n;
+  *rows = m;
+  *dropped = c->prof_dropped;
   return BCI_OK;
 }
 

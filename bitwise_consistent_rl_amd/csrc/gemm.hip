@@ -10,10 +10,13 @@
 // Invariance argument.  Output element (i, j) is accumulated in one fp32
 // MFMA accumulator that starts at zero and receives
 // v_mfma_f32_16x16x32_bf16(A[i, k:k+32], W[j, k:k+32]) for k = 0, 32, 64, ...
-// in ascending order; nothing else is ever added to it.  The tile shape
-// (256 x 256 x 64, 8 waves) is the same for every M, there is no split-K, and
-// an MFMA output element depends only on its own A row and W row, so the
-// bits of row i are the same whatever M is and wherever row i sits in a tile.
+// in ascending order; nothing else is ever added to it.  The schedules below
+// (256 x 256 x 64 tiles with 8 waves; the skinny one-wave-per-16-columns
+// schedule for M <= 128; 16- and 64-row lm_head tiles for few scored rows) are
+// chosen by M, but each runs exactly this chain for every element it owns, with
+// no split-K, and an MFMA output element depends only on its own A row and W
+// row, so the bits of row i are the same whatever M is, whichever schedule runs
+// and wherever row i sits in a tile.
 //
 // Data path.  Global -> LDS directly (global_load_lds_dwordx4 into two
 // buffers of XOR-swizzled 16-byte chunks, conflict-free for the MFMA operand

@@ -29,9 +29,16 @@
  *   - No entry point throws or aborts across the ABI.
  *
  * Numeric contract (identical in every entry point and every phase)
- *   - GEMMs: bf16 operands, fp32 accumulation in ascending 32-wide K steps of
- *     one MFMA instruction (v_mfma_f32_16x16x32_bf16), no split-K, one tile
- *     shape for every M.
+ *   - GEMMs: bf16 operands; each output element is ONE fp32 accumulator that
+ *     starts at zero and receives v_mfma_f32_16x16x32_bf16 of its own A row and
+ *     W row over ascending 32-wide K steps, and nothing else.  Several schedules
+ *     assign elements to workgroups -- 256 x 256 tiles, a skinny one-wave-per-16-
+ *     columns schedule for M <= 128, 16- and 64-row lm_head tiles for few scored
+ *     rows -- and which one runs depends on M, but every schedule performs this
+ *     same per-element chain (no split-K, no atomics), so the bits of a row never
+ *     depend on M or on the row's place in a tile (page "Finish RL Training
+ *     Faster" digest, section "让训练前向使用推理的数值": batch-invariant dense GEMM
+ *     that gives up small-batch kernel switches).
  *   - Norm and softmax reductions: fixed shuffle/LDS trees that depend only on
  *     the column position, never on the row count.
  *   - Attention: keys walked in 64-key chunks at absolute positions (chunk c =
@@ -162,7 +169,11 @@ bci_status bci_bind_kv_cache(bci_ctx* ctx, void* k, void* v, float* k_scale, flo
  * calls that take no explicit shape. */
 bci_status bci_set_batch(bci_ctx* ctx, const bci_batch* batch, void* stream);
 
-/* The whole forward of the current batch: embedding, n_layers x [add+RMSNorm,
+/* The whole forward of the current batch (page "Finish RL Training Faster" digest,
+ * section "零差异需要一个精确的比较对象": the quantity compared between rollout and
+ * training is the logprob of every valid response token under one weight version
+ * and one token prefix; the same section requires one computation path whatever
+ * the batch and the phase): embedding, n_layers x [add+RMSNorm,
  * QKV GEMM, RoPE + KV write, attention, O GEMM, add+RMSNorm, gate_up GEMM with
  * SiLU*up, down GEMM], final add+RMSNorm, lm_head + fp32 log-softmax + gather.
  * Writes d_logprobs[n_scored] (fp32).  This is the "rollout" entry point.  Batches
@@ -197,7 +208,10 @@ bci_status bci_graph_reset(bci_ctx* ctx);
 /* ---- per-operator entry points ("the training forward calls the inference
  *      kernels"); each is bitwise identical to its use inside the forward ---- */
 
-/* r[i] = E[tokens[i]] for the current batch (exact row copy).  E [vocab, hidden]. */
+/* r[i] = E[tokens[i]] for the current batch (exact row copy): the first step of the
+ * forward that recomputes the token probabilities of a prefix (page "Finish RL
+ * Training Faster" digest, opening paragraph and section "零差异需要一个精确的比较对象").
+ * E [vocab, hidden] bf16, r [n_tokens, hidden] bf16; BCI_E_STATE without a batch. */
 bci_status bci_op_embed(bci_ctx* ctx, const void* E, void* r, void* stream);
 
 /* Fused residual add + RMSNorm over `rows` rows of `cols` bf16 values
@@ -244,10 +258,17 @@ bci_status bci_op_gemm_bf16_ksplit(bci_ctx* ctx, const void* A, const void* W, v
 bci_status bci_op_rope_kv_write(bci_ctx* ctx, const void* qkv, void* q_out, int32_t layer,
                                 void* stream);
 
-/* Gathers sequence `seq` of the current batch, positions 0 .. n_pos - 1, of one
- * layer out of the paged cache and dequantises to bf16: k_out, v_out
- * [n_pos, n_kv_heads, head_dim] = bf(fp32(code) * scale) (a plain copy for a
- * bf16 cache).  The same conversion the attention kernel applies on load. */
+/* FP8 KV gather / dequantise (page "Finish RL Training Faster" digest, section
+ * "让训练前向使用推理的数值", the FP8 KV paragraph and the figure caption before it:
+ * the cache stays FP8, and prefill, decode and the training recompute all gather
+ * and dequantise it to BF16 before one attention operator, the recompute from a
+ * private cache copy written through the same FP8 round trip).  Gathers sequence
+ * `seq` of the current batch, positions 0 .. n_pos - 1, of one layer out of the
+ * paged cache: k_out, v_out [n_pos, n_kv_heads, head_dim] bf16 = bf(fp32(code) *
+ * scale) (a plain copy for a bf16 cache), caller owned.  This is the conversion
+ * the attention kernel applies on load, through the same device function, so the
+ * materialised and the fused paths give the same bits.  n_pos <= pos0 + q_len of
+ * the sequence (BCI_E_INVALID otherwise); BCI_E_STATE without a batch. */
 bci_status bci_op_kv_gather_dequant(bci_ctx* ctx, int32_t seq, int32_t n_pos, int32_t layer,
                                     void* k_out, void* v_out, void* stream);
 
@@ -317,7 +338,10 @@ bci_status bci_op_sparse_topk(bci_ctx* ctx, const float* scores, int64_t score_s
 bci_status bci_op_sparse_attention(bci_ctx* ctx, const void* q, int32_t layer, const int32_t* sel,
                                    int32_t topk, void* o, void* stream);
 
-/* out[r] = src[score_rows[r]] for the current batch: [n_scored, cols] bf16. */
+/* Scored-row select: out[r] = src[score_rows[r]] for the current batch, [n_scored,
+ * cols] bf16 (an exact copy).  Only valid response tokens are compared (page
+ * "Finish RL Training Faster" digest, section "零差异需要一个精确的比较对象"), so
+ * the lm_head runs on these rows only.  cols % 8 == 0; BCI_E_STATE without a batch. */
 bci_status bci_op_gather_scored(bci_ctx* ctx, const void* src, int32_t cols, void* out,
                                 void* stream);
 
@@ -499,11 +523,16 @@ bci_status bci_ssd_forward(bci_ssd* ctx, const void* x, const float* dt, const f
 
 /* While enabled, bci_forward_logprobs records a HIP event pair on its stream
  * around every launch of the gate_up GEMM (the SiLU*up-epilogue kernel, the
- * largest single kernel of the forward; up to 8192 launches).  bci_profile_end
- * synchronises those events and returns the summed kernel time in ms and the
- * number of launches timed. */
-bci_status bci_profile_begin(bci_ctx* ctx);
-bci_status bci_profile_end(bci_ctx* ctx, double* total_ms, int32_t* launches);
+ * largest single kernel of the forward) together with the launch's row count M.
+ * bci_profile_begin creates the events for `capacity` launches up front (0 means
+ * 8192), so no event is created inside a timed region; launches beyond the
+ * capacity are not timed and are counted in *dropped.  bci_profile_end
+ * synchronises the events and returns the summed kernel time in ms, the number
+ * of launches timed and the sum of their M (so that the caller counts the FLOPs
+ * of exactly the timed launches: 2 * rows * 2 * intermediate * hidden). */
+bci_status bci_profile_begin(bci_ctx* ctx, int32_t capacity);
+bci_status bci_profile_end(bci_ctx* ctx, double* total_ms, int32_t* launches, int64_t* rows,
+                           int32_t* dropped);
 
 #ifdef __cplusplus
 }

@@ -80,3 +80,4 @@ def test_null_context_calls_return_invalid(lib):
     assert lib.bci_forward_logprobs(None, None, None) == _abi.BCI_E_INVALID
     assert lib.bci_op_gemm_bf16(None, None, None, None, 1, 128, 64, 0, None) == _abi.BCI_E_INVALID
     lib.bci_destroy(None)
+

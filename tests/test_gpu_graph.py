@@ -143,6 +143,24 @@ def test_graphed_rollout_equals_recompute(tiny):
         assert abi().bci_graph_count(model.ctx) >= 1
 
 
+def test_graphed_rollout_parity_with_oracle(tiny):
+    """The graph-replayed decode against the fp64 oracle (not only against the eager
+    path): every logprob of the captured rollout within the end-to-end tolerance."""
+    from oracle import model as om
+    cfg, weights, seqs, model, cache, blocks = tiny
+    abi().bci_graph_reset(model.ctx)
+    roll = eng().rollout(model, seqs, model.new_cache(64), cap=3, graph=True)
+    assert abi().bci_graph_count(model.ctx) >= 1
+    W = om.Weights({k: synth.bf16_bits(v) for k, v in weights.items()})
+    worst = 0.0
+    for s, got in zip(seqs, roll):
+        ref = om.sequence_logprobs(cfg, W, s.tokens, s.prompt_len)
+        assert got.shape == ref.shape and np.all(got <= 0)
+        worst = max(worst, float(np.max(np.abs(got.astype(np.float64) - ref))))
+    print(f"graphed rollout: max |dlogprob| vs oracle = {worst:.3e}", flush=True)
+    assert worst <= 2e-2
+
+
 def test_qwen3_shaped_decode_graph_equals_eager():
     """Full-size decode step (Qwen3-shaped, 28 layers) at B = 4: captured == eager."""
     cfg = synth.QWEN3_1P7B

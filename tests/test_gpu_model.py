@@ -150,30 +150,40 @@ def qwen():
     seqs = synth.rl_sequences(cfg, n_prompts=2, n_responses=8)
     r = Rig(cfg, seqs, "bf16", 2048, gain_noise=False, max_tokens=8192, max_seqs=16,
             max_position=1024, n_blocks=256)
+    r.lp = None
+    r.W = om.Weights({k: synth.bf16_bits(v) for k, v in r.weights.items()}, cache=False)
     yield r
     r.model.close()
 
 
 # End-to-end tolerance at 28 layers.  The random-init 28-layer model amplifies
-# rounding-level differences: the fp64 oracle itself, re-run with fp32 GEMM
-# accumulation (what any MFMA path does), moves the logprobs of this workload's
-# shortest sequence by max 7.5e-2 / mean 2.3e-2.  The end-to-end bound is twice
-# that noise; the structural check at full size is the per-layer test below.
-E2E_MAX, E2E_MEAN = 0.15, 0.05
+# rounding-level differences: the fp64 oracle itself, re-run with fp32 accumulation in
+# every linear layer (what any MFMA path does), moves the logprobs of these 16
+# sequences by up to E2E_NOISE_MAX / E2E_NOISE_MEAN (tests/golden/
+# qwen3_oracle_fp32_sensitivity.txt, written by make_qwen3_sensitivity.py from the
+# oracle alone).  The end-to-end bound is twice that noise; the structural check at
+# full size is the per-layer test below.
+E2E_NOISE_MAX, E2E_NOISE_MEAN = 0.075, 0.025
+E2E_MAX, E2E_MEAN = 2 * E2E_NOISE_MAX, 2 * E2E_NOISE_MEAN
+
+# the shortest, two middle and the longest of the 16 sequences (by length rank)
+QWEN_RANKS = [0, 5, 10, 15]
 
 
-def test_qwen3_shaped_parity_sampled(qwen):
-    """Full-size model, 2 of the 16 sequences against the oracle (fp64 on the host)."""
-    lp = qwen.recompute()
-    W = om.Weights({k: synth.bf16_bits(v) for k, v in qwen.weights.items()}, cache=False)
-    idx = sorted(range(len(qwen.seqs)), key=lambda i: qwen.seqs[i].length)[:2]
-    for i in idx:
-        s = qwen.seqs[i]
-        ref = om.sequence_logprobs(qwen.cfg, W, s.tokens, s.prompt_len)
-        d = np.abs(lp[i].astype(np.float64) - ref)
-        print(f"seq {i} (L={s.length}): max |dlogprob| = {d.max():.3e} mean {d.mean():.3e}", flush=True)
-        assert np.all(lp[i] <= 0)
-        assert d.max() <= E2E_MAX and d.mean() <= E2E_MEAN
+@pytest.mark.parametrize("rank", QWEN_RANKS)
+def test_qwen3_shaped_parity_sampled(qwen, rank):
+    """Full-size model: one sequence of the 16 (by length rank; the longest included)
+    against the oracle (fp64 on the host); the GPU recompute of all 16 runs once."""
+    if qwen.lp is None:
+        qwen.lp = qwen.recompute()
+    i = sorted(range(len(qwen.seqs)), key=lambda j: qwen.seqs[j].length)[rank]
+    s = qwen.seqs[i]
+    ref = om.sequence_logprobs(qwen.cfg, qwen.W, s.tokens, s.prompt_len)
+    got = qwen.lp[i]
+    d = np.abs(got.astype(np.float64) - ref)
+    print(f"seq {i} (L={s.length}): max |dlogprob| = {d.max():.3e} mean {d.mean():.3e}", flush=True)
+    assert got.shape == ref.shape and np.all(got <= 0)
+    assert d.max() <= E2E_MAX and d.mean() <= E2E_MEAN
 
 
 def _gpu_layers(model, seq):
@@ -208,33 +218,48 @@ def _gpu_layers(model, seq):
     return layers, h
 
 
-# Per-layer bound of the relative RMS gap between the GPU's layer outputs and the
-# oracle's own forward: layer 0 sees identical inputs (the embeddings), so one
-# layer of rounding separates them; deeper layers inherit the gap of the layers
-# before them, which the random-init model amplifies.
+# Per-layer bounds of the gap between the GPU's layer outputs and the oracle's own
+# forward.  Layer 0 sees identical inputs (the embeddings), so one layer of rounding
+# separates them; deeper layers inherit the gap of the layers before them, which the
+# random-init model amplifies.  Three views, each at every layer: the relative RMS over
+# the whole [T, hidden] tensor, the relative RMS of every token row (a fault confined
+# to a few tokens -- a mask slip at a tile edge, a wrong cache slot -- fails it), and
+# every element within 4 bf16 ulp plus a multiple of its row's RMS (a fault in a few
+# columns or heads fails it).
 LAYER0_REL, LAYER_REL = 1e-2, 0.08
+LAYER0_ROW_REL, LAYER_ROW_REL = 2e-2, 0.12
+LAYER0_ELEM, LAYER_ELEM = 0.15, 0.6
 
 
 def test_qwen3_shaped_layerwise_parity(qwen):
     """Each of the 28 GPU layers against the same layer of the oracle's own forward
     of the sequence (no GPU value enters the oracle)."""
-    from gpu_util import f64
+    from gpu_util import bf16_ulp, f64
     qwen.model.bind_cache(qwen.cache_train)
     s = min(qwen.seqs, key=lambda q: q.length)
     layers, hf = _gpu_layers(qwen.model, s)
-    W = om.Weights({k: synth.bf16_bits(v) for k, v in qwen.weights.items()}, cache=False)
     T = s.length - 1
     dump = []
-    ref_hf = om.forward_chunks(qwen.cfg, W, s.tokens, [T], "bf16", dump)
+    ref_hf = om.forward_chunks(qwen.cfg, qwen.W, s.tokens, [T], "bf16", dump)
     gaps = []
     for l, (m_in, r_in, r_out, m_out) in enumerate(layers):
         out = dump[l]
         for name, got, ref in (("r", f64(r_out), out["r"]), ("m", f64(m_out), out["m"])):
             rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
-            gaps.append((l, name, round(float(rel), 5)))
+            rms_row = np.sqrt(np.mean(ref * ref, axis=1))
+            row_rel = np.sqrt(np.mean((got - ref) ** 2, axis=1)) / rms_row
+            d = np.abs(got - ref)
+            elem = np.max(np.maximum(d - 4 * bf16_ulp(np.maximum(np.abs(got), np.abs(ref))), 0.0)
+                          / rms_row[:, None])
+            gaps.append((l, name, round(float(rel), 5), round(float(row_rel.max()), 5),
+                         round(float(elem), 4)))
             assert rel <= (LAYER0_REL if l == 0 else LAYER_REL), (l, name, rel)
+            assert row_rel.max() <= (LAYER0_ROW_REL if l == 0 else LAYER_ROW_REL), \
+                (l, name, int(row_rel.argmax()), float(row_rel.max()))
+            assert elem <= (LAYER0_ELEM if l == 0 else LAYER_ELEM), (l, name, float(elem))
     rel_hf = np.linalg.norm(f64(hf) - ref_hf) / np.linalg.norm(ref_hf)
-    print("layer gaps (layer, tensor, relative RMS):", gaps, "final hidden:", rel_hf, flush=True)
+    print("layer gaps (layer, tensor, relative RMS, worst row relative RMS, worst element "
+          "beyond 4 ulp in row RMS):", gaps, "final hidden:", rel_hf, flush=True)
     assert rel_hf <= LAYER_REL
 
 
