@@ -38,7 +38,7 @@ EXPORTS = [
     "bci_ssd_slot_bytes", "bci_ssd_set_batch", "bci_ssd_forward", "bci_op_transpose_bf16",
     "bci_op_add_rmsnorm_backward", "bci_op_silu_mul_backward", "bci_op_logprob_backward_dz",
     "bci_op_rope_backward",
-    "bci_op_attention_backward",
+    "bci_op_attention_backward", "bci_lmhead_logprob_noalloc",
 ]
 
 
@@ -109,6 +109,7 @@ def load() -> ctypes.CDLL:
         "bci_op_attention": (st, [vp, vp, i32, vp, vp]),
         "bci_op_gather_scored": (st, [vp, vp, i32, vp, vp]),
         "bci_op_lmhead_logprob": (st, [vp, vp, vp, vp, i32, i32, i32, vp, vp]),
+        "bci_lmhead_logprob_noalloc": (st, [vp, vp, vp, i32, i32, i32, vp, vp]),
         "bci_op_moe_topk": (st, [vp, vp, i32, vp, vp, vp]),
         "bci_op_moe_forward": (st, [vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp]),
         "bci_op_index_key_write": (st, [vp, vp, i32, vp, vp, i32, vp]),
@@ -281,6 +282,17 @@ def bci_op_gather_scored(ctx: int, src, cols: int, out, stream=None) -> None:
 def bci_op_lmhead_logprob(ctx: int, hf, E, ids, M: int, H: int, V: int, lp, stream=None) -> None:
     _check(ctx, load().bci_op_lmhead_logprob(ctx, _ptr(hf), _ptr(E), _ptr(ids), M, H, V, _ptr(lp),
                                              _stream(stream)))
+
+
+BCI_LMHEAD_NOALLOC_MAX_ROWS, BCI_LMHEAD_NOALLOC_MAX_PAIRS = 1024, 304128
+
+
+def bci_lmhead_logprob_noalloc(hf, E, ids, M: int, H: int, V: int, lp, stream=None) -> None:
+    """No context, no allocation: the partials live in the library's fixed device array."""
+    st = load().bci_lmhead_logprob_noalloc(_ptr(hf), _ptr(E), _ptr(ids), M, H, V, _ptr(lp),
+                                           _stream(stream))
+    if st != BCI_OK:
+        raise BciError(st, "bci_lmhead_logprob_noalloc rejected the call (see bci.h for its limits)")
 
 
 def bci_op_moe_topk(ctx: int, logits, T: int, ids, w, stream=None) -> None:

@@ -24,7 +24,7 @@ OBJ_DIR = os.path.join(ROOT, "_build", "obj")
 
 SOURCES = ["norm.hip", "gemm.hip", "rope_kv.hip", "attention.hip", "moe.hip", "sparse.hip", "ssd.hip", "backward.hip",
            "attn_backward.hip",
-           "bci.cpp", "ssd_api.cpp"]
+           "bci.cpp", "ssd_api.cpp", "lmhead_noalloc.cpp"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

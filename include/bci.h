@@ -354,6 +354,27 @@ bci_status bci_op_gather_scored(bci_ctx* ctx, const void* src, int32_t cols, voi
 bci_status bci_op_lmhead_logprob(bci_ctx* ctx, const void* hf, const void* E, const int32_t* ids,
                                  int32_t M, int32_t H, int32_t V, float* lp, void* stream);
 
+/* bci_op_lmhead_logprob for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  It needs
+ * no context and allocates nothing (no hipMalloc, hipFree or allocating library
+ * call): the per-(row, vocab chunk) partials live in a fixed device array of the
+ * library, 2 * BCI_LMHEAD_NOALLOC_MAX_PAIRS + BCI_LMHEAD_NOALLOC_MAX_ROWS fp32
+ * (2.4 MiB), that each GPU the library runs on holds until the process ends; its
+ * address is looked up on the first call made with that device current.  Same
+ * arguments and the same kernels, hence the same bits, as bci_op_lmhead_logprob:
+ * hf [M, H] bf16, E [V, H] bf16, ids [M] int32 (an id outside [0, V) yields NaN),
+ * lp [M] fp32, all device pointers; H % 64 == 0.  Limits: M <=
+ * BCI_LMHEAD_NOALLOC_MAX_ROWS and M * ceil(V / 256) <= BCI_LMHEAD_NOALLOC_MAX_PAIRS
+ * (M <= 512 at V = 151936), else BCI_E_WORKSPACE with nothing enqueued; bad
+ * pointers or shapes give BCI_E_INVALID, a failed launch BCI_E_HIP (there is no
+ * context, so no error text).  Every call on one GPU shares that GPU's array: calls
+ * that overlap on one GPU (two streams, two host threads) race and must be ordered
+ * by the caller; nothing in the array needs clearing between calls. */
+#define BCI_LMHEAD_NOALLOC_MAX_ROWS 1024
+#define BCI_LMHEAD_NOALLOC_MAX_PAIRS 304128
+bci_status bci_lmhead_logprob_noalloc(const void* hf, const void* E, const int32_t* ids, int32_t M,
+                                      int32_t H, int32_t V, float* lp, void* stream);
+
 /* ---- MoE (configured through n_experts / top_k / expert_intermediate) ------ */
 
 /* Router top-K with a fixed tie rule (digest, section "零差异需要一个精确的比较对象":

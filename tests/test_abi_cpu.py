@@ -81,3 +81,15 @@ def test_null_context_calls_return_invalid(lib):
     assert lib.bci_op_gemm_bf16(None, None, None, None, 1, 128, 64, 0, None) == _abi.BCI_E_INVALID
     lib.bci_destroy(None)
 
+
+def test_lmhead_noalloc_rejects_on_the_host(lib):
+    """The allocation-free lm_head entry point checks every argument before any HIP
+    call: bad pointers or shapes, and sizes beyond its fixed device array."""
+    from bitwise_consistent_rl_amd import _abi
+    f = lib.bci_lmhead_logprob_noalloc
+    p = ctypes.c_void_p(256)          # never dereferenced: the checks come first
+    assert f(None, p, p, 1, 2048, 151936, p, None) == _abi.BCI_E_INVALID
+    assert f(p, p, p, 1, 2000, 151936, p, None) == _abi.BCI_E_INVALID      # H % 64
+    assert f(p, p, p, -1, 2048, 151936, p, None) == _abi.BCI_E_INVALID
+    assert f(p, p, p, 513, 2048, 151936, p, None) == _abi.BCI_E_WORKSPACE  # 513 x 594 pairs
+    assert f(p, p, p, _abi.BCI_LMHEAD_NOALLOC_MAX_ROWS + 1, 2048, 256, p, None) == _abi.BCI_E_WORKSPACE
