@@ -18,11 +18,15 @@
 // row, so the bits of row i are the same whatever M is, whichever schedule runs
 // and wherever row i sits in a tile.
 //
-// Data path.  Global -> LDS directly (global_load_lds_dwordx4 into two
+// Data path.  Global -> LDS directly (buffer_load_dwordx4 ... lds into two
 // buffers of XOR-swizzled 16-byte chunks, conflict-free for the MFMA operand
 // reads) -> MFMA.  While the waves multiply out of one LDS buffer, the next
 // K-slab streams into the other, so one barrier per 64-wide K-slab suffices
-// and a load has a whole slab of MFMA work to arrive.  8 waves (4 x 2) each own a 64 x 128 sub-tile, i.e.
+// and a load has a whole slab of MFMA work to arrive.  The copies use the
+// MUBUF form rather than global_load_lds: the compiler treats a pending FLAT
+// copy into LDS as an outstanding LDS access of unknown order and then waits
+// for every LDS read in flight (lgkmcnt(0)) before each use of a fragment,
+// while with the MUBUF form it waits only for the fragment's own read.  8 waves (4 x 2) each own a 64 x 128 sub-tile, i.e.
 // 4 x 8 MFMA blocks (128 fp32 accumulators per lane); two waves per SIMD, and
 // a wave raises its priority while it issues MFMAs.
 // Workgroups are remapped so each XCD (8 per chip, each with its own L2) gets
@@ -37,6 +41,26 @@
 namespace bci {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+
+// buffer_load_dwordx4 ... lds (the LLVM intrinsic llvm.amdgcn.raw.buffer.load.lds):
+// each lane copies 16 bytes from the buffer at voffset + soffset into LDS at the
+// wave-uniform base + 16 * lane.
+__device__ void raw_buffer_load_lds(i32x4_t rsrc, __attribute__((address_space(3))) void* lds, int size,
+                                    int voffset, int soffset, int offset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+// Raw buffer descriptor (stride 0) of a global address with a 2 GiB range; callers
+// rebase it at the first row a workgroup reads, so every offset stays far below it.
+__device__ __forceinline__ i32x4_t buffer_rsrc(const void* base) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4_t r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));
+  r.z = 0x7FFFFFFF;
+  r.w = 0x00020000;
+  return r;
+}
 
 constexpr int BM = GEMM_BM, BN = GEMM_BN, BK = GEMM_BK;
 constexpr int KCH = BK / 8;  // 16-byte chunks per LDS row
@@ -142,43 +166,53 @@ __global__ __launch_bounds__((TBM >= 64 ? TBM / 64 : 1) * NWN * 64, 1) void gemm
     W += (size_t)grp * p.w_group_stride;
   }
 
-  // ---- loads: global -> LDS directly (global_load_lds_dwordx4, no VGPR staging).
+  // ---- loads: global -> LDS directly (buffer_load_dwordx4 ... lds, no VGPR staging).
   // One such load of a wave fills 64 consecutive 16-byte LDS chunks, lane l the
   // l-th, so the XOR swizzle is applied on the global side: the lane whose LDS
   // chunk position is P loads logical chunk (P % 8) ^ ((row >> 1) & 7) of row
   // P / 8 of the stacked [A tile; B tile].  Wave w issues loads i = 0..NL-1
-  // covering positions (w * NL + i) * 64 + lane (waves 0-3: A, 4-7: B).
+  // covering positions (w * NL + i) * 64 + lane.  A load covers 8 whole LDS rows and
+  // the A rows (the first KBM) end on a load boundary, so whether load i of a wave
+  // reads A or W is the same for all its lanes.  Descriptors start at the tile's
+  // first A row (the source base when rows are gathered) and first W row.
   constexpr int NL = KSTAGE / 64 / (KTHREADS / 64);
-  const bf16_t* src[NL];
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const bf16_t* a_base = GATHER ? p.A : p.A + (size_t)row_base * K;
+  int w_row0 = tn * BN;
+  if constexpr (KIND == K_SILU) w_row0 = tn * (BN / 2);
+  const i32x4_t rsA = buffer_rsrc(a_base);
+  const i32x4_t rsW = buffer_rsrc(W + (size_t)w_row0 * K);
+  int voff[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
-    const int P = (wave * NL + i) * 64 + lane;
+    const int P = (wv * NL + i) * 64 + lane;
     const int row = P / KCH;
     const int ch = (P % KCH) ^ ((row >> 1) & 7);
     if (row < KBM) {
       // rows past the tile's end duplicate its last row and are never stored
-      int r = row_base + min(row, row_cnt - 1);
-      if constexpr (GATHER) r = p.a_rows[r] / p.a_div;
-      src[i] = p.A + (size_t)r * K + ch * 8;
+      int r = min(row, row_cnt - 1);
+      if constexpr (GATHER) r = p.a_rows[row_base + r] / p.a_div;
+      voff[i] = (int)(((size_t)r * K + ch * 8) * 2);
     } else {
       const int br = row - KBM;
       int n;
       if constexpr (KIND == K_SILU) {
         const int I = p.N >> 1;
-        n = (br < BN / 2) ? tn * (BN / 2) + br : I + tn * (BN / 2) + (br - BN / 2);
+        n = (br < BN / 2) ? br : I + (br - BN / 2);
       } else {
-        n = min(tn * BN + br, p.N - 1);  // columns past N are masked in the epilogue
+        n = min(br, p.N - 1 - w_row0);  // columns past N are masked in the epilogue
       }
-      src[i] = W + (size_t)n * K + ch * 8;
+      voff[i] = (int)(((size_t)n * K + ch * 8) * 2);
     }
   }
   auto issue = [&](int st, int k0) {
 #pragma unroll
-    for (int i = 0; i < NL; ++i)
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(src[i] + k0),
-          (__attribute__((address_space(3))) void*)(smem + st * KSTAGE + (wave * NL + i) * 64), 16, 0,
-          0);
+    for (int i = 0; i < NL; ++i) {
+      const bool is_a = (wv * NL + i) * 64 < KBM * KCH;
+      raw_buffer_load_lds(is_a ? rsA : rsW,
+                          (__attribute__((address_space(3))) void*)(smem + st * KSTAGE + (wv * NL + i) * 64), 16,
+                          voff[i], k0 * 2, 0, 0);
+    }
   };
 
   f32x4_t acc[KMI][NI];
@@ -276,7 +310,10 @@ __global__ __launch_bounds__((TBM >= 64 ? TBM / 64 : 1) * NWN * 64, 1) void gemm
   step_a(0);
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
-  // the loop boundary sits right after a barrier, where no LDS read is in flight
+  // the loop boundary sits right after a barrier, where no LDS read is in flight.  All
+  // of a slab's copies are issued before its first MFMA: each layer's weights arrive
+  // from HBM, and a copy issued later (spread over the MFMA groups) measured slower
+  // in the recompute although faster with the operands already in the last-level cache.
   for (int kt = 0; kt + 1 < nk; ++kt) {
     const int st = kt & 1;
     if (kt + 2 < nk) issue(st, kb + (kt + 2) * BK);
@@ -540,7 +577,7 @@ __global__ __launch_bounds__((TBM >= 64 ? TBM / 64 : 1) * NWN * 64, 1) void gemm
 // (16 gate + 16 up for SiLU) and all ceil(M/16) row blocks, so N/16 waves
 // stream the weights instead of N/256 workgroups.  K is cut into stages of
 // SK_KC (512 for a single row block when K allows); each stage's W rows and A
-// rows are copied by global_load_lds into a private LDS ring of D stages, so D
+// rows are copied by buffer_load ... lds into a private LDS ring of D stages, so D
 // stages of loads are in flight while the MFMAs consume the oldest.  A single
 // wave needs no barrier, only vmcnt.  The stage width and the A rows a stage
 // holds change which loads run, never the MFMA chain of an output element.
@@ -596,8 +633,14 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmArgs p) {
     row_base = p.gtiles[3 * blockIdx.y + 1];
     M = p.gtiles[3 * blockIdx.y + 2];
   }
-  // load j of a stage fills ring chunks [j*64, j*64+64): lane's chunk P = j*64 + lane
-  const bf16_t* src[LPS];
+  // load j of a stage fills ring chunks [j*64, j*64+64): lane's chunk P = j*64 + lane.
+  // WCH is a multiple of 64, so a load reads W or A for all its lanes.  Descriptors
+  // start at the wave's first W row and its first A row (the source base when rows
+  // are gathered).
+  const int w_row0 = (KIND == K_ROPE) ? rh * 128 : cb * 16;
+  const i32x4_t rsW = buffer_rsrc(W + (size_t)w_row0 * K);
+  const i32x4_t rsA = buffer_rsrc(GATHER ? p.A : p.A + (size_t)row_base * K);
+  int voff[LPS];
 #pragma unroll
   for (int j = 0; j < LPS; ++j) {
     const int P = j * 64 + lane;
@@ -605,26 +648,26 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmArgs p) {
       const int r = P / ROWCH, ch = (P % ROWCH) ^ (r & 15);
       int wr;
       if constexpr (KIND == K_ROPE) {
-        wr = rh * 128 + re0 + (r & 15) + (r >= 16 ? 64 : 0);
+        wr = re0 + (r & 15) + (r >= 16 ? 64 : 0);
       } else {
-        wr = min(cb * 16 + (r & 15), ncols - 1);
+        wr = min(cb * 16 + (r & 15), ncols - 1) - w_row0;
         if (NB == 2 && r >= 16) wr += ncols;             // up rows follow the gate rows
       }
-      src[j] = W + (size_t)wr * K + ch * 8;
+      voff[j] = (int)(((size_t)wr * K + ch * 8) * 2);
     } else {
       const int P2 = P - WCH;
       const int r = P2 / ROWCH, ch = (P2 % ROWCH) ^ (r & 15);
-      int ar = row_base + min(r, M - 1);
-      if constexpr (GATHER) ar = p.a_rows[ar] / p.a_div;
-      src[j] = p.A + (size_t)ar * K + ch * 8;
+      int ar = min(r, M - 1);
+      if constexpr (GATHER) ar = p.a_rows[row_base + ar] / p.a_div;
+      voff[j] = (int)(((size_t)ar * K + ch * 8) * 2);
     }
   }
   auto issue = [&](int slot, int k0) {
 #pragma unroll
     for (int j = 0; j < LPS; ++j)
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(src[j] + k0),
-          (__attribute__((address_space(3))) void*)(ring + slot * SCH + j * 64), 16, 0, 0);
+      raw_buffer_load_lds(j * 64 < WCH ? rsW : rsA,
+                          (__attribute__((address_space(3))) void*)(ring + slot * SCH + j * 64), 16, voff[j],
+                          k0 * 2, 0, 0);
   };
   f32x4_t acc[NB][MT];
 #pragma unroll

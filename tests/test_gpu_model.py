@@ -159,12 +159,12 @@ def qwen():
 # End-to-end tolerance at 28 layers.  The random-init 28-layer model amplifies
 # rounding-level differences: the fp64 oracle itself, re-run with fp32 accumulation in
 # every linear layer (what any MFMA path does), moves the logprobs of these 16
-# sequences by up to E2E_NOISE_MAX / E2E_NOISE_MEAN (tests/golden/
-# qwen3_oracle_fp32_sensitivity.txt, written by make_qwen3_sensitivity.py from the
-# oracle alone).  The end-to-end bound is twice that noise; the structural check at
-# full size is the per-layer test below.
-E2E_NOISE_MAX, E2E_NOISE_MEAN = 0.075, 0.025
-E2E_MAX, E2E_MEAN = 2 * E2E_NOISE_MAX, 2 * E2E_NOISE_MEAN
+# sequences by up to E2E_NOISE_MAX / E2E_NOISE_MEAN (worst sequence of each;
+# tests/golden/qwen3_oracle_fp32_sensitivity.txt, written by make_qwen3_sensitivity.py
+# from the oracle alone).  The bounds are 1.67x and 2x that noise; the structural
+# check at full size is the per-layer test below.
+E2E_NOISE_MAX, E2E_NOISE_MEAN = 0.0899, 0.0227
+E2E_MAX, E2E_MEAN = 0.15, 0.045
 
 # the shortest, two middle and the longest of the 16 sequences (by length rank)
 QWEN_RANKS = [0, 5, 10, 15]
@@ -226,9 +226,12 @@ def _gpu_layers(model, seq):
 # to a few tokens -- a mask slip at a tile edge, a wrong cache slot -- fails it), and
 # every element within 4 bf16 ulp plus a multiple of its row's RMS (a fault in a few
 # columns or heads fails it).
+# Each bound is about twice the largest gap measured on MI355X (relative RMS 2.9e-3 /
+# 6.8e-3 for r / m at layer 0 and 0.043 at layer 27; worst row 7.6e-3 at layer 0 and
+# 0.055 deeper; worst element beyond 4 ulp 0.024 and 0.21 of its row's RMS).
 LAYER0_REL, LAYER_REL = 1e-2, 0.08
-LAYER0_ROW_REL, LAYER_ROW_REL = 2e-2, 0.12
-LAYER0_ELEM, LAYER_ELEM = 0.15, 0.6
+LAYER0_ROW_REL, LAYER_ROW_REL = 1.5e-2, 0.11
+LAYER0_ELEM, LAYER_ELEM = 0.05, 0.42
 
 
 def test_qwen3_shaped_layerwise_parity(qwen):
