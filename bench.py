@@ -368,24 +368,35 @@ def rollout_bench(args, cfg):
     stats = engine.acceptance(fast["lp"], inv["lp"])
     weight_bytes = sum(v.numel() for v in weights.values()) * 2
 
-    # (3) invariant rollout throughput at each batch cap, and one run with a random cap
-    # (1..256) per step; every run's logprobs must equal the recompute's bit for bit
+    # (3) rollout throughput at each batch cap in both modes (the same host scheduler,
+    # eager launches), and one invariant run with a random cap (1..256) per step; every
+    # invariant run's logprobs must equal the recompute's bit for bit
     seqs_all = synth.rl_sequences(cfg, n_prompts=32, n_responses=8)
-    m = engine.Model(cfg, weights, max_tokens=8192, max_seqs=256, max_scored=8192,
-                     max_position=1024, seg_keys=QWEN_SEG_KEYS)
-    cache = m.new_cache(256 * 11 + 16)
-    rec = engine.recompute(m, seqs_all, cache)
+    cap_plan = ((1, 2), (8, 16), (32, 64), (128, 128), (256, 256))
     caps = {}
-    for cap, n in ((1, 2), (8, 16), (32, 64), (128, 128), (256, 256)):
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        lp = engine.rollout(m, seqs_all[:n], cache, cap=cap)
-        torch.cuda.synchronize()
-        dt = time.perf_counter() - t0
-        caps[str(cap)] = {"sequences": n, "tokens_per_s": round(sum(len(x) for x in lp) / dt, 1),
-                          "bitwise_equal_to_recompute": all(a.tobytes() == b.tobytes()
-                                                            for a, b in zip(lp, rec[:n]))}
-        log(f"rollout cap {cap}: {caps[str(cap)]}")
+    for mode in ("fast", "invariant"):
+        m = engine.Model(cfg, weights, max_tokens=8192, max_seqs=256, max_scored=8192,
+                         max_position=1024, seg_keys=QWEN_SEG_KEYS, mode=mode)
+        cache = m.new_cache(256 * 11 + 16)
+        rec = engine.recompute(m, seqs_all, cache)
+        engine.rollout(m, seqs_all[:8], cache, cap=8)           # warm-up
+        for cap, n in cap_plan:
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            lp = engine.rollout(m, seqs_all[:n], cache, cap=cap)
+            torch.cuda.synchronize()
+            dt = time.perf_counter() - t0
+            row = caps.setdefault(str(cap), {"sequences": n})
+            row[f"{mode}_tokens_per_s"] = round(sum(len(x) for x in lp) / dt, 1)
+            if mode == "invariant":
+                row["bitwise_equal_to_recompute"] = all(a.tobytes() == b.tobytes()
+                                                        for a, b in zip(lp, rec[:n]))
+                row["invariant_over_fast"] = round(row["invariant_tokens_per_s"] / row["fast_tokens_per_s"], 4)
+            log(f"rollout cap {cap} ({mode}): {row}")
+        if mode == "fast":
+            m.close()
+            del cache
+            torch.cuda.empty_cache()
     rng = np.random.default_rng(9012)
     lp = engine.rollout(m, seqs_all, cache, cap=256,
                         cap_schedule=lambda step: int(rng.integers(1, 257)))
@@ -406,7 +417,7 @@ def rollout_bench(args, cfg):
         "graph_step_bitwise_equal": graph_equal,
         "graph_rollout_cap128": graph_rollout,
         "fast_vs_invariant_logprobs": stats,
-        "invariant_by_cap": caps,
+        "rollout_by_cap": caps,
         "random_cap_bitwise_equal_to_recompute": random_cap_equal}), flush=True)
 
 

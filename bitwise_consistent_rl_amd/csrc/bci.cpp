@@ -545,6 +545,8 @@ static bci_status gemm_checked(bci_ctx* c, const void* A, const int32_t* rows, c
                                int M, int N, int K, int epi, hipStream_t s) {
   // non-invariant mode: split-K with atomics where it beats the invariant
   // schedules (between the skinny range and 256 rows); elsewhere the same kernels
+  // (on the skinny schedule, split-K measured slower: its zero-fill and epilogue
+  // launches cost more than the extra waves gain)
   if (c->cfg.mode == BCI_MODE_FAST && !rows && M > SKINNY_MAX_M && M <= FAST_SPLITK_MAX_M &&
       N <= c->splitk_max_n && K >= 4 * GEMM_BK) {
     HIP_TRY(c, launch_gemm_splitk(A, W, C, M, N, K, epi, c->splitk_ws, s));

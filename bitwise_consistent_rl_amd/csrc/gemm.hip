@@ -30,8 +30,8 @@
 // 4 x 8 MFMA blocks (128 fp32 accumulators per lane); two waves per SIMD, and
 // a wave raises its priority while it issues MFMAs.
 // Workgroups are remapped so each XCD (8 per chip, each with its own L2) gets
-// a contiguous range of tiles, grouped 8 M-tiles at a time so that they share
-// W tiles in L2.
+// a contiguous range of tiles, grouped 4 or 8 M-tiles at a time so that they
+// share W tiles in L2.
 #include "common.h"
 #include "kernels.h"
 
@@ -139,12 +139,15 @@ __global__ __launch_bounds__((TBM >= 64 ? TBM / 64 : 1) * NWN * 64, 1) void gemm
   constexpr int KSTAGE = (KBM + BN) * KCH;
   __shared__ u32x4_t smem[2 * KSTAGE];  // two buffers (2 x 64 KiB at TBM = 256)
 
-  // ---- tile id: XCD-contiguous ranges, then groups of 8 M-tiles
+  // ---- tile id: XCD-contiguous ranges, then groups of GM M-tiles whose tiles run
+  // column by column (GM tiles sharing a W tile in L2).  GM = 4 for the gate_up and
+  // QKV GEMMs, 8 for the others: measured in the recompute (a 4 % faster gate_up; the
+  // O / down projections and the lm_head were slower with 4)
   const int n_tiles = p.tiles_m * p.tiles_n;
   const int per_xcd = gridDim.x >> 3;  // grid is a multiple of 8
   const int tile = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (tile >= n_tiles) return;
-  constexpr int GM = 8;
+  constexpr int GM = (KIND == K_SILU || KIND == K_ROPE) ? 4 : 8;
   const int width = GM * p.tiles_n;
   const int first_m = (tile / width) * GM;
   const int gsz = min(p.tiles_m - first_m, GM);
