@@ -24,8 +24,10 @@ OBJ_DIR = os.path.join(ROOT, "_build", "obj")
 
 SOURCES = ["norm.hip", "gemm.hip", "rope_kv.hip", "attention.hip", "moe.hip", "sparse.hip", "ssd.hip", "backward.hip",
            "attn_backward.hip",
-           "bci.cpp", "ssd_api.cpp", "lmhead_noalloc.cpp"]
+           "bci.cpp", "ssd_api.cpp", "lmhead_noalloc.cpp", "vendor_gemm.cpp"]
 ARCH = "gfx950"
+# hipBLASLt: the non-invariant mode's large-M projections only (vendor_gemm.cpp)
+LINK = ["-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wno-unused-command-line-argument", "-I", os.path.join(ROOT, "include")]
@@ -54,7 +56,7 @@ def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs + LINK
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

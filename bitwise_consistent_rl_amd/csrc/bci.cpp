@@ -23,6 +23,10 @@ namespace {
 
 constexpr int KV_BLOCK = 64;
 constexpr int DEFAULT_PROFILE = 8192;
+constexpr size_t VENDOR_WS_BYTES = (size_t)64 << 20;  // the vendor GEMM's workspace (fast mode)
+#ifndef FAST_VENDOR_QKV
+#define FAST_VENDOR_QKV 1  // fast mode: QKV on the vendor GEMM plus the RoPE kernel
+#endif
 
 struct DevBuf {
   void* p = nullptr;
@@ -56,9 +60,12 @@ struct bci_ctx {
   // and the attention backward's per-row statistics [max_tokens][nq] fp32 (x2)
   float* bw_part = nullptr;
   float *ab_lse = nullptr, *ab_dsum = nullptr;
-  // non-invariant mode: split-K accumulation buffer [FAST_SPLITK_MAX_M, max_n] fp32
+  // non-invariant mode: split-K accumulation buffer [FAST_SPLITK_MAX_M, max_n] fp32, and
+  // the vendor GEMM for large-M projections (null if the library offers no algorithm)
   float* splitk_ws = nullptr;
   int splitk_max_n = 0;
+  void* vendor_ws = nullptr;
+  VendorGemm* vg = nullptr;
   int32_t* meta = nullptr;  // device metadata region
   size_t meta_words = 0;
   // metadata offsets (int32 words)
@@ -228,6 +235,7 @@ bci_status bci_create(const bci_model_config* cfg_in, int32_t device, bci_ctx** 
     c->max_seg = std::min(64, (g.max_position + KV_BLOCK - 1) / KV_BLOCK);
     c->splitk_max_n = std::max({c->qkv_w, 2 * g.intermediate, g.hidden});
     parts.push_back({(void**)&c->splitk_ws, (size_t)FAST_SPLITK_MAX_M * c->splitk_max_n * 4});
+    parts.push_back({(void**)&c->vendor_ws, VENDOR_WS_BYTES});
   }
   if (c->max_seg > 1 && g.attn_split_mode != 1) {
     c->split_tokens = g.max_seqs_per_call;
@@ -264,6 +272,7 @@ bci_status bci_create(const bci_model_config* cfg_in, int32_t device, bci_ctx** 
     *p.dst = (char*)c->ws + off;
     off += align_up(p.bytes, 256);
   }
+  if (g.mode == BCI_MODE_FAST && !vendor_gemm_create(&c->vg, c->vendor_ws, VENDOR_WS_BYTES)) c->vg = nullptr;
   for (int i = 0; i < 2; ++i) {
     if (hipHostMalloc((void**)&c->stage[i], c->meta_words * 4, hipHostMallocDefault) != hipSuccess ||
         hipEventCreateWithFlags(&c->stage_ev[i], hipEventDisableTiming) != hipSuccess) {
@@ -307,6 +316,7 @@ void bci_destroy(bci_ctx* c) {
   if (!c) return;
   (void)hipSetDevice(c->device);
   drop_graphs(c);
+  vendor_gemm_destroy(c->vg);
   if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
   for (auto& e : c->prof_ev)
     if (e) (void)hipEventDestroy(e);
@@ -938,18 +948,27 @@ static bci_status forward_impl(bci_ctx* c, float* lp, hipStream_t s) {
   // QKV epilogue and the residual add into the O and down epilogues (the norm after
   // them then only normalises); the bits are those of the unfused op sequence.
   const bool tiled = T > SKINNY_MAX_M && (g.mode != BCI_MODE_FAST || T > FAST_SPLITK_MAX_M);
+  // the non-invariant mode runs the tiled-range projections (QKV, O, down) on the vendor
+  // GEMM, with RoPE and the residual adds in their own kernels
+  const bool vendor = g.mode == BCI_MODE_FAST && tiled && c->vg != nullptr;
   // calls of at most 4 tokens (latency-bound decode) fuse RoPE into the skinny QKV
   // schedule too, for bf16 caches; above that its two weight streams per wave (half the
   // waves of the plain skinny GEMM) cost more than the launch they save
-  const bool fuse_rope = g.head_dim == 128 && c->qkv_w % GEMM_BN == 0 &&
+  const bool fuse_rope = g.head_dim == 128 && c->qkv_w % GEMM_BN == 0 && !(vendor && FAST_VENDOR_QKV) &&
                          (tiled || (T <= 4 && g.kv_dtype != BCI_KV_FP8_E4M3 && H % 512 == 0));
-  const bool fuse_add = tiled && H % GEMM_BN == 0;
+  const bool fuse_add = tiled && H % GEMM_BN == 0 && !vendor;
+  auto vgemm = [&](const void* A, const void* W, void* C, int N, int K) -> bci_status {
+    if (!vendor_gemm(c->vg, A, W, C, T, N, K, s))
+      return gemm_checked(c, A, nullptr, W, C, T, N, K, EPI_BF16, s);
+    return BCI_OK;
+  };
   // the O or down projection, into bufX or (fused) added into the residual bufR
   auto project = [&](const void* A, const void* W, int K) -> bci_status {
     if (fuse_add) {
       HIP_TRY(c, launch_gemm(A, nullptr, W, c->bufR, T, H, K, EPI_ADD, s));
       return BCI_OK;
     }
+    if (vendor) return vgemm(A, W, c->bufX, H, K);
     return gemm_checked(c, A, nullptr, W, c->bufX, T, H, K, EPI_BF16, s);
   };
   const void* addend = fuse_add ? nullptr : c->bufX;  // what the norms still add
@@ -965,8 +984,11 @@ static bci_status forward_impl(bci_ctx* c, float* lp, hipStream_t s) {
                                       c->meta + c->o_slot, c->rope_cos, c->rope_sin, kv_layer(c, l),
                                       g.n_q_heads, g.n_kv_heads, g.kv_dtype == BCI_KV_FP8_E4M3, s));
     } else {
-      if (bci_status st = gemm_checked(c, c->bufH, nullptr, lw[1], c->bufQKV, T, c->qkv_w, H, EPI_BF16, s))
+      if (vendor) {
+        if (bci_status st = vgemm(c->bufH, lw[1], c->bufQKV, c->qkv_w, H)) return st;
+      } else if (bci_status st = gemm_checked(c, c->bufH, nullptr, lw[1], c->bufQKV, T, c->qkv_w, H, EPI_BF16, s)) {
         return st;
+      }
       if (bci_status st = op_rope(c, c->bufQKV, c->bufQ, l, s)) return st;
     }
     if (bci_status st = op_attn(c, c->bufQ, c->bufO, l, s)) return st;

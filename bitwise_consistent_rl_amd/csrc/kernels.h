@@ -32,6 +32,12 @@ constexpr int SKINNY_MAX_M = 128;
 constexpr int FAST_SPLITK_MAX_M = 256;
 hipError_t launch_gemm_splitk(const void* A, const void* W, void* C, int M, int N, int K, int epi,
                               float* ws, hipStream_t s);
+// ---- vendor_gemm.cpp (BCI_MODE_FAST only): C [M, N] bf16 = A [M, K] . W [N, K]^T
+// through hipBLASLt, whose kernel choice depends on the shape (not batch-invariant).
+struct VendorGemm;
+bool vendor_gemm_create(VendorGemm** out, void* ws, size_t ws_bytes);
+void vendor_gemm_destroy(VendorGemm* v);
+bool vendor_gemm(VendorGemm* v, const void* A, const void* W, void* C, int M, int N, int K, hipStream_t s);
 // Deterministic split-K (any mode): ws holds ceil(K / k_split) * M * N fp32 partials,
 // summed in slice order.  k_split % GEMM_BK == 0; epi EPI_BF16 or EPI_F32.
 hipError_t launch_gemm_ksplit(const void* A, const void* W, void* C, int M, int N, int K, int k_split, int epi,
