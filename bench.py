@@ -1043,6 +1043,9 @@ def main():
 
     tr = gate_up_traffic()
     traffic = tr["bytes_per_launch"] if tr else None
+    # the chip's sustained MFMA rate on random operands (power-limited clock), measured here
+    log("measuring the sustained MFMA rate")
+    sustained = abi.bci_measure_mfma_rate(0, True)
     out = {
         "metric": "invariant logprob-recompute tokens/sec @1 GPU, % roofline; diff/k3-KL must be 0",
         "value": round(scored / (dt / args.steps), 1),
@@ -1065,7 +1068,11 @@ def main():
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "traffic_unit": "HBM bytes per launch at M = 16384 (rocprofv3 FETCH_SIZE + "
                                      "WRITE_SIZE, copy-calibrated)",
-                     "launches": gu_launches, "avg_launch_us": round(gu_ms * 1e3 / max(gu_launches, 1), 2)},
+                     "launches": gu_launches, "avg_launch_us": round(gu_ms * 1e3 / max(gu_launches, 1), 2),
+                     "sustained_peak": round(sustained, 1),
+                     "frac_of_sustained": round(achieved / sustained, 4) if sustained > 0 else None,
+                     "sustained_peak_note": "measured dense bf16 MFMA issue on pseudo-random register "
+                                            "operands, all SIMDs, two waves each (bci_measure_mfma_rate)"},
         "step_roofline": {"algorithmic_tflop_per_step": round(step_flops / 1e12, 3),
                           "achieved_tflops": round(step_flops / (dt / args.steps) / 1e12, 1),
                           "frac_of_mfma_peak": round(step_flops / (dt / args.steps) / 1e12 / PEAK_BF16_TFLOPS, 4)},

@@ -38,7 +38,7 @@ EXPORTS = [
     "bci_ssd_slot_bytes", "bci_ssd_set_batch", "bci_ssd_forward", "bci_op_transpose_bf16",
     "bci_op_add_rmsnorm_backward", "bci_op_silu_mul_backward", "bci_op_logprob_backward_dz",
     "bci_op_rope_backward",
-    "bci_op_attention_backward", "bci_lmhead_logprob_noalloc",
+    "bci_op_attention_backward", "bci_lmhead_logprob_noalloc", "bci_measure_mfma_rate",
 ]
 
 
@@ -129,6 +129,7 @@ def load() -> ctypes.CDLL:
         "bci_ssd_set_batch": (st, [vp, i32, _P32, _P32, _P32, vp]),
         "bci_ssd_forward": (st, [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp]),
         "bci_profile_begin": (st, [vp, i32]),
+        "bci_measure_mfma_rate": (st, [i32, i32, ctypes.POINTER(ctypes.c_double)]),
         "bci_profile_end": (st, [vp, ctypes.POINTER(ctypes.c_double), _P32, ctypes.POINTER(ctypes.c_int64), _P32]),
     }
     for name, (res, args) in sig.items():
@@ -399,6 +400,15 @@ def bci_ssd_forward(ctx: int, x, dt, A, B, C, D, state, chunk_buf, n_slots: int,
     _ssd_check(ctx, load().bci_ssd_forward(ctx, _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
                                            _ptr(D), _ptr(state), _ptr(chunk_buf), n_slots, _ptr(y),
                                            _stream(stream)))
+
+
+def bci_measure_mfma_rate(device: int = 0, random_operands: bool = True) -> float:
+    """Sustained dense bf16 MFMA rate of the device in TFLOP/s (see bci.h)."""
+    t = ctypes.c_double()
+    st = load().bci_measure_mfma_rate(device, int(bool(random_operands)), ctypes.byref(t))
+    if st != BCI_OK:
+        raise BciError(st, "bci_measure_mfma_rate failed")
+    return float(t.value)
 
 
 def bci_profile_begin(ctx: int, capacity: int = 0) -> None:

@@ -22,7 +22,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libbci.so")
 OBJ_DIR = os.path.join(ROOT, "_build", "obj")
 
-SOURCES = ["norm.hip", "gemm.hip", "rope_kv.hip", "attention.hip", "moe.hip", "sparse.hip", "ssd.hip", "backward.hip",
+SOURCES = ["norm.hip", "gemm.hip", "probe.hip", "rope_kv.hip", "attention.hip", "moe.hip", "sparse.hip", "ssd.hip", "backward.hip",
            "attn_backward.hip",
            "bci.cpp", "ssd_api.cpp", "lmhead_noalloc.cpp", "vendor_gemm.cpp"]
 ARCH = "gfx950"

@@ -1133,4 +1133,35 @@ bci_status bci_profile_end(bci_ctx* c, double* total_ms, int32_t* launches, int6
   return BCI_OK;
 }
 
+bci_status bci_measure_mfma_rate(int32_t device, int32_t random_operands, double* tflops) {
+  if (!tflops) return BCI_E_INVALID;
+  *tflops = 0.0;
+  if (hipSetDevice(device) != hipSuccess) return BCI_E_HIP;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess) return BCI_E_HIP;
+  const int blocks = 2 * prop.multiProcessorCount, iters = 100000;
+  float* out = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  bci_status st = BCI_E_HIP;
+  if (hipMalloc(&out, (size_t)blocks * PROBE_BLOCK_THREADS * sizeof(float)) == hipSuccess &&
+      hipEventCreate(&e0) == hipSuccess && hipEventCreate(&e1) == hipSuccess) {
+    // warm up (clocks settle), then time one launch of ~50 ms
+    bool ok = launch_mfma_rate(out, blocks, iters / 2, random_operands, nullptr) == hipSuccess &&
+              launch_mfma_rate(out, blocks, iters / 2, random_operands, nullptr) == hipSuccess &&
+              hipEventRecord(e0, nullptr) == hipSuccess &&
+              launch_mfma_rate(out, blocks, iters, random_operands, nullptr) == hipSuccess &&
+              hipEventRecord(e1, nullptr) == hipSuccess && hipEventSynchronize(e1) == hipSuccess;
+    float ms = 0.0f;
+    if (ok && hipEventElapsedTime(&ms, e0, e1) == hipSuccess && ms > 0.0f) {
+      const double flops = (double)blocks * (PROBE_BLOCK_THREADS / 64) * iters * 16 * 16384.0;
+      *tflops = flops / (ms * 1e-3) / 1e12;
+      st = BCI_OK;
+    }
+  }
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (out) (void)hipFree(out);
+  return st;
+}
+
 }  // extern "C"

@@ -32,6 +32,9 @@ constexpr int SKINNY_MAX_M = 128;
 constexpr int FAST_SPLITK_MAX_M = 256;
 hipError_t launch_gemm_splitk(const void* A, const void* W, void* C, int M, int N, int K, int epi,
                               float* ws, hipStream_t s);
+// ---- probe.hip: back-to-back MFMAs on every SIMD (out: blocks * 512 floats)
+hipError_t launch_mfma_rate(float* out, int blocks, int iters, int random, hipStream_t s);
+constexpr int PROBE_BLOCK_THREADS = 512;
 // ---- vendor_gemm.cpp (BCI_MODE_FAST only): C [M, N] bf16 = A [M, K] . W [N, K]^T
 // through hipBLASLt, whose kernel choice depends on the shape (not batch-invariant).
 struct VendorGemm;

@@ -557,6 +557,14 @@ bci_status bci_profile_begin(bci_ctx* ctx, int32_t capacity);
 bci_status bci_profile_end(bci_ctx* ctx, double* total_ms, int32_t* launches, int64_t* rows,
                            int32_t* dropped);
 
+/* The sustained dense bf16 MFMA rate of HIP device `device`, measured: every SIMD issues
+ * v_mfma_f32_16x16x32_bf16 back to back for ~50 ms (16 independent chains per wave, two
+ * waves per SIMD, operands in registers: pseudo-random bf16 values when random_operands
+ * is non-zero, zeros otherwise) after a warm-up.  *tflops receives the rate in TFLOP/s:
+ * a denominator beside the datasheet peak that includes the power-limited clock.
+ * Allocates and frees a small buffer; synchronises the device's null stream. */
+bci_status bci_measure_mfma_rate(int32_t device, int32_t random_operands, double* tflops);
+
 #ifdef __cplusplus
 }
 #endif
