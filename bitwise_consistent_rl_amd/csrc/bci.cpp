@@ -904,6 +904,7 @@ bci_status bci_op_moe_forward(bci_ctx* c, const void* h, const int32_t* ids, con
     return fail(c, BCI_E_INVALID, "op_moe_forward: shared-expert weights must match n_shared_experts");
   if (T > g.max_tokens_per_call)
     return fail(c, BCI_E_WORKSPACE, "op_moe_forward: T %d > max_tokens_per_call %d", T, g.max_tokens_per_call);
+  if (!aligned16(out)) return fail(c, BCI_E_INVALID, "op_moe_forward: out must be 16-byte aligned");
   if (T == 0) return BCI_OK;
   const hipStream_t s = S(stream);
   const int H = g.hidden, I = g.expert_intermediate, E = g.n_experts, k = g.top_k, P = T * k;

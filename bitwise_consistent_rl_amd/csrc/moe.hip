@@ -93,38 +93,36 @@ __device__ __forceinline__ int block_rank(bool flag, int* wsum, int& total) {
   return before + in_wave;
 }
 
-// Pass 1: one workgroup per expert counts its (token, slot) pairs.
-__global__ __launch_bounds__(256) void moe_count_kernel(const int32_t* __restrict__ ids, int P,
-                                                        int32_t* __restrict__ counts) {
-  __shared__ int wsum[4];
-  const int e = blockIdx.x;
-  int n = 0;
-  for (int base = 0; base < P; base += 256) {
-    const int p = base + threadIdx.x;
-    int tot;
-    block_rank(p < P && ids[p] == e, wsum, tot);
-    n += tot;
-  }
-  if (threadIdx.x == 0) counts[e] = n;
-}
+// Pass 1 (one workgroup): per-expert counts of the (token, slot) pairs by integer
+// LDS atomics (exact in any order), then the expert offsets and the tile list of
+// the grouped GEMMs: tile = (expert, first row, rows), rows <= 256, in expert order.
+constexpr int MOE_PLAN_THREADS = 1024;
 
-// Pass 2 (one workgroup): expert offsets and the tile list of the grouped GEMMs:
-// tile = (expert, first row, rows), rows <= 256, in expert order.
-__global__ __launch_bounds__(64) void moe_plan_kernel(const int32_t* __restrict__ counts, int E,
-                                                      int32_t* __restrict__ offsets,
-                                                      int32_t* __restrict__ tiles,
-                                                      int32_t* __restrict__ n_tiles) {
+__global__ __launch_bounds__(MOE_PLAN_THREADS) void moe_plan_kernel(const int32_t* __restrict__ ids, int P, int E,
+                                                                    int32_t* __restrict__ counts,
+                                                                    int32_t* __restrict__ offsets,
+                                                                    int32_t* __restrict__ tiles,
+                                                                    int32_t* __restrict__ n_tiles) {
+  __shared__ int hist[64];
+  if (threadIdx.x < 64) hist[threadIdx.x] = 0;
+  __syncthreads();
+  for (int p = threadIdx.x; p < P; p += MOE_PLAN_THREADS) {
+    const int e = ids[p];
+    if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+  }
+  __syncthreads();
+  if (threadIdx.x < E) counts[threadIdx.x] = hist[threadIdx.x];
   if (threadIdx.x != 0) return;
   int off = 0, nt = 0;
   for (int e = 0; e < E; ++e) {
     offsets[e] = off;
-    for (int r = 0; r < counts[e]; r += GEMM_BM) {
+    for (int r = 0; r < hist[e]; r += GEMM_BM) {
       tiles[3 * nt] = e;
       tiles[3 * nt + 1] = off + r;
-      tiles[3 * nt + 2] = min(GEMM_BM, counts[e] - r);
+      tiles[3 * nt + 2] = min(GEMM_BM, hist[e] - r);
       ++nt;
     }
-    off += counts[e];
+    off += hist[e];
   }
   offsets[E] = off;
   *n_tiles = nt;
@@ -155,39 +153,66 @@ __global__ __launch_bounds__(256) void moe_scatter_kernel(const int32_t* __restr
 hipError_t launch_moe_sort(const int32_t* ids, int P, int E, int32_t* counts, int32_t* offsets,
                            int32_t* perm, int32_t* inv, int32_t* tiles, int32_t* n_tiles,
                            hipStream_t s) {
-  hipLaunchKernelGGL(moe_count_kernel, dim3(E), dim3(256), 0, s, ids, P, counts);
-  hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(64), 0, s, counts, E, offsets, tiles, n_tiles);
+  hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(MOE_PLAN_THREADS), 0, s, ids, P, E, counts, offsets, tiles,
+                     n_tiles);
   hipLaunchKernelGGL(moe_scatter_kernel, dim3(E), dim3(256), 0, s, ids, P, offsets, perm, inv);
   return hipGetLastError();
 }
 
 // out[t] = bf( fma-chain over s = 0..k-1 of w[t,s] * y[inv[t*k+s]] , then + y_shared[t] ).
 // A slot whose expert id is outside [0, E) poisons the row with NaN instead of
-// reading an unset position.
-__global__ __launch_bounds__(256) void moe_combine_kernel(const bf16_t* __restrict__ y,
-                                                          const bf16_t* __restrict__ ys,
-                                                          const int32_t* __restrict__ ids,
-                                                          const float* __restrict__ w,
-                                                          const int32_t* __restrict__ inv, int k,
-                                                          int E, int H, bf16_t* __restrict__ out) {
+// reading an unset position.  Each thread owns 8 consecutive columns (16-byte loads of
+// every slot's row); every element is the same chain whatever thread computes it.
+constexpr int COMBINE_THREADS = 256;
+
+__global__ __launch_bounds__(COMBINE_THREADS) void moe_combine_kernel(const bf16_t* __restrict__ y,
+                                                                      const bf16_t* __restrict__ ys,
+                                                                      const int32_t* __restrict__ ids,
+                                                                      const float* __restrict__ w,
+                                                                      const int32_t* __restrict__ inv, int k,
+                                                                      int E, int H, bf16_t* __restrict__ out) {
   const int t = blockIdx.x;
   bool ok = true;
-  for (int s = 0; s < k; ++s) {
-    const int e = ids[(size_t)t * k + s];
-    ok = ok && e >= 0 && e < E;
-  }
-  for (int c = threadIdx.x; c < H; c += 256) {
-    float acc = 0.0f;
-    if (ok) {
-      for (int s = 0; s < k; ++s) {
-        const size_t row = (size_t)inv[(size_t)t * k + s];
-        acc = __builtin_fmaf(w[(size_t)t * k + s], bf2f(y[row * H + c]), acc);
-      }
-      if (ys) acc = acc + bf2f(ys[(size_t)t * H + c]);
-    } else {
-      acc = __uint_as_float(0x7fc00000u);
+  float ws[MOE_MAX_K];
+  size_t rows[MOE_MAX_K];
+#pragma unroll
+  for (int s = 0; s < MOE_MAX_K; ++s) {
+    if (s < k) {
+      const int e = ids[(size_t)t * k + s];
+      ok = ok && e >= 0 && e < E;
+      ws[s] = w[(size_t)t * k + s];
+      rows[s] = (size_t)inv[(size_t)t * k + s];
     }
-    out[(size_t)t * H + c] = f2bf(acc);
+  }
+  for (int c0 = threadIdx.x * 8; c0 < H; c0 += COMBINE_THREADS * 8) {
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    if (ok) {
+#pragma unroll
+      for (int s = 0; s < MOE_MAX_K; ++s) {
+        if (s < k) {
+          const uint4 v = *reinterpret_cast<const uint4*>(y + rows[s] * H + c0);
+          const bf16_t* vp = reinterpret_cast<const bf16_t*>(&v);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(ws[s], bf2f(vp[i]), acc[i]);
+        }
+      }
+      if (ys) {
+        const uint4 v = *reinterpret_cast<const uint4*>(ys + (size_t)t * H + c0);
+        const bf16_t* vp = reinterpret_cast<const bf16_t*>(&v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = acc[i] + bf2f(vp[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = __uint_as_float(0x7fc00000u);
+    }
+    uint4 o;
+    uint32_t* op = reinterpret_cast<uint32_t*>(&o);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) op[i] = pack_bf2(f2bf(acc[2 * i]), f2bf(acc[2 * i + 1]));
+    *reinterpret_cast<uint4*>(out + (size_t)t * H + c0) = o;
   }
 }
 
@@ -195,7 +220,8 @@ hipError_t launch_moe_combine(const void* y, const void* ys, const int32_t* ids,
                               const int32_t* inv, int T, int k, int E, int H, void* out,
                               hipStream_t s) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(moe_combine_kernel, dim3(T), dim3(256), 0, s, (const bf16_t*)y,
+  if (H % 8) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(moe_combine_kernel, dim3(T), dim3(COMBINE_THREADS), 0, s, (const bf16_t*)y,
                      (const bf16_t*)ys, ids, w, inv, k, E, H, (bf16_t*)out);
   return hipGetLastError();
 }

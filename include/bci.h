@@ -398,7 +398,8 @@ bci_status bci_op_moe_topk(bci_ctx* ctx, const float* logits, int32_t T, int32_t
  *   outside [0, n_experts) makes that token's row NaN);
  *   wgu [n_experts, 2 I, hidden] (gate rows then up rows), wd [n_experts, hidden, I];
  *   swgu [2 I, hidden], swd [hidden, I] the ungated shared expert (NULL when
- *   n_shared_experts == 0); out [T, hidden] bf16.  T <= max_tokens_per_call. */
+ *   n_shared_experts == 0); out [T, hidden] bf16, 16-byte aligned.
+ *   T <= max_tokens_per_call. */
 bci_status bci_op_moe_forward(bci_ctx* ctx, const void* h, const int32_t* ids, const float* w,
                               int32_t T, const void* wgu, const void* wd, const void* swgu,
                               const void* swd, void* out, void* stream);
