@@ -523,15 +523,18 @@ static bci_status op_attn(bci_ctx* c, const void* q, void* o, int layer, hipStre
   const bool few_tiles = c->n_tiles * g.n_kv_heads < 1024;
   if (g.mode == BCI_MODE_FAST) {
     // non-invariant: segment size chosen from this call's shape (prefill: one
-    // segment; decode: enough segments for ~1024 workgroups), so the same query
-    // meets different reduction trees in different calls
+    // segment; calls with fewer workgroups than CUs, i.e. small decode batches:
+    // enough segments for ~1024 workgroups), so the same query meets different
+    // reduction trees in different calls.  (Splitting calls of 256-1023 workgroups
+    // measured slower: B = 64 decode 2.78 -> 2.99 ms.)
+    const bool fast_split = c->n_tiles * g.n_kv_heads < 256;
     int max_pos = 0;
     for (int i = 0; i < c->n_seqs; ++i)
       max_pos = std::max(max_pos, c->h_pos0[i] + c->h_cu[i + 1] - c->h_cu[i] - 1);
     const int chunks = max_pos / KV_BLOCK + 1;
-    int n_split = few_tiles ? std::min({c->max_seg, chunks, (1024 + c->n_tiles * g.n_kv_heads - 1) /
+    int n_split = fast_split ? std::min({c->max_seg, chunks, (1024 + c->n_tiles * g.n_kv_heads - 1) /
                                                               (c->n_tiles * g.n_kv_heads)})
-                            : 1;
+                             : 1;
     if (c->n_tokens > c->split_tokens || !c->attn_part_acc) n_split = 1;
     const int cps = (chunks + n_split - 1) / n_split;
     a.seg_keys = cps * KV_BLOCK;
@@ -553,12 +556,13 @@ static bci_status op_attn(bci_ctx* c, const void* q, void* o, int layer, hipStre
 
 static bci_status gemm_checked(bci_ctx* c, const void* A, const int32_t* rows, const void* W, void* C,
                                int M, int N, int K, int epi, hipStream_t s) {
-  // non-invariant mode: split-K with atomics where it beats the invariant
-  // schedules (between the skinny range and 256 rows); elsewhere the same kernels
-  // (on the skinny schedule, split-K measured slower: its zero-fill and epilogue
-  // launches cost more than the extra waves gain)
+  // non-invariant mode: split-K with atomics where it beats the invariant schedules --
+  // between the skinny range and 256 rows, for long contractions (K >= 4096: the down
+  // projection, 114 -> 50-71 us at 160-256 rows); with K = 2048 the zero-fill and
+  // epilogue launches cost more than the split gains (e.g. QKV 42 -> 78-125 us), and on the
+  // skinny schedule too (decode step B = 1 1.76 -> 2.05 ms), so those keep the same kernels
   if (c->cfg.mode == BCI_MODE_FAST && !rows && M > SKINNY_MAX_M && M <= FAST_SPLITK_MAX_M &&
-      N <= c->splitk_max_n && K >= 4 * GEMM_BK) {
+      N <= c->splitk_max_n && K >= 4096) {
     HIP_TRY(c, launch_gemm_splitk(A, W, C, M, N, K, epi, c->splitk_ws, s));
     return BCI_OK;
   }

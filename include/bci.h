@@ -77,10 +77,11 @@ typedef enum {
  * they are faster: the QKV, O and down projections of calls above 256 tokens run
  * on the vendor GEMM (hipBLASLt, whose kernel choice depends on the shape), with
  * RoPE, the cache write and the residual adds in separate kernels; GEMMs with
- * 128 < M <= 256 split K across workgroups and add fp32 partials with atomics
- * (order, hence bits, depend on timing); and attention sizes its KV segments from
- * each call's shape (prefill and decode meet different reduction trees).  Its
- * results are NOT batch-invariant. */
+ * 128 < M <= 256 and K >= 4096 split K across workgroups and add fp32 partials
+ * with atomics (order, hence bits, depend on timing); and attention sizes its KV
+ * segments from each call's shape, splitting calls with fewer workgroups than CUs
+ * (prefill and decode meet different reduction trees).  Its results are NOT
+ * batch-invariant. */
 typedef enum { BCI_MODE_INVARIANT = 0, BCI_MODE_FAST = 1 } bci_mode;
 typedef enum { BCI_KV_BF16 = 0, BCI_KV_FP8_E4M3 = 1 } bci_kv_dtype;
 typedef enum { BCI_EPI_BF16 = 0, BCI_EPI_F32 = 1, BCI_EPI_SILU_MUL = 2 } bci_epilogue;
