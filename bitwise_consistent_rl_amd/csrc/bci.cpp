@@ -961,7 +961,12 @@ static bci_status forward_impl(bci_ctx* c, float* lp, hipStream_t s) {
   // waves of the plain skinny GEMM) cost more than the launch they save
   const bool fuse_rope = g.head_dim == 128 && c->qkv_w % GEMM_BN == 0 && !(vendor && FAST_VENDOR_QKV) &&
                          (tiled || (T <= 4 && g.kv_dtype != BCI_KV_FP8_E4M3 && H % 512 == 0));
-  const bool fuse_add = tiled && H % GEMM_BN == 0 && !vendor;
+  // calls of at most 4 tokens (decode) fold the norms into the GEMMs after them: the O
+  // and down projections add into the residual in their epilogue and the QKV and gate_up
+  // projections normalise their A rows themselves (launch_gemm_norm), so of the add+RMSNorm
+  // launches only the embedding's and the final one remain; the bits are unchanged
+  const bool fuse_norm = !tiled && T <= 4 && H % 512 == 0 && H <= 2048;
+  const bool fuse_add = (tiled && H % GEMM_BN == 0 && !vendor) || fuse_norm;
   auto vgemm = [&](const void* A, const void* W, void* C, int N, int K) -> bci_status {
     if (!vendor_gemm(c->vg, A, W, C, T, N, K, s))
       return gemm_checked(c, A, nullptr, W, C, T, N, K, EPI_BF16, s);
@@ -979,10 +984,19 @@ static bci_status forward_impl(bci_ctx* c, float* lp, hipStream_t s) {
   const void* addend = fuse_add ? nullptr : c->bufX;  // what the norms still add
   for (int l = 0; l < g.n_layers; ++l) {
     const void* const* lw = &c->w[1 + 6 * l];  // attn_norm, wqkv, wo, mlp_norm, wgu, wd
-    if (l > 0)
+    // the layer's A rows: bufH, or normalised inside the QKV GEMM from the residual
+    const bool qkv_norm = fuse_norm && l > 0;
+    if (l > 0 && !qkv_norm)
       HIP_TRY(c, launch_add_rmsnorm(addend, c->bufR, c->bufR, c->bufH, lw[0], nullptr, nullptr, T, H,
                                     g.rms_eps, s));
-    if (fuse_rope) {
+    if (fuse_rope && qkv_norm) {
+      HIP_TRY(c, launch_gemm_qkv_rope_norm(c->bufR, lw[0], g.rms_eps, lw[1], T, c->qkv_w, H, c->bufQ,
+                                           c->meta + c->o_pos, c->meta + c->o_slot, c->rope_cos, c->rope_sin,
+                                           kv_layer(c, l), g.n_q_heads, g.n_kv_heads, s));
+    } else if (qkv_norm) {
+      HIP_TRY(c, launch_gemm_norm(c->bufR, lw[0], g.rms_eps, lw[1], c->bufQKV, T, c->qkv_w, H, EPI_BF16, s));
+      if (bci_status st = op_rope(c, c->bufQKV, c->bufQ, l, s)) return st;
+    } else if (fuse_rope) {
       // tiled QKV GEMM with RoPE and the KV write in its epilogue: the same bits as the
       // GEMM into bufQKV followed by op_rope (the op-by-op path), without bufQKV
       HIP_TRY(c, launch_gemm_qkv_rope(c->bufH, lw[1], T, c->qkv_w, H, c->bufQ, c->meta + c->o_pos,
@@ -998,14 +1012,19 @@ static bci_status forward_impl(bci_ctx* c, float* lp, hipStream_t s) {
     }
     if (bci_status st = op_attn(c, c->bufQ, c->bufO, l, s)) return st;
     if (bci_status st = project(c->bufO, lw[2], c->qd)) return st;
-    HIP_TRY(c, launch_add_rmsnorm(addend, c->bufR, c->bufR, c->bufH, lw[3], nullptr, nullptr, T, H,
-                                  g.rms_eps, s));
+    if (!fuse_norm)
+      HIP_TRY(c, launch_add_rmsnorm(addend, c->bufR, c->bufR, c->bufH, lw[3], nullptr, nullptr, T, H,
+                                    g.rms_eps, s));
     const bool prof = c->prof_on && !c->graph_mode && c->prof_n < c->prof_cap;
     if (c->prof_on && !c->graph_mode && !prof) ++c->prof_dropped;
     if (prof) HIP_TRY(c, hipEventRecord(c->prof_ev[2 * c->prof_n], s));
-    if (bci_status st = gemm_checked(c, c->bufH, nullptr, lw[4], c->bufACT, T, 2 * g.intermediate, H,
-                                     EPI_SILU, s))
+    if (fuse_norm) {
+      HIP_TRY(c, launch_gemm_norm(c->bufR, lw[3], g.rms_eps, lw[4], c->bufACT, T, 2 * g.intermediate, H, EPI_SILU,
+                                  s));
+    } else if (bci_status st = gemm_checked(c, c->bufH, nullptr, lw[4], c->bufACT, T, 2 * g.intermediate, H,
+                                            EPI_SILU, s)) {
       return st;
+    }
     if (prof) {
       HIP_TRY(c, hipEventRecord(c->prof_ev[2 * c->prof_n + 1], s));
       c->prof_rows[c->prof_n++] = T;

@@ -104,6 +104,10 @@ struct GemmArgs {
   const float* rsin;
   KvLayer kv;
   int nq, nkv, fp8;
+  // skinny NORM (M <= 4): A rows are RMSNorm(res rows) * gamma, computed in the kernel
+  const bf16_t* res;
+  const bf16_t* gamma;
+  float eps;
 };
 
 // Row r of an LDS tile holds 8 chunks of 16 bytes; chunk c is stored at
@@ -585,6 +589,7 @@ __global__ __launch_bounds__((TBM >= 64 ? TBM / 64 : 1) * NWN * 64, 1) void gemm
 // wave needs no barrier, only vmcnt.  The stage width and the A rows a stage
 // holds change which loads run, never the MFMA chain of an output element.
 constexpr int SK_KC = 128;                  // K per stage (default)
+constexpr int SK_NORM_MAX_K = 2048;         // NORM: K (the hidden size) up to one norm slice per thread
 
 
 // s_waitcnt immediate for "vmcnt <= v" (gfx9 encoding; lgkmcnt/expcnt unconstrained)
@@ -594,6 +599,31 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((V & 15) | ((V >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// The value of lane l ^ O, without a trip through LDS addressing where the hardware
+// has a lane pattern for it: DPP quad permutes (O = 1, 2) and row rotate by 8 (O = 8),
+// swizzle in bitmask mode (O = 4, 16) and the gfx950 half-wave swap (O = 32).  The bits
+// are moved, not computed, so a butterfly built on it adds the same values in the same
+// pairs as one built on __shfl_xor.
+template <int O>
+__device__ __forceinline__ float lane_xor(float v) {
+  const int u = __float_as_int(v);
+  if constexpr (O == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap((unsigned)u, (unsigned)u, false, false);
+    return __uint_as_float(__lane_id() < 32 ? r[1] : r[0]);
+  } else if constexpr (O == 16) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(u, 0x401F));
+  } else if constexpr (O == 8) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(u, 0x128, 0xF, 0xF, true));
+  } else if constexpr (O == 4) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(u, 0x101F));
+  } else if constexpr (O == 2) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(u, 0x4E, 0xF, 0xF, true));
+  } else {
+    static_assert(O == 1, "xor distance");
+    return __int_as_float(__builtin_amdgcn_mov_dpp(u, 0xB1, 0xF, 0xF, true));
+  }
+}
+
 // GROUPED (the MoE expert GEMMs with few rows per expert): blockIdx.y is an entry of
 // the device tile list (group, first row, rows <= 16), W is the group's slice, A rows
 // are gathered through a_rows when GATHER.
@@ -601,17 +631,24 @@ __device__ __forceinline__ void wait_vmcnt() {
 // AR read row AR - 1 (their outputs are never stored), so a stage copies 4 A rows
 // instead of 16.  KC: K per stage (SK_KC, or 512 for one row block: each W row is then
 // read in 1 KiB runs rather than 256-byte ones).
-template <int KIND, int MT, bool GATHER = false, bool GROUPED = false, int AR = 16 * MT, int KC = SK_KC>
+// NORM (M <= 4, K <= 2048, no gather): the A rows are not copied from memory but
+// normalised by the wave itself from the residual rows p.res and the weight p.gamma,
+// with the add+RMSNorm kernel's expressions and reduction tree (see norm_rows below),
+// into an LDS region of their own; the weight stream starts before that work.
+template <int KIND, int MT, bool GATHER = false, bool GROUPED = false, int AR = 16 * MT, int KC = SK_KC,
+          bool NORM = false>
 __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmArgs p) {
   static_assert(AR == 16 * MT || (MT == 1 && AR == 4), "A rows per stage");
+  static_assert(!NORM || (MT == 1 && AR == 4 && !GATHER && !GROUPED), "norm-fused A: M <= 4, plain rows");
   constexpr int ROWCH = KC / 8;                         // 16-byte chunks per row per stage
   // weight streams: (gate, up) rows for SiLU; for RoPE the rows e and e + 64 of a head
   constexpr int NB = (KIND == K_SILU || KIND == K_ROPE) ? 2 : 1;
   constexpr int WCH = NB * 16 * ROWCH;                  // W chunks per stage
-  constexpr int SCH = WCH + AR * ROWCH;                 // chunks per stage
+  constexpr int SCH = WCH + (NORM ? 0 : AR * ROWCH);    // chunks per stage
   constexpr int LPS = SCH / 64;                         // wave loads per stage
   static_assert(SCH % 64 == 0, "whole wave loads per stage");
-  constexpr int D_LDS = (128 * 1024 / 16) / SCH;
+  constexpr int NA_ROW = SK_NORM_MAX_K / 8;             // NORM: A chunks per row (rows 4 KiB apart)
+  constexpr int D_LDS = (128 * 1024 / 16 - (NORM ? AR * NA_ROW : 0)) / SCH;
   constexpr int D_VM = 1 + 63 / LPS;
   constexpr int D0 = D_LDS < D_VM ? D_LDS : D_VM;
   constexpr int D = D0 > 16 ? 16 : D0;                  // ring depth (stages in flight)
@@ -620,6 +657,7 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmArgs p) {
   auto swz = [](int row, int ch) { return row * ROWCH + (ch ^ (row & 15)); };
   static_assert(D >= 2, "ring too shallow");
   __shared__ u32x4_t ring[D * SCH];
+  __shared__ u32x4_t a_nrm[NORM ? AR * NA_ROW : 1];
   const int lane = threadIdx.x;
   const int K = p.K;
   const int ncols = (KIND == K_SILU || KIND == K_ROPE) ? p.N / 2 : p.N;
@@ -678,9 +716,98 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmArgs p) {
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi) acc[b][mi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int nst = K / KC;
+  // NORM: the residual rows and the norm weight are loaded before the weight stream is
+  // issued (loads complete in issue order, so waiting for them then waits for nothing
+  // else) and normalised while the first stages stream in
+  // (unconditional, at clamped addresses -- rows past M repeat row M - 1, columns past K
+  // repeat the last 8 -- so that they issue back to back and are waited for once)
+  uint4 xv[NORM ? 4 : 1][4], gv[4];
+  if constexpr (NORM) {
 #pragma unroll
-  for (int st = 0; st < D; ++st)
-    if (st < nst) issue(st, st * KC);
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int c0 = min((w * 64 + lane) * 8, K - 8);
+        xv[r][w] = *reinterpret_cast<const uint4*>(p.res + (size_t)min(r, M - 1) * K + c0);
+      }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) gv[w] = *reinterpret_cast<const uint4*>(p.gamma + min((w * 64 + lane) * 8, K - 8));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int st = 0; st < D; ++st) {
+    // NORM issues every stage unconditionally (a stage past the last one re-reads the
+    // last into a slot never read): with a branch here the compiler's wait for the
+    // residual rows would have to cover the path without copies and so wait for them
+    if constexpr (NORM) issue(st, min(st, nst - 1) * KC);
+    else if (st < nst) issue(st, st * KC);
+  }
+  if constexpr (NORM) {
+    // The add+RMSNorm kernel runs 256 threads on a row, thread t over columns
+    // [8t, 8t + 8) (one slice: K <= 2048): its sum of squares in column order, the
+    // xor butterfly over each 64-thread wave, the four wave sums added in wave order,
+    // inv = 1 / sqrt(sum / K + eps), h = bf((x * inv) * g).  Lane l plays threads
+    // l, l + 64, l + 128 and l + 192, so every value and every addition is the same.
+    // Row r's chunk c (8 columns) is stored at r * NA_ROW + (c ^ 4r): the MFMA reads
+    // 4 consecutive chunks of 4 rows, which then fall in 16 distinct bank groups.
+    // sums of squares of the M rows, then their butterflies step by step together
+    // (the exchanges of the 4 per row overlap)
+    float ssw[4][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        float ss = 0.0f;
+        if (r < M && (w * 64 + lane) * 8 < K) {
+          const bf16_t* xp = reinterpret_cast<const bf16_t*>(&xv[r][w]);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float x = bf2f(xp[i]);
+            ss = ss + x * x;
+          }
+        }
+        ssw[r][w] = ss;
+      }
+    auto bfly = [&](auto O) {
+      constexpr int o = decltype(O)::value;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (r < M) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) ssw[r][w] = ssw[r][w] + lane_xor<o>(ssw[r][w]);
+        }
+    };
+    bfly(std::integral_constant<int, 32>{});
+    bfly(std::integral_constant<int, 16>{});
+    bfly(std::integral_constant<int, 8>{});
+    bfly(std::integral_constant<int, 4>{});
+    bfly(std::integral_constant<int, 2>{});
+    bfly(std::integral_constant<int, 1>{});
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (r >= M) break;
+      float tot = ssw[r][0];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) tot = tot + ssw[r][w];
+      const float inv = 1.0f / sqrtf(tot / (float)K + p.eps);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int t = w * 64 + lane;
+        if (t * 8 < K) {
+          const bf16_t* gp = reinterpret_cast<const bf16_t*>(&gv[w]);
+          const bf16_t* xp = reinterpret_cast<const bf16_t*>(&xv[r][w]);
+          u32x4_t hv;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float h0 = (bf2f(xp[2 * i]) * inv) * bf2f(gp[2 * i]);
+            const float h1 = (bf2f(xp[2 * i + 1]) * inv) * bf2f(gp[2 * i + 1]);
+            hv[i] = pack_bf2(f2bf(h0), f2bf(h1));
+          }
+          a_nrm[r * NA_ROW + (t ^ (4 * r))] = hv;
+        }
+      }
+    }
+  }
   for (int c = 0; c < nst; ++c) {
     if (c + D - 1 < nst) wait_vmcnt<(D - 1) * LPS>();   // stage c has landed
     else wait_vmcnt<0>();
@@ -693,8 +820,14 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmArgs p) {
       for (int b = 0; b < NB; ++b) bw[b] = __builtin_bit_cast(bf16x8_t, stg[swz(b * 16 + (lane & 15), ch)]);
 #pragma unroll
       for (int mi = 0; mi < MT; ++mi) {
-        const int ar = AR == 16 * MT ? mi * 16 + (lane & 15) : min(lane & 15, AR - 1);
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, stg[WCH + swz(ar, ch)]);
+        bf16x8_t a;
+        if constexpr (NORM) {
+          const int ar = min(lane & 15, M - 1);
+          a = __builtin_bit_cast(bf16x8_t, a_nrm[ar * NA_ROW + ((c * ROWCH + ch) ^ (4 * ar))]);
+        } else {
+          const int ar = AR == 16 * MT ? mi * 16 + (lane & 15) : min(lane & 15, AR - 1);
+          a = __builtin_bit_cast(bf16x8_t, stg[WCH + swz(ar, ch)]);
+        }
 #pragma unroll
         for (int b = 0; b < NB; ++b)
           acc[b][mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bw[b], acc[b][mi], 0, 0, 0);
@@ -745,6 +878,11 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmArgs p) {
         dst[64 + e] = f2bf(y2);
       } else if constexpr (KIND == K_BF16) {
         reinterpret_cast<bf16_t*>(p.C)[(size_t)row * p.N + col] = f2bf(acc[0][mi][r]);
+      } else if constexpr (KIND == K_ADD) {
+        // the residual add in place, with the tiled epilogue's expression bf(bf(x) + r);
+        // each element is read and written by this lane only
+        bf16_t* cp = reinterpret_cast<bf16_t*>(p.C) + (size_t)row * p.N + col;
+        *cp = f2bf(bf2f(f2bf(acc[0][mi][r])) + bf2f(*cp));
       } else {
         reinterpret_cast<float*>(p.C)[(size_t)row * p.N + col] = acc[0][mi][r];
       }
@@ -792,9 +930,12 @@ hipError_t launch_gemm(const void* A, const int32_t* a_rows, const void* W, void
   a.a_div = 1;
   a.tiles_m = (M + BM - 1) / BM;
   a.tiles_n = (epi == EPI_SILU) ? (N / 2) / (BN / 2) : (N + BN - 1) / BN;
-  if (epi == EPI_ADD)
-    return (a_rows || N % BN || (reinterpret_cast<uintptr_t>(C) & 7)) ? hipErrorInvalidValue
-                                                                       : dispatch<K_ADD>(a, false, s);
+  if (epi == EPI_ADD) {
+    if (a_rows) return hipErrorInvalidValue;
+    // calls of at most 4 rows: the skinny schedule with the same in-place add
+    if (M <= 4 && K % SK_KC == 0 && N % 16 == 0) return dispatch_skinny<K_ADD>(a, s);
+    return (N % BN || (reinterpret_cast<uintptr_t>(C) & 7)) ? hipErrorInvalidValue : dispatch<K_ADD>(a, false, s);
+  }
   // decode-sized M: the skinny schedule (same per-element arithmetic, more waves)
   if (!a_rows && M <= SKINNY_MAX_M && K % SK_KC == 0 && N % 16 == 0) {
     switch (epi) {
@@ -993,6 +1134,64 @@ hipError_t launch_gemm_qkv_rope(const void* A, const void* W, int M, int N, int 
   }
   const int grid = (a.tiles_m * a.tiles_n + 7) / 8 * 8;
   hipLaunchKernelGGL((gemm_kernel<K_ROPE, false, false>), dim3(grid), dim3(THREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+// Calls of at most 4 rows whose A is RMSNorm(res) * gamma (the norm before the QKV and
+// gate_up projections): the skinny schedule normalises the rows itself, with the
+// add+RMSNorm kernel's arithmetic, so the bits equal that kernel followed by the GEMM.
+static bool norm_shape_ok(int M, int N, int K) {
+  return M >= 1 && M <= 4 && K % 512 == 0 && K <= SK_NORM_MAX_K && N % 16 == 0;
+}
+
+hipError_t launch_gemm_norm(const void* res, const void* gamma, float eps, const void* W, void* C, int M, int N,
+                            int K, int epi, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  if (!norm_shape_ok(M, N, K) || (epi != EPI_BF16 && epi != EPI_SILU)) return hipErrorInvalidValue;
+  GemmArgs a{};
+  a.W = (const bf16_t*)W;
+  a.C = C;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.a_div = 1;
+  a.res = (const bf16_t*)res;
+  a.gamma = (const bf16_t*)gamma;
+  a.eps = eps;
+  if (epi == EPI_SILU) {
+    if ((N / 2) % 16) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_skinny_kernel<K_SILU, 1, false, false, 4, 512, true>), dim3(N / 32), dim3(64), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((gemm_skinny_kernel<K_BF16, 1, false, false, 4, 512, true>), dim3(N / 16), dim3(64), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_qkv_rope_norm(const void* res, const void* gamma, float eps, const void* W, int M, int N,
+                                     int K, void* q_out, const int32_t* tok_pos, const int32_t* tok_slot,
+                                     const float* rope_cos, const float* rope_sin, KvLayer kv, int nq, int nkv,
+                                     hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  if (!norm_shape_ok(M, N, K) || N % BN != 0 || N != (nq + 2 * nkv) * 128) return hipErrorInvalidValue;
+  GemmArgs a{};
+  a.W = (const bf16_t*)W;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.a_div = 1;
+  a.q_out = (bf16_t*)q_out;
+  a.tok_pos = tok_pos;
+  a.tok_slot = tok_slot;
+  a.rcos = rope_cos;
+  a.rsin = rope_sin;
+  a.kv = kv;
+  a.nq = nq;
+  a.nkv = nkv;
+  a.fp8 = 0;
+  a.res = (const bf16_t*)res;
+  a.gamma = (const bf16_t*)gamma;
+  a.eps = eps;
+  hipLaunchKernelGGL((gemm_skinny_kernel<K_ROPE, 1, false, false, 4, 512, true>), dim3(N / 32), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

@@ -19,8 +19,9 @@ hipError_t launch_gather_rows(const void* src, const int32_t* rows, void* dst, i
                               int cols, hipStream_t s);
 
 // ---- gemm.hip
-// EPI_ADD (tiled schedule only): C is a bf16 residual [M, N] updated in place,
-// C = bf(bf(A W^T) + C) -- the residual add of the add+RMSNorm that follows.
+// EPI_ADD (tiled schedule, or the skinny one for M <= 4): C is a bf16 residual [M, N]
+// updated in place, C = bf(bf(A W^T) + C) -- the residual add of the add+RMSNorm that
+// follows.
 enum GemmEpi { EPI_BF16 = 0, EPI_F32 = 1, EPI_SILU = 2, EPI_ADD = 3 };
 // C = A . W^T.  A [M, K] (rows gathered through a_rows when non-null), W [N, K].
 hipError_t launch_gemm(const void* A, const int32_t* a_rows, const void* W, void* C, int M, int N,
@@ -28,6 +29,12 @@ hipError_t launch_gemm(const void* A, const int32_t* a_rows, const void* W, void
 // launch_gemm runs M <= SKINNY_MAX_M (when K % 128 == 0 and N % 16 == 0) on a
 // skinny schedule with the same per-element arithmetic as the 256x256 tiles.
 constexpr int SKINNY_MAX_M = 128;
+// M <= 4, K % 512 == 0, K <= 2048: A = RMSNorm(res [M, K]) * gamma [K] computed inside
+// the skinny GEMM with the add+RMSNorm kernel's arithmetic (its bits, without its
+// launch); epi EPI_BF16 or EPI_SILU.  The QKV form has the RoPE / bf16 KV-write
+// epilogue of launch_gemm_qkv_rope.
+hipError_t launch_gemm_norm(const void* res, const void* gamma, float eps, const void* W, void* C, int M, int N,
+                            int K, int epi, hipStream_t s);
 // Non-invariant split-K for small M (BCI_MODE_FAST only): ws holds M*N fp32.
 constexpr int FAST_SPLITK_MAX_M = 256;
 hipError_t launch_gemm_splitk(const void* A, const void* W, void* C, int M, int N, int K, int epi,
@@ -80,6 +87,10 @@ hipError_t launch_gemm_qkv_rope(const void* A, const void* W, int M, int N, int 
                                 const int32_t* tok_pos, const int32_t* tok_slot, const float* rope_cos,
                                 const float* rope_sin, KvLayer kv, int nq, int nkv, bool fp8,
                                 hipStream_t s);
+hipError_t launch_gemm_qkv_rope_norm(const void* res, const void* gamma, float eps, const void* W, int M, int N,
+                                     int K, void* q_out, const int32_t* tok_pos, const int32_t* tok_slot,
+                                     const float* rope_cos, const float* rope_sin, KvLayer kv, int nq, int nkv,
+                                     hipStream_t s);
 hipError_t launch_rope_kv_write(const void* qkv, void* q_out, const int32_t* tok_pos,
                                 const int32_t* tok_slot, const float* rope_cos,
                                 const float* rope_sin, KvLayer kv, int T, int nq, int nkv, int d,

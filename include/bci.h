@@ -182,8 +182,12 @@ bci_status bci_set_batch(bci_ctx* ctx, const bci_batch* batch, void* stream);
  * Writes d_logprobs[n_scored] (fp32).  This is the "rollout" entry point.  Batches
  * of more than 128 tokens (256 in BCI_MODE_FAST) run RoPE + KV write inside the QKV
  * GEMM's epilogue (head_dim 128) and the residual adds inside the O and down GEMMs'
- * epilogues (hidden % 256 == 0); every logprob and cache byte equals what the same
- * sequence of bci_op_* calls produces. */
+ * epilogues (hidden % 256 == 0).  Batches of at most 4 tokens with hidden % 512
+ * == 0 and hidden <= 2048 add the O and down projections into the residual in those
+ * GEMMs' epilogues and normalise the QKV and gate_up GEMMs' A rows inside those GEMMs
+ * (with RoPE + a bf16 KV write in the QKV epilogue when head_dim is 128), so only
+ * the first and the final add+RMSNorm run as kernels of their own.  Every logprob
+ * and cache byte equals what the same sequence of bci_op_* calls produces. */
 bci_status bci_forward_logprobs(bci_ctx* ctx, float* d_logprobs, void* stream);
 
 /* bci_forward_logprobs replayed from a HIP graph.  On the first call for a batch

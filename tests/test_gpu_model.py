@@ -326,3 +326,35 @@ def test_qkv_rope_fusion_bitwise(kv):
         assert bits_equal(roll, split)
     finally:
         r.model.close()
+
+
+# ---- decode calls of at most 4 tokens: norms folded into the GEMMs around them
+@pytest.mark.parametrize("head_dim", [64, 128])
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_decode_norm_fusion_bitwise(kv, head_dim):
+    """Calls of at most 4 tokens with hidden % 512 == 0 (<= 2048) add the O and down
+    projections into the residual in their epilogue and normalise the QKV and gate_up
+    A rows inside those GEMMs (with RoPE and a bf16 KV write in the QKV epilogue when
+    head_dim is 128); every other call runs the add+RMSNorm kernel.  Token-by-token
+    rollouts at caps 1, 2 and 4 (fused) and 8 (not) must equal the whole-prefill and
+    op-by-op recomputes bit for bit, and the oracle within 2e-2."""
+    nq = 512 // head_dim
+    cfg = synth.ModelConfig(f"hidden-512-d{head_dim}", 2, 512, nq, nq // 2, head_dim, 1536, 4096)
+    seqs = synth.tiny_sequences(cfg, n=6, min_len=40, max_len=160, seed=91)
+    r = Rig(cfg, seqs, kv, 64, gain_noise=True, max_tokens=1024, max_seqs=16, max_position=1024,
+            n_blocks=96)
+    try:
+        ref = r.recompute()
+        assert bits_equal(r.recompute(op_by_op=True), ref)
+        for cap in (1, 2, 4, 8):
+            assert bits_equal(r.rollout(cap, None), ref), cap
+        assert bits_equal(r.rollout(4, 3), ref)     # chunked prefill of 3, then decode
+        W = om.Weights({k: synth.bf16_bits(v) for k, v in r.weights.items()})
+        worst = 0.0
+        for s, got in zip(seqs[:2], ref[:2]):
+            want = om.sequence_logprobs(cfg, W, s.tokens, s.prompt_len, kv)
+            worst = max(worst, float(np.max(np.abs(got.astype(np.float64) - want))))
+        print(f"{kv} d{head_dim}: max |dlogprob| vs oracle = {worst:.3e}", flush=True)
+        assert worst <= 2e-2
+    finally:
+        r.model.close()
