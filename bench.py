@@ -240,7 +240,7 @@ def decode_bench(args, cfg):
                      max_position=1024, seg_keys=QWEN_SEG_KEYS)
     cache = m.new_cache(64 * 11 + 16)
     m.bind_cache(cache)
-    steps = {}
+    steps, graph_steps, graph_equal = {}, {}, {}
     for B in (1, 64):
         sub = seqs[:B]
         mids = [s.prompt_len + s.n_scored // 2 for s in sub]
@@ -267,9 +267,30 @@ def decode_bench(args, cfg):
         torch.cuda.synchronize()
         steps[str(B)] = round(e0.elapsed_time(e1) / args.steps, 3)
         log(f"decode B = {B}: {steps[str(B)]} ms per step")
+        # the same step replayed from a captured HIP graph (block table padded to the
+        # context's width, as the graphed rollout pads it); the bits must not change
+        width = -(-m.max_position // engine.KV_BLOCK)
+        abi.bci_set_batch(m.ctx, np.array([s.tokens[mid] for s, mid in zip(sub, mids)], np.int32),
+                          np.arange(B + 1, dtype=np.int32), np.array(mids, np.int32),
+                          np.array([b + [0] * (width - len(b)) for b in blocks], np.int32),
+                          np.arange(B, dtype=np.int32),
+                          np.array([s.tokens[mid + 1] for s, mid in zip(sub, mids)], np.int32))
+        gout = torch.empty(B, dtype=torch.float32, device="cuda")
+        for _ in range(3):
+            abi.bci_forward_logprobs_graph(m.ctx, gout)
+        e0.record()
+        for _ in range(args.steps):
+            abi.bci_forward_logprobs_graph(m.ctx, gout)
+        e1.record()
+        torch.cuda.synchronize()
+        graph_steps[str(B)] = round(e0.elapsed_time(e1) / args.steps, 3)
+        graph_equal[str(B)] = bool(torch.equal(gout.view(torch.int32), out.view(torch.int32)))
+        log(f"decode B = {B}, graph replay: {graph_steps[str(B)]} ms per step, "
+            f"bitwise equal to eager: {graph_equal[str(B)]}")
     m.close()
     weight_bytes = sum(v.numel() for v in weights.values()) * 2
     print(json.dumps({"workload": "qwen3-1.7b-shaped decode steps", "decode_step_ms": steps,
+                      "decode_step_ms_graph": graph_steps, "graph_step_bitwise_equal": graph_equal,
                       "steps": args.steps,
                       "weight_streaming_floor_ms": round(weight_bytes / (PEAK_HBM_GBS * 1e6), 3)}),
           flush=True)

@@ -74,6 +74,10 @@ struct ChunkLoader {
   static constexpr int VPT = (VUN + ATHREADS - 1) / ATHREADS;
   static constexpr int KUN = CHUNK * CH16;          // FP8 K units (1 key, 16 codes)
   static constexpr int KPT = FP8 ? (KUN + ATHREADS - 1) / ATHREADS : 0;
+  // every thread owns a whole number of units: no per-unit bound test (a branch around
+  // a load makes the compiler's wait before each later use cover the path without it)
+  static constexpr bool V_EVEN = VUN % ATHREADS == 0;
+  static constexpr bool K_EVEN = KUN % ATHREADS == 0;
 
   // registers in flight
   u32x4_t va[VPT], vb[VPT];
@@ -103,7 +107,7 @@ struct ChunkLoader {
 #pragma unroll
       for (int j = 0; j < VPT; ++j) {
         const int u = j * ATHREADS + tid;
-        if (u < VUN) {
+        if (V_EVEN || u < VUN) {
           int kp, ch;
           vunit(u, kp, ch);
           va[j] = *reinterpret_cast<const u32x4_t*>(vg + (2 * kp) * D + ch * 8);
@@ -118,7 +122,7 @@ struct ChunkLoader {
 #pragma unroll
       for (int j = 0; j < KPT; ++j) {
         const int u = j * ATHREADS + tid;
-        if (u < KUN) {
+        if (K_EVEN || u < KUN) {
           const int key = u / CH16, c16 = u % CH16;
           kr[j] = *reinterpret_cast<const u32x4_t*>(kg + key * D + c16 * 16);
           ksc[j] = ksg[key];
@@ -127,7 +131,7 @@ struct ChunkLoader {
 #pragma unroll
       for (int j = 0; j < VPT; ++j) {
         const int u = j * ATHREADS + tid;
-        if (u < VUN) {
+        if (V_EVEN || u < VUN) {
           int kp, c16;
           vunit(u, kp, c16);
           va[j] = *reinterpret_cast<const u32x4_t*>(vg + (2 * kp) * D + c16 * 16);
@@ -151,7 +155,7 @@ struct ChunkLoader {
 #pragma unroll
       for (int j = 0; j < KPT; ++j) {
         const int u = j * ATHREADS + tid;
-        if (u < KUN) {
+        if (K_EVEN || u < KUN) {
           const int key = u / CH16, c16 = u % CH16;
           float x[16];
           kv_decode16_f32(reinterpret_cast<const uint32_t*>(&kr[j]), ksc[j], x);
@@ -169,7 +173,7 @@ struct ChunkLoader {
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
       const int u = j * ATHREADS + tid;
-      if (u < VUN) {
+      if (V_EVEN || u < VUN) {
         int kp, ch;
         vunit(u, kp, ch);
         const int k0 = 2 * kp;
@@ -286,9 +290,16 @@ __device__ __forceinline__ void load_chunk_sync(const AttnArgs& p, int blk, int 
 // multiplied.  !PIPE (the split schedule, used for decode-like calls with few
 // rows per tile): one LDS buffer and short register lifetimes, so twice as
 // many workgroups fit on a CU to hide the load latency.
-template <int D, bool FP8, bool SPLIT>
+// PF2 (PIPE, tiles of at most 16 rows: decode): two chunks in flight instead of one.
+// A decode tile's chunk costs one memory latency per chunk when only the next chunk is
+// fetched, while its arithmetic is a small fraction of that; with the loads of chunks
+// c + 1 and c + 2 outstanding while chunk c is multiplied, and the issues unconditional
+// (a chunk index past the last is clamped, its copy never used), the wait before
+// storing chunk c + 1 leaves chunk c + 2's loads in flight.
+template <int D, bool FP8, bool SPLIT, bool PF2 = false>
 __global__ __launch_bounds__(ATHREADS, SPLIT ? 4 : 2) void attention_kernel(AttnArgs p) {
   constexpr bool PIPE = !SPLIT;
+  static_assert(!(PF2 && SPLIT), "two chunks in flight: pipelined schedule only");
   constexpr int NBUF = PIPE ? 2 : 1;
   __shared__ __attribute__((aligned(16))) u32x4_t Ks[NBUF][CHUNK * D / 8];
   __shared__ __attribute__((aligned(16))) bf16_t Vt[NBUF][D * VT_STRIDE];
@@ -326,6 +337,8 @@ __global__ __launch_bounds__(ATHREADS, SPLIT ? 4 : 2) void attention_kernel(Attn
   // smallest position among this wave's valid rows (rows are token-major)
   const int wave_tk0 = (wave * 16) / group;
   const int wave_qpos_min = wave_tk0 < n_tok ? pos_begin + wave_tk0 : INT_MAX;
+  // a wave without a valid row (decode tiles fill one wave of 16 rows) only loads
+  const bool wave_active = wave_tk0 < n_tok;
 
   const int last_chunk = kmax / CHUNK;
   const int seg_chunks = p.seg_keys / CHUNK;
@@ -337,8 +350,9 @@ __global__ __launch_bounds__(ATHREADS, SPLIT ? 4 : 2) void attention_kernel(Attn
     c_stop = min(c_first + seg_chunks - 1, last_chunk);
   }
 
-  ChunkLoader<D, FP8> ld;
+  ChunkLoader<D, FP8> ld, ld2;
   if constexpr (PIPE) ld.issue(p, btab[c_first], g, tid);
+  if constexpr (PF2) ld2.issue(p, btab[min(c_first + 1, c_stop)], g, tid);
 
   bf16x8_t qf[D / 32];
 #pragma unroll
@@ -362,17 +376,10 @@ __global__ __launch_bounds__(ATHREADS, SPLIT ? 4 : 2) void attention_kernel(Attn
     ld.store(kmax - c_first * CHUNK, Ks[0], Vt[0], tid);
     __syncthreads();
   }
+  if constexpr (PF2) ld.issue(p, btab[min(c_first + 2, c_stop)], g, tid);
 
-  for (int c = c_first; c <= c_stop; ++c) {
-    const int b = PIPE ? (c - c_first) & 1 : 0;
-    const bool more = c < c_stop;
-    if constexpr (PIPE) {
-      if (more) ld.issue(p, btab[c + 1], g, tid);
-    } else {
-      if (c > c_first) __syncthreads();  // the previous chunk's LDS reads are done
-      load_chunk_sync<D, FP8>(p, btab[c], g, kmax - c * CHUNK, Ks[0], Vt[0], tid);
-      __syncthreads();
-    }
+  // the arithmetic of chunk c out of LDS buffer b (identical for every schedule)
+  auto compute_chunk = [&](int c, int b) __attribute__((always_inline)) {
     const bool seg_start = (c % seg_chunks) == 0 || c == c_first;
     if (seg_start) m = -INFINITY;
     const u32x4_t* Kb = Ks[b];
@@ -546,10 +553,42 @@ __global__ __launch_bounds__(ATHREADS, SPLIT ? 4 : 2) void attention_kernel(Attn
       }
     }
 
-    if constexpr (PIPE) {
-      // buffer b^1 was released by the previous iteration's barrier
-      if (more) ld.store(kmax - (c + 1) * CHUNK, Ks[b ^ 1], Vt[b ^ 1], tid);
+  };
+
+  if constexpr (PF2) {
+    // chunk c_first + i is held by ld (i even) or ld2 (i odd) until stored; at step i
+    // the other set (chunk i + 1) is stored, then refilled with chunk i + 3
+    auto step = [&](auto odd, int c) __attribute__((always_inline)) {
+      constexpr int b = decltype(odd)::value ? 1 : 0;
+      if (wave_active) compute_chunk(c, b);
+      if constexpr (b == 0) ld2.store(kmax - (c + 1) * CHUNK, Ks[1], Vt[1], tid);
+      else ld.store(kmax - (c + 1) * CHUNK, Ks[0], Vt[0], tid);
       __syncthreads();  // publishes buffer b^1, releases buffer b
+      if constexpr (b == 0) ld2.issue(p, btab[min(c + 3, c_stop)], g, tid);
+      else ld.issue(p, btab[min(c + 3, c_stop)], g, tid);
+    };
+    for (int c = c_first; c <= c_stop; c += 2) {
+      step(std::false_type{}, c);
+      if (c + 1 > c_stop) break;
+      step(std::true_type{}, c + 1);
+    }
+  } else {
+    for (int c = c_first; c <= c_stop; ++c) {
+      const int b = PIPE ? (c - c_first) & 1 : 0;
+      const bool more = c < c_stop;
+      if constexpr (PIPE) {
+        if (more) ld.issue(p, btab[c + 1], g, tid);
+      } else {
+        if (c > c_first) __syncthreads();  // the previous chunk's LDS reads are done
+        load_chunk_sync<D, FP8>(p, btab[c], g, kmax - c * CHUNK, Ks[0], Vt[0], tid);
+        __syncthreads();
+      }
+      if (wave_active) compute_chunk(c, b);
+      if constexpr (PIPE) {
+        // buffer b^1 was released by the previous iteration's barrier
+        if (more) ld.store(kmax - (c + 1) * CHUNK, Ks[b ^ 1], Vt[b ^ 1], tid);
+        __syncthreads();  // publishes buffer b^1, releases buffer b
+      }
     }
   }
 
@@ -614,6 +653,9 @@ static void launch_d(const AttnArgs& a, hipStream_t s) {
                        dim3(ATHREADS), 0, s, a);
     hipLaunchKernelGGL((attention_merge_kernel<D>), dim3(a.n_tokens, (a.nq * D + 255) / 256),
                        dim3(256), 0, s, a);
+  } else if (a.pf2) {
+    hipLaunchKernelGGL((attention_kernel<D, FP8, false, true>), dim3(a.n_tiles, a.nkv), dim3(ATHREADS),
+                       0, s, a);
   } else {
     hipLaunchKernelGGL((attention_kernel<D, FP8, false>), dim3(a.n_tiles, a.nkv), dim3(ATHREADS),
                        0, s, a);

@@ -550,6 +550,14 @@ static bci_status op_attn(bci_ctx* c, const void* q, void* o, int layer, hipStre
   }
   a.part_acc = c->attn_part_acc;
   a.part_ml = c->attn_part_ml;
+  // every tile at most 16 rows (one wave's worth) and fewer workgroups than CUs (small
+  // decode batches, where each chunk's loads would otherwise wait a memory latency):
+  // the unsplit schedule with two chunks in flight.  Measured, same box: B = 1 decode
+  // step 1.752 -> 1.727 ms; at B = 64 (512 workgroups) its two extra clamped chunk
+  // loads per tile cost more than they hide (2.77 -> 2.83 ms), so it stays off there
+  int max_q = 0;
+  for (int i = 0; i < c->n_seqs; ++i) max_q = std::max(max_q, c->h_cu[i + 1] - c->h_cu[i]);
+  a.pf2 = max_q * (g.n_q_heads / g.n_kv_heads) <= 16 && c->n_tiles * g.n_kv_heads < 256;
   HIP_TRY(c, launch_attention(a, s));
   return BCI_OK;
 }

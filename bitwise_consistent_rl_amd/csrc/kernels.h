@@ -115,6 +115,8 @@ struct AttnArgs {
   int n_seg, n_tokens;
   float* part_acc;             // [n_seg][T][nq][d]
   float* part_ml;              // [n_seg][T][nq][2]
+  // unsplit schedule with two chunks in flight (tiles of at most 16 rows: decode)
+  bool pf2;
 };
 constexpr int ATTN_ROWS = 64;  // query rows (token x head-in-group) per tile
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
