@@ -966,7 +966,9 @@ static bci_status forward_impl(bci_ctx* c, float* lp, hipStream_t s) {
   const bool vendor = g.mode == BCI_MODE_FAST && tiled && c->vg != nullptr;
   // calls of at most 4 tokens (latency-bound decode) fuse RoPE into the skinny QKV
   // schedule too, for bf16 caches; above that its two weight streams per wave (half the
-  // waves of the plain skinny GEMM) cost more than the launch they save
+  // waves of the plain skinny GEMM) cost about what the launch saves (up to 128 tokens,
+  // same box: B = 64 decode step 2.559 vs 2.560 ms, rollout caps 8 / 32 / 128 -0.3 /
+  // -1.0 / +1.6 %)
   const bool fuse_rope = g.head_dim == 128 && c->qkv_w % GEMM_BN == 0 && !(vendor && FAST_VENDOR_QKV) &&
                          (tiled || (T <= 4 && g.kv_dtype != BCI_KV_FP8_E4M3 && H % 512 == 0));
   // calls of at most 4 tokens (decode) fold the norms into the GEMMs after them: the O

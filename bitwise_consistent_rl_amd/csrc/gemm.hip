@@ -1136,14 +1136,14 @@ hipError_t launch_gemm_qkv_rope(const void* A, const void* W, int M, int N, int 
     // decode-sized calls, bf16 cache (an FP8 scale needs a head's 128 values, spread
     // over 4 waves here): the skinny schedule, one wave per 16 rotation pairs
     if (fp8 || K % SK_KC) return hipErrorInvalidValue;
-    const dim3 grid(N / 32);
-    const int mt = (M + 15) / 16;
+    const int mt = std::min((M + 15) / 16, SKINNY_ROW_BLOCKS_PER_WAVE);
+    const dim3 grid(N / 32), gm(N / 32, (M + 16 * mt - 1) / (16 * mt));
     if (M <= 4 && K % 512 == 0)
       hipLaunchKernelGGL((gemm_skinny_kernel<K_ROPE, 1, false, false, 4, 512>), grid, dim3(64), 0, s, a);
-    else if (mt == 1) hipLaunchKernelGGL((gemm_skinny_kernel<K_ROPE, 1>), grid, dim3(64), 0, s, a);
-    else if (mt == 2) hipLaunchKernelGGL((gemm_skinny_kernel<K_ROPE, 2>), grid, dim3(64), 0, s, a);
-    else if (mt <= 4) hipLaunchKernelGGL((gemm_skinny_kernel<K_ROPE, 4>), grid, dim3(64), 0, s, a);
-    else hipLaunchKernelGGL((gemm_skinny_kernel<K_ROPE, 8>), grid, dim3(64), 0, s, a);
+    else if (mt == 1) hipLaunchKernelGGL((gemm_skinny_kernel<K_ROPE, 1>), gm, dim3(64), 0, s, a);
+    else if (mt == 2) hipLaunchKernelGGL((gemm_skinny_kernel<K_ROPE, 2>), gm, dim3(64), 0, s, a);
+    else if (mt <= 4) hipLaunchKernelGGL((gemm_skinny_kernel<K_ROPE, 4>), gm, dim3(64), 0, s, a);
+    else hipLaunchKernelGGL((gemm_skinny_kernel<K_ROPE, 8>), gm, dim3(64), 0, s, a);
     return hipGetLastError();
   }
   const int grid = (a.tiles_m * a.tiles_n + 7) / 8 * 8;
