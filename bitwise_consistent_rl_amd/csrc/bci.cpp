@@ -570,7 +570,7 @@ static bci_status gemm_checked(bci_ctx* c, const void* A, const int32_t* rows, c
   // epilogue launches cost more than the split gains (e.g. QKV 42 -> 78-125 us), and on the
   // skinny schedule too (decode step B = 1 1.76 -> 2.05 ms), so those keep the same kernels
   if (c->cfg.mode == BCI_MODE_FAST && !rows && M > SKINNY_MAX_M && M <= FAST_SPLITK_MAX_M &&
-      N <= c->splitk_max_n && K >= 4096) {
+      N <= c->splitk_max_n && K >= 4096 && !gemm_prefers_skinny(M, N, K, epi, false)) {
     HIP_TRY(c, launch_gemm_splitk(A, W, C, M, N, K, epi, c->splitk_ws, s));
     return BCI_OK;
   }

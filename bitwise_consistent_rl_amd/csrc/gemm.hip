@@ -12,8 +12,9 @@
 // v_mfma_f32_16x16x32_bf16(A[i, k:k+32], W[j, k:k+32]) for k = 0, 32, 64, ...
 // in ascending order; nothing else is ever added to it.  The schedules below
 // (256 x 256 x 64 tiles with 8 waves; the skinny one-wave-per-16-columns
-// schedule for M <= 128; 16- and 64-row lm_head tiles for few scored rows) are
-// chosen by M, but each runs exactly this chain for every element it owns, with
+// schedule for M <= 128, and up to 512 where it is faster; 16- and 64-row lm_head
+// tiles for few scored rows) are chosen by the shape, but each runs exactly this chain
+// for every element it owns, with
 // no split-K, and an MFMA output element depends only on its own A row and W
 // row, so the bits of row i are the same whatever M is, whichever schedule runs
 // and wherever row i sits in a tile.
@@ -919,6 +920,24 @@ static hipError_t dispatch_skinny(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Schedule choice for M in (SKINNY_MAX_M, SKINNY_DENSE_MAX_M]: a 256 x 256 tile takes
+// ~42 us per 2048 of K, and a call with no more tiles than CUs takes one tile's time;
+// the skinny schedule takes ~11 ns per (wave x 2048 of K x weight stream) plus ~5 us,
+// with N/16 waves (N/32 for the two-stream SiLU and RoPE forms) per 32 rows.  Measured
+// (us, tiled / skinny): M = 160: O 41 / 12, down 112 / 31, QKV 41 / 20, gate_up 42 / 39;
+// M = 512: O 42 / 26, down 116 / 64, QKV 43 / 51, gate_up 46 / 111.  Either way every
+// output element is the same chain.
+bool gemm_prefers_skinny(int M, int N, int K, int epi, bool rope) {
+  if (M <= SKINNY_MAX_M) return true;
+  if (M > SKINNY_DENSE_MAX_M || K % SK_KC != 0 || N % 16 != 0) return false;
+  const bool two = rope || epi == EPI_SILU;
+  const double waves = (double)(two ? N / 32 : N / 16) * ((M + 31) / 32);
+  const double skinny_us = 5.0 + 0.011 * waves * (K / 2048.0) * (two ? 2 : 1);
+  const int tiles = ((M + BM - 1) / BM) * (two ? (N / 2) / (BN / 2) : (N + BN - 1) / BN);
+  const double tiled_us = 42.0 * (K / 2048.0) * ((tiles + 255) / 256);
+  return skinny_us < tiled_us;
+}
+
 template <int KIND>
 static hipError_t dispatch(const GemmArgs& a, bool gather, hipStream_t s) {
   const int n_tiles = a.tiles_m * a.tiles_n;
@@ -946,12 +965,13 @@ hipError_t launch_gemm(const void* A, const int32_t* a_rows, const void* W, void
   a.tiles_n = (epi == EPI_SILU) ? (N / 2) / (BN / 2) : (N + BN - 1) / BN;
   if (epi == EPI_ADD) {
     if (a_rows) return hipErrorInvalidValue;
-    // calls of at most 4 rows: the skinny schedule with the same in-place add
-    if (M <= 4 && K % SK_KC == 0 && N % 16 == 0) return dispatch_skinny<K_ADD>(a, s);
+    // decode-sized and mid-sized calls: the skinny schedule with the same in-place add
+    if (K % SK_KC == 0 && N % 16 == 0 && gemm_prefers_skinny(M, N, K, epi, false)) return dispatch_skinny<K_ADD>(a, s);
     return (N % BN || (reinterpret_cast<uintptr_t>(C) & 7)) ? hipErrorInvalidValue : dispatch<K_ADD>(a, false, s);
   }
-  // decode-sized M: the skinny schedule (same per-element arithmetic, more waves)
-  if (!a_rows && M <= SKINNY_MAX_M && K % SK_KC == 0 && N % 16 == 0) {
+  // decode-sized M, and mid-sized M where it is faster: the skinny schedule (same
+  // per-element arithmetic, more waves)
+  if (!a_rows && K % SK_KC == 0 && N % 16 == 0 && gemm_prefers_skinny(M, N, K, epi, false)) {
     switch (epi) {
       case EPI_BF16: return dispatch_skinny<K_BF16>(a, s);
       case EPI_F32: return dispatch_skinny<K_F32>(a, s);
@@ -1132,9 +1152,10 @@ hipError_t launch_gemm_qkv_rope(const void* A, const void* W, int M, int N, int 
   a.nq = nq;
   a.nkv = nkv;
   a.fp8 = fp8 ? 1 : 0;
-  if (M <= SKINNY_MAX_M) {
-    // decode-sized calls, bf16 cache (an FP8 scale needs a head's 128 values, spread
-    // over 4 waves here): the skinny schedule, one wave per 16 rotation pairs
+  if (M <= SKINNY_MAX_M || (!fp8 && gemm_prefers_skinny(M, N, K, EPI_BF16, true))) {
+    // decode-sized calls (and mid-sized ones where it is faster), bf16 cache (an FP8
+    // scale needs a head's 128 values, spread over 4 waves here): the skinny schedule,
+    // one wave per 16 rotation pairs
     if (fp8 || K % SK_KC) return hipErrorInvalidValue;
     const int mt = std::min((M + 15) / 16, SKINNY_ROW_BLOCKS_PER_WAVE);
     const dim3 grid(N / 32), gm(N / 32, (M + 16 * mt - 1) / (16 * mt));

@@ -29,6 +29,13 @@ hipError_t launch_gemm(const void* A, const int32_t* a_rows, const void* W, void
 // launch_gemm runs M <= SKINNY_MAX_M (when K % 128 == 0 and N % 16 == 0) on a
 // skinny schedule with the same per-element arithmetic as the 256x256 tiles.
 constexpr int SKINNY_MAX_M = 128;
+// Between SKINNY_MAX_M and SKINNY_DENSE_MAX_M rows a dense GEMM (launch_gemm, the QKV +
+// RoPE form with a bf16 cache) takes whichever schedule a latency model of the two
+// predicts faster (gemm_prefers_skinny); the grouped expert GEMMs keep SKINNY_MAX_M.
+constexpr int SKINNY_DENSE_MAX_M = 512;
+// epi: EPI_BF16 / EPI_F32 / EPI_SILU / EPI_ADD; rope: the QKV + RoPE form (two weight
+// streams per wave, like SiLU)
+bool gemm_prefers_skinny(int M, int N, int K, int epi, bool rope);
 // M <= 4, K % 512 == 0, K <= 2048: A = RMSNorm(res [M, K]) * gamma [K] computed inside
 // the skinny GEMM with the add+RMSNorm kernel's arithmetic (its bits, without its
 // launch); epi EPI_BF16 or EPI_SILU.  The QKV form has the RoPE / bf16 KV-write

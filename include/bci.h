@@ -33,8 +33,9 @@
  *     starts at zero and receives v_mfma_f32_16x16x32_bf16 of its own A row and
  *     W row over ascending 32-wide K steps, and nothing else.  Several schedules
  *     assign elements to workgroups -- 256 x 256 tiles, a skinny one-wave-per-16-
- *     columns schedule for M <= 128, 16- and 64-row lm_head tiles for few scored
- *     rows -- and which one runs depends on M, but every schedule performs this
+ *     columns-and-32-rows schedule for M <= 128 (and up to 512 where a latency
+ *     model of the call's M, N and K favours it), 16- and 64-row lm_head tiles for
+ *     few scored rows -- and which one runs depends on the shape, but every one performs this
  *     same per-element chain (no split-K, no atomics), so the bits of a row never
  *     depend on M or on the row's place in a tile (page "Finish RL Training
  *     Faster" digest, section "让训练前向使用推理的数值": batch-invariant dense GEMM

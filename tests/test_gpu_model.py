@@ -324,6 +324,12 @@ def test_qkv_rope_fusion_bitwise(kv):
         c3 = r.model.new_cache(128)
         roll = eng().rollout(r.model, seqs, c3, cap=3)
         assert bits_equal(roll, split)
+        # calls of ~200-400 tokens (2 sequences x 200-token prefill chunks): above the
+        # decode range, where each projection takes the skinny or the tiled schedule by
+        # a latency model, with the RoPE / KV-write and residual-add epilogues either way
+        c4 = r.model.new_cache(128)
+        roll2 = eng().rollout(r.model, seqs, c4, cap=2, prefill_chunk=200)
+        assert bits_equal(roll2, split)
     finally:
         r.model.close()
 
