@@ -328,14 +328,21 @@ __global__ __launch_bounds__(ATHREADS, SPLIT ? 4 : 2) void attention_kernel(Attn
   const int* btab = p.block_table + (size_t)seq * p.max_blocks;
   const size_t qstride = (size_t)p.nq * D;
 
-  // this lane's query row (B operand of S^T and column of O^T)
-  const int row = wave * 16 + lc;
+  // this lane's query row (B operand of S^T and column of O^T).  PF2 (tiles of at most
+  // 16 rows): every wave takes rows 0-15, computes the same scores and softmax
+  // statistics, and owns D/64 of the D/16 head-dimension blocks of P.V, the rescales
+  // and the output, so the four waves split the chunk's PV work instead of three idling
+  constexpr int DT = D / 16;                    // 16-wide head-dimension blocks
+  constexpr int DPW = PF2 ? DT / 4 : DT;        // blocks this wave accumulates
+  const int rw = PF2 ? 0 : wave;
+  const int dt0 = PF2 ? wave * DPW : 0;
+  const int row = rw * 16 + lc;
   const int tk = row / group;
   const int hq = g * group + row % group;
   const bool row_ok = tk < n_tok;
   const int qpos = row_ok ? pos_begin + tk : -1;
   // smallest position among this wave's valid rows (rows are token-major)
-  const int wave_tk0 = (wave * 16) / group;
+  const int wave_tk0 = (rw * 16) / group;
   const int wave_qpos_min = wave_tk0 < n_tok ? pos_begin + wave_tk0 : INT_MAX;
   // a wave without a valid row (decode tiles fill one wave of 16 rows) only loads
   const bool wave_active = wave_tk0 < n_tok;
@@ -366,11 +373,11 @@ __global__ __launch_bounds__(ATHREADS, SPLIT ? 4 : 2) void attention_kernel(Attn
   }
 
   float M = -INFINITY, L = 0.0f;
-  f32x4_t ACC[D / 16];
+  f32x4_t ACC[DPW];
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) ACC[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < DPW; ++j) ACC[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.0f;
-  f32x4_t acc[D / 16];
+  f32x4_t acc[DPW];
 
   if constexpr (PIPE) {
     ld.store(kmax - c_first * CHUNK, Ks[0], Vt[0], tid);
@@ -476,21 +483,21 @@ __global__ __launch_bounds__(ATHREADS, SPLIT ? 4 : 2) void attention_kernel(Attn
         pw[3] = pack_f2bf2(pr[2 * k2 + 1][2], pr[2 * k2 + 1][3]);
         const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pw);
         const int ko = k2 * 32 + 4 * lg;
-        u32x4_t vw[D / 16];  // all fragments of the step are read, then multiplied
+        u32x4_t vw[DPW];  // all fragments of the step are read, then multiplied
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-          const bf16_t* vr = Vb + (dt * 16 + lc) * VT_STRIDE;
+        for (int j = 0; j < DPW; ++j) {
+          const bf16_t* vr = Vb + ((dt0 + j) * 16 + lc) * VT_STRIDE;
           const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vr + ko);
           const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vr + ko + 16);
-          vw[dt] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+          vw[j] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
         }
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-          const f32x4_t c0 = (decltype(from_zero)::value && k2 == 0) ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc[dt];
-          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vw[dt]), pf, c0, 0, 0, 0);
+        for (int j = 0; j < DPW; ++j) {
+          const f32x4_t c0 = (decltype(from_zero)::value && k2 == 0) ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc[j];
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vw[j]), pf, c0, 0, 0, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, D / 16, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, DPW, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, DPW, 0);
       }
     };
     // (m, l, acc) = (-inf, 0, 0) at a segment start: alpha = 2^(-inf) = 0, so
@@ -509,7 +516,7 @@ __global__ __launch_bounds__(ATHREADS, SPLIT ? 4 : 2) void attention_kernel(Attn
       if (seg_start) {
         l = rs;
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < DPW; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       } else {
         const float alpha = fexp2(m - mu);
         l = mul_unless_one(l, alpha) + rs;
@@ -525,12 +532,12 @@ __global__ __launch_bounds__(ATHREADS, SPLIT ? 4 : 2) void attention_kernel(Attn
         const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pw);
         const int ko = k2 * 32 + 4 * lg;
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-          const bf16_t* vr = Vb + (dt * 16 + lc) * VT_STRIDE;
+        for (int j = 0; j < DPW; ++j) {
+          const bf16_t* vr = Vb + ((dt0 + j) * 16 + lc) * VT_STRIDE;
           const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vr + ko);
           const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vr + ko + 16);
           const u32x4_t vw = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vw), pf, acc[dt], 0, 0, 0);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vw), pf, acc[j], 0, 0, 0);
         }
       }
     }
@@ -546,9 +553,9 @@ __global__ __launch_bounds__(ATHREADS, SPLIT ? 4 : 2) void attention_kernel(Attn
         scale_unless_one(ACC, a);
         scale_unless_one(acc, bb);
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt)
+        for (int j = 0; j < DPW; ++j)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) ACC[dt][r] = ACC[dt][r] + acc[dt][r];
+          for (int r = 0; r < 4; ++r) ACC[j][r] = ACC[j][r] + acc[j][r];
         M = Mn;
       }
     }
@@ -597,8 +604,8 @@ __global__ __launch_bounds__(ATHREADS, SPLIT ? 4 : 2) void attention_kernel(Attn
       const size_t prow = ((size_t)blockIdx.z * p.n_tokens + tok_begin + tk) * p.nq + hq;
       float* pa = p.part_acc + prow * D;
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt)
-        *reinterpret_cast<f32x4_t*>(pa + dt * 16 + 4 * lg) = acc[dt];
+      for (int j = 0; j < DPW; ++j)
+        *reinterpret_cast<f32x4_t*>(pa + (dt0 + j) * 16 + 4 * lg) = acc[j];
       if (lg == 0) {
         p.part_ml[prow * 2] = m;
         p.part_ml[prow * 2 + 1] = l;
@@ -611,11 +618,11 @@ __global__ __launch_bounds__(ATHREADS, SPLIT ? 4 : 2) void attention_kernel(Attn
     bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + (size_t)(tok_begin + tk) * qstride + hq * D;
     const float il = attn_inv_l(L);
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
+    for (int j = 0; j < DPW; ++j) {
       u32x2_t w;
-      w[0] = pack_f2bf2(ACC[dt][0] * il, ACC[dt][1] * il);
-      w[1] = pack_f2bf2(ACC[dt][2] * il, ACC[dt][3] * il);
-      *reinterpret_cast<u32x2_t*>(orow + dt * 16 + 4 * lg) = w;
+      w[0] = pack_f2bf2(ACC[j][0] * il, ACC[j][1] * il);
+      w[1] = pack_f2bf2(ACC[j][2] * il, ACC[j][3] * il);
+      *reinterpret_cast<u32x2_t*>(orow + (dt0 + j) * 16 + 4 * lg) = w;
     }
   }
 }
