@@ -904,10 +904,16 @@ template <int KIND>
 #ifndef SKINNY_ROW_BLOCKS_PER_WAVE
 #define SKINNY_ROW_BLOCKS_PER_WAVE 2
 #endif
+// The SiLU form streams two weight rows per output column, so a second row group
+// costs twice the re-read: 64 rows per wave there (B = 64 decode step 2.557 -> 2.470 ms
+// against 32, the same as 128).
+#ifndef SKINNY_SILU_ROW_BLOCKS_PER_WAVE
+#define SKINNY_SILU_ROW_BLOCKS_PER_WAVE 4
+#endif
 static hipError_t dispatch_skinny(const GemmArgs& a, hipStream_t s) {
   const int ncols = (KIND == K_SILU) ? a.N / 2 : a.N;
   const int grid = ncols / 16;
-  const int mt = std::min((a.M + 15) / 16, SKINNY_ROW_BLOCKS_PER_WAVE);
+  const int mt = std::min((a.M + 15) / 16, KIND == K_SILU ? SKINNY_SILU_ROW_BLOCKS_PER_WAVE : SKINNY_ROW_BLOCKS_PER_WAVE);
   const bool wide = a.K % 512 == 0;
   const dim3 g1(grid), gm(grid, (a.M + 16 * mt - 1) / (16 * mt));
   if (a.M <= 4 && wide) hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 1, false, false, 4, 512>), g1, dim3(64), 0, s, a);
