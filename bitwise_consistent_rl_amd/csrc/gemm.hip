@@ -282,10 +282,12 @@ __global__ __launch_bounds__((TBM >= 64 ? TBM / 64 : 1) * NWN * 64, 1) void gemm
     }
     __builtin_amdgcn_s_setprio(0);
   };
-  auto step_b = [&](int st, auto prefetch) {
+  // copies(ni) runs before the MFMAs of column block ni (the slab copies' issue point)
+  auto step_b = [&](int st, auto prefetch, auto copies) {
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
+      copies(ni);
 #pragma unroll
       for (int mi = 0; mi < KMI; ++mi) acc[mi][ni] = mfma(fa1[mi], fb[ni], acc[mi][ni]);
       if constexpr (decltype(prefetch)::value) {
@@ -318,19 +320,26 @@ __global__ __launch_bounds__((TBM >= 64 ? TBM / 64 : 1) * NWN * 64, 1) void gemm
   step_a(0);
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
-  // the loop boundary sits right after a barrier, where no LDS read is in flight.  All
-  // of a slab's copies are issued before its first MFMA: each layer's weights arrive
-  // from HBM, and a copy issued later (spread over the MFMA groups) measured slower
-  // in the recompute although faster with the operands already in the last-level cache.
+  // The loop boundary sits right after a barrier, where no LDS read is in flight.  A wave
+  // stalls while its copies are accepted, so the two waves of a SIMD issue theirs at
+  // different points: the first half of the waves before the slab's first MFMAs, the
+  // second half after the first half of the first K step's MFMA groups, while the first
+  // half multiplies.  Measured against all waves issuing together: gate_up 647 -> 584 us,
+  // QKV 228 -> 209, down 302 -> 281, lm_head (M = 8192) 4340 -> 4093; issuing later (the
+  // second K step) or at four points was slower, copies spread over every MFMA group of
+  // every wave slower in the recompute.
+  const int copy_at = wv < (KTHREADS / 64) / 2 ? 0 : NI / 2;
   for (int kt = 0; kt + 1 < nk; ++kt) {
     const int st = kt & 1;
-    if (kt + 2 < nk) issue(st, kb + (kt + 2) * BK);
-    step_b(st, std::true_type{});
+    const bool more = kt + 2 < nk;
+    step_b(st, std::true_type{}, [&](int ni) {
+      if (more && ni == copy_at) issue(st, kb + (kt + 2) * BK);
+    });
     step_a(st ^ 1);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's loads of slab kt+2 have landed
     __syncthreads();
   }
-  step_b((nk - 1) & 1, std::false_type{});
+  step_b((nk - 1) & 1, std::false_type{}, [](int) {});
 
   // ---- epilogues.  Lane holds C[4*(lane>>4) + r][lane & 15] of each 16x16 block.
   const int lrow0 = wm * KWTM + 4 * (lane >> 4);  // row within the tile
