@@ -170,6 +170,23 @@ def test_gemm_rows_invariant_to_M_and_order(ctx, epi):
     assert same_bits(out[150:151], full[17:18])
 
 
+@pytest.mark.parametrize("N,K,epi", [(12288, 2048, "silu"), (4096, 2048, "bf16"), (2048, 6144, "bf16")])
+def test_gemm_mid_m_schedule_choice_bitwise(ctx, N, K, epi):
+    """Between 129 and 512 rows each launch takes the skinny or the tiled schedule by a
+    latency model of its shape (at these widths the choice flips with M: gate_up goes to
+    tiles above 128 rows, QKV above ~400, down stays skinny to 512); every row must equal
+    the same row of a 1024-row call, which runs on tiles."""
+    a_ = abi()
+    a, w = synth.gemm_inputs(1024, N, K, index=N + K)
+    ga, gw = cuda(a), cuda(w)
+    e = a_.BCI_EPI_BF16 if epi == "bf16" else a_.BCI_EPI_SILU_MUL
+    cols = N if epi == "bf16" else N // 2
+    full = gemm(ctx, ga, gw, e, out_cols=cols)
+    for M in (100, 129, 160, 256, 384, 511, 512, 600):
+        part = gemm(ctx, ga[1024 - M:].contiguous(), gw, e, out_cols=cols)
+        assert same_bits(part, full[1024 - M:]), (N, K, M)
+
+
 def test_gemm_rejects_bad_shapes(ctx):
     a_ = abi()
     x = torch.empty(4, 64, dtype=BF, device="cuda")
