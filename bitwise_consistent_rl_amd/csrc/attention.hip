@@ -296,7 +296,8 @@ __device__ __forceinline__ void load_chunk_sync(const AttnArgs& p, int blk, int 
 // c + 1 and c + 2 outstanding while chunk c is multiplied, and the issues unconditional
 // (a chunk index past the last is clamped, its copy never used), the wait before
 // storing chunk c + 1 leaves chunk c + 2's loads in flight.
-template <int D, bool FP8, bool SPLIT, bool PF2 = false>
+// DS (decode tiles, at most 16 rows; implied by PF2): the four waves split the PV work.
+template <int D, bool FP8, bool SPLIT, bool PF2 = false, bool DS = PF2>
 __global__ __launch_bounds__(ATHREADS, SPLIT ? 4 : 2) void attention_kernel(AttnArgs p) {
   constexpr bool PIPE = !SPLIT;
   static_assert(!(PF2 && SPLIT), "two chunks in flight: pipelined schedule only");
@@ -328,14 +329,14 @@ __global__ __launch_bounds__(ATHREADS, SPLIT ? 4 : 2) void attention_kernel(Attn
   const int* btab = p.block_table + (size_t)seq * p.max_blocks;
   const size_t qstride = (size_t)p.nq * D;
 
-  // this lane's query row (B operand of S^T and column of O^T).  PF2 (tiles of at most
+  // this lane's query row (B operand of S^T and column of O^T).  DS (tiles of at most
   // 16 rows): every wave takes rows 0-15, computes the same scores and softmax
   // statistics, and owns D/64 of the D/16 head-dimension blocks of P.V, the rescales
   // and the output, so the four waves split the chunk's PV work instead of three idling
   constexpr int DT = D / 16;                    // 16-wide head-dimension blocks
-  constexpr int DPW = PF2 ? DT / 4 : DT;        // blocks this wave accumulates
-  const int rw = PF2 ? 0 : wave;
-  const int dt0 = PF2 ? wave * DPW : 0;
+  constexpr int DPW = DS ? DT / 4 : DT;         // blocks this wave accumulates
+  const int rw = DS ? 0 : wave;
+  const int dt0 = DS ? wave * DPW : 0;
   const int row = rw * 16 + lc;
   const int tk = row / group;
   const int hq = g * group + row % group;
@@ -663,6 +664,9 @@ static void launch_d(const AttnArgs& a, hipStream_t s) {
   } else if (a.pf2) {
     hipLaunchKernelGGL((attention_kernel<D, FP8, false, true>), dim3(a.n_tiles, a.nkv), dim3(ATHREADS),
                        0, s, a);
+  } else if (a.dsplit) {
+    hipLaunchKernelGGL((attention_kernel<D, FP8, false, false, true>), dim3(a.n_tiles, a.nkv),
+                       dim3(ATHREADS), 0, s, a);
   } else {
     hipLaunchKernelGGL((attention_kernel<D, FP8, false>), dim3(a.n_tiles, a.nkv), dim3(ATHREADS),
                        0, s, a);

@@ -557,7 +557,8 @@ static bci_status op_attn(bci_ctx* c, const void* q, void* o, int layer, hipStre
   // loads per tile cost more than they hide (2.77 -> 2.83 ms), so it stays off there
   int max_q = 0;
   for (int i = 0; i < c->n_seqs; ++i) max_q = std::max(max_q, c->h_cu[i + 1] - c->h_cu[i]);
-  a.pf2 = max_q * (g.n_q_heads / g.n_kv_heads) <= 16 && c->n_tiles * g.n_kv_heads < 256;
+  a.dsplit = max_q * (g.n_q_heads / g.n_kv_heads) <= 16;
+  a.pf2 = a.dsplit && c->n_tiles * g.n_kv_heads < 256;
   HIP_TRY(c, launch_attention(a, s));
   return BCI_OK;
 }

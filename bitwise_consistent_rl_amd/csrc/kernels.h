@@ -124,6 +124,8 @@ struct AttnArgs {
   float* part_ml;              // [n_seg][T][nq][2]
   // unsplit schedule with two chunks in flight (tiles of at most 16 rows: decode)
   bool pf2;
+  // tiles of at most 16 rows: the four waves split the PV work (implied by pf2)
+  bool dsplit;
 };
 constexpr int ATTN_ROWS = 64;  // query rows (token x head-in-group) per tile
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
