@@ -24,9 +24,7 @@ namespace {
 constexpr int KV_BLOCK = 64;
 constexpr int DEFAULT_PROFILE = 8192;
 constexpr size_t VENDOR_WS_BYTES = (size_t)64 << 20;  // the vendor GEMM's workspace (fast mode)
-#ifndef FAST_VENDOR_QKV
-#define FAST_VENDOR_QKV 1  // fast mode: QKV on the vendor GEMM plus the RoPE kernel
-#endif
+constexpr bool FAST_VENDOR_QKV = true;  // fast mode: QKV on the vendor GEMM plus the RoPE kernel
 
 struct DevBuf {
   void* p = nullptr;

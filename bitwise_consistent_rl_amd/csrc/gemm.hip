@@ -587,12 +587,12 @@ __global__ __launch_bounds__((TBM >= 64 ? TBM / 64 : 1) * NWN * 64, 1) void gemm
 }
 
 
-// ---- skinny schedule for M <= 128 (decode).  The same per-element arithmetic
-// as gemm_kernel -- one fp32 accumulator from zero, v_mfma_f32_16x16x32_bf16
-// over ascending 32-wide K steps, the same epilogue -- with a different
-// assignment of output elements: a one-wave workgroup owns 16 output columns
-// (16 gate + 16 up for SiLU) and all ceil(M/16) row blocks, so N/16 waves
-// stream the weights instead of N/256 workgroups.  K is cut into stages of
+// ---- skinny schedule for M <= 128 (decode), and up to 512 rows where a latency model
+// favours it.  The same per-element arithmetic as gemm_kernel -- one fp32 accumulator
+// from zero, v_mfma_f32_16x16x32_bf16 over ascending 32-wide K steps, the same epilogue
+// -- with a different assignment of output elements: a one-wave workgroup owns 16
+// output columns (16 gate + 16 up for SiLU) and up to 2 (SiLU: 4) blocks of 16 rows,
+// so N/16 waves per row group stream the weights instead of N/256 workgroups.  K is cut into stages of
 // SK_KC (512 for a single row block when K allows); each stage's W rows and A
 // rows are copied by buffer_load ... lds into a private LDS ring of D stages, so D
 // stages of loads are in flight while the MFMAs consume the oldest.  A single
@@ -903,26 +903,23 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmArgs p) {
     }
 }
 
-template <int KIND>
-// A skinny wave multiplies its 16 weight rows with at most SKINNY_ROW_BLOCKS_PER_WAVE
-// blocks of 16 A rows; more rows go to more waves (grid.y), which stream the same weight
-// rows again from L2.  Each wave's bandwidth is capped by the copies it can keep in
-// flight, and with 64 rows its A stream (256 KiB at K = 2048) was 4x its weight stream.
-// Measured on the decode step at B = 64, rows per wave 16 / 32 / 64: 3.08 / 2.57 / 2.79
-// ms; the rollout at a cap of 128 sequences 20.2 K -> 23.6 K tokens/s with 32.
-#ifndef SKINNY_ROW_BLOCKS_PER_WAVE
-#define SKINNY_ROW_BLOCKS_PER_WAVE 2
-#endif
-// The SiLU form streams two weight rows per output column, so a second row group
-// costs twice the re-read: 64 rows per wave there (B = 64 decode step 2.557 -> 2.470 ms
+// A skinny wave multiplies its 16 weight rows with at most SK_ROW_BLOCKS blocks of 16 A
+// rows; more rows go to more waves (grid.y), which stream the same weight rows again from
+// L2.  Each wave's bandwidth is capped by the copies it can keep in flight, and with 64
+// rows its A stream (256 KiB at K = 2048) was 4x its weight stream.  Measured on the
+// decode step at B = 64, rows per wave 16 / 32 / 64: 3.08 / 2.57 / 2.79 ms; the rollout at
+// a cap of 128 sequences 20.2 K -> 23.6 K tokens/s with 32.
+constexpr int SK_ROW_BLOCKS = 2;
+// The SiLU form streams two weight rows per output column, so a second row group costs
+// twice the re-read: 64 rows per wave there (B = 64 decode step 2.557 -> 2.470 ms
 // against 32, the same as 128).
-#ifndef SKINNY_SILU_ROW_BLOCKS_PER_WAVE
-#define SKINNY_SILU_ROW_BLOCKS_PER_WAVE 4
-#endif
+constexpr int SK_SILU_ROW_BLOCKS = 4;
+
+template <int KIND>
 static hipError_t dispatch_skinny(const GemmArgs& a, hipStream_t s) {
   const int ncols = (KIND == K_SILU) ? a.N / 2 : a.N;
   const int grid = ncols / 16;
-  const int mt = std::min((a.M + 15) / 16, KIND == K_SILU ? SKINNY_SILU_ROW_BLOCKS_PER_WAVE : SKINNY_ROW_BLOCKS_PER_WAVE);
+  const int mt = std::min((a.M + 15) / 16, KIND == K_SILU ? SK_SILU_ROW_BLOCKS : SK_ROW_BLOCKS);
   const bool wide = a.K % 512 == 0;
   const dim3 g1(grid), gm(grid, (a.M + 16 * mt - 1) / (16 * mt));
   if (a.M <= 4 && wide) hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 1, false, false, 4, 512>), g1, dim3(64), 0, s, a);
@@ -1172,7 +1169,7 @@ hipError_t launch_gemm_qkv_rope(const void* A, const void* W, int M, int N, int 
     // scale needs a head's 128 values, spread over 4 waves here): the skinny schedule,
     // one wave per 16 rotation pairs
     if (fp8 || K % SK_KC) return hipErrorInvalidValue;
-    const int mt = std::min((M + 15) / 16, SKINNY_ROW_BLOCKS_PER_WAVE);
+    const int mt = std::min((M + 15) / 16, SK_ROW_BLOCKS);
     const dim3 grid(N / 32), gm(N / 32, (M + 16 * mt - 1) / (16 * mt));
     if (M <= 4 && K % 512 == 0)
       hipLaunchKernelGGL((gemm_skinny_kernel<K_ROPE, 1, false, false, 4, 512>), grid, dim3(64), 0, s, a);
