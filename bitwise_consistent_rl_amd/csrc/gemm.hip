@@ -651,6 +651,9 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmArgs p) {
   static_assert(AR == 16 * MT || (MT == 1 && AR == 4), "A rows per stage");
   static_assert(!NORM || (MT == 1 && AR == 4 && !GATHER && !GROUPED), "norm-fused A: M <= 4, plain rows");
   constexpr int ROWCH = KC / 8;                         // 16-byte chunks per row per stage
+  // the copy swizzle (chunk ^ (row & 15)) must stay inside a row's stage: at fewer than
+  // 16 chunks it would read past the stage, and past the matrix on its last row
+  static_assert(ROWCH % 16 == 0, "a stage row holds a multiple of 16 chunks");
   // weight streams: (gate, up) rows for SiLU; for RoPE the rows e and e + 64 of a head
   constexpr int NB = (KIND == K_SILU || KIND == K_ROPE) ? 2 : 1;
   constexpr int WCH = NB * 16 * ROWCH;                  // W chunks per stage

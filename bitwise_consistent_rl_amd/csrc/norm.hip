@@ -24,6 +24,12 @@ __global__ __launch_bounds__(NORM_THREADS) void add_rmsnorm_kernel(
   __shared__ float wsum[NORM_THREADS / WAVE];
 
   const bf16_t* src = ids ? E + (size_t)ids[row] * cols : r_in + (size_t)row * cols;
+  // the norm weight is loaded with the row, so that its latency is not paid after the
+  // reduction (columns past the row repeat its last 8)
+  uint4 gv[NORM_MAX_SLICES];
+#pragma unroll
+  for (int sl = 0; sl < NORM_MAX_SLICES; ++sl)
+    gv[sl] = *reinterpret_cast<const uint4*>(g + min((sl * NORM_THREADS + tid) * 8, cols - 8));
   float x[NORM_MAX_SLICES][8];
   float ss = 0.0f;
 #pragma unroll
@@ -65,8 +71,7 @@ __global__ __launch_bounds__(NORM_THREADS) void add_rmsnorm_kernel(
   for (int sl = 0; sl < NORM_MAX_SLICES; ++sl) {
     const int c0 = (sl * NORM_THREADS + tid) * 8;
     if (c0 < cols) {
-      uint4 gv = *reinterpret_cast<const uint4*>(g + c0);
-      const bf16_t* gp = reinterpret_cast<const bf16_t*>(&gv);
+      const bf16_t* gp = reinterpret_cast<const bf16_t*>(&gv[sl]);
       uint4 ov;
       uint32_t* op = reinterpret_cast<uint32_t*>(&ov);
 #pragma unroll
