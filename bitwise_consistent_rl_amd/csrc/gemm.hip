@@ -593,7 +593,7 @@ __global__ __launch_bounds__((TBM >= 64 ? TBM / 64 : 1) * NWN * 64, 1) void gemm
 // -- with a different assignment of output elements: a one-wave workgroup owns 16
 // output columns (16 gate + 16 up for SiLU) and up to 2 (SiLU: 4) blocks of 16 rows,
 // so N/16 waves per row group stream the weights instead of N/256 workgroups.  K is cut into stages of
-// SK_KC (512 for a single row block when K allows); each stage's W rows and A
+// SK_KC (512 for a single row block and 256 for two when K allows); each stage's W rows and A
 // rows are copied by buffer_load ... lds into a private LDS ring of D stages, so D
 // stages of loads are in flight while the MFMAs consume the oldest.  A single
 // wave needs no barrier, only vmcnt.  The stage width and the A rows a stage
@@ -911,7 +911,9 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmArgs p) {
 // L2.  Each wave's bandwidth is capped by the copies it can keep in flight, and with 64
 // rows its A stream (256 KiB at K = 2048) was 4x its weight stream.  Measured on the
 // decode step at B = 64, rows per wave 16 / 32 / 64: 3.08 / 2.57 / 2.79 ms; the rollout at
-// a cap of 128 sequences 20.2 K -> 23.6 K tokens/s with 32.
+// a cap of 128 sequences 20.2 K -> 23.6 K tokens/s with 32.  Such 32-row waves take
+// 256-wide K stages where K allows (each weight row read in 512-byte runs; same ring
+// size): down at 64 rows 15.8 -> 14.6 us, the B = 64 decode step 2.437 -> 2.413 ms.
 constexpr int SK_ROW_BLOCKS = 2;
 // The SiLU form streams two weight rows per output column, so a second row group costs
 // twice the re-read: 64 rows per wave there (B = 64 decode step 2.557 -> 2.470 ms
@@ -929,6 +931,8 @@ static hipError_t dispatch_skinny(const GemmArgs& a, hipStream_t s) {
   else if (a.M <= 4) hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 1, false, false, 4>), g1, dim3(64), 0, s, a);
   else if (mt == 1 && wide) hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 1, false, false, 16, 512>), gm, dim3(64), 0, s, a);
   else if (mt == 1) hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 1>), gm, dim3(64), 0, s, a);
+  else if (mt == 2 && KIND != K_SILU && a.K % 256 == 0)
+    hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 2, false, false, 32, 256>), gm, dim3(64), 0, s, a);
   else if (mt == 2) hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 2>), gm, dim3(64), 0, s, a);
   else if (mt <= 4) hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 4>), gm, dim3(64), 0, s, a);
   else hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 8>), gm, dim3(64), 0, s, a);
