@@ -1296,13 +1296,17 @@ hipError_t launch_lmhead_partials(const void* A, const int32_t* a_rows, const vo
 // run over consecutive rows, so every load of the chunk-major partials is
 // coalesced.  lp = (z[id] - max) - log(sum).
 constexpr int COMB_ROWS = 64, COMB_SPLIT = 8;
+constexpr int COMB_BATCH = 40;   // partials loaded together per thread (two batches per range at V = 151936)
 
+// The rescale factors are 2^((m - m') log2 e) on v_exp_f32, the exponential of the
+// chunks' own sums: the merge is one dependent chain per range, and the library expf's
+// range reduction made it several times longer.
 __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
   if (m2 > m) {
-    s = s * fexp(m - m2) + s2;
+    s = s * fexp2((m - m2) * LOG2E) + s2;
     m = m2;
   } else if (m2 != -INFINITY) {
-    s = s + s2 * fexp(m2 - m);
+    s = s + s2 * fexp2((m2 - m) * LOG2E);
   }
 }
 
@@ -1314,18 +1318,33 @@ __global__ __launch_bounds__(COMB_ROWS * COMB_SPLIT) void lmhead_combine_kernel(
   const int i = blockIdx.x * COMB_ROWS + r;
   const int per = (nc + COMB_SPLIT - 1) / COMB_SPLIT;
   float mx = -INFINITY, s = 0.0f;
+  // the token id and its logit are loaded first, so their latency overlaps the merge
+  const int ir = min(i, M - 1);
+  const int id = ids[ir];
+  const float z = zid[ir];
   if (i < M) {
-    const int c1 = min(nc, (q + 1) * per);
-    for (int c = q * per; c < c1; ++c)
-      lse_merge(mx, s, pm[(size_t)c * M + i], ps[(size_t)c * M + i]);
+    // the partials of COMB_BATCH chunks are loaded together (at clamped indices, so the
+    // loads issue back to back and are waited for once), then merged in chunk order
+    const int c0 = q * per, c1 = min(nc, (q + 1) * per);
+    for (int c = c0; c < c1; c += COMB_BATCH) {
+      float bm[COMB_BATCH], bs[COMB_BATCH];
+#pragma unroll
+      for (int u = 0; u < COMB_BATCH; ++u) {
+        const size_t k = (size_t)min(c + u, c1 - 1) * M + i;
+        bm[u] = pm[k];
+        bs[u] = ps[k];
+      }
+#pragma unroll
+      for (int u = 0; u < COMB_BATCH; ++u)
+        if (c + u < c1) lse_merge(mx, s, bm[u], bs[u]);
+    }
   }
   sm[q][r] = mx;
   ss[q][r] = s;
   __syncthreads();
   if (q == 0 && i < M) {
     for (int k = 1; k < COMB_SPLIT; ++k) lse_merge(mx, s, sm[k][r], ss[k][r]);
-    const int id = ids[i];
-    lp[i] = (id < 0 || id >= V) ? __uint_as_float(0x7fc00000u) : (zid[i] - mx) - flog(s);
+    lp[i] = (id < 0 || id >= V) ? __uint_as_float(0x7fc00000u) : (z - mx) - flog(s);
   }
 }
 
