@@ -183,14 +183,48 @@ __device__ __forceinline__ float xrow_sum(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// The value of lane l ^ O, without a trip through LDS addressing where the hardware
+// has a lane pattern for it: DPP quad permutes (O = 1, 2) and row rotate by 8 (O = 8),
+// swizzle in bitmask mode (O = 4, 16) and the gfx950 half-wave swap (O = 32).  The bits
+// are moved, not computed, so a butterfly built on it adds the same values in the same
+// pairs as one built on __shfl_xor.
+template <int O>
+__device__ __forceinline__ float lane_xor(float v) {
+  const int u = __float_as_int(v);
+  if constexpr (O == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap((unsigned)u, (unsigned)u, false, false);
+    return __uint_as_float(__lane_id() < 32 ? r[1] : r[0]);
+  } else if constexpr (O == 16) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(u, 0x401F));
+  } else if constexpr (O == 8) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(u, 0x128, 0xF, 0xF, true));
+  } else if constexpr (O == 4) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(u, 0x101F));
+  } else if constexpr (O == 2) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(u, 0x4E, 0xF, 0xF, true));
+  } else {
+    static_assert(O == 1, "xor distance");
+    return __int_as_float(__builtin_amdgcn_mov_dpp(u, 0xB1, 0xF, 0xF, true));
+  }
+}
+
+// xor butterflies over all 64 lanes, distances 32, 16, 8, 4, 2, 1
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = v + __shfl_xor(v, o, WAVE);
+  v = v + lane_xor<32>(v);
+  v = v + lane_xor<16>(v);
+  v = v + lane_xor<8>(v);
+  v = v + lane_xor<4>(v);
+  v = v + lane_xor<2>(v);
+  v = v + lane_xor<1>(v);
   return v;
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+  v = fmaxf(v, lane_xor<32>(v));
+  v = fmaxf(v, lane_xor<16>(v));
+  v = fmaxf(v, lane_xor<8>(v));
+  v = fmaxf(v, lane_xor<4>(v));
+  v = fmaxf(v, lane_xor<2>(v));
+  v = fmaxf(v, lane_xor<1>(v));
   return v;
 }
 

@@ -494,8 +494,10 @@ __global__ __launch_bounds__((TBM >= 64 ? TBM / 64 : 1) * NWN * 64, 1) void gemm
           float amax = 0.0f;
 #pragma unroll
           for (int ni = 0; ni < NI / 2; ++ni) amax = fmaxf(amax, fmaxf(fabsf(y1[ni]), fabsf(y2[ni])));
-#pragma unroll
-          for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, WAVE));
+          amax = fmaxf(amax, lane_xor<1>(amax));
+          amax = fmaxf(amax, lane_xor<2>(amax));
+          amax = fmaxf(amax, lane_xor<4>(amax));
+          amax = fmaxf(amax, lane_xor<8>(amax));
           const float sc = kv_scale_from_amax(amax);
           uint8_t* dst = reinterpret_cast<uint8_t*>(is_k ? p.kv.k : p.kv.v) + crow * 128;
           if (ok) {
@@ -535,8 +537,10 @@ __global__ __launch_bounds__((TBM >= 64 ? TBM / 64 : 1) * NWN * 64, 1) void gemm
         float mx = -INFINITY;
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) mx = fmaxf(mx, acc[mi][ni][r]);
-#pragma unroll
-        for (int o = 1; o <= 8; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, WAVE));
+        mx = fmaxf(mx, lane_xor<1>(mx));
+        mx = fmaxf(mx, lane_xor<2>(mx));
+        mx = fmaxf(mx, lane_xor<4>(mx));
+        mx = fmaxf(mx, lane_xor<8>(mx));
         if ((lane & 15) == 0) redm[wn * KBM + lrow0 + mi * 16 + r] = mx;
       }
     __syncthreads();
@@ -553,8 +557,10 @@ __global__ __launch_bounds__((TBM >= 64 ? TBM / 64 : 1) * NWN * 64, 1) void gemm
         // instead of the library expf's dozen, in every lm_head schedule alike
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) s = s + fexp2((acc[mi][ni][r] - m) * LOG2E);
-#pragma unroll
-        for (int o = 1; o <= 8; o <<= 1) s = s + __shfl_xor(s, o, WAVE);
+        s = s + lane_xor<1>(s);
+        s = s + lane_xor<2>(s);
+        s = s + lane_xor<4>(s);
+        s = s + lane_xor<8>(s);
         if ((lane & 15) == 0) reds[wn * KBM + lr] = s;
       }
     __syncthreads();
@@ -609,30 +615,6 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((V & 15) | ((V >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// The value of lane l ^ O, without a trip through LDS addressing where the hardware
-// has a lane pattern for it: DPP quad permutes (O = 1, 2) and row rotate by 8 (O = 8),
-// swizzle in bitmask mode (O = 4, 16) and the gfx950 half-wave swap (O = 32).  The bits
-// are moved, not computed, so a butterfly built on it adds the same values in the same
-// pairs as one built on __shfl_xor.
-template <int O>
-__device__ __forceinline__ float lane_xor(float v) {
-  const int u = __float_as_int(v);
-  if constexpr (O == 32) {
-    const auto r = __builtin_amdgcn_permlane32_swap((unsigned)u, (unsigned)u, false, false);
-    return __uint_as_float(__lane_id() < 32 ? r[1] : r[0]);
-  } else if constexpr (O == 16) {
-    return __int_as_float(__builtin_amdgcn_ds_swizzle(u, 0x401F));
-  } else if constexpr (O == 8) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(u, 0x128, 0xF, 0xF, true));
-  } else if constexpr (O == 4) {
-    return __int_as_float(__builtin_amdgcn_ds_swizzle(u, 0x101F));
-  } else if constexpr (O == 2) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(u, 0x4E, 0xF, 0xF, true));
-  } else {
-    static_assert(O == 1, "xor distance");
-    return __int_as_float(__builtin_amdgcn_mov_dpp(u, 0xB1, 0xF, 0xF, true));
-  }
-}
 
 // GROUPED (the MoE expert GEMMs with few rows per expert): blockIdx.y is an entry of
 // the device tile list (group, first row, rows <= 16), W is the group's slice, A rows
