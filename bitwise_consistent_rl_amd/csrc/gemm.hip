@@ -361,17 +361,26 @@ __global__ __launch_bounds__((TBM >= 64 ? TBM / 64 : 1) * NWN * 64, 1) void gemm
   } else if constexpr (KIND == K_ADD) {
     // Residual add in place (N % 256 == 0, C 8-byte aligned): with the swapped operand
     // order a lane holds 4 consecutive columns of one row per block, so it reads the
-    // row's 8 residual words of a block row first, then rewrites them, each element
-    // with the add+RMSNorm kernel's expression bf(bf(x) + r)
+    // residual words of all its block rows first (one memory latency for the tile; rows
+    // past the tile read its last row and are not written), then rewrites them, each
+    // element with the add+RMSNorm kernel's expression bf(bf(x) + r)
+    uint2 old_all[KMI][NI];
+#pragma unroll
+    for (int mi = 0; mi < KMI; ++mi) {
+      const int lr = min(wm * KWTM + mi * 16 + (lane & 15), row_cnt - 1);
+      const bf16_t* rowp = reinterpret_cast<const bf16_t*>(p.C) + (size_t)(row_base + lr) * p.N +
+                           tn * BN + wn * WTN + 4 * (lane >> 4);
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) old_all[mi][ni] = *reinterpret_cast<const uint2*>(rowp + ni * 16);
+    }
+    asm volatile("" ::: "memory");   // keeps the loads above from being sunk into the guarded blocks
 #pragma unroll
     for (int mi = 0; mi < KMI; ++mi) {
       const int lr = wm * KWTM + mi * 16 + (lane & 15);
       if (lr < row_cnt) {
         bf16_t* rowp = reinterpret_cast<bf16_t*>(p.C) + (size_t)(row_base + lr) * p.N +
                        tn * BN + wn * WTN + 4 * (lane >> 4);
-        uint2 old[NI];
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) old[ni] = *reinterpret_cast<const uint2*>(rowp + ni * 16);
+        const uint2* old = old_all[mi];
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) {
           const bf16_t* o = reinterpret_cast<const bf16_t*>(&old[ni]);
@@ -446,8 +455,34 @@ __global__ __launch_bounds__((TBM >= 64 ? TBM / 64 : 1) * NWN * 64, 1) void gemm
     const bool is_k = !is_q && rot;
     const int gk = is_q ? 0 : (is_k ? hd - p.nq : hd - p.nq - p.nkv);
     const int lc = lane & 15;
+    // The loads are gathered ahead of the stores (which the compiler must otherwise
+    // assume may alias them, serialising every row behind the previous one): the
+    // positions and cache slots of the lane's rows first, then the rotation factors of
+    // one block of 16 rows at a time (more at once would not fit the registers).
+    int posr[KMI][4], slotr[KMI][4];
 #pragma unroll
     for (int mi = 0; mi < KMI; ++mi)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int lr = lrow0 + mi * 16 + r;
+        const int t = row_base + (lr < row_cnt ? lr : 0);
+        posr[mi][r] = rot ? p.tok_pos[t] : 0;
+        slotr[mi][r] = is_q ? 0 : p.tok_slot[t];
+      }
+#pragma unroll
+    for (int mi = 0; mi < KMI; ++mi) {
+      float rc[4][NI / 2], rs[4][NI / 2];
+      if (rot) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int ni = 0; ni < NI / 2; ++ni) {
+            const size_t k = (size_t)posr[mi][r] * 64 + ni * 16 + lc;
+            rc[r][ni] = p.rcos[k];
+            rs[r][ni] = p.rsin[k];
+          }
+      }
+      asm volatile("" ::: "memory");   // the loads above stay ahead of the stores below
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int lr = lrow0 + mi * 16 + r;
@@ -455,11 +490,9 @@ __global__ __launch_bounds__((TBM >= 64 ? TBM / 64 : 1) * NWN * 64, 1) void gemm
         const int t = row_base + (ok ? lr : 0);
         float y1[NI / 2], y2[NI / 2];
         if (rot) {
-          const int pos = p.tok_pos[t];
 #pragma unroll
           for (int ni = 0; ni < NI / 2; ++ni) {
-            const int e = ni * 16 + lc;
-            const float c = p.rcos[(size_t)pos * 64 + e], sn = p.rsin[(size_t)pos * 64 + e];
+            const float c = rc[r][ni], sn = rs[r][ni];
             const float x1 = bf2f(f2bf(acc[mi][ni][r])), x2 = bf2f(f2bf(acc[mi][ni + NI / 2][r]));
             const float a1 = x1 * c, b1 = x2 * sn;
             const float a2 = x2 * c, b2 = x1 * sn;
@@ -475,7 +508,7 @@ __global__ __launch_bounds__((TBM >= 64 ? TBM / 64 : 1) * NWN * 64, 1) void gemm
         }
         size_t crow = 0;  // cache row of (block, kv head, slot)
         if (!is_q) {
-          const int slot = p.tok_slot[t];
+          const int slot = slotr[mi][r];
           crow = ((size_t)(slot >> 6) * p.nkv + gk) * 64 + (slot & 63);
         }
         if (is_q || !p.fp8) {
@@ -510,6 +543,7 @@ __global__ __launch_bounds__((TBM >= 64 ? TBM / 64 : 1) * NWN * 64, 1) void gemm
           }
         }
       }
+    }
   } else {  // K_LMHEAD: per row, (max, sum exp) over this 256-column vocab chunk
     // Row lr's chunk max is max over the NWN waves of redm[w][lr]; its sum is
     // s_0 + s_1 (+ ...) over reds[w][lr] in wave order; within a wave the
@@ -517,6 +551,13 @@ __global__ __launch_bounds__((TBM >= 64 ? TBM / 64 : 1) * NWN * 64, 1) void gemm
     const int V = p.N;
     float* redm = reinterpret_cast<float*>(smem);  // [NWN][KBM]; the loop ended on a barrier
     float* reds = redm + NWN * KBM;                  // [NWN][KBM]
+    // the rows' token ids, loaded first so that their latency overlaps the two passes
+    // (rows past the tile repeat its last row; they are never stored)
+    int idr[KMI][4];
+#pragma unroll
+    for (int mi = 0; mi < KMI; ++mi)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) idr[mi][r] = p.ids[row_base + min(lrow0 + mi * 16 + r, row_cnt - 1)];
     if (tn * BN + BN > V) {
       // the vocabulary's last, partial chunk: columns past V become -inf, which adds
       // nothing to the max and exactly +0 (2^-inf) to the sum, so the passes below need
@@ -581,7 +622,7 @@ __global__ __launch_bounds__((TBM >= 64 ? TBM / 64 : 1) * NWN * 64, 1) void gemm
             p.part_m[(size_t)tn * p.M + row] = m;
             p.part_s[(size_t)tn * p.M + row] = s;
           }
-          const int id = p.ids[row];
+          const int id = idr[mi][r];
 #pragma unroll
           for (int ni = 0; ni < NI; ++ni) {
             const int col = tn * BN + wn * WTN + ni * 16 + (lane & 15);
