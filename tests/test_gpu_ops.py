@@ -52,8 +52,9 @@ def gemm(ctx, a, w, epi, out_cols=None, dtype=BF):
 
 # ------------------------------------------------------------------- GEMM
 
-@pytest.mark.parametrize("M,N,K", [(1, 128, 64), (37, 256, 128), (300, 512, 256),
-                                   (513, 384, 2048), (256, 128, 6144), (1000, 4096, 2048)])
+@pytest.mark.parametrize("M,N,K", [(1, 128, 64), (37, 256, 128), (24, 256, 2048), (64, 512, 6144),
+                                   (300, 512, 256), (513, 384, 2048), (256, 128, 6144),
+                                   (1000, 4096, 2048)])
 def test_gemm_bf16_parity(ctx, M, N, K):
     a, w = synth.gemm_inputs(M, N, K, index=M + N + K)
     C = gemm(ctx, cuda(a), cuda(w), abi().BCI_EPI_BF16)
@@ -157,7 +158,7 @@ def test_gemm_rows_invariant_to_M_and_order(ctx, epi):
     e = a_.BCI_EPI_BF16 if epi == "bf16" else a_.BCI_EPI_SILU_MUL
     cols = N if epi == "bf16" else N // 2
     full = gemm(ctx, ga, gw, e, out_cols=cols)
-    for M in (1, 2, 7, 64, 255, 256, 257, 1000, 4095):
+    for M in (1, 2, 7, 24, 64, 255, 256, 257, 1000, 4095):
         part = gemm(ctx, ga[:M].contiguous(), gw, e, out_cols=cols)
         assert same_bits(part, full[:M]), M
     perm = torch.from_numpy(np.array(synth.shuffled(list(range(4096))))).cuda()
