@@ -320,10 +320,14 @@ __global__ __launch_bounds__(ATHREADS, SPLIT ? 4 : 2) void attention_kernel(Attn
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int lg = lane >> 4, lc = lane & 15;
-  const int seq = p.tiles[tile * 4 + 0];
-  const int tok_begin = p.tiles[tile * 4 + 1];
-  const int n_tok = p.tiles[tile * 4 + 2];
-  const int pos_begin = p.tiles[tile * 4 + 3];
+  const int* trec = p.tiles + (size_t)tile * ATTN_TILE_WORDS;
+  const int seq = trec[0];
+  const int tok_begin = trec[1];
+  const int n_tok = trec[2];
+  const int pos_begin = trec[3];
+  // physical blocks of chunks 0 and 1, from the tile record itself: the first loads of
+  // an unsplit tile do not wait for the block table (a second dependent memory latency)
+  const int blk_c0 = trec[4], blk_c1 = trec[5];
   const int group = p.nq / p.nkv;
   const int kmax = pos_begin + n_tok - 1;  // last key position any row of the tile needs
   const int* btab = p.block_table + (size_t)seq * p.max_blocks;
@@ -359,8 +363,9 @@ __global__ __launch_bounds__(ATHREADS, SPLIT ? 4 : 2) void attention_kernel(Attn
   }
 
   ChunkLoader<D, FP8> ld, ld2;
-  if constexpr (PIPE) ld.issue(p, btab[c_first], g, tid);
-  if constexpr (PF2) ld2.issue(p, btab[min(c_first + 1, c_stop)], g, tid);
+  // PIPE schedules start at chunk 0 (c_first = 0)
+  if constexpr (PIPE) ld.issue(p, blk_c0, g, tid);
+  if constexpr (PF2) ld2.issue(p, c_stop >= 1 ? blk_c1 : blk_c0, g, tid);
 
   bf16x8_t qf[D / 32];
 #pragma unroll

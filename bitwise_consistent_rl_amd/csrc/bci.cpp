@@ -196,7 +196,7 @@ bci_status bci_create(const bci_model_config* cfg_in, int32_t device, bci_ctx** 
   c->o_pos = c->o_tok + T;
   c->o_slot = c->o_pos + T;
   c->o_tiles = c->o_slot + T;
-  c->o_btab = c->o_tiles + 4 * (size_t)c->max_tiles;
+  c->o_btab = c->o_tiles + ATTN_TILE_WORDS * (size_t)c->max_tiles;
   c->o_srow = c->o_btab + (size_t)g.max_seqs_per_call * c->max_blocks;
   c->o_sid = c->o_srow + R;
   c->max_itiles = (int)(T / IDX_TILE_TOKENS) + g.max_seqs_per_call;
@@ -456,12 +456,17 @@ bci_status bci_set_batch(bci_ctx* c, const bci_batch* b, void* stream) {
       h[c->o_pos + q0 + t] = p;
       h[c->o_slot + q0 + t] = c->h_btab[(size_t)i * c->max_blocks + p / KV_BLOCK] * KV_BLOCK + p % KV_BLOCK;
     }
+    const int32_t* brow = c->h_btab.data() + (size_t)i * c->max_blocks;
+    const int need = (p0 + ql + KV_BLOCK - 1) / KV_BLOCK;
     for (int t0 = 0; t0 < ql; t0 += c->tpt) {
-      int32_t* tl = h + c->o_tiles + 4 * (size_t)tix++;
+      int32_t* tl = h + c->o_tiles + ATTN_TILE_WORDS * (size_t)tix++;
       tl[0] = i;
       tl[1] = q0 + t0;
       tl[2] = std::min(c->tpt, ql - t0);
       tl[3] = p0 + t0;
+      tl[4] = brow[0];
+      tl[5] = brow[need > 1 ? 1 : 0];
+      tl[6] = tl[7] = 0;
     }
   }
   if (b->n_scored) {

@@ -110,7 +110,10 @@ struct AttnArgs {
   const void* q;               // [T, nq*d] bf16
   void* o;                     // [T, nq*d] bf16
   KvLayer kv;
-  const int32_t* tiles;        // [n_tiles, 4]: seq, tok_begin, n_tok, pos_begin
+  // [n_tiles, ATTN_TILE_WORDS]: seq, tok_begin, n_tok, pos_begin, then the physical
+  // blocks of the sequence's chunks 0 and 1 (chunk 1's = chunk 0's when it has one), which
+  // the unsplit schedules load without waiting for the block table
+  const int32_t* tiles;
   const int32_t* block_table;  // [n_seqs, max_blocks]
   const int32_t* tok_pos;      // [T] absolute position of each token (split merge)
   int n_tiles, max_blocks, nq, nkv, d, seg_keys;
@@ -128,6 +131,7 @@ struct AttnArgs {
   bool dsplit;
 };
 constexpr int ATTN_ROWS = 64;  // query rows (token x head-in-group) per tile
+constexpr int ATTN_TILE_WORDS = 8;  // ints per attention tile record (32 bytes)
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 
 // ---- sparse.hip (sparse attention over a Top-K selected key set)
