@@ -229,16 +229,15 @@ __global__ __launch_bounds__((TBM >= 64 ? TBM / 64 : 1) * NWN * 64, 1) void gemm
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Operand order: for the SiLU kind W is the MFMA's first operand and A its
-  // second, so a lane ends up holding 4 consecutive output columns of one row
-  // (8-byte stores); the other kinds keep A first, where 16 lanes store 16
-  // consecutive columns of a row (measured faster for plain bf16 C than the
-  // 8-byte pattern).  Either way each output element is the same ascending
-  // chain of the same 32-wide dot products.
-  constexpr bool SWAP = (KIND == K_SILU || KIND == K_ADD);
+  // Operand order: the A fragment is the MFMA's first operand and the W fragment its
+  // second for every kind, so a lane holds rows 4 (lane >> 4) + r and column lane & 15
+  // of each 16x16 block.  The swapped order (W first, a lane holding 4 consecutive
+  // columns of a row, for 8-byte epilogue accesses) gives every output element the same
+  // chain and the same bits, but measured slower in the K loop: gate_up 609 -> 598 us
+  // on this order, the recompute +1.1 % with the SiLU and residual-add epilogues moved
+  // to it, and the QKV epilogue moved the other way 5 % slower.
   auto mfma = [&](const bf16x8_t& fa, const bf16x8_t& fb, f32x4_t c) {
-    if constexpr (SWAP) return __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb, fa, c, 0, 0, 0);
-    else return __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, c, 0, 0, 0);
   };
   auto lda = [&](int st, int ks, int mi) {
     return __builtin_bit_cast(
@@ -359,40 +358,37 @@ __global__ __launch_bounds__((TBM >= 64 ? TBM / 64 : 1) * NWN * 64, 1) void gemm
         }
       }
   } else if constexpr (KIND == K_ADD) {
-    // Residual add in place (N % 256 == 0, C 8-byte aligned): with the swapped operand
-    // order a lane holds 4 consecutive columns of one row per block, so it reads the
-    // residual words of all its block rows first (one memory latency for the tile; rows
-    // past the tile read its last row and are not written), then rewrites them, each
-    // element with the add+RMSNorm kernel's expression bf(bf(x) + r)
-    uint2 old_all[KMI][NI];
+    // Residual add in place: a lane holds rows 4 (lane >> 4) + r, column lane & 15 of each
+    // block; each element with the add+RMSNorm kernel's expression bf(bf(x) + r).  The
+    // residual values of two row blocks are loaded together (rows past the tile read its
+    // last row and are not written), then rewritten.
+    static_assert(KMI % 2 == 0, "row blocks in pairs");
 #pragma unroll
-    for (int mi = 0; mi < KMI; ++mi) {
-      const int lr = min(wm * KWTM + mi * 16 + (lane & 15), row_cnt - 1);
-      const bf16_t* rowp = reinterpret_cast<const bf16_t*>(p.C) + (size_t)(row_base + lr) * p.N +
-                           tn * BN + wn * WTN + 4 * (lane >> 4);
+    for (int mp = 0; mp < KMI; mp += 2) {
+      bf16_t old[2][4][NI];
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni) old_all[mi][ni] = *reinterpret_cast<const uint2*>(rowp + ni * 16);
-    }
-    asm volatile("" ::: "memory");   // keeps the loads above from being sunk into the guarded blocks
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int mi = 0; mi < KMI; ++mi) {
-      const int lr = wm * KWTM + mi * 16 + (lane & 15);
-      if (lr < row_cnt) {
-        bf16_t* rowp = reinterpret_cast<bf16_t*>(p.C) + (size_t)(row_base + lr) * p.N +
-                       tn * BN + wn * WTN + 4 * (lane >> 4);
-        const uint2* old = old_all[mi];
+        for (int r = 0; r < 4; ++r) {
+          const int lr = min(lrow0 + (mp + h) * 16 + r, row_cnt - 1);
+          const bf16_t* rp = reinterpret_cast<const bf16_t*>(p.C) + (size_t)(row_base + lr) * p.N;
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni) {
-          const bf16_t* o = reinterpret_cast<const bf16_t*>(&old[ni]);
-          bf16_t v[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = f2bf(bf2f(f2bf(acc[mi][ni][r])) + bf2f(o[r]));
-          uint2 w;
-          w.x = pack_bf2(v[0], v[1]);
-          w.y = pack_bf2(v[2], v[3]);
-          *reinterpret_cast<uint2*>(rowp + ni * 16) = w;
+          for (int ni = 0; ni < NI; ++ni) old[h][r][ni] = rp[tn * BN + wn * WTN + ni * 16 + (lane & 15)];
         }
-      }
+      asm volatile("" ::: "memory");   // the loads above stay ahead of the stores below
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int lr = lrow0 + (mp + h) * 16 + r;
+          if (lr < row_cnt) {
+            bf16_t* rp = reinterpret_cast<bf16_t*>(p.C) + (size_t)(row_base + lr) * p.N;
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni)
+              rp[tn * BN + wn * WTN + ni * 16 + (lane & 15)] =
+                  f2bf(bf2f(f2bf(acc[mp + h][ni][r])) + bf2f(old[h][r][ni]));
+          }
+        }
     }
   } else if constexpr (KIND == K_BF16 || KIND == K_F32 || KIND == K_PART) {
     void* Cout = p.C;
@@ -415,35 +411,25 @@ __global__ __launch_bounds__((TBM >= 64 ? TBM / 64 : 1) * NWN * 64, 1) void gemm
         }
       }
   } else if constexpr (KIND == K_SILU) {
+    // silu(g) * u: the gate and up values of an output (row, column) sit in blocks ni and
+    // ni + NI/2 of the same lane; 16 lanes store 16 consecutive columns of a row
     const int I = p.N >> 1;
-    const bool vec = (reinterpret_cast<uintptr_t>(p.C) & 7) == 0;
 #pragma unroll
-    for (int mi = 0; mi < KMI; ++mi) {
-      const int lr = wm * KWTM + mi * 16 + (lane & 15);
-      if (lr < row_cnt) {
-        bf16_t* out = reinterpret_cast<bf16_t*>(p.C) + (size_t)(row_base + lr) * I;
+    for (int mi = 0; mi < KMI; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < NI / 2; ++ni) {
-          const int c0 = tn * (BN / 2) + wn * (WTN / 2) + ni * 16 + 4 * (lane >> 4);
-          bf16_t o[4];
+      for (int r = 0; r < 4; ++r) {
+        const int row = row0 + mi * 16 + r;
+        if (lrow0 + mi * 16 + r < row_cnt) {
+          bf16_t* out = reinterpret_cast<bf16_t*>(p.C) + (size_t)row * I;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
+          for (int ni = 0; ni < NI / 2; ++ni) {
+            const int col = tn * (BN / 2) + wn * (WTN / 2) + ni * 16 + (lane & 15);
             const float g = bf2f(f2bf(acc[mi][ni][r]));
             const float u = bf2f(f2bf(acc[mi][ni + NI / 2][r]));
-            o[r] = f2bf(silu_f32(g) * u);
-          }
-          if (vec) {  // I % 128 == 0: whole tiles; 8-byte stores when C is aligned
-            uint2 w;
-            w.x = pack_bf2(o[0], o[1]);
-            w.y = pack_bf2(o[2], o[3]);
-            *reinterpret_cast<uint2*>(out + c0) = w;
-          } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) out[c0 + r] = o[r];
+            out[col] = f2bf(silu_f32(g) * u);
           }
         }
       }
-    }
   } else if constexpr (KIND == K_ROPE) {
     // Head dimension 128: wave wn of column tile tn holds head 2 tn + wn, and the
     // rotation pair (e, e + 64) of a row sits in blocks ni and ni + 4 of the same
@@ -1009,7 +995,7 @@ hipError_t launch_gemm(const void* A, const int32_t* a_rows, const void* W, void
     if (a_rows) return hipErrorInvalidValue;
     // decode-sized and mid-sized calls: the skinny schedule with the same in-place add
     if (K % SK_KC == 0 && N % 16 == 0 && gemm_prefers_skinny(M, N, K, epi, false)) return dispatch_skinny<K_ADD>(a, s);
-    return (N % BN || (reinterpret_cast<uintptr_t>(C) & 7)) ? hipErrorInvalidValue : dispatch<K_ADD>(a, false, s);
+    return (N % BN) ? hipErrorInvalidValue : dispatch<K_ADD>(a, false, s);
   }
   // decode-sized M, and mid-sized M where it is faster: the skinny schedule (same
   // per-element arithmetic, more waves)
