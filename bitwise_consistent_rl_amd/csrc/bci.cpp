@@ -24,7 +24,13 @@ namespace {
 constexpr int KV_BLOCK = 64;
 constexpr int DEFAULT_PROFILE = 8192;
 constexpr size_t VENDOR_WS_BYTES = (size_t)64 << 20;  // the vendor GEMM's workspace (fast mode)
-constexpr bool FAST_VENDOR_QKV = true;  // fast mode: QKV on the vendor GEMM plus the RoPE kernel
+// Fast mode on the tiled range: the O and down projections on the vendor GEMM with the
+// residual adds in the norms; the QKV projection keeps the fused GEMM + RoPE + KV write
+// (measured on the recompute, same box, fast-mode tokens/s: vendor QKV and O/down 224.1 /
+// 223.7 K, vendor O/down only 224.8 / 224.5 K, vendor QKV only 223.2 / 223.0 K, neither
+// 224.0 / 225.1 K: within noise of each other and of the invariant mode's 225 K)
+constexpr bool FAST_VENDOR_QKV = false;
+constexpr bool FAST_VENDOR_OD = true;
 
 struct DevBuf {
   void* p = nullptr;
@@ -980,7 +986,8 @@ static bci_status forward_impl(bci_ctx* c, float* lp, hipStream_t s) {
   // projections normalise their A rows themselves (launch_gemm_norm), so of the add+RMSNorm
   // launches only the embedding's and the final one remain; the bits are unchanged
   const bool fuse_norm = !tiled && T <= 4 && H % 512 == 0 && H <= 2048;
-  const bool fuse_add = (tiled && H % GEMM_BN == 0 && !vendor) || fuse_norm;
+  const bool vendor_od = vendor && FAST_VENDOR_OD;
+  const bool fuse_add = (tiled && H % GEMM_BN == 0 && !vendor_od) || fuse_norm;
   auto vgemm = [&](const void* A, const void* W, void* C, int N, int K) -> bci_status {
     if (!vendor_gemm(c->vg, A, W, C, T, N, K, s))
       return gemm_checked(c, A, nullptr, W, C, T, N, K, EPI_BF16, s);
@@ -992,7 +999,7 @@ static bci_status forward_impl(bci_ctx* c, float* lp, hipStream_t s) {
       HIP_TRY(c, launch_gemm(A, nullptr, W, c->bufR, T, H, K, EPI_ADD, s));
       return BCI_OK;
     }
-    if (vendor) return vgemm(A, W, c->bufX, H, K);
+    if (vendor_od) return vgemm(A, W, c->bufX, H, K);
     return gemm_checked(c, A, nullptr, W, c->bufX, T, H, K, EPI_BF16, s);
   };
   const void* addend = fuse_add ? nullptr : c->bufX;  // what the norms still add
@@ -1017,7 +1024,7 @@ static bci_status forward_impl(bci_ctx* c, float* lp, hipStream_t s) {
                                       c->meta + c->o_slot, c->rope_cos, c->rope_sin, kv_layer(c, l),
                                       g.n_q_heads, g.n_kv_heads, g.kv_dtype == BCI_KV_FP8_E4M3, s));
     } else {
-      if (vendor) {
+      if (vendor && FAST_VENDOR_QKV) {
         if (bci_status st = vgemm(c->bufH, lw[1], c->bufQKV, c->qkv_w, H)) return st;
       } else if (bci_status st = gemm_checked(c, c->bufH, nullptr, lw[1], c->bufQKV, T, c->qkv_w, H, EPI_BF16, s)) {
         return st;

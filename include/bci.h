@@ -75,9 +75,9 @@ typedef enum {
 
 /* BCI_MODE_FAST is the non-invariant reference schedule, kept only to quote
  * the cost of invariance.  It takes the choices a throughput engine takes where
- * they are faster: the QKV, O and down projections of calls above 256 tokens run
- * on the vendor GEMM (hipBLASLt, whose kernel choice depends on the shape), with
- * RoPE, the cache write and the residual adds in separate kernels; GEMMs with
+ * they are faster: the O and down projections of calls above 256 tokens run on
+ * the vendor GEMM (hipBLASLt, whose kernel choice depends on the shape), with the
+ * residual adds in the norms after them; GEMMs with
  * 128 < M <= 256 and K >= 4096 split K across workgroups and add fp32 partials
  * with atomics (order, hence bits, depend on timing); and attention sizes its KV
  * segments from each call's shape, splitting calls with fewer workgroups than CUs
@@ -182,8 +182,8 @@ bci_status bci_set_batch(bci_ctx* ctx, const bci_batch* batch, void* stream);
  * SiLU*up, down GEMM], final add+RMSNorm, lm_head + fp32 log-softmax + gather.
  * Writes d_logprobs[n_scored] (fp32).  This is the "rollout" entry point.  Batches
  * of more than 128 tokens (256 in BCI_MODE_FAST) run RoPE + KV write inside the QKV
- * GEMM's epilogue (head_dim 128) and the residual adds inside the O and down GEMMs'
- * epilogues (hidden % 256 == 0).  Batches of at most 4 tokens with hidden % 512
+ * GEMM's epilogue (head_dim 128) and (not in BCI_MODE_FAST) the residual adds inside
+ * the O and down GEMMs' epilogues (hidden % 256 == 0).  Batches of at most 4 tokens with hidden % 512
  * == 0 and hidden <= 2048 add the O and down projections into the residual in those
  * GEMMs' epilogues and normalise the QKV and gate_up GEMMs' A rows inside those GEMMs
  * (with RoPE + a bf16 KV write in the QKV epilogue when head_dim is 128), so only
