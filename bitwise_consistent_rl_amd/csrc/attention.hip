@@ -297,11 +297,18 @@ __device__ __forceinline__ void load_chunk_sync(const AttnArgs& p, int blk, int 
 // (a chunk index past the last is clamped, its copy never used), the wait before
 // storing chunk c + 1 leaves chunk c + 2's loads in flight.
 // DS (decode tiles, at most 16 rows; implied by PF2): the four waves split the PV work.
-template <int D, bool FP8, bool SPLIT, bool PF2 = false, bool DS = PF2>
-__global__ __launch_bounds__(ATHREADS, SPLIT ? 4 : 2) void attention_kernel(AttnArgs p) {
+// ONESEG (PIPE, calls whose every position lies in the first segment): the running state
+// of finished segments (M, L, ACC) is never needed; the one merge, into the empty state, is
+// (0 + l, 0 + acc), which the epilogue computes directly.  With those 32 registers fewer the
+// schedule keeps one LDS buffer (the next chunk waits in registers until every wave has
+// finished reading the current one: two barriers per chunk) and three workgroups fit on a
+// CU instead of two.
+template <int D, bool FP8, bool SPLIT, bool PF2 = false, bool DS = PF2, bool ONESEG = false>
+__global__ __launch_bounds__(ATHREADS, SPLIT ? 4 : (ONESEG ? 3 : 2)) void attention_kernel(AttnArgs p) {
   constexpr bool PIPE = !SPLIT;
   static_assert(!(PF2 && SPLIT), "two chunks in flight: pipelined schedule only");
-  constexpr int NBUF = PIPE ? 2 : 1;
+  static_assert(!(ONESEG && SPLIT), "one segment: unsplit schedules only");
+  constexpr int NBUF = (PIPE && !ONESEG) ? 2 : 1;
   __shared__ __attribute__((aligned(16))) u32x4_t Ks[NBUF][CHUNK * D / 8];
   __shared__ __attribute__((aligned(16))) bf16_t Vt[NBUF][D * VT_STRIDE];
 
@@ -549,7 +556,7 @@ __global__ __launch_bounds__(ATHREADS, SPLIT ? 4 : 2) void attention_kernel(Attn
     }
     m = mn;
 
-    if constexpr (!SPLIT) {
+    if constexpr (!SPLIT && !ONESEG) {
       if (c == c_stop || ((c + 1) % seg_chunks) == 0) {
         // merge the finished segment into the running state (ascending segment order)
         const float Mn = fmaxf(M, m);
@@ -587,7 +594,7 @@ __global__ __launch_bounds__(ATHREADS, SPLIT ? 4 : 2) void attention_kernel(Attn
     }
   } else {
     for (int c = c_first; c <= c_stop; ++c) {
-      const int b = PIPE ? (c - c_first) & 1 : 0;
+      const int b = (PIPE && !ONESEG) ? (c - c_first) & 1 : 0;
       const bool more = c < c_stop;
       if constexpr (PIPE) {
         if (more) ld.issue(p, btab[c + 1], g, tid);
@@ -597,7 +604,11 @@ __global__ __launch_bounds__(ATHREADS, SPLIT ? 4 : 2) void attention_kernel(Attn
         __syncthreads();
       }
       if (wave_active) compute_chunk(c, b);
-      if constexpr (PIPE) {
+      if constexpr (PIPE && ONESEG) {
+        __syncthreads();  // every wave is done with the buffer
+        if (more) ld.store(kmax - (c + 1) * CHUNK, Ks[0], Vt[0], tid);
+        __syncthreads();  // publishes chunk c + 1
+      } else if constexpr (PIPE) {
         // buffer b^1 was released by the previous iteration's barrier
         if (more) ld.store(kmax - (c + 1) * CHUNK, Ks[b ^ 1], Vt[b ^ 1], tid);
         __syncthreads();  // publishes buffer b^1, releases buffer b
@@ -622,13 +633,26 @@ __global__ __launch_bounds__(ATHREADS, SPLIT ? 4 : 2) void attention_kernel(Attn
 
   if (row_ok) {
     bf16_t* orow = reinterpret_cast<bf16_t*>(p.o) + (size_t)(tok_begin + tk) * qstride + hq * D;
-    const float il = attn_inv_l(L);
+    if constexpr (ONESEG) {
+      // the merge of the only segment into (M, L, ACC) = (-inf, 0, +0): its scale factors
+      // are 2^-inf = 0 and 2^0 = 1 exactly, leaving L = 0 + l and ACC = +0 + acc
+      const float il = attn_inv_l(0.0f + l);
 #pragma unroll
-    for (int j = 0; j < DPW; ++j) {
-      u32x2_t w;
-      w[0] = pack_f2bf2(ACC[j][0] * il, ACC[j][1] * il);
-      w[1] = pack_f2bf2(ACC[j][2] * il, ACC[j][3] * il);
-      *reinterpret_cast<u32x2_t*>(orow + (dt0 + j) * 16 + 4 * lg) = w;
+      for (int j = 0; j < DPW; ++j) {
+        u32x2_t w;
+        w[0] = pack_f2bf2((0.0f + acc[j][0]) * il, (0.0f + acc[j][1]) * il);
+        w[1] = pack_f2bf2((0.0f + acc[j][2]) * il, (0.0f + acc[j][3]) * il);
+        *reinterpret_cast<u32x2_t*>(orow + (dt0 + j) * 16 + 4 * lg) = w;
+      }
+    } else {
+      const float il = attn_inv_l(L);
+#pragma unroll
+      for (int j = 0; j < DPW; ++j) {
+        u32x2_t w;
+        w[0] = pack_f2bf2(ACC[j][0] * il, ACC[j][1] * il);
+        w[1] = pack_f2bf2(ACC[j][2] * il, ACC[j][3] * il);
+        *reinterpret_cast<u32x2_t*>(orow + (dt0 + j) * 16 + 4 * lg) = w;
+      }
     }
   }
 }
@@ -671,6 +695,9 @@ static void launch_d(const AttnArgs& a, hipStream_t s) {
                        0, s, a);
   } else if (a.dsplit) {
     hipLaunchKernelGGL((attention_kernel<D, FP8, false, false, true>), dim3(a.n_tiles, a.nkv),
+                       dim3(ATHREADS), 0, s, a);
+  } else if (a.one_seg) {
+    hipLaunchKernelGGL((attention_kernel<D, FP8, false, false, false, true>), dim3(a.n_tiles, a.nkv),
                        dim3(ATHREADS), 0, s, a);
   } else {
     hipLaunchKernelGGL((attention_kernel<D, FP8, false>), dim3(a.n_tiles, a.nkv), dim3(ATHREADS),

@@ -568,6 +568,8 @@ static bci_status op_attn(bci_ctx* c, const void* q, void* o, int layer, hipStre
   for (int i = 0; i < c->n_seqs; ++i) max_q = std::max(max_q, c->h_cu[i + 1] - c->h_cu[i]);
   a.dsplit = max_q * (g.n_q_heads / g.n_kv_heads) <= 16;
   a.pf2 = a.dsplit && c->n_tiles * g.n_kv_heads < 256;
+  // a captured forward is replayed with other positions, so it keeps the general kernel
+  a.one_seg = !c->graph_mode && a.n_seg == 0 && c->batch_max_pos < a.seg_keys;
   HIP_TRY(c, launch_attention(a, s));
   return BCI_OK;
 }

@@ -129,6 +129,8 @@ struct AttnArgs {
   bool pf2;
   // tiles of at most 16 rows: the four waves split the PV work (implied by pf2)
   bool dsplit;
+  // every position of the call lies in the first segment (prefill schedule only)
+  bool one_seg;
 };
 constexpr int ATTN_ROWS = 64;  // query rows (token x head-in-group) per tile
 constexpr int ATTN_TILE_WORDS = 8;  // ints per attention tile record (32 bytes)

@@ -479,6 +479,26 @@ def test_attention_parity(nq, nkv, d, seg, kv):
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("nq,nkv,d", [(4, 2, 64), (16, 8, 128)])
+def test_attention_one_segment_schedule_bitwise(nq, nkv, d, kv):
+    """A call whose positions all lie in the first segment runs the one-segment schedule
+    (one LDS buffer, no segment state); the same rows in a call that also holds a sequence
+    past the first segment run the general schedule.  Both give the same bits (the
+    oracle comparison of the one-segment schedule is test_attention_parity's seg = 2048
+    cases, whose calls all lie in the first segment)."""
+    seg = 1024
+    lengths = [150, 67, 1, 300, 1100]
+    T = sum(lengths)
+    qkv = synth.normal_bf16((T, (nq + 2 * nkv) * d), index=43)
+    short = [(i, 0, L) for i, L in enumerate(lengths[:4])]
+    o_one, _, _ = _attention_run(nq, nkv, d, kv, seg, lengths, qkv, [short, [(4, 0, 1100)]], split=1)
+    o_gen, _, _ = _attention_run(nq, nkv, d, kv, seg, lengths, qkv, [short + [(4, 0, 1100)]], split=1)
+    n_short = sum(lengths[:4])
+    assert same_bits(o_one[:n_short], o_gen[:n_short])
+    assert same_bits(o_one[n_short:], o_gen[n_short:])
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
 @pytest.mark.parametrize("nq,nkv,d,seg", [(4, 2, 64, 128), (16, 8, 128, 2048), (32, 4, 128, 128)])
 def test_attention_prefill_decode_chunked_bitwise(nq, nkv, d, seg, kv):
     """The same rows through whole prefill, token-by-token decode, chunked prefill and
