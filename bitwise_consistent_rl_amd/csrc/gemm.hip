@@ -654,10 +654,15 @@ __device__ __forceinline__ void wait_vmcnt() {
 // normalised by the wave itself from the residual rows p.res and the weight p.gamma,
 // with the add+RMSNorm kernel's expressions and reduction tree (see norm_rows below),
 // into an LDS region of their own; the weight stream starts before that work.
+// CW: output columns per wave, 16, or 8 for calls that would otherwise launch fewer waves
+// than CUs: the wave streams 8 weight rows, its MFMA lanes 8-15 read rows 0-7 again and
+// their outputs are not stored, so twice as many CUs stream the weights.
 template <int KIND, int MT, bool GATHER = false, bool GROUPED = false, int AR = 16 * MT, int KC = SK_KC,
-          bool NORM = false>
+          bool NORM = false, int CW = 16>
 __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmArgs p) {
   static_assert(AR == 16 * MT || (MT == 1 && AR == 4), "A rows per stage");
+  static_assert(CW == 16 || (CW == 8 && KIND != K_SILU && KIND != K_ROPE && !GROUPED),
+                "8 columns per wave: single weight stream, dense calls");
   static_assert(!NORM || (MT == 1 && AR == 4 && !GATHER && !GROUPED), "norm-fused A: M <= 4, plain rows");
   constexpr int ROWCH = KC / 8;                         // 16-byte chunks per row per stage
   // the copy swizzle (chunk ^ (row & 15)) must stay inside a row's stage: at fewer than
@@ -665,7 +670,7 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmArgs p) {
   static_assert(ROWCH % 16 == 0, "a stage row holds a multiple of 16 chunks");
   // weight streams: (gate, up) rows for SiLU; for RoPE the rows e and e + 64 of a head
   constexpr int NB = (KIND == K_SILU || KIND == K_ROPE) ? 2 : 1;
-  constexpr int WCH = NB * 16 * ROWCH;                  // W chunks per stage
+  constexpr int WCH = NB * CW * ROWCH;                  // W chunks per stage
   constexpr int SCH = WCH + (NORM ? 0 : AR * ROWCH);    // chunks per stage
   constexpr int LPS = SCH / 64;                         // wave loads per stage
   static_assert(SCH % 64 == 0, "whole wave loads per stage");
@@ -684,7 +689,7 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmArgs p) {
   const int K = p.K;
   const int ncols = (KIND == K_SILU || KIND == K_ROPE) ? p.N / 2 : p.N;
   const int cb = blockIdx.x;
-  const int col = cb * 16 + (lane & 15);
+  const int col = cb * CW + (lane & 15);
   // K_ROPE (head_dim 128): wave cb holds rotation pairs e = 16 (cb % 4) + 0..15 of head
   // cb / 4, i.e. QKV columns 128 h + e (stream 0) and 128 h + 64 + e (stream 1)
   const int rh = cb >> 2, re0 = (cb & 3) * 16;
@@ -704,7 +709,7 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmArgs p) {
   // WCH is a multiple of 64, so a load reads W or A for all its lanes.  Descriptors
   // start at the wave's first W row and its first A row (the source base when rows
   // are gathered).
-  const int w_row0 = (KIND == K_ROPE) ? rh * 128 : cb * 16;
+  const int w_row0 = (KIND == K_ROPE) ? rh * 128 : cb * CW;
   const i32x4_t rsW = buffer_rsrc(W + (size_t)w_row0 * K);
   const i32x4_t rsA = buffer_rsrc(GATHER ? p.A : p.A + (size_t)row_base * K);
   int voff[LPS];
@@ -717,7 +722,7 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmArgs p) {
       if constexpr (KIND == K_ROPE) {
         wr = re0 + (r & 15) + (r >= 16 ? 64 : 0);
       } else {
-        wr = min(cb * 16 + (r & 15), ncols - 1) - w_row0;
+        wr = min(cb * CW + (r & (CW - 1)), ncols - 1) - w_row0;
         if (NB == 2 && r >= 16) wr += ncols;             // up rows follow the gate rows
       }
       voff[j] = (int)(((size_t)wr * K + ch * 8) * 2);
@@ -843,7 +848,7 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmArgs p) {
       const int ch = s * 4 + (lane >> 4);
       bf16x8_t bw[NB];
 #pragma unroll
-      for (int b = 0; b < NB; ++b) bw[b] = __builtin_bit_cast(bf16x8_t, stg[swz(b * 16 + (lane & 15), ch)]);
+      for (int b = 0; b < NB; ++b) bw[b] = __builtin_bit_cast(bf16x8_t, stg[swz(b * CW + (lane & (CW - 1)), ch)]);
 #pragma unroll
       for (int mi = 0; mi < MT; ++mi) {
         bf16x8_t a;
@@ -864,7 +869,7 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmArgs p) {
       issue(c % D, (c + D) * KC);
     }
   }
-  if (cb * 16 >= ncols) return;
+  if (cb * CW >= ncols || (lane & 15) >= CW) return;
   // lane holds C[16 mi + 4 (lane >> 4) + r][col]
 #pragma unroll
   for (int mi = 0; mi < MT; ++mi)
@@ -928,6 +933,7 @@ constexpr int SK_ROW_BLOCKS = 2;
 // twice the re-read: 64 rows per wave there (B = 64 decode step 2.557 -> 2.470 ms
 // against 32, the same as 128).
 constexpr int SK_SILU_ROW_BLOCKS = 4;
+constexpr int SKINNY_CUS = 256;  // compute units of the part
 
 template <int KIND>
 static hipError_t dispatch_skinny(const GemmArgs& a, hipStream_t s) {
@@ -936,7 +942,17 @@ static hipError_t dispatch_skinny(const GemmArgs& a, hipStream_t s) {
   const int mt = std::min((a.M + 15) / 16, KIND == K_SILU ? SK_SILU_ROW_BLOCKS : SK_ROW_BLOCKS);
   const bool wide = a.K % 512 == 0;
   const dim3 g1(grid), gm(grid, (a.M + 16 * mt - 1) / (16 * mt));
-  if (a.M <= 4 && wide) hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 1, false, false, 4, 512>), g1, dim3(64), 0, s, a);
+  // at most 4 rows, a single weight stream and fewer 16-column waves than CUs: 8 columns
+  // per wave, so that every CU streams weights (same box, M = 1: O 5.4 -> 5.2 us, down 9.7 ->
+  // 9.0, the B = 1 decode step 1.693 -> 1.652 ms).  With 16 or 32 A rows per wave the doubled
+  // A stream cancels the gain (down at 24-32 rows 14.4 -> 14.7-14.9 us), so those keep 16.
+  constexpr bool one_stream = KIND != K_SILU && KIND != K_ROPE;
+  constexpr int CW8 = one_stream ? 8 : 16;
+  const bool narrow = one_stream && grid < SKINNY_CUS && ncols % 8 == 0;
+  const dim3 g1n(2 * grid);
+  if (a.M <= 4 && wide && narrow)
+    hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 1, false, false, 4, 512, false, CW8>), g1n, dim3(64), 0, s, a);
+  else if (a.M <= 4 && wide) hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 1, false, false, 4, 512>), g1, dim3(64), 0, s, a);
   else if (a.M <= 4) hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 1, false, false, 4>), g1, dim3(64), 0, s, a);
   else if (mt == 1 && wide) hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 1, false, false, 16, 512>), gm, dim3(64), 0, s, a);
   else if (mt == 1) hipLaunchKernelGGL((gemm_skinny_kernel<KIND, 1>), gm, dim3(64), 0, s, a);

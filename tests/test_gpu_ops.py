@@ -54,7 +54,7 @@ def gemm(ctx, a, w, epi, out_cols=None, dtype=BF):
 
 @pytest.mark.parametrize("M,N,K", [(1, 128, 64), (37, 256, 128), (24, 256, 2048), (64, 512, 6144),
                                    (300, 512, 256), (513, 384, 2048), (256, 128, 6144),
-                                   (1000, 4096, 2048)])
+                                   (1000, 4096, 2048), (3, 1024, 2048), (4, 2032, 1024)])
 def test_gemm_bf16_parity(ctx, M, N, K):
     a, w = synth.gemm_inputs(M, N, K, index=M + N + K)
     C = gemm(ctx, cuda(a), cuda(w), abi().BCI_EPI_BF16)
