@@ -654,15 +654,15 @@ __device__ __forceinline__ void wait_vmcnt() {
 // normalised by the wave itself from the residual rows p.res and the weight p.gamma,
 // with the add+RMSNorm kernel's expressions and reduction tree (see norm_rows below),
 // into an LDS region of their own; the weight stream starts before that work.
-// CW: output columns per wave, 16, or 8 for calls that would otherwise launch fewer waves
-// than CUs: the wave streams 8 weight rows, its MFMA lanes 8-15 read rows 0-7 again and
-// their outputs are not stored, so twice as many CUs stream the weights.
+// CW: output columns (RoPE: rotation pairs) per wave, 16, or 8 for calls that would
+// otherwise launch fewer waves than CUs: the wave streams 8 weight rows per stream, its
+// MFMA lanes 8-15 read rows 0-7 again and their outputs are not stored, so twice as many
+// CUs stream the weights.
 template <int KIND, int MT, bool GATHER = false, bool GROUPED = false, int AR = 16 * MT, int KC = SK_KC,
           bool NORM = false, int CW = 16>
 __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmArgs p) {
   static_assert(AR == 16 * MT || (MT == 1 && AR == 4), "A rows per stage");
-  static_assert(CW == 16 || (CW == 8 && KIND != K_SILU && KIND != K_ROPE && !GROUPED),
-                "8 columns per wave: single weight stream, dense calls");
+  static_assert(CW == 16 || (CW == 8 && KIND != K_SILU && !GROUPED), "8 columns per wave: dense calls");
   static_assert(!NORM || (MT == 1 && AR == 4 && !GATHER && !GROUPED), "norm-fused A: M <= 4, plain rows");
   constexpr int ROWCH = KC / 8;                         // 16-byte chunks per row per stage
   // the copy swizzle (chunk ^ (row & 15)) must stay inside a row's stage: at fewer than
@@ -690,9 +690,9 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmArgs p) {
   const int ncols = (KIND == K_SILU || KIND == K_ROPE) ? p.N / 2 : p.N;
   const int cb = blockIdx.x;
   const int col = cb * CW + (lane & 15);
-  // K_ROPE (head_dim 128): wave cb holds rotation pairs e = 16 (cb % 4) + 0..15 of head
-  // cb / 4, i.e. QKV columns 128 h + e (stream 0) and 128 h + 64 + e (stream 1)
-  const int rh = cb >> 2, re0 = (cb & 3) * 16;
+  // K_ROPE (head_dim 128): wave cb holds rotation pairs e = CW (cb % (64 / CW)) + 0..CW-1 of
+  // head cb / (64 / CW), i.e. QKV columns 128 h + e (stream 0) and 128 h + 64 + e (stream 1)
+  const int rh = cb / (64 / CW), re0 = (cb % (64 / CW)) * CW;
   int row_base = 0, M = p.M;
   const bf16_t* W = p.W;
   if constexpr (GROUPED) {
@@ -720,7 +720,7 @@ __global__ __launch_bounds__(64) void gemm_skinny_kernel(GemmArgs p) {
       const int r = P / ROWCH, ch = (P % ROWCH) ^ (r & 15);
       int wr;
       if constexpr (KIND == K_ROPE) {
-        wr = re0 + (r & 15) + (r >= 16 ? 64 : 0);
+        wr = re0 + (r & (CW - 1)) + (r >= CW ? 64 : 0);
       } else {
         wr = min(cb * CW + (r & (CW - 1)), ncols - 1) - w_row0;
         if (NB == 2 && r >= 16) wr += ncols;             // up rows follow the gate rows
@@ -1270,7 +1270,11 @@ hipError_t launch_gemm_qkv_rope_norm(const void* res, const void* gamma, float e
   a.res = (const bf16_t*)res;
   a.gamma = (const bf16_t*)gamma;
   a.eps = eps;
-  hipLaunchKernelGGL((gemm_skinny_kernel<K_ROPE, 1, false, false, 4, 512, true>), dim3(N / 32), dim3(64), 0, s, a);
+  // 8 rotation pairs per wave: N / 16 waves (one per CU for the Qwen3 shape) instead of N / 32
+  // (same box: B = 1 decode step 1.655 -> 1.628 ms; the SiLU form, already at 384 waves, got
+  // slower with 768, each wave normalising its A rows itself)
+  hipLaunchKernelGGL((gemm_skinny_kernel<K_ROPE, 1, false, false, 4, 512, true, 8>), dim3(N / 16), dim3(64), 0, s,
+                     a);
   return hipGetLastError();
 }
 
