@@ -1271,8 +1271,9 @@ hipError_t launch_gemm_qkv_rope_norm(const void* res, const void* gamma, float e
   a.gamma = (const bf16_t*)gamma;
   a.eps = eps;
   // 8 rotation pairs per wave: N / 16 waves (one per CU for the Qwen3 shape) instead of N / 32
-  // (same box: B = 1 decode step 1.655 -> 1.628 ms; the SiLU form, already at 384 waves, got
-  // slower with 768, each wave normalising its A rows itself)
+  // (same box: B = 1 decode step 1.655 -> 1.628 ms).  The SiLU form, already at 384 waves, keeps
+  // 16 columns: with 768 its ring and normalised rows (80 KiB) fit two waves per CU and the
+  // step got slower; with a 2-stage ring (48 KiB, three per CU) it measured even.
   hipLaunchKernelGGL((gemm_skinny_kernel<K_ROPE, 1, false, false, 4, 512, true, 8>), dim3(N / 16), dim3(64), 0, s,
                      a);
   return hipGetLastError();
