@@ -225,6 +225,63 @@ def micro(args, cfg):
                       "copy_bytes": 2 * (1 << 30)}), flush=True)
 
 
+def micro_attention(args, cfg):
+    """The attention op alone on one packed recompute call: sequences of the seeded workload
+    from position 0 up to --max-tokens tokens, the model's heads, bf16 KV cache written by
+    the RoPE + KV-write op from N(0,1) q/k/v rows, 1024-key segments (every position in the
+    first: the one-segment schedule).  Prints us per launch (HIP events, --steps launches)."""
+    import numpy as np
+    import torch
+    import synth
+    from bitwise_consistent_rl_amd import _abi as abi
+    nq, nkv, d = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    mc = abi.ModelConfig()
+    for k, v in dict(n_layers=1, hidden=cfg.hidden, n_q_heads=nq, n_kv_heads=nkv, head_dim=d,
+                     intermediate=cfg.intermediate, vocab=128, rms_eps=1e-6, rope_theta=1e6,
+                     kv_dtype=abi.BCI_KV_BF16, kv_block_tokens=64, attn_segment_keys=QWEN_SEG_KEYS,
+                     max_tokens_per_call=args.max_tokens, max_seqs_per_call=64, max_scored_per_call=1,
+                     max_position=1024, mode=abi.BCI_MODE_INVARIANT, attn_split_mode=0).items():
+        setattr(mc, k, v)
+    ctx = abi.bci_create(mc, 0)
+    seqs = synth.rl_sequences(cfg, n_prompts=8, n_responses=8)
+    lengths, tot = [], 0
+    for sq in seqs:
+        if tot + sq.length > args.max_tokens:
+            break
+        lengths.append(sq.length)
+        tot += sq.length
+    nb = sum((L + 63) // 64 for L in lengths)
+    kc = torch.zeros((1, nb, nkv, 64, d), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    abi.bci_bind_kv_cache(ctx, kc, vc, None, None, nb)
+    blocks, nxt = [], 0
+    for L in lengths:
+        blocks.append(list(range(nxt, nxt + (L + 63) // 64)))
+        nxt += (L + 63) // 64
+    maxb = max(len(b) for b in blocks)
+    bt = np.array([b + [0] * (maxb - len(b)) for b in blocks], np.int32)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(cu[-1])
+    abi.bci_set_batch(ctx, np.zeros(T, np.int32), cu, np.zeros(len(lengths), np.int32), bt, [], [])
+    qkv = synth.normal_bf16((T, (nq + 2 * nkv) * d), index=44).cuda()
+    q = torch.empty(T, nq * d, dtype=torch.bfloat16, device="cuda")
+    o = torch.empty_like(q)
+    abi.bci_op_rope_kv_write(ctx, qkv, q, 0)
+    for _ in range(3):
+        abi.bci_op_attention(ctx, q, 0, o)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        abi.bci_op_attention(ctx, q, 0, o)
+    end.record()
+    torch.cuda.synchronize()
+    us = start.elapsed_time(end) * 1e3 / args.steps
+    abi.bci_destroy(ctx)
+    print(json.dumps({"micro": "attention", "tokens": T, "sequences": len(lengths), "avg_us": round(us, 2)}),
+          flush=True)
+
+
 def decode_bench(args, cfg):
     """Decode steps alone, for a kernel trace: sequences of the Qwen3-shaped workload are
     prefilled to their response midpoint, then `--steps` decode steps (one new token and
@@ -920,7 +977,7 @@ def main():
     ap.add_argument("--mode", choices=["invariant", "fast"], default="invariant",
                     help="the recompute's timed pass in the invariant (default) or the "
                          "non-invariant mode (for profiling the latter alone)")
-    ap.add_argument("--micro", choices=["gate_up", "gate_up_hipblaslt"], default=None,
+    ap.add_argument("--micro", choices=["gate_up", "gate_up_hipblaslt", "attention"], default=None,
                     help="time one kernel alone at the workload's shape (for counter runs)")
     ap.add_argument("--micro-data", choices=["random", "zeros"], default="random")
     ap.add_argument("--workload", choices=["recompute", "longctx", "rollout", "decode", "lmhead", "moe",
@@ -945,6 +1002,8 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     cfg = synth.QWEN3_1P7B
+    if args.micro == "attention":
+        return micro_attention(args, cfg)
     if args.micro:
         return micro(args, cfg)
     if args.workload == "longctx":
