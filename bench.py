@@ -1074,7 +1074,8 @@ def main():
     achieved = gu_flops / (gu_ms * 1e-3) / 1e12 if gu_ms > 0 else 0.0
     ms_per_step = dt * 1e3 / args.steps
 
-    # whole-step algorithmic work: linear + attention + lm_head flops
+    # whole-step algorithmic work: the projections' flops per processed token, causal
+    # attention's 4 d n_q flops per (query, key <= query) pair, the lm_head per scored row
     lin = 2.0 * cfg.n_layers * cfg.hidden * (cfg.qkv_rows + cfg.hidden + 2 * cfg.intermediate
                                              + cfg.intermediate)
     attn = sum(2.0 * 2 * cfg.n_layers * cfg.n_q_heads * cfg.head_dim * (t + 1)
