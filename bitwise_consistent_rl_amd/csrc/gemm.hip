@@ -145,14 +145,15 @@ __global__ __launch_bounds__((TBM >= 64 ? TBM / 64 : 1) * NWN * 64, 1) void gemm
   __shared__ u32x4_t smem[2 * KSTAGE];  // two buffers (2 x 64 KiB at TBM = 256)
 
   // ---- tile id: XCD-contiguous ranges, then groups of GM M-tiles whose tiles run
-  // column by column (GM tiles sharing a W tile in L2).  GM = 4 for the gate_up and
-  // QKV GEMMs, 8 for the others: measured in the recompute (a 4 % faster gate_up; the
-  // O / down projections and the lm_head were slower with 4)
+  // column by column (GM tiles sharing a W tile in L2).  GM = 6 for the gate_up GEMM, 4 for
+  // QKV, 8 for the others, measured in the recompute: gate_up 4 % faster with 4 than 8, then
+  // 598 -> 592 us with 6 (2 and 3 slower; QKV and the others even with 6); the O / down
+  // projections and the lm_head were slower with 4
   const int n_tiles = p.tiles_m * p.tiles_n;
   const int per_xcd = gridDim.x >> 3;  // grid is a multiple of 8
   const int tile = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (tile >= n_tiles) return;
-  constexpr int GM = (KIND == K_SILU || KIND == K_ROPE) ? 4 : 8;
+  constexpr int GM = (KIND == K_SILU) ? 6 : (KIND == K_ROPE) ? 4 : 8;
   const int width = GM * p.tiles_n;
   const int first_m = (tile / width) * GM;
   const int gsz = min(p.tiles_m - first_m, GM);
