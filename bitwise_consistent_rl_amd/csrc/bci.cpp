@@ -9,6 +9,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -619,6 +620,15 @@ bci_status bci_op_gemm_bf16(bci_ctx* c, const void* A, const void* W, void* C, i
   } else {
     return fail(c, BCI_E_INVALID, "op_gemm: unknown epilogue %d", epi);
   }
+  // the operand copies are 16-byte loads at row offsets of K * 2 bytes
+  if (!aligned16(A) || !aligned16(W)) return fail(c, BCI_E_INVALID, "op_gemm: A and W must be 16-byte aligned");
+  // buffer descriptors cover 2 GiB from a tile's first row: the SiLU form reads its up
+  // rows N / 2 rows past its gate rows, and the skinny schedule reads all M rows of A
+  const size_t row_bytes = (size_t)K * 2;
+  if ((epi == BCI_EPI_SILU_MUL && (size_t)(N / 2 + 256) * row_bytes > (size_t)INT32_MAX) ||
+      (size_t)(M < 512 ? M : 512) * row_bytes > (size_t)INT32_MAX || 256 * row_bytes > (size_t)INT32_MAX)
+    return fail(c, BCI_E_INVALID, "op_gemm: operand rows beyond the 2 GiB a copy descriptor covers (N %d, K %d)",
+                N, K);
   return gemm_checked(c, A, nullptr, W, C, M, N, K, epi, S(stream));
 }
 
@@ -892,6 +902,8 @@ bci_status bci_op_lmhead_logprob(bci_ctx* c, const void* hf, const void* E, cons
   if (!c) return BCI_E_INVALID;
   if (!hf || !E || !ids || !lp || M < 0 || V < 1 || H < 64 || H % GEMM_BK)
     return fail(c, BCI_E_INVALID, "op_lmhead_logprob: bad pointer or shape");
+  if (!aligned16(hf) || !aligned16(E))
+    return fail(c, BCI_E_INVALID, "op_lmhead_logprob: hf and E must be 16-byte aligned");
   if (M > c->cfg.max_scored_per_call)
     return fail(c, BCI_E_WORKSPACE, "op_lmhead_logprob: M %d > max_scored_per_call %d", M,
                 c->cfg.max_scored_per_call);

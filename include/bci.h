@@ -238,7 +238,9 @@ bci_status bci_op_add_rmsnorm(bci_ctx* ctx, const void* a, void* r, void* h, con
  *   BCI_EPI_F32:      C [M, N] fp32 = acc
  *   BCI_EPI_SILU_MUL: W holds gate rows then up rows (N = 2 I); C [M, I] bf16 =
  *                     bf(silu(bf(acc_gate)) * bf(acc_up))   (fused SiLU MLP)
- * K % 64 == 0; N >= 1 (BCI_EPI_SILU_MUL: I % 128 == 0); M >= 0. */
+ * K % 64 == 0; N >= 1 (BCI_EPI_SILU_MUL: I % 128 == 0); M >= 0; A and W 16-byte aligned;
+ * (I + 256) * K * 2 and min(M, 512) * K * 2 below 2^31 (the copies' descriptor range);
+ * otherwise BCI_E_INVALID and nothing is launched. */
 bci_status bci_op_gemm_bf16(bci_ctx* ctx, const void* A, const void* W, void* C, int32_t M,
                             int32_t N, int32_t K, int32_t epilogue, void* stream);
 
@@ -357,8 +359,8 @@ bci_status bci_op_gather_scored(bci_ctx* ctx, const void* src, int32_t cols, voi
  * "零差异需要一个精确的比较对象": the compared quantity):
  *   z = hf . E^T in fp32 (never stored), lp[i] = z[i, ids[i]] - logsumexp(z[i, :]).
  * hf [M, H] bf16, E [V, H] bf16, ids [M] int32 (device; an id outside [0, V)
- * yields NaN), lp [M] fp32.  H % 64 == 0; M <= max_scored_per_call (the
- * partials live in the workspace). */
+ * yields NaN), lp [M] fp32.  H % 64 == 0; hf and E 16-byte aligned; M <=
+ * max_scored_per_call (the partials live in the workspace). */
 bci_status bci_op_lmhead_logprob(bci_ctx* ctx, const void* hf, const void* E, const int32_t* ids,
                                  int32_t M, int32_t H, int32_t V, float* lp, void* stream);
 

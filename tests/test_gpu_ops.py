@@ -197,6 +197,11 @@ def test_gemm_rejects_bad_shapes(ctx):
         a_.bci_op_gemm_bf16(ctx, x, x, x, 4, 384, 64, a_.BCI_EPI_SILU_MUL)   # I % 128
     with pytest.raises(a_.BciError):
         a_.bci_op_gemm_bf16(ctx, x, x, x, 4, 128, 64, 7)   # unknown epilogue
+    y = torch.empty(4 * 64 + 8, dtype=BF, device="cuda")
+    with pytest.raises(a_.BciError):   # A 2 bytes past a 16-byte boundary
+        a_.bci_op_gemm_bf16(ctx, y[1:], x, x, 4, 4, 64, a_.BCI_EPI_BF16)
+    with pytest.raises(a_.BciError):   # W likewise
+        a_.bci_op_gemm_bf16(ctx, x, y[1:], x, 4, 4, 64, a_.BCI_EPI_BF16)
 
 
 def test_gemm_ragged_n_parity_and_invariance(ctx):
